@@ -1,0 +1,147 @@
+"""Seeded synthetic inputs for the five QK-Norm workloads.
+
+This module is the only code shared by the GPU path's callers and the CPU oracle's callers. It
+draws random tensors and rounds them to the storage precision; it holds none of the method's
+arithmetic (no sums of squares, no scaling, no folding, no products).
+
+The workloads stand in for activations and weights of the models the pages measure on (OLMo
+models in "SwiftQK: Fast and Communication-Efficient Tensor Parallelism for Query-Key
+Normalization", abstract; SmolLM2-135M / Llama-7B scale in "FlashNorm: Fast Normalization for
+Transformers", abstract), which are not available here. Shapes and distributions:
+
+  1  tiny fp32:     Q, K [T, 512] fp32, x ~ N(0, 1), gamma ~ N(1, 0.1), eps 1e-6, T = 64
+  2  OLMo-2-7B:     Q, K [T, 4096] bf16 (32 heads x 128), x ~ N(0, 2), gamma ~ N(1, 0.05)
+  3  GQA, 32B-like: Q [T, 5120] (40 x 128), K [T, 1024] (8 x 128) bf16, x ~ N(0, 1),
+                    1% of the columns of each tensor multiplied by 20 (channel outliers),
+                    independent gammas ~ N(1, 0.05)
+  4  TP shard:      Q, K [T, 512] bf16 (one 4096/8 column slice), x ~ N(0, 1), the shard's own
+                    gamma slices ~ N(1, 0.05), and 7 peers' partial sums of squares per row and
+                    tensor, each a chi-square draw with 512 degrees of freedom (the sum of 512
+                    squared N(0, 1)), fp32, laid out [7, T] peer-major
+  5  FlashNorm:     x [T, 2048] ~ N(0, 1), W [2048, 2048] ~ N(0, 0.02), gamma [2048] ~ N(1, 0.05),
+                    all bf16
+
+N(mu, s) names the standard deviation s. Every (config, T, seed) gets its own PCG64 stream
+(``numpy.random.default_rng(seed)``); draws happen in a fixed order (weights first, then
+activations, then outlier columns or peer partials), so weights are identical across T within
+a config. Draws are float32 and are rounded to bf16 with round-to-nearest-even.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+EPS_DEFAULT = 1e-6
+
+# config id -> shapes and token counts the workload is defined for
+CONFIGS = {
+    1: dict(name="tiny-fp32", dq=512, dk=512, dtype="f32", Ts=(64,)),
+    2: dict(name="olmo2-7b", dq=4096, dk=4096, dtype="bf16", Ts=(1, 16, 256, 4096, 8192)),
+    3: dict(name="gqa-olmo2-32b-like", dq=5120, dk=1024, dtype="bf16", Ts=(1, 512, 8192)),
+    4: dict(name="tp8-shard", dq=512, dk=512, dq_full=4096, dk_full=4096, n_ext=7,
+            dtype="bf16", Ts=(131072,)),
+    5: dict(name="flashnorm-2048", K=2048, N=2048, dtype="bf16", Ts=(1, 2048, 16384)),
+}
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (nearest, ties to even); return the raw uint16 bits.
+
+    NaN stays NaN (quiet bit forced), infinities stay infinite, overflow rounds to infinity.
+    """
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    rounded = ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)).astype(np.uint16)
+    nan = np.isnan(a)
+    if nan.any():
+        rounded[nan] = ((u[nan] >> np.uint64(16)).astype(np.uint16) | np.uint16(0x0040))
+    return rounded.reshape(a.shape)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen raw bf16 bits to float32 (exact)."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).reshape(b.shape)
+
+
+def _normal(rng: np.random.Generator, mu: float, sd: float, shape) -> np.ndarray:
+    return rng.normal(mu, sd, size=shape).astype(np.float32)
+
+
+def _store(a: np.ndarray, dtype: str) -> np.ndarray:
+    return f32_to_bf16_bits(a) if dtype == "bf16" else np.ascontiguousarray(a, np.float32)
+
+
+def make_case(cfg: int, T: int, seed: int = 0) -> dict:
+    """Return the tensors of workload ``cfg`` at ``T`` tokens as host numpy arrays.
+
+    bf16 tensors are uint16 arrays of raw bits; fp32 tensors are float32 arrays. Keys:
+      configs 1-3: q, k [T, d], gamma_q, gamma_k, eps, dtype, gamma_dtype
+      config 4:    the same plus ext_q, ext_k [7, T] fp32, dq_full, dk_full
+      config 5:    x [T, K], w [K, N], gamma [K], eps
+    """
+    if cfg not in CONFIGS:
+        raise ValueError(f"unknown config {cfg}")
+    if T < 0:
+        raise ValueError("T must be >= 0")
+    c = CONFIGS[cfg]
+    rng = np.random.default_rng(seed)
+    out = dict(cfg=cfg, T=T, seed=seed, eps=EPS_DEFAULT, dtype=c["dtype"], name=c["name"])
+    if cfg == 1:
+        gq = _normal(rng, 1.0, 0.1, (c["dq"],))
+        gk = _normal(rng, 1.0, 0.1, (c["dk"],))
+        xq = _normal(rng, 0.0, 1.0, (T, c["dq"]))
+        xk = _normal(rng, 0.0, 1.0, (T, c["dk"]))
+        out.update(q=xq, k=xk, gamma_q=gq, gamma_k=gk, gamma_dtype="f32")
+    elif cfg == 2:
+        gq = _normal(rng, 1.0, 0.05, (c["dq"],))
+        gk = _normal(rng, 1.0, 0.05, (c["dk"],))
+        xq = _normal(rng, 0.0, 2.0, (T, c["dq"]))
+        xk = _normal(rng, 0.0, 2.0, (T, c["dk"]))
+        out.update(q=_store(xq, "bf16"), k=_store(xk, "bf16"), gamma_q=_store(gq, "bf16"),
+                   gamma_k=_store(gk, "bf16"), gamma_dtype="bf16")
+    elif cfg == 3:
+        gq = _normal(rng, 1.0, 0.05, (c["dq"],))
+        gk = _normal(rng, 1.0, 0.05, (c["dk"],))
+        xq = _normal(rng, 0.0, 1.0, (T, c["dq"]))
+        xk = _normal(rng, 0.0, 1.0, (T, c["dk"]))
+        cols_q = rng.choice(c["dq"], size=c["dq"] // 100, replace=False)
+        cols_k = rng.choice(c["dk"], size=c["dk"] // 100, replace=False)
+        xq[:, cols_q] *= np.float32(20.0)
+        xk[:, cols_k] *= np.float32(20.0)
+        out.update(q=_store(xq, "bf16"), k=_store(xk, "bf16"), gamma_q=_store(gq, "bf16"),
+                   gamma_k=_store(gk, "bf16"), gamma_dtype="bf16",
+                   outlier_cols_q=np.sort(cols_q), outlier_cols_k=np.sort(cols_k))
+    elif cfg == 4:
+        gq = _normal(rng, 1.0, 0.05, (c["dq"],))
+        gk = _normal(rng, 1.0, 0.05, (c["dk"],))
+        xq = _normal(rng, 0.0, 1.0, (T, c["dq"]))
+        xk = _normal(rng, 0.0, 1.0, (T, c["dk"]))
+        ext_q = rng.chisquare(512, size=(c["n_ext"], T)).astype(np.float32)
+        ext_k = rng.chisquare(512, size=(c["n_ext"], T)).astype(np.float32)
+        out.update(q=_store(xq, "bf16"), k=_store(xk, "bf16"), gamma_q=_store(gq, "bf16"),
+                   gamma_k=_store(gk, "bf16"), gamma_dtype="bf16", ext_q=ext_q, ext_k=ext_k,
+                   dq_full=c["dq_full"], dk_full=c["dk_full"], n_ext=c["n_ext"])
+    else:
+        K, N = c["K"], c["N"]
+        w = _normal(rng, 0.0, 0.02, (K, N))
+        g = _normal(rng, 1.0, 0.05, (K,))
+        x = _normal(rng, 0.0, 1.0, (T, K))
+        out.update(x=_store(x, "bf16"), w=_store(w, "bf16"), gamma=_store(g, "bf16"),
+                   gamma_dtype="bf16", K=K, N=N)
+    return out
+
+
+def random_rows(rng: np.random.Generator, T: int, d: int, dtype: str, scale: float = 1.0,
+                ld: int | None = None) -> np.ndarray:
+    """Seeded N(0, scale) rows for edge-case tests; with ``ld`` > d the array is [T, ld] and the
+    padding columns hold a recognisable sentinel draw (N(0, 1000))."""
+    ld = d if ld is None else ld
+    a = rng.normal(0.0, 1000.0, size=(T, ld)).astype(np.float32)
+    a[:, :d] = rng.normal(0.0, scale, size=(T, d)).astype(np.float32)
+    return _store(a, dtype)
+
+
+def random_gamma(rng: np.random.Generator, d: int, dtype: str, sd: float = 0.05) -> np.ndarray:
+    return _store(_normal(rng, 1.0, sd, (d,)), dtype)
