@@ -1,0 +1,312 @@
+"""Benchmark of the layerwise QK-Norm hot path on one MI355X.
+
+A step is one fused Q + K launch (sum of squares, 1/rms, gamma scale of both tensors) over one
+batch of the OLMo-2-7B-shaped workload: Q and K [8192, 4096] bf16, seeded synthetic inputs
+already resident in HBM. Working buffers rotate over >= 1 GiB so that every launch streams
+from HBM rather than from the 256 MB Infinity Cache.
+
+Prints ONE JSON line: tokens/s, ms per step, the roofline of the fused kernel (algorithmic
+bytes / average launch duration, from HIP events on the launch stream, against 8 TB/s), the
+fp64 CPU oracle's rate on a bounded sample of the same workload, and per-workload timings of
+the other entry points ("cases").
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 matrix peak, published
+METRIC = "fused Q+K QK-Norm tokens/s + achieved HBM GB/s (% of peak), OLMo-7B shape, 1 GPU"
+ROTATE_BYTES = 1 << 30
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "qknorm_fused_olmo2_7b_T8192_pmc.md")
+KERNEL_SOURCES = ["layerwise_qk_norm_amd/csrc/rows.hip", "layerwise_qk_norm_amd/csrc/device.h"]
+
+
+def rows_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per launch from the committed counter summary, or None when it is absent or
+    was taken on different kernel sources."""
+    try:
+        text = open(PMC_SUMMARY).read()
+    except OSError:
+        return None
+    m_hash = re.search(r"kernel source hash:\s*`?([0-9a-f]{16})", text)
+    m_bytes = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != rows_source_hash():
+        return None
+    return int(m_bytes.group(1))
+
+
+def fused_bytes(T, dq, dk, es=2, gs=2):
+    """Algorithmic bytes of one fused launch: each row read once and written once, gamma once."""
+    return T * (dq + dk) * 2 * es + (dq + dk) * gs
+
+
+class Timer:
+    """HIP events recorded on the stream the kernels are launched on."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+
+    def run(self, fn, iters, warmup):
+        torch = self.torch
+        with torch.cuda.stream(self.stream):
+            for i in range(warmup):
+                fn(i)
+            torch.cuda.synchronize()
+            start = torch.cuda.Event(enable_timing=True)
+            end = torch.cuda.Event(enable_timing=True)
+            start.record(self.stream)
+            for i in range(iters):
+                fn(i)
+            end.record(self.stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / iters  # ms per call
+
+
+def rotation_count(bytes_per_set):
+    return max(1, -(-ROTATE_BYTES // bytes_per_set))
+
+
+def dev(torch, a):
+    import numpy as np
+
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+# ----------------------------------------------------------------------------- workloads
+def fused_setup(torch, Q, inputs, cfg, T):
+    c = inputs.make_case(cfg, T)
+    q, k = dev(torch, c["q"]), dev(torch, c["k"])
+    gq, gk = dev(torch, c["gamma_q"]), dev(torch, c["gamma_k"])
+    es = q.element_size()
+    nbytes = fused_bytes(T, q.shape[1], k.shape[1], es, gq.element_size())
+    n = rotation_count(2 * T * (q.shape[1] + k.shape[1]) * es)
+    sets = [(q.clone(), k.clone(), torch.empty_like(q), torch.empty_like(k)) for _ in range(n)]
+    del q, k
+
+    def step(i):
+        qi, ki, qo, ko = sets[i % n]
+        Q.qknorm_fused(qi, gq, ki, gk, eps=c["eps"], q_out=qo, k_out=ko)
+
+    return step, nbytes
+
+
+def shard_setup(torch, Q, inputs, T):
+    c = inputs.make_case(4, T)
+    q, k = dev(torch, c["q"]), dev(torch, c["k"])
+    gq, gk = dev(torch, c["gamma_q"]), dev(torch, c["gamma_k"])
+    eq, ek = dev(torch, c["ext_q"]), dev(torch, c["ext_k"])
+    per_set = 2 * T * 512 * 2 * 2 + 2 * T * 4
+    n = rotation_count(per_set)
+    sets = []
+    for _ in range(n):
+        sets.append((q.clone(), k.clone(), torch.empty_like(q), torch.empty_like(k),
+                     torch.empty(T, device="cuda"), torch.empty(T, device="cuda")))
+
+    def k1(i):
+        qi, ki, _, _, pq, pk = sets[i % n]
+        Q.qknorm_partial_sumsq(qi, ki, psq_q=pq, psq_k=pk)
+
+    def k2(i):
+        qi, ki, qo, ko, pq, pk = sets[i % n]
+        Q.qknorm_apply_with_stats(qi, gq, pq, eq, 4096, ki, gk, pk, ek, 4096, eps=c["eps"],
+                                  q_out=qo, k_out=ko)
+
+    b1 = T * 2 * (512 * 2 + 4)
+    b2 = T * 2 * (512 * 2 * 2 + 4 + 7 * 4) + 2 * 512 * 2
+    return k1, k2, b1, b2
+
+
+def normproj_setup(torch, Q, inputs, T, unfused=False):
+    c = inputs.make_case(5, T)
+    x, w, g = dev(torch, c["x"]), dev(torch, c["w"]), dev(torch, c["gamma"])
+    K, N = w.shape
+    wf = Q.normproj_fold_weight(w, g)
+    wp = Q.normproj_fold_weight(w, None)
+    n = rotation_count(T * (K + N) * 2 + (T * K * 2 if unfused else 0))
+    sets = [(x.clone(), torch.empty((T, N), dtype=torch.bfloat16, device="cuda"),
+             torch.empty((T, K), dtype=torch.bfloat16, device="cuda") if unfused else None)
+            for _ in range(n)]
+
+    def deferred(i):
+        xi, yi, _ = sets[i % n]
+        Q.normproj_deferred(xi, wf, eps=c["eps"], y=yi)
+
+    def unf(i):
+        xi, yi, xn = sets[i % n]
+        Q.normproj_unfused(xi, g, wp, eps=c["eps"], xn=xn, y=yi)
+
+    flops = 2.0 * T * K * N
+    nbytes = T * K * 2 + K * N * 2 + T * N * 2
+    return (unf if unfused else deferred), flops, nbytes
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+def cpu_baseline(inputs, T_full, budget_s=10.0):
+    """The fp64 oracle on the host, single thread, on a bounded sample of the workload: the
+    first 1024 tokens of Q and K, repeated until the budget is spent."""
+    import oracle
+
+    c = inputs.make_case(2, 1024)
+    done, t0 = 0, time.perf_counter()
+    while True:
+        oracle.rmsnorm_rows(c["q"], c["gamma_q"], c["eps"])
+        oracle.rmsnorm_rows(c["k"], c["gamma_k"], c["eps"])
+        done += 1024
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": done / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first 1024 tokens of Q and K [T, 4096] bf16 (of T={T_full}), fp64 "
+                      f"oracle, 1 thread, {done // 1024} passes in {el:.1f} s"}
+
+
+# ----------------------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--tokens", type=int, default=8192)
+    ap.add_argument("--cases", default="all", help="'all' or 'none': per-workload timings")
+    ap.add_argument("--case-iters", type=int, default=100)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (rows shard with no "
+              "exchange; the column-sharded exchange is not built). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import layerwise_qk_norm_amd as Q
+    from layerwise_qk_norm_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    Q.lib()
+    stream = torch.cuda.Stream()
+    timer = Timer(torch, stream)
+
+    T = args.tokens
+    step, nbytes = fused_setup(torch, Q, inputs, 2, T)
+    torch.cuda.synchronize()
+    ms = timer.run(step, args.steps, args.warmup)
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    print(f"# headline: fused Q+K [{T}, 4096] bf16: {ms * 1e3:.2f} us/call, {achieved:.0f} GB/s",
+          file=sys.stderr, flush=True)
+
+    cases = []
+    if args.cases == "all":
+        it, wu = args.case_iters, max(5, args.case_iters // 10)
+
+        # empirical copy ceiling over the same bytes (read nbytes/2, write nbytes/2)
+        half = (nbytes // 2) // 16 * 16
+        n_copy = rotation_count(2 * half)
+        bufs = [(torch.empty(half, dtype=torch.uint8, device="cuda"),
+                 torch.empty(half, dtype=torch.uint8, device="cuda")) for _ in range(n_copy)]
+        cms = timer.run(lambda i: Q.qkn_device_copy(bufs[i % n_copy][1], bufs[i % n_copy][0]),
+                        it, wu)
+        cases.append({"case": f"device copy {half} B (same traffic as the headline)",
+                      "us_per_call": cms * 1e3, "GB_s": 2 * half / (cms * 1e-3) / 1e9})
+        del bufs
+
+        for cfg, Ts in ((1, (64,)), (2, (1, 16, 256, 4096)), (3, (1, 512, 8192))):
+            for t in Ts:
+                fn, b = fused_setup(torch, Q, inputs, cfg, t)
+                cms = timer.run(fn, it, wu)
+                cases.append({"case": f"qknorm_fused cfg{cfg} {inputs.CONFIGS[cfg]['name']} T={t}",
+                              "us_per_call": cms * 1e3, "GB_s": b / (cms * 1e-3) / 1e9,
+                              "frac_hbm": b / (cms * 1e-3) / 1e9 / PEAK_HBM_GBS})
+                del fn
+                torch.cuda.empty_cache()
+
+        k1, k2, b1, b2 = shard_setup(torch, Q, inputs, 131072)
+        m1 = timer.run(k1, it, wu)
+        m2 = timer.run(k2, it, wu)
+        for name, m, b in (("qknorm_partial_sumsq", m1, b1), ("qknorm_apply_with_stats", m2, b2)):
+            cases.append({"case": f"{name} cfg4 tp8-shard T=131072", "us_per_call": m * 1e3,
+                          "GB_s": b / (m * 1e-3) / 1e9,
+                          "frac_hbm": b / (m * 1e-3) / 1e9 / PEAK_HBM_GBS})
+        del k1, k2
+        torch.cuda.empty_cache()
+
+        for t in (1, 2048, 16384):
+            for unfused in (False, True):
+                if unfused and t == 1:
+                    continue
+                fn, flops, b = normproj_setup(torch, Q, inputs, t, unfused)
+                cms = timer.run(fn, it, wu)
+                name = "normproj_unfused" if unfused else "normproj_deferred"
+                entry = {"case": f"{name} cfg5 flashnorm-2048 T={t}", "us_per_call": cms * 1e3,
+                         "TFLOP_s": flops / (cms * 1e-3) / 1e12}
+                if t == 1:
+                    entry["GB_s"] = b / (cms * 1e-3) / 1e9
+                    entry["frac_hbm"] = entry["GB_s"] / PEAK_HBM_GBS
+                else:
+                    entry["frac_mfma_bf16"] = entry["TFLOP_s"] / PEAK_BF16_TFLOPS
+                cases.append(entry)
+                del fn
+                torch.cuda.empty_cache()
+        for cs in cases:
+            print("# " + json.dumps(cs), file=sys.stderr, flush=True)
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(inputs, T, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"layerwise QK-Norm, OLMo-2-7B shape: Q and K [{T}, 4096] bf16 "
+                               f"(32 heads x 128), one fused Q+K launch per step, x~N(0,2), "
+                               f"gamma~N(1,0.05), eps=1e-6",
+                   "tokens": T, "dq": 4096, "dk": 4096, "parallelism": "none (1 GPU)",
+                   "rotating_buffers_bytes": ROTATE_BYTES},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": recorded_traffic(),
+                     "algorithmic_bytes_per_launch": nbytes,
+                     "kernel": "rows_kernel<kFused, bf16, 8, 8> (qknorm_fused)"},
+        "cpu_baseline": cpu,
+        "cases": cases,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

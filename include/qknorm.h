@@ -1,0 +1,181 @@
+/*
+ * qknorm.h - C ABI of libqknorm.so: layerwise QK-Norm and deferred norm-then-project on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Operations (sources are the pages' titles and the part that states the operation):
+ *
+ *   RMSNorm of a row x of width d with per-column weight gamma and epsilon inside the root:
+ *       r = 1 / sqrt( (1/d) * sum_i x_i^2 + eps ),     y_i = x_i * gamma_i * r
+ *   Layerwise QK-Norm applies it to each token's full (heads * head_dim) Q and K projection
+ *   vectors; the factor depends on the full vector ("SwiftQK: Fast and Communication-Efficient
+ *   Tensor Parallelism for Query-Key Normalization", abstract).
+ *
+ * Conventions shared by every call:
+ *   - Tensors are row-major [T, d] with a row stride ld (in elements, ld >= d).
+ *   - Every pointer argument is a DEVICE pointer that the caller allocates and owns; the
+ *     library allocates no memory and keeps no workspace between calls.
+ *   - `stream` is a hipStream_t passed as void*; NULL selects the null stream. Calls enqueue
+ *     work and return; they never synchronise the host. There is no global mutable state
+ *     except a thread-local copy of the last HIP error, so calls are thread-safe.
+ *   - dtype codes: QKN_F32 (float) and QKN_BF16 (bfloat16). Outputs have the input's dtype;
+ *     arithmetic is fp32 with one rounding at the output (round to nearest even for bf16).
+ *   - Arguments are validated before any HIP call; a non-zero status is returned without
+ *     touching the device. T == 0 is a valid no-op. Launch failures return QKN_ERR_HIP and
+ *     the raw hipError_t is kept for qkn_last_hip_error(). No exception crosses the ABI.
+ *   - An output may alias its own input exactly (same pointer, same ld): the row is read in
+ *     full before it is written. Any other overlap between an output and an input or another
+ *     output is QKN_ERR_ALIAS.
+ *   - Misaligned pointers or strides are accepted by the row operations (a scalar-load path
+ *     runs instead of the 16-byte one). The norm-then-project calls need 16-byte aligned
+ *     rows (QKN_ERR_ALIGN otherwise).
+ *   - Results are deterministic: no atomics, fixed reduction order.
+ */
+#ifndef QKNORM_H
+#define QKNORM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QKN_API __attribute__((visibility("default")))
+
+enum { QKN_F32 = 0, QKN_BF16 = 1 };
+
+enum {
+    QKN_OK = 0,
+    QKN_ERR_NULL = 1,  /* a required pointer is NULL                                   */
+    QKN_ERR_SHAPE = 2, /* negative or inconsistent sizes / strides                     */
+    QKN_ERR_DTYPE = 3, /* unknown dtype code, or a dtype the operation does not support */
+    QKN_ERR_EPS = 4,   /* eps is negative, NaN or infinite                               */
+    QKN_ERR_ALIAS = 5, /* an output partially overlaps an input or another output        */
+    QKN_ERR_ALIGN = 6, /* 16-byte alignment required and not met                         */
+    QKN_ERR_HIP = 7    /* the HIP runtime reported an error; see qkn_last_hip_error()    */
+};
+
+/*
+ * qknorm_fused - layerwise QK-Norm of Q and K in ONE launch.
+ *
+ * ("SwiftQK: ...", abstract: RMSNorm over each token's full Q and K vectors.)
+ * For every token t < T:  q_out[t,:] = RMSNorm(q[t, 0:dq]; gamma_q, eps)
+ *                         k_out[t,:] = RMSNorm(k[t, 0:dk]; gamma_k, eps)
+ *   T           tokens (>= 0)
+ *   eps         finite, >= 0
+ *   dtype       QKN_F32 or QKN_BF16: storage of q, k, q_out, k_out
+ *   gamma_dtype QKN_F32 or QKN_BF16: storage of gamma_q [dq] and gamma_k [dk]
+ *   q, ldq      input [T, dq], row stride ldq >= dq;  q_out, ldq_out likewise
+ *   k, ...      the same for K. K is optional: pass k == k_out == gamma_k == NULL and dk == 0
+ *               to normalise Q alone.
+ * Sum of squares and scaling are fp32; the sum is reduced in a fixed order.
+ */
+QKN_API int qknorm_fused(int64_t T, float eps, int dtype, int gamma_dtype,
+                         const void* q, int64_t ldq, void* q_out, int64_t ldq_out,
+                         const void* gamma_q, int64_t dq,
+                         const void* k, int64_t ldk, void* k_out, int64_t ldk_out,
+                         const void* gamma_k, int64_t dk, void* stream);
+
+/*
+ * qknorm_partial_sumsq - first half of the scalar-statistics split (one GPU's shard stage).
+ *
+ * ("SwiftQK: ...", abstract: ranks exchange scalar partial sums instead of activation vectors.)
+ * psq_q[t] = sum_{i < dq_local} q[t,i]^2 and psq_k[t] likewise, in fp32, one launch for both.
+ *   q [T, dq_local] with stride ldq (the shard's column slice), psq_q [T] fp32 output.
+ *   K is optional (k == psq_k == NULL, dk_local == 0).
+ */
+QKN_API int qknorm_partial_sumsq(int64_t T, int dtype,
+                                 const void* q, int64_t ldq, int64_t dq_local, float* psq_q,
+                                 const void* k, int64_t ldk, int64_t dk_local, float* psq_k,
+                                 void* stream);
+
+/*
+ * qknorm_apply_with_stats - second half: aggregate the statistics, then scale the slice.
+ *
+ * ("SwiftQK: ...", abstract: scalar aggregation, then the element-wise scale.) For row t:
+ *   S = psq[t] + ext[0*ld_ext + t] + ... + ext[(n_ext-1)*ld_ext + t]   (fp32, in this order)
+ *   r = 1 / sqrt(S / d_full + eps)        -- mean over the FULL width d_full, not the slice
+ *   out[t, i] = x[t, i] * gamma[i] * r    for i < d_local
+ *   n_ext       number of peers' partials (>= 0; 0 means the slice is the whole row)
+ *   psq_*       [T] fp32 own partials (e.g. from qknorm_partial_sumsq)
+ *   ext_*       [n_ext, T] fp32, peer-major, row stride ld_ext >= T (may be NULL if n_ext==0)
+ *   d_*_full    full row width, >= d_*_local >= 1
+ *   gamma_*     the slice's own gamma values [d_local]
+ *   K is optional (k, k_out, gamma_k, psq_k, ext_k NULL and dk_local == 0).
+ */
+QKN_API int qknorm_apply_with_stats(int64_t T, float eps, int dtype, int gamma_dtype,
+                                    int64_t n_ext,
+                                    const void* q, int64_t ldq, void* q_out, int64_t ldq_out,
+                                    const void* gamma_q, int64_t dq_local, int64_t dq_full,
+                                    const float* psq_q, const float* ext_q, int64_t ld_ext_q,
+                                    const void* k, int64_t ldk, void* k_out, int64_t ldk_out,
+                                    const void* gamma_k, int64_t dk_local, int64_t dk_full,
+                                    const float* psq_k, const float* ext_k, int64_t ld_ext_k,
+                                    void* stream);
+
+/*
+ * normproj_fold_weight - fold the norm weights into the following projection (once, offline).
+ *
+ * ("FlashNorm: Fast Normalization for Transformers", abstract, item (i).)
+ * For the projection y = x W with W [K, N] row-major (stride ldw >= N):
+ *   w_fold[n * ldw_fold + k] = bf16( gamma[k] * W[k, n] )     (fp32 product, one rounding)
+ * i.e. W' = diag(gamma) W is written TRANSPOSED, [N, K] with K contiguous, the layout the
+ * matrix-core kernel of normproj_deferred reads. gamma == NULL means gamma = 1 (a plain
+ * re-layout, used to pack the unfolded weight of the unfused baseline).
+ *   dtype       storage of W and w_fold: QKN_BF16 only
+ *   gamma_dtype QKN_F32 or QKN_BF16
+ *   ldw_fold    >= K, a multiple of 8; w_fold 16-byte aligned (QKN_ERR_ALIGN otherwise)
+ */
+QKN_API int normproj_fold_weight(int64_t K, int64_t N, int dtype, int gamma_dtype,
+                                 const void* w, int64_t ldw, const void* gamma,
+                                 void* w_fold, int64_t ldw_fold, void* stream);
+
+/*
+ * normproj_deferred - RMSNorm followed by the projection, with the scale deferred.
+ *
+ * ("FlashNorm: ...", abstract, item (ii): the scalar 1/RMS is applied to the output of the
+ * matrix product, so the reduction and the product proceed together.) For t < T, n < N:
+ *   r_t     = 1 / sqrt( (1/K) sum_k x[t,k]^2 + eps )         (fp32, from the same x tiles)
+ *   y[t,n]  = bf16( r_t * sum_k x[t,k] * w_fold[n,k] )        (bf16 products, fp32 accumulate)
+ *   x       [T, K] bf16, stride ldx
+ *   w_fold  [N, K] bf16 from normproj_fold_weight, stride ldw
+ *   y       [T, N] bf16, stride ldy; must not overlap x or w_fold
+ *   dtype   QKN_BF16 only
+ * K, ldx and ldw must be multiples of 8 and x, w_fold 16-byte aligned (QKN_ERR_ALIGN).
+ * T <= 16 runs a streaming matrix-vector kernel; larger T runs the matrix-core (MFMA) kernel.
+ */
+QKN_API int normproj_deferred(int64_t T, int64_t K, int64_t N, float eps, int dtype,
+                              const void* x, int64_t ldx, const void* w_fold, int64_t ldw,
+                              void* y, int64_t ldy, void* stream);
+
+/*
+ * normproj_unfused - the order the fold replaces, kept as the measured baseline.
+ *
+ * ("FlashNorm: ...", abstract: the RMS reduction blocks the following product.)
+ *   xn[t,k] = bf16( x[t,k] * gamma[k] * r_t )      (an RMSNorm launch, caller's buffer xn)
+ *   y[t,n]  = bf16( sum_k xn[t,k] * w_packed[n,k] ) (a plain matrix-core launch)
+ *   w_packed [N, K] bf16 is the UNFOLDED weight re-laid out by normproj_fold_weight with
+ *   gamma == NULL. xn [T, K] bf16 (stride ldxn) is scratch owned by the caller.
+ * Same dtype and alignment rules as normproj_deferred.
+ */
+QKN_API int normproj_unfused(int64_t T, int64_t K, int64_t N, float eps, int dtype,
+                             int gamma_dtype, const void* x, int64_t ldx, const void* gamma,
+                             const void* w_packed, int64_t ldw, void* xn, int64_t ldxn,
+                             void* y, int64_t ldy, void* stream);
+
+/*
+ * qkn_device_copy - plain streaming copy of nbytes (16-byte vectors where aligned).
+ * Used to calibrate measured bandwidth and memory counters against a kernel of known traffic.
+ * dst and src must not overlap.
+ */
+QKN_API int qkn_device_copy(void* dst, const void* src, int64_t nbytes, void* stream);
+
+/* Static description of a status code (never NULL). */
+QKN_API const char* qkn_status_string(int status);
+
+/* Raw hipError_t of the last QKN_ERR_HIP returned on the calling thread (0 if none). */
+QKN_API int qkn_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QKNORM_H */

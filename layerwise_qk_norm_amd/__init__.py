@@ -1,0 +1,13 @@
+"""Layerwise QK-Norm for AMD Instinct MI355X (gfx950).
+
+The computation lives in libqknorm.so (hand-written HIP kernels behind a C ABI declared in
+include/qknorm.h); this package is its thin Python binding plus the seeded input generator.
+"""
+
+from ._lib import (QKN_BF16, QKN_F32, QknError, lib, normproj_deferred, normproj_fold_weight,
+                   normproj_unfused, qkn_device_copy, qknorm_apply_with_stats, qknorm_fused,
+                   qknorm_partial_sumsq)
+
+__all__ = ["QKN_BF16", "QKN_F32", "QknError", "lib", "normproj_deferred",
+           "normproj_fold_weight", "normproj_unfused", "qkn_device_copy",
+           "qknorm_apply_with_stats", "qknorm_fused", "qknorm_partial_sumsq"]

@@ -1,0 +1,240 @@
+"""ctypes binding of libqknorm.so: argument marshalling only.
+
+Every function here takes torch tensors (device memory) and forwards raw pointers, sizes,
+strides and the current HIP stream to the C entry point of the same name; all computation
+happens in the library's gfx950 kernels. There is no fallback: if the library is missing or a
+call fails, an exception is raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libqknorm.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "qknorm.h")
+
+QKN_F32, QKN_BF16 = 0, 1
+STATUS = {0: "QKN_OK", 1: "QKN_ERR_NULL", 2: "QKN_ERR_SHAPE", 3: "QKN_ERR_DTYPE",
+          4: "QKN_ERR_EPS", 5: "QKN_ERR_ALIAS", 6: "QKN_ERR_ALIGN", 7: "QKN_ERR_HIP"}
+
+
+class QknError(RuntimeError):
+    def __init__(self, func: str, status: int, lib):
+        msg = lib.qkn_status_string(status).decode()
+        extra = f" (hipError {lib.qkn_last_hip_error()})" if status == 7 else ""
+        super().__init__(f"{func}: {STATUS.get(status, status)}: {msg}{extra}")
+        self.status = status
+
+
+_lib = None
+_i64, _f32, _int, _vp = ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctypes.c_void_p
+_PROTOS = {
+    "qknorm_fused": [_i64, _f32, _int, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
+                     _i64, _vp, _i64, _vp],
+    "qknorm_partial_sumsq": [_i64, _int, _vp, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _vp],
+    "qknorm_apply_with_stats": [_i64, _f32, _int, _int, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
+                                _i64, _vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64,
+                                _vp, _vp, _i64, _vp],
+    "normproj_fold_weight": [_i64, _i64, _int, _int, _vp, _i64, _vp, _vp, _i64, _vp],
+    "normproj_deferred": [_i64, _i64, _i64, _f32, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp],
+    "normproj_unfused": [_i64, _i64, _i64, _f32, _int, _int, _vp, _i64, _vp, _vp, _i64, _vp,
+                         _i64, _vp, _i64, _vp],
+    "qkn_device_copy": [_vp, _vp, _i64, _vp],
+    "qkn_status_string": [_int],
+    "qkn_last_hip_error": [],
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load libqknorm.so (built in-tree by layerwise_qk_norm_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m layerwise_qk_norm_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, args in _PROTOS.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_char_p if name == "qkn_status_string" else ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def header_entry_points() -> list[str]:
+    """Names of the functions include/qknorm.h declares with QKN_API."""
+    text = open(HEADER).read()
+    return re.findall(r"QKN_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+def _check(name: str, status: int):
+    if status != 0:
+        raise QknError(name, status, lib())
+
+
+# ----------------------------------------------------------------------------- marshalling
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return QKN_BF16
+    if t.dtype == torch.float32:
+        return QKN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _ld(t) -> int:
+    """Row stride of a 2-D tensor whose rows are contiguous."""
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError("expected a 2-D tensor with unit column stride")
+    ld = t.stride(0)
+    return ld if t.shape[0] > 1 else max(ld, t.shape[1])
+
+
+def _stream(t):
+    torch = _torch()
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _check_device(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+
+
+# ----------------------------------------------------------------------------- entry points
+def qknorm_fused(q, gamma_q, k=None, gamma_k=None, eps: float = 1e-6, q_out=None, k_out=None,
+                 dq: int | None = None, dk: int | None = None):
+    """RMSNorm of each row of q (and k) over its full width, in one launch.
+    Returns (q_out, k_out); outputs may be the inputs themselves (in place)."""
+    torch = _torch()
+    _check_device(q, k, gamma_q, gamma_k)
+    T = q.shape[0]
+    dq = q.shape[1] if dq is None else dq
+    if q_out is None:
+        q_out = torch.empty((T, dq), dtype=q.dtype, device=q.device)
+    if k is not None:
+        dk = k.shape[1] if dk is None else dk
+        if k_out is None:
+            k_out = torch.empty((T, dk), dtype=k.dtype, device=k.device)
+    gdt = _dtype_code(gamma_q)
+    _check("qknorm_fused", lib().qknorm_fused(
+        T, float(eps), _dtype_code(q), gdt,
+        _ptr(q), _ld(q), _ptr(q_out), _ld(q_out), _ptr(gamma_q), dq,
+        _ptr(k), _ld(k) if k is not None else 0, _ptr(k_out),
+        _ld(k_out) if k is not None else 0, _ptr(gamma_k), dk if k is not None else 0,
+        _stream(q)))
+    return q_out, k_out
+
+
+def qknorm_partial_sumsq(q, k=None, psq_q=None, psq_k=None, dq_local: int | None = None,
+                         dk_local: int | None = None):
+    """Per-row fp32 sums of squares of the slices; returns (psq_q, psq_k)."""
+    torch = _torch()
+    _check_device(q, k)
+    T = q.shape[0]
+    dq_local = q.shape[1] if dq_local is None else dq_local
+    if psq_q is None:
+        psq_q = torch.empty((T,), dtype=torch.float32, device=q.device)
+    if k is not None:
+        dk_local = k.shape[1] if dk_local is None else dk_local
+        if psq_k is None:
+            psq_k = torch.empty((T,), dtype=torch.float32, device=q.device)
+    _check("qknorm_partial_sumsq", lib().qknorm_partial_sumsq(
+        T, _dtype_code(q), _ptr(q), _ld(q), dq_local, _ptr(psq_q),
+        _ptr(k), _ld(k) if k is not None else 0, dk_local if k is not None else 0,
+        _ptr(psq_k), _stream(q)))
+    return psq_q, psq_k
+
+
+def qknorm_apply_with_stats(q, gamma_q, psq_q, ext_q, dq_full: int, k=None, gamma_k=None,
+                            psq_k=None, ext_k=None, dk_full: int | None = None,
+                            eps: float = 1e-6, q_out=None, k_out=None,
+                            dq_local: int | None = None, dk_local: int | None = None):
+    """Aggregate own + peers' partials ([n_ext, T] fp32, or None) and scale the slices."""
+    torch = _torch()
+    _check_device(q, k, gamma_q, gamma_k, psq_q, psq_k, ext_q, ext_k)
+    T = q.shape[0]
+    dq_local = q.shape[1] if dq_local is None else dq_local
+    n_ext = 0 if ext_q is None else ext_q.shape[0]
+    if q_out is None:
+        q_out = torch.empty((T, dq_local), dtype=q.dtype, device=q.device)
+    if k is not None:
+        dk_local = k.shape[1] if dk_local is None else dk_local
+        if k_out is None:
+            k_out = torch.empty((T, dk_local), dtype=k.dtype, device=k.device)
+        n_ext_k = 0 if ext_k is None else ext_k.shape[0]
+        if n_ext_k != n_ext:
+            raise ValueError("ext_q and ext_k must hold the same number of peers")
+    gdt = _dtype_code(gamma_q)
+    _check("qknorm_apply_with_stats", lib().qknorm_apply_with_stats(
+        T, float(eps), _dtype_code(q), gdt, n_ext,
+        _ptr(q), _ld(q), _ptr(q_out), _ld(q_out), _ptr(gamma_q), dq_local, dq_full,
+        _ptr(psq_q), _ptr(ext_q), _ld(ext_q) if n_ext else 0,
+        _ptr(k), _ld(k) if k is not None else 0, _ptr(k_out),
+        _ld(k_out) if k is not None else 0, _ptr(gamma_k), dk_local if k is not None else 0,
+        dk_full if k is not None else 0, _ptr(psq_k), _ptr(ext_k) if k is not None else None,
+        _ld(ext_k) if (k is not None and n_ext) else 0, _stream(q)))
+    return q_out, k_out
+
+
+def normproj_fold_weight(w, gamma=None, w_fold=None):
+    """W [K, N] bf16 -> W' = diag(gamma) W stored transposed, [N, K] bf16 (K contiguous)."""
+    torch = _torch()
+    _check_device(w, gamma)
+    K, N = w.shape
+    if w_fold is None:
+        w_fold = torch.empty((N, K), dtype=torch.bfloat16, device=w.device)
+    _check("normproj_fold_weight", lib().normproj_fold_weight(
+        K, N, _dtype_code(w), _dtype_code(gamma) if gamma is not None else QKN_BF16,
+        _ptr(w), _ld(w), _ptr(gamma), _ptr(w_fold), _ld(w_fold), _stream(w)))
+    return w_fold
+
+
+def normproj_deferred(x, w_fold, eps: float = 1e-6, y=None):
+    """y [T, N] = (x @ W') * (1/rms(x)) with w_fold [N, K] from normproj_fold_weight."""
+    torch = _torch()
+    _check_device(x, w_fold)
+    T, K = x.shape
+    N = w_fold.shape[0]
+    if y is None:
+        y = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    _check("normproj_deferred", lib().normproj_deferred(
+        T, K, N, float(eps), _dtype_code(x), _ptr(x), _ld(x), _ptr(w_fold), _ld(w_fold),
+        _ptr(y), _ld(y), _stream(x)))
+    return y
+
+
+def normproj_unfused(x, gamma, w_packed, eps: float = 1e-6, xn=None, y=None):
+    """RMSNorm launch into xn, then a plain product with the packed unfolded weight."""
+    torch = _torch()
+    _check_device(x, gamma, w_packed)
+    T, K = x.shape
+    N = w_packed.shape[0]
+    if xn is None:
+        xn = torch.empty((T, K), dtype=torch.bfloat16, device=x.device)
+    if y is None:
+        y = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    _check("normproj_unfused", lib().normproj_unfused(
+        T, K, N, float(eps), _dtype_code(x), _dtype_code(gamma), _ptr(x), _ld(x), _ptr(gamma),
+        _ptr(w_packed), _ld(w_packed), _ptr(xn), _ld(xn), _ptr(y), _ld(y), _stream(x)))
+    return xn, y
+
+
+def qkn_device_copy(dst, src, nbytes: int | None = None):
+    _check_device(dst, src)
+    n = src.numel() * src.element_size() if nbytes is None else nbytes
+    _check("qkn_device_copy", lib().qkn_device_copy(_ptr(dst), _ptr(src), n, _stream(src)))
+    return dst

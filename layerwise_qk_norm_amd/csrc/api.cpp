@@ -1,0 +1,328 @@
+// C-ABI entry points of libqknorm.so: argument validation (before any HIP call) and dispatch
+// onto the caller's stream. The operations and conventions are documented in qknorm.h.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/qknorm.h"
+#include "launch.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_status(hipError_t e)
+{
+    if (e == hipSuccess) return QKN_OK;
+    g_last_hip_error = (int)e;
+    return QKN_ERR_HIP;
+}
+
+bool valid_dtype(int dt) { return dt == QKN_F32 || dt == QKN_BF16; }
+int64_t elem_size(int dt) { return dt == QKN_F32 ? 4 : 2; }
+bool valid_eps(float eps) { return std::isfinite(eps) && eps >= 0.0f; }
+
+// Byte range [lo, hi) touched by a [rows, cols] tensor with row stride ld.
+struct Range {
+    uintptr_t lo = 0, hi = 0;
+    bool empty() const { return hi <= lo; }
+};
+
+Range span(const void* p, int64_t rows, int64_t cols, int64_t ld, int64_t es)
+{
+    Range r;
+    if (p == nullptr || rows <= 0 || cols <= 0) return r;
+    r.lo = (uintptr_t)p;
+    r.hi = r.lo + (uintptr_t)(((rows - 1) * ld + cols) * es);
+    return r;
+}
+
+bool overlap(const Range& a, const Range& b)
+{
+    return !a.empty() && !b.empty() && a.lo < b.hi && b.lo < a.hi;
+}
+
+// An output may alias its own input exactly (same base, same stride); any other overlap is an
+// error. `others` are ranges the output must not touch at all.
+bool out_ok(const void* out, int64_t ld_out, const void* in, int64_t ld_in, const Range& r_out,
+            const Range& r_in, const Range* others, int n_others)
+{
+    const bool exact = out == in && ld_out == ld_in;
+    if (!exact && overlap(r_out, r_in)) return false;
+    for (int i = 0; i < n_others; ++i)
+        if (overlap(r_out, others[i])) return false;
+    return true;
+}
+
+// Common checks of one row tensor: pointers present, 1 <= d <= ld.
+int check_rows(int64_t T, const void* x, int64_t ldx, const void* y, int64_t ldy, int64_t d,
+               bool need_y)
+{
+    if (d < 1 || ldx < d || (need_y && ldy < d)) return QKN_ERR_SHAPE;
+    if (T > 0 && (x == nullptr || (need_y && y == nullptr))) return QKN_ERR_NULL;
+    return QKN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+QKN_API const char* qkn_status_string(int status)
+{
+    switch (status) {
+    case QKN_OK: return "ok";
+    case QKN_ERR_NULL: return "a required pointer is NULL";
+    case QKN_ERR_SHAPE: return "invalid or inconsistent sizes or strides";
+    case QKN_ERR_DTYPE: return "unsupported dtype code";
+    case QKN_ERR_EPS: return "eps must be finite and >= 0";
+    case QKN_ERR_ALIAS: return "an output partially overlaps an input or another output";
+    case QKN_ERR_ALIGN: return "16-byte alignment required";
+    case QKN_ERR_HIP: return "HIP runtime error (see qkn_last_hip_error)";
+    default: return "unknown status";
+    }
+}
+
+QKN_API int qkn_last_hip_error(void) { return g_last_hip_error; }
+
+QKN_API int qknorm_fused(int64_t T, float eps, int dtype, int gamma_dtype, const void* q,
+                         int64_t ldq, void* q_out, int64_t ldq_out, const void* gamma_q,
+                         int64_t dq, const void* k, int64_t ldk, void* k_out, int64_t ldk_out,
+                         const void* gamma_k, int64_t dk, void* stream)
+{
+    if (T < 0) return QKN_ERR_SHAPE;
+    if (!valid_dtype(dtype) || !valid_dtype(gamma_dtype)) return QKN_ERR_DTYPE;
+    if (!valid_eps(eps)) return QKN_ERR_EPS;
+    const bool has_k = !(k == nullptr && k_out == nullptr && gamma_k == nullptr && dk == 0);
+    int st = check_rows(T, q, ldq, q_out, ldq_out, dq, true);
+    if (st != QKN_OK) return st;
+    if (T > 0 && gamma_q == nullptr) return QKN_ERR_NULL;
+    if (has_k) {
+        st = check_rows(T, k, ldk, k_out, ldk_out, dk, true);
+        if (st != QKN_OK) return st;
+        if (T > 0 && gamma_k == nullptr) return QKN_ERR_NULL;
+    }
+    if (T == 0) return QKN_OK;
+
+    const int64_t es = elem_size(dtype), gs = elem_size(gamma_dtype);
+    const Range rq = span(q, T, dq, ldq, es), rqo = span(q_out, T, dq, ldq_out, es);
+    const Range rgq = span(gamma_q, 1, dq, dq, gs);
+    Range rk, rko, rgk;
+    if (has_k) {
+        rk = span(k, T, dk, ldk, es);
+        rko = span(k_out, T, dk, ldk_out, es);
+        rgk = span(gamma_k, 1, dk, dk, gs);
+    }
+    const Range others_q[] = {rgq, rk, rko, rgk};
+    if (!out_ok(q_out, ldq_out, q, ldq, rqo, rq, others_q, has_k ? 4 : 1)) return QKN_ERR_ALIAS;
+    if (has_k) {
+        const Range others_k[] = {rgk, rq, rgq};
+        if (!out_ok(k_out, ldk_out, k, ldk, rko, rk, others_k, 3)) return QKN_ERR_ALIAS;
+    }
+
+    qkn::RowJob job = {};
+    job.nseg = has_k ? 2 : 1;
+    job.T = T;
+    job.eps = eps;
+    job.mode = qkn::kFused;
+    job.bf16 = dtype == QKN_BF16;
+    job.gamma_bf16 = gamma_dtype == QKN_BF16;
+    job.seg[0] = {q, q_out, gamma_q, ldq, ldq_out, dq, (float)(1.0 / (double)dq),
+                  nullptr, nullptr, 0, 0, nullptr};
+    if (has_k)
+        job.seg[1] = {k, k_out, gamma_k, ldk, ldk_out, dk, (float)(1.0 / (double)dk),
+                      nullptr, nullptr, 0, 0, nullptr};
+    return hip_status(qkn::launch_rows(job, (hipStream_t)stream));
+}
+
+QKN_API int qknorm_partial_sumsq(int64_t T, int dtype, const void* q, int64_t ldq,
+                                 int64_t dq_local, float* psq_q, const void* k, int64_t ldk,
+                                 int64_t dk_local, float* psq_k, void* stream)
+{
+    if (T < 0) return QKN_ERR_SHAPE;
+    if (!valid_dtype(dtype)) return QKN_ERR_DTYPE;
+    const bool has_k = !(k == nullptr && psq_k == nullptr && dk_local == 0);
+    int st = check_rows(T, q, ldq, nullptr, 0, dq_local, false);
+    if (st != QKN_OK) return st;
+    if (T > 0 && psq_q == nullptr) return QKN_ERR_NULL;
+    if (has_k) {
+        st = check_rows(T, k, ldk, nullptr, 0, dk_local, false);
+        if (st != QKN_OK) return st;
+        if (T > 0 && psq_k == nullptr) return QKN_ERR_NULL;
+    }
+    if (T == 0) return QKN_OK;
+
+    const int64_t es = elem_size(dtype);
+    const Range rq = span(q, T, dq_local, ldq, es), rk = has_k ? span(k, T, dk_local, ldk, es) : Range();
+    const Range rpq = span(psq_q, 1, T, T, 4), rpk = has_k ? span(psq_k, 1, T, T, 4) : Range();
+    if (overlap(rpq, rq) || overlap(rpq, rk) || overlap(rpq, rpk) || overlap(rpk, rq) ||
+        overlap(rpk, rk))
+        return QKN_ERR_ALIAS;
+
+    qkn::RowJob job = {};
+    job.nseg = has_k ? 2 : 1;
+    job.T = T;
+    job.mode = qkn::kPartial;
+    job.bf16 = dtype == QKN_BF16;
+    job.seg[0] = {q, nullptr, nullptr, ldq, 0, dq_local, 0.0f, nullptr, nullptr, 0, 0, psq_q};
+    if (has_k) job.seg[1] = {k, nullptr, nullptr, ldk, 0, dk_local, 0.0f, nullptr, nullptr, 0, 0, psq_k};
+    return hip_status(qkn::launch_rows(job, (hipStream_t)stream));
+}
+
+QKN_API int qknorm_apply_with_stats(int64_t T, float eps, int dtype, int gamma_dtype,
+                                    int64_t n_ext, const void* q, int64_t ldq, void* q_out,
+                                    int64_t ldq_out, const void* gamma_q, int64_t dq_local,
+                                    int64_t dq_full, const float* psq_q, const float* ext_q,
+                                    int64_t ld_ext_q, const void* k, int64_t ldk, void* k_out,
+                                    int64_t ldk_out, const void* gamma_k, int64_t dk_local,
+                                    int64_t dk_full, const float* psq_k, const float* ext_k,
+                                    int64_t ld_ext_k, void* stream)
+{
+    if (T < 0 || n_ext < 0) return QKN_ERR_SHAPE;
+    if (!valid_dtype(dtype) || !valid_dtype(gamma_dtype)) return QKN_ERR_DTYPE;
+    if (!valid_eps(eps)) return QKN_ERR_EPS;
+    const bool has_k = !(k == nullptr && k_out == nullptr && gamma_k == nullptr &&
+                         psq_k == nullptr && ext_k == nullptr && dk_local == 0);
+    int st = check_rows(T, q, ldq, q_out, ldq_out, dq_local, true);
+    if (st != QKN_OK) return st;
+    if (dq_full < dq_local) return QKN_ERR_SHAPE;
+    if (n_ext > 0 && ld_ext_q < T) return QKN_ERR_SHAPE;
+    if (T > 0 && (gamma_q == nullptr || psq_q == nullptr || (n_ext > 0 && ext_q == nullptr)))
+        return QKN_ERR_NULL;
+    if (has_k) {
+        st = check_rows(T, k, ldk, k_out, ldk_out, dk_local, true);
+        if (st != QKN_OK) return st;
+        if (dk_full < dk_local) return QKN_ERR_SHAPE;
+        if (n_ext > 0 && ld_ext_k < T) return QKN_ERR_SHAPE;
+        if (T > 0 && (gamma_k == nullptr || psq_k == nullptr || (n_ext > 0 && ext_k == nullptr)))
+            return QKN_ERR_NULL;
+    }
+    if (T == 0) return QKN_OK;
+
+    const int64_t es = elem_size(dtype), gs = elem_size(gamma_dtype);
+    const Range rq = span(q, T, dq_local, ldq, es), rqo = span(q_out, T, dq_local, ldq_out, es);
+    const Range rgq = span(gamma_q, 1, dq_local, dq_local, gs);
+    const Range rpq = span(psq_q, 1, T, T, 4);
+    const Range req = n_ext > 0 ? span(ext_q, n_ext, T, ld_ext_q, 4) : Range();
+    Range rk, rko, rgk, rpk, rek;
+    if (has_k) {
+        rk = span(k, T, dk_local, ldk, es);
+        rko = span(k_out, T, dk_local, ldk_out, es);
+        rgk = span(gamma_k, 1, dk_local, dk_local, gs);
+        rpk = span(psq_k, 1, T, T, 4);
+        rek = n_ext > 0 ? span(ext_k, n_ext, T, ld_ext_k, 4) : Range();
+    }
+    const Range others_q[] = {rgq, rpq, req, rk, rko, rgk, rpk, rek};
+    if (!out_ok(q_out, ldq_out, q, ldq, rqo, rq, others_q, 8)) return QKN_ERR_ALIAS;
+    if (has_k) {
+        const Range others_k[] = {rgk, rpk, rek, rq, rgq, rpq, req};
+        if (!out_ok(k_out, ldk_out, k, ldk, rko, rk, others_k, 7)) return QKN_ERR_ALIAS;
+    }
+
+    qkn::RowJob job = {};
+    job.nseg = has_k ? 2 : 1;
+    job.T = T;
+    job.eps = eps;
+    job.mode = qkn::kApply;
+    job.bf16 = dtype == QKN_BF16;
+    job.gamma_bf16 = gamma_dtype == QKN_BF16;
+    job.seg[0] = {q, q_out, gamma_q, ldq, ldq_out, dq_local, (float)(1.0 / (double)dq_full),
+                  psq_q, ext_q, ld_ext_q, n_ext, nullptr};
+    if (has_k)
+        job.seg[1] = {k, k_out, gamma_k, ldk, ldk_out, dk_local, (float)(1.0 / (double)dk_full),
+                      psq_k, ext_k, ld_ext_k, n_ext, nullptr};
+    return hip_status(qkn::launch_rows(job, (hipStream_t)stream));
+}
+
+QKN_API int normproj_fold_weight(int64_t K, int64_t N, int dtype, int gamma_dtype,
+                                 const void* w, int64_t ldw, const void* gamma, void* w_fold,
+                                 int64_t ldw_fold, void* stream)
+{
+    if (K < 0 || N < 0 || ldw < N || ldw_fold < K) return QKN_ERR_SHAPE;
+    if (dtype != QKN_BF16 || !valid_dtype(gamma_dtype)) return QKN_ERR_DTYPE;
+    if (K == 0 || N == 0) return QKN_OK;
+    if (w == nullptr || w_fold == nullptr) return QKN_ERR_NULL;
+    if (((uintptr_t)w_fold & 15u) != 0 || ldw_fold % 8 != 0) return QKN_ERR_ALIGN;
+    const Range rw = span(w, K, N, ldw, 2), rf = span(w_fold, N, K, ldw_fold, 2);
+    const Range rg = gamma ? span(gamma, 1, K, K, elem_size(gamma_dtype)) : Range();
+    if (overlap(rf, rw) || overlap(rf, rg)) return QKN_ERR_ALIAS;
+    return hip_status(qkn::launch_fold(K, N, w, ldw, gamma, gamma_dtype == QKN_BF16, w_fold,
+                                       ldw_fold, (hipStream_t)stream));
+}
+
+namespace {
+
+int check_normproj(int64_t T, int64_t K, int64_t N, float eps, int dtype, const void* x,
+                   int64_t ldx, const void* w, int64_t ldw, const void* y, int64_t ldy)
+{
+    if (T < 0 || K < 1 || N < 0 || ldx < K || ldw < K || ldy < N) return QKN_ERR_SHAPE;
+    if (dtype != QKN_BF16) return QKN_ERR_DTYPE;
+    if (!valid_eps(eps)) return QKN_ERR_EPS;
+    if (T == 0 || N == 0) return QKN_OK;
+    if (x == nullptr || w == nullptr || y == nullptr) return QKN_ERR_NULL;
+    if (K % 8 != 0 || ldx % 8 != 0 || ldw % 8 != 0 || ((uintptr_t)x & 15u) != 0 ||
+        ((uintptr_t)w & 15u) != 0)
+        return QKN_ERR_ALIGN;
+    const Range ry = span(y, T, N, ldy, 2);
+    if (overlap(ry, span(x, T, K, ldx, 2)) || overlap(ry, span(w, N, K, ldw, 2)))
+        return QKN_ERR_ALIAS;
+    return QKN_OK;
+}
+
+}  // namespace
+
+QKN_API int normproj_deferred(int64_t T, int64_t K, int64_t N, float eps, int dtype,
+                              const void* x, int64_t ldx, const void* w_fold, int64_t ldw,
+                              void* y, int64_t ldy, void* stream)
+{
+    const int st = check_normproj(T, K, N, eps, dtype, x, ldx, w_fold, ldw, y, ldy);
+    if (st != QKN_OK || T == 0 || N == 0) return st;
+    return hip_status(qkn::launch_normproj(T, K, N, eps, true, x, ldx, w_fold, ldw, y, ldy,
+                                           (hipStream_t)stream));
+}
+
+QKN_API int normproj_unfused(int64_t T, int64_t K, int64_t N, float eps, int dtype,
+                             int gamma_dtype, const void* x, int64_t ldx, const void* gamma,
+                             const void* w_packed, int64_t ldw, void* xn, int64_t ldxn, void* y,
+                             int64_t ldy, void* stream)
+{
+    int st = check_normproj(T, K, N, eps, dtype, x, ldx, w_packed, ldw, y, ldy);
+    if (st != QKN_OK) return st;
+    if (!valid_dtype(gamma_dtype)) return QKN_ERR_DTYPE;
+    if (ldxn < K) return QKN_ERR_SHAPE;
+    if (T == 0 || N == 0) return QKN_OK;
+    if (xn == nullptr || gamma == nullptr) return QKN_ERR_NULL;
+    if (((uintptr_t)xn & 15u) != 0 || ldxn % 8 != 0) return QKN_ERR_ALIGN;
+    const Range rxn = span(xn, T, K, ldxn, 2);
+    if (overlap(rxn, span(x, T, K, ldx, 2)) || overlap(rxn, span(w_packed, N, K, ldw, 2)) ||
+        overlap(rxn, span(y, T, N, ldy, 2)) ||
+        overlap(rxn, span(gamma, 1, K, K, elem_size(gamma_dtype))))
+        return QKN_ERR_ALIAS;
+
+    qkn::RowJob job = {};
+    job.nseg = 1;
+    job.T = T;
+    job.eps = eps;
+    job.mode = qkn::kFused;
+    job.bf16 = 1;
+    job.gamma_bf16 = gamma_dtype == QKN_BF16;
+    job.seg[0] = {x, xn, gamma, ldx, ldxn, K, (float)(1.0 / (double)K), nullptr, nullptr, 0, 0,
+                  nullptr};
+    hipError_t e = qkn::launch_rows(job, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(qkn::launch_normproj(T, K, N, eps, false, xn, ldxn, w_packed, ldw, y, ldy,
+                                           (hipStream_t)stream));
+}
+
+QKN_API int qkn_device_copy(void* dst, const void* src, int64_t nbytes, void* stream)
+{
+    if (nbytes < 0) return QKN_ERR_SHAPE;
+    if (nbytes == 0) return QKN_OK;
+    if (dst == nullptr || src == nullptr) return QKN_ERR_NULL;
+    if (overlap(span(dst, 1, nbytes, nbytes, 1), span(src, 1, nbytes, nbytes, 1)))
+        return QKN_ERR_ALIAS;
+    return hip_status(qkn::launch_copy(dst, src, nbytes, (hipStream_t)stream));
+}
+
+}  // extern "C"

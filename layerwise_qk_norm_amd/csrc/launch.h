@@ -1,0 +1,57 @@
+// Host-side launch interface between the C-ABI layer (api.cpp) and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qkn {
+
+// What a row launch computes for each row of its tensors.
+enum RowMode : int {
+    kFused = 0,    // sum of squares -> 1/rms over the row -> x * gamma * (1/rms)
+    kPartial = 1,  // sum of squares of the slice -> psq_out[row]
+    kApply = 2,    // psq_in[row] + ext[..][row] -> 1/rms over d_full -> x * gamma * (1/rms)
+};
+
+// One tensor (Q or K) of a row launch.
+struct RowSeg {
+    const void* x;       // [T, d] input, row stride ldx elements
+    void* y;             // [T, d] output (kFused / kApply), row stride ldy
+    const void* g;       // gamma [d] (kFused / kApply)
+    int64_t ldx, ldy;
+    int64_t d;           // columns processed
+    float inv_dfull;     // 1 / width the mean is taken over (d for kFused, d_full for kApply)
+    const float* psq_in; // kApply: own partial [T]
+    const float* ext;    // kApply: peers' partials [n_ext, T], row stride ld_ext
+    int64_t ld_ext;
+    int64_t n_ext;
+    float* psq_out;      // kPartial: [T]
+};
+
+struct RowJob {
+    RowSeg seg[2];       // seg[1] is used only when nseg == 2
+    int nseg;
+    int64_t T;
+    float eps;
+    int mode;            // RowMode
+    int bf16;            // storage of x / y: 1 = bf16, 0 = fp32
+    int gamma_bf16;      // storage of gamma: 1 = bf16, 0 = fp32
+};
+
+// Chooses the register-resident kernel (one wavefront per row group, 16-byte accesses) when
+// every tensor is 16-byte aligned and fits in registers; otherwise a workgroup-per-row
+// two-pass kernel (16-byte or element accesses).
+hipError_t launch_rows(const RowJob& job, hipStream_t stream);
+
+// W [K, N] (stride ldw) -> w_fold [N, K] (stride ldwf) = bf16(gamma[k] * W[k, n]).
+hipError_t launch_fold(int64_t K, int64_t N, const void* w, int64_t ldw, const void* gamma,
+                       int gamma_bf16, void* w_fold, int64_t ldwf, hipStream_t stream);
+
+// y [T, N] = bf16( (x [T, K] . w [N, K]^T) * (norm ? 1/rms(x row) : 1) ).
+hipError_t launch_normproj(int64_t T, int64_t K, int64_t N, float eps, bool norm,
+                           const void* x, int64_t ldx, const void* w, int64_t ldw, void* y,
+                           int64_t ldy, hipStream_t stream);
+
+hipError_t launch_copy(void* dst, const void* src, int64_t nbytes, hipStream_t stream);
+
+}  // namespace qkn

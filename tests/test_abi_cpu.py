@@ -1,0 +1,169 @@
+"""The C-ABI library without a GPU: it loads, exports what include/qknorm.h declares, and its
+argument validation answers before any HIP call (no compute calls here)."""
+
+import ctypes
+import math
+import os
+import shutil
+import subprocess
+
+import pytest
+
+from layerwise_qk_norm_amd import _lib
+
+OK, NULL, SHAPE, DTYPE, EPS, ALIAS, ALIGN, HIPERR = range(8)
+F32, BF16 = 0, 1
+
+
+def _gpu_present() -> bool:
+    # Counting devices does not initialise HIP; validation tests hand the library fake device
+    # addresses, which are only ever rejected, but they stay off machines with a GPU anyway.
+    try:
+        import torch
+
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+no_gpu = pytest.mark.skipif(_gpu_present(), reason="fake-pointer validation runs on CPU only")
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _lib.header_entry_points()
+    assert set(names) >= {"qknorm_fused", "qknorm_partial_sumsq", "qknorm_apply_with_stats",
+                          "normproj_fold_weight", "normproj_deferred", "normproj_unfused",
+                          "qkn_device_copy", "qkn_status_string", "qkn_last_hip_error"}
+    for n in names:
+        assert hasattr(L, n), n
+    nm = shutil.which("nm")
+    if nm:
+        out = subprocess.run([nm, "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                             text=True).stdout
+        exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+        assert set(names) <= exported
+        # nothing but the C entry points is exported from the library's own code
+        ours = {s for s in exported if s.startswith(("qkn", "qknorm", "normproj"))}
+        assert ours == set(names)
+
+
+def test_status_strings(L):
+    for s in range(8):
+        assert L.qkn_status_string(s)
+    assert L.qkn_status_string(99) == b"unknown status"
+    assert L.qkn_last_hip_error() == 0
+
+
+# Fake, never-dereferenced device addresses (16-byte aligned, far apart).
+A, B, C, D, G1, G2 = (0x7F0000000000 + i * 0x10000000 for i in range(6))
+
+
+def fused(L, T=4, eps=1e-6, dt=BF16, gdt=BF16, q=A, ldq=64, qo=B, ldqo=64, gq=G1, dq=64,
+          k=C, ldk=64, ko=D, ldko=64, gk=G2, dk=64):
+    return L.qknorm_fused(T, eps, dt, gdt, q, ldq, qo, ldqo, gq, dq, k, ldk, ko, ldko, gk, dk,
+                          None)
+
+
+@no_gpu
+def test_fused_validation(L):
+    assert fused(L, T=-1) == SHAPE
+    assert fused(L, dt=7) == DTYPE
+    assert fused(L, gdt=-1) == DTYPE
+    assert fused(L, eps=float("nan")) == EPS
+    assert fused(L, eps=-1.0) == EPS
+    assert fused(L, eps=math.inf) == EPS
+    assert fused(L, q=None) == NULL
+    assert fused(L, qo=None) == NULL
+    assert fused(L, gq=None) == NULL
+    assert fused(L, gk=None) == NULL
+    assert fused(L, dq=0) == SHAPE
+    assert fused(L, ldq=32) == SHAPE          # ld < d
+    assert fused(L, ldko=10) == SHAPE
+    # T == 0 is a no-op whatever the pointers
+    assert fused(L, T=0, q=None, qo=None, gq=None, k=None, ko=None, gk=None) == OK
+    # partial overlap of q_out with q (shifted by one row) is rejected; so is K's output
+    # landing on Q's input, or Q's output on a gamma
+    assert fused(L, qo=A + 128) == ALIAS
+    assert fused(L, ko=A) == ALIAS
+    assert fused(L, qo=G1) == ALIAS
+    assert fused(L, qo=A, ldqo=128, ldq=64) == ALIAS     # same base, different stride
+
+
+@no_gpu
+def test_partial_and_apply_validation(L):
+    P = L.qknorm_partial_sumsq
+    assert P(-1, BF16, A, 64, 64, B, C, 64, 64, D, None) == SHAPE
+    assert P(4, 5, A, 64, 64, B, C, 64, 64, D, None) == DTYPE
+    assert P(4, BF16, A, 64, 64, None, C, 64, 64, D, None) == NULL
+    assert P(4, BF16, A, 64, 65, B, C, 64, 64, D, None) == SHAPE
+    assert P(4, BF16, A, 64, 64, A, C, 64, 64, D, None) == ALIAS   # psq on top of q
+    assert P(4, BF16, A, 64, 64, B, C, 64, 64, B + 4, None) == ALIAS
+    assert P(0, BF16, None, 1, 1, None, None, 0, 0, None, None) == OK
+
+    def apply(T=4, eps=1e-6, n_ext=7, q=A, ldq=64, qo=B, ldqo=64, gq=G1, dl=64, df=512, pq=D,
+              eq=D + 0x1000, lde=4):
+        return L.qknorm_apply_with_stats(T, eps, BF16, BF16, n_ext, q, ldq, qo, ldqo, gq, dl, df,
+                                         pq, eq, lde, None, 0, None, 0, None, 0, 0, None, None, 0,
+                                         None)
+
+    assert apply(n_ext=-1) == SHAPE
+    assert apply(df=32) == SHAPE               # d_full < d_local
+    assert apply(lde=3) == SHAPE               # ld_ext < T
+    assert apply(eq=None) == NULL
+    assert apply(pq=None) == NULL
+    assert apply(eps=float("inf")) == EPS
+    assert apply(qo=D) == ALIAS                # output over the own partials
+    assert apply(qo=D + 0x1000 - 64) == ALIAS  # output running into ext
+
+
+@no_gpu
+def test_normproj_validation(L):
+    F = L.normproj_fold_weight
+    assert F(16, 16, F32, BF16, A, 16, G1, B, 16, None) == DTYPE
+    assert F(16, 16, BF16, BF16, A, 8, G1, B, 16, None) == SHAPE      # ldw < N
+    assert F(16, 16, BF16, BF16, A, 16, G1, B + 2, 16, None) == ALIGN
+    assert F(16, 16, BF16, BF16, A, 16, G1, A, 16, None) == ALIAS
+    assert F(16, 16, BF16, BF16, None, 16, G1, B, 16, None) == NULL
+    P = L.normproj_deferred
+    assert P(4, 16, 16, 1e-6, F32, A, 16, B, 16, C, 16, None) == DTYPE
+    assert P(4, 12, 16, 1e-6, BF16, A, 12, B, 12, C, 16, None) == ALIGN   # K % 8
+    assert P(4, 16, 16, 1e-6, BF16, A + 2, 16, B, 16, C, 16, None) == ALIGN
+    assert P(4, 16, 16, 1e-6, BF16, A, 16, B, 16, A + 32, 16, None) == ALIAS
+    assert P(4, 16, 16, -1.0, BF16, A, 16, B, 16, C, 16, None) == EPS
+    assert P(4, 16, 16, 1e-6, BF16, A, 16, B, 16, None, 16, None) == NULL
+    assert P(0, 16, 16, 1e-6, BF16, None, 16, None, 16, None, 16, None) == OK
+    U = L.normproj_unfused
+    assert U(4, 16, 16, 1e-6, BF16, BF16, A, 16, G1, B, 16, A, 16, C, 16, None) == ALIAS
+    assert U(4, 16, 16, 1e-6, BF16, BF16, A, 16, G1, B, 16, None, 16, C, 16, None) == NULL
+    assert U(4, 16, 16, 1e-6, BF16, 9, A, 16, G1, B, 16, D, 16, C, 16, None) == DTYPE
+    assert L.qkn_device_copy(A, A + 8, 64, None) == ALIAS
+    assert L.qkn_device_copy(A, B, -1, None) == SHAPE
+    assert L.qkn_device_copy(None, B, 0, None) == OK
+
+
+def test_library_has_gfx950_code_object():
+    """The shared object embeds a gfx950 offload bundle (checked on the file's bytes for the
+    target id the build embeds)."""
+    data = open(_lib.LIB_PATH, "rb").read()
+    assert b"gfx950" in data
+
+
+def test_python_binding_refuses_host_tensors():
+    torch = pytest.importorskip("torch")
+    import layerwise_qk_norm_amd as q
+
+    x = torch.zeros((2, 8), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        q.qknorm_fused(x, torch.ones(8, dtype=torch.bfloat16))
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "absent.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(ImportError):
+        _lib.lib()
