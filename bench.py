@@ -30,7 +30,8 @@ PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 matrix peak, published
 METRIC = "fused Q+K QK-Norm tokens/s + achieved HBM GB/s (% of peak), OLMo-7B shape, 1 GPU"
 ROTATE_BYTES = 1 << 30
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "qknorm_fused_olmo2_7b_T8192_pmc.md")
-KERNEL_SOURCES = ["layerwise_qk_norm_amd/csrc/rows.hip", "layerwise_qk_norm_amd/csrc/device.h"]
+KERNEL_SOURCES = ["layerwise_qk_norm_amd/csrc/rows_impl.h", "layerwise_qk_norm_amd/csrc/rows_inst.hip",
+                  "layerwise_qk_norm_amd/csrc/device.h"]
 
 
 def rows_source_hash() -> str:
@@ -301,7 +302,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": recorded_traffic(),
                      "algorithmic_bytes_per_launch": nbytes,
-                     "kernel": "rows_kernel<kFused, bf16, 8, 8> (qknorm_fused)"},
+                     "kernel": "rows_team_kernel<kFused, bf16, bf16, 3, 3> (qknorm_fused)"},
         "cpu_baseline": cpu,
         "cases": cases,
     }

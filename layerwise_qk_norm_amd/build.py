@@ -13,7 +13,16 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqknorm.so")
 ROOT = os.path.dirname(PKG)
 
-SOURCES = ["api.cpp", "rows.hip", "gemm.hip"]
+# (source, extra flags, object name); the row kernels are compiled once per storage pair
+UNITS = [
+    ("api.cpp", [], "api"),
+    ("rows.hip", [], "rows"),
+    ("rows_inst.hip", ["-DQKN_ROWS_BF=1", "-DQKN_ROWS_GBF=1"], "rows_bf16_gbf16"),
+    ("rows_inst.hip", ["-DQKN_ROWS_BF=1", "-DQKN_ROWS_GBF=0"], "rows_bf16_gf32"),
+    ("rows_inst.hip", ["-DQKN_ROWS_BF=0", "-DQKN_ROWS_GBF=1"], "rows_f32_gbf16"),
+    ("rows_inst.hip", ["-DQKN_ROWS_BF=0", "-DQKN_ROWS_GBF=0"], "rows_f32_gf32"),
+    ("gemm.hip", [], "gemm"),
+]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU instructions.
@@ -30,9 +39,10 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *CFLAGS]
+def _compile(unit) -> str:
+    src, extra, name = unit
+    obj = os.path.join(BUILD, name + ".o")
+    cmd = [hipcc(), *CFLAGS, *extra]
     if src.endswith(".cpp"):
         cmd += ["-x", "hip"]
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
@@ -49,8 +59,9 @@ def _compile(src: str) -> str:
 def build(verbose: bool = False) -> str:
     """Compile every source for gfx950 and link libqknorm.so; returns the library path."""
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+    workers = max(1, min(len(UNITS), os.cpu_count() or 1))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        objs = list(ex.map(_compile, UNITS))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)

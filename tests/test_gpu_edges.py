@@ -45,10 +45,11 @@ def test_empty_T_is_a_noop(Q):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("dq,dk", [(1, 3), (520, 4104), (8, 16), (4096, 512), (12288, 64),
-                                   (8192, 2048)])
+                                   (8192, 2048), (1024, 5120), (16384, 768), (20000, 16392)])
 def test_odd_and_wide_widths(Q, dtype, dq, dk):
-    """Widths that are not multiples of a wavefront's vector width, and rows wider than the
-    register-resident kernel holds (two-pass path); T ragged."""
+    """Widths that are not multiples of a wavefront's vector width, every team shape (1, 2 and 4
+    wavefronts per row, 1-8 vectors per lane, with partly filled last vectors), K wider than Q,
+    and rows wider than the register-resident kernel holds (two-pass path); T ragged."""
     rng = np.random.default_rng(dq * 7 + dk)
     T = 37
     q = inputs.random_rows(rng, T, dq, dtype, scale=1.5)
