@@ -82,6 +82,32 @@ class Timer:
         torch.cuda.synchronize()
         return start.elapsed_time(end) / iters  # ms per call
 
+    def run_graph(self, fn, per_graph, replays, warmup):
+        """The same launches captured into one HIP graph (per_graph calls, one per rotating
+        buffer set) and replayed: GPU time per call without the host's launch overhead."""
+        torch = self.torch
+        with torch.cuda.stream(self.stream):
+            for i in range(per_graph):
+                fn(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=self.stream):
+            for i in range(per_graph):
+                fn(i)
+        with torch.cuda.stream(self.stream):
+            for _ in range(warmup):
+                g.replay()
+            torch.cuda.synchronize()
+            start = torch.cuda.Event(enable_timing=True)
+            end = torch.cuda.Event(enable_timing=True)
+            start.record(self.stream)
+            for _ in range(replays):
+                g.replay()
+            end.record(self.stream)
+        torch.cuda.synchronize()
+        del g
+        return start.elapsed_time(end) / (replays * per_graph)
+
 
 def rotation_count(bytes_per_set):
     return max(1, -(-ROTATE_BYTES // bytes_per_set))
@@ -111,6 +137,7 @@ def fused_setup(torch, Q, inputs, cfg, T):
         qi, ki, qo, ko = sets[i % n]
         Q.qknorm_fused(qi, gq, ki, gk, eps=c["eps"], q_out=qo, k_out=ko)
 
+    step.sets = n
     return step, nbytes
 
 
@@ -134,6 +161,8 @@ def shard_setup(torch, Q, inputs, T):
         qi, ki, qo, ko, pq, pk = sets[i % n]
         Q.qknorm_apply_with_stats(qi, gq, pq, eq, 4096, ki, gk, pk, ek, 4096, eps=c["eps"],
                                   q_out=qo, k_out=ko)
+
+    k1.sets = k2.sets = n
 
     b1 = T * 2 * (512 * 2 + 4)
     b2 = T * 2 * (512 * 2 * 2 + 4 + 7 * 4) + 2 * 512 * 2
@@ -161,7 +190,16 @@ def normproj_setup(torch, Q, inputs, T, unfused=False):
 
     flops = 2.0 * T * K * N
     nbytes = T * K * 2 + K * N * 2 + T * N * 2
+    deferred.sets = unf.sets = n
     return (unf if unfused else deferred), flops, nbytes
+
+
+def time_case(timer, fn, iters, warmup):
+    """(eager ms per call, graph-replay ms per call)."""
+    eager = timer.run(fn, iters, warmup)
+    per_graph = max(fn.sets, 8 if fn.sets == 1 else fn.sets)
+    graph = timer.run_graph(fn, per_graph, max(2, iters // per_graph), 2)
+    return eager, graph
 
 
 # ----------------------------------------------------------------------------- CPU baseline
@@ -195,6 +233,9 @@ def main():
     ap.add_argument("--case-iters", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calib-copies", type=int, default=0,
+                    help="after the timed region, run this many qkn_device_copy launches of "
+                         "half the headline's algorithmic bytes (memory-counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -224,6 +265,17 @@ def main():
     print(f"# headline: fused Q+K [{T}, 4096] bf16: {ms * 1e3:.2f} us/call, {achieved:.0f} GB/s",
           file=sys.stderr, flush=True)
 
+    if args.calib_copies > 0:
+        half = (nbytes // 2) // 16 * 16
+        src = torch.empty(half, dtype=torch.uint8, device="cuda")
+        dst = torch.empty(half, dtype=torch.uint8, device="cuda")
+        with torch.cuda.stream(stream):
+            for _ in range(args.calib_copies):
+                Q.qkn_device_copy(dst, src)
+        torch.cuda.synchronize()
+        print(f"# calibration: {args.calib_copies} copies of {half} B", file=sys.stderr)
+        del src, dst
+
     cases = []
     if args.cases == "all":
         it, wu = args.case_iters, max(5, args.case_iters // 10)
@@ -239,23 +291,23 @@ def main():
                       "us_per_call": cms * 1e3, "GB_s": 2 * half / (cms * 1e-3) / 1e9})
         del bufs
 
-        for cfg, Ts in ((1, (64,)), (2, (1, 16, 256, 4096)), (3, (1, 512, 8192))):
+        for cfg, Ts in ((1, (64,)), (2, (1, 16, 256, 4096, 8192)), (3, (1, 512, 8192))):
             for t in Ts:
                 fn, b = fused_setup(torch, Q, inputs, cfg, t)
-                cms = timer.run(fn, it, wu)
+                cms, gms = time_case(timer, fn, it, wu)
                 cases.append({"case": f"qknorm_fused cfg{cfg} {inputs.CONFIGS[cfg]['name']} T={t}",
-                              "us_per_call": cms * 1e3, "GB_s": b / (cms * 1e-3) / 1e9,
-                              "frac_hbm": b / (cms * 1e-3) / 1e9 / PEAK_HBM_GBS})
+                              "us_per_call": cms * 1e3, "us_per_call_graph": gms * 1e3,
+                              "GB_s": b / (gms * 1e-3) / 1e9,
+                              "frac_hbm": b / (gms * 1e-3) / 1e9 / PEAK_HBM_GBS})
                 del fn
                 torch.cuda.empty_cache()
 
         k1, k2, b1, b2 = shard_setup(torch, Q, inputs, 131072)
-        m1 = timer.run(k1, it, wu)
-        m2 = timer.run(k2, it, wu)
-        for name, m, b in (("qknorm_partial_sumsq", m1, b1), ("qknorm_apply_with_stats", m2, b2)):
+        for name, fn, b in (("qknorm_partial_sumsq", k1, b1), ("qknorm_apply_with_stats", k2, b2)):
+            m, gm = time_case(timer, fn, it, wu)
             cases.append({"case": f"{name} cfg4 tp8-shard T=131072", "us_per_call": m * 1e3,
-                          "GB_s": b / (m * 1e-3) / 1e9,
-                          "frac_hbm": b / (m * 1e-3) / 1e9 / PEAK_HBM_GBS})
+                          "us_per_call_graph": gm * 1e3, "GB_s": b / (gm * 1e-3) / 1e9,
+                          "frac_hbm": b / (gm * 1e-3) / 1e9 / PEAK_HBM_GBS})
         del k1, k2
         torch.cuda.empty_cache()
 
@@ -264,12 +316,12 @@ def main():
                 if unfused and t == 1:
                     continue
                 fn, flops, b = normproj_setup(torch, Q, inputs, t, unfused)
-                cms = timer.run(fn, it, wu)
+                cms, gms = time_case(timer, fn, it, wu)
                 name = "normproj_unfused" if unfused else "normproj_deferred"
                 entry = {"case": f"{name} cfg5 flashnorm-2048 T={t}", "us_per_call": cms * 1e3,
-                         "TFLOP_s": flops / (cms * 1e-3) / 1e12}
+                         "us_per_call_graph": gms * 1e3, "TFLOP_s": flops / (gms * 1e-3) / 1e12}
                 if t == 1:
-                    entry["GB_s"] = b / (cms * 1e-3) / 1e9
+                    entry["GB_s"] = b / (gms * 1e-3) / 1e9
                     entry["frac_hbm"] = entry["GB_s"] / PEAK_HBM_GBS
                 else:
                     entry["frac_mfma_bf16"] = entry["TFLOP_s"] / PEAK_BF16_TFLOPS
