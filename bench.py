@@ -29,6 +29,7 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 matrix peak, published
 METRIC = "fused Q+K QK-Norm tokens/s + achieved HBM GB/s (% of peak), OLMo-7B shape, 1 GPU"
 ROTATE_BYTES = 1 << 30
+MAX_SETS = 128  # small workloads are latency-bound; their graphs stay a few hundred nodes long
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "qknorm_fused_olmo2_7b_T8192_pmc.md")
 KERNEL_SOURCES = ["layerwise_qk_norm_amd/csrc/rows_impl.h", "layerwise_qk_norm_amd/csrc/rows_inst.hip",
                   "layerwise_qk_norm_amd/csrc/device.h"]
@@ -110,7 +111,8 @@ class Timer:
 
 
 def rotation_count(bytes_per_set):
-    return max(1, -(-ROTATE_BYTES // bytes_per_set))
+    """Buffer sets so that successive launches sweep >= 1 GiB (capped at MAX_SETS)."""
+    return min(MAX_SETS, max(1, -(-ROTATE_BYTES // bytes_per_set)))
 
 
 def dev(torch, a):
