@@ -2,14 +2,23 @@
 // ("FlashNorm: Fast Normalization for Transformers", abstract, items (i) and (ii)), plus the
 // one-time weight fold and a plain streaming copy used for calibration.
 //
-// Matrix-core kernel: y[t, n] = r_t * sum_k x[t, k] * w[n, k] with both operands K-contiguous
-// (the fold writes W' transposed). A 256-thread workgroup owns a 128 x 128 output tile; its
-// four wavefronts each own 64 x 64 as 2 x 2 blocks of v_mfma_f32_32x32x16_bf16. Tiles of
-// 128 x 64 of x and W' are staged through LDS (row pitch padded by 16 bytes so the 16-byte
-// fragment reads of 16 consecutive rows hit distinct banks), with the next tile's global loads
-// in flight while the current tile feeds the matrix cores. The same x vectors that go to LDS
-// are squared and summed by the VALU, so 1/rms is ready at the epilogue without another pass
-// over x: the reduction runs beside the product instead of before it.
+// y[t, n] = r_t * sum_k x[t, k] * w[n, k] with both operands K-contiguous (the fold writes W'
+// transposed), on v_mfma_f32_32x32x16_bf16. The 1/rms factor comes from the same x values that
+// feed the matrix cores, squared and summed on the VALU while the MFMAs run, so no extra pass
+// over x is needed and the reduction proceeds beside the product instead of before it.
+//
+// Pipelined kernel (K a multiple of the k-tile, N of 8): a workgroup owns a BM x BN output tile.
+// Its k-tiles of x and W' stream into an NST-deep LDS ring by direct global->LDS DMA
+// (global_load_lds_dwordx4, 1 KB per wavefront instruction), NST-1 tiles ahead of the one being
+// multiplied; each tile row's 16-byte chunks are XOR-swizzled so the fragment reads of 16
+// consecutive rows fall in 16 distinct bank groups. Wavefronts own WM x WN sub-tiles of 32 x 32
+// MFMA blocks; those in the first column also accumulate the rows' sums of squares from the x
+// fragments they already hold. The epilogue scales by 1/rms, rounds to bf16 and stages the tile
+// through LDS so each lane stores 16 contiguous bytes. Blocks are remapped so that each XCD
+// works on a contiguous range of row panels (one L2 holds each x panel).
+//
+// Generic kernel (any K % 8 == 0, any N): 128 x 128 tiles through padded LDS rows with register
+// staging of the next k-tile.
 //
 // Small T (<= 16) is a matrix-vector product bound by streaming W' once: a wavefront per pair
 // of output columns, fp32 dot products reduced across the wave.
@@ -36,6 +45,206 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
+
+// ------------------------------------------------------------------------------------------
+// Pipelined kernel.
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from global memory straight into LDS at lds_off + 16 * lane. Issued through
+// inline assembly so that the compiler does not wait for it before unrelated LDS reads; the
+// kernel awaits completion with s_waitcnt vmcnt (vector loads complete in issue order). One
+// wait state separates the M0 write from the DMA (a gfx9-family hazard). M0 is declared
+// clobbered; no other instruction in these kernels uses it (checked in the generated code).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_off)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 ::"s"(__builtin_amdgcn_readfirstlane(lds_off)), "v"(gsrc) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    // s_waitcnt fields: vmcnt[3:0] and [15:14], expcnt[6:4] = 7 (no wait), lgkmcnt[11:8] = 15
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Physical 16-byte chunk of logical chunk kc in tile row r. ds_read_b128 is served 16 lanes
+// (256 bytes, 64 banks) at a time and the fragment reads touch 16 consecutive rows at one
+// logical chunk: rows of 128 B (k-tile 64) pair up per 256 B, so kc is xored with
+// (r >> 1) & 7; rows of 64 B (k-tile 32) come four per 256 B: (r >> 2) & 3.
+template <int BK>
+__device__ __forceinline__ int swz(int kc, int r)
+{
+    return BK == 64 ? (kc ^ ((r >> 1) & 7)) : (kc ^ ((r >> 2) & 3));
+}
+
+template <int BM, int BN, int WM, int WN, int NST, int BK, bool NORM>
+__global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
+    int64_t T, int64_t K, int64_t N, float eps, float inv_k, const uint16_t* __restrict__ x,
+    int64_t ldx, const uint16_t* __restrict__ w, int64_t ldw, uint16_t* __restrict__ y,
+    int64_t ldy, int nbm, int nbn)
+{
+    constexpr int NW = WM * WN, NT = NW * kWave;
+    constexpr int ROWB = BK * 2;            // bytes per tile row
+    constexpr int RPC = 1024 / ROWB;        // tile rows per 1 KB DMA chunk
+    constexpr int LPR = ROWB / 16;          // lanes per tile row within a chunk
+    constexpr int STAGE_A = BM * ROWB, STAGE = (BM + BN) * ROWB;
+    constexpr int CA = BM / RPC, CT = (BM + BN) / RPC;
+    static_assert(CT % NW == 0, "DMA chunks must divide among the wavefronts");
+    constexpr int CPW = CT / NW;            // DMA instructions per wavefront per k-tile
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int TM = WTM / 32, TN = WTN / 32;
+    constexpr int CP = BN + 8;              // epilogue tile pitch (bf16)
+    constexpr int PIPE = NST * STAGE, CTILE = BM * CP * 2;
+    constexpr int SMEM = PIPE > CTILE ? PIPE : CTILE;
+    __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+    __shared__ float rs_lds[BM];
+
+    const int tid = (int)threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int wm = wave / WN, wn = wave % WN;
+    const int nb = nbm * nbn;
+    int bid = (int)blockIdx.x;
+    if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+    const int64_t m0 = (int64_t)(bid / nbn) * BM, n0 = (int64_t)(bid % nbn) * BN;
+
+    // Source of each DMA chunk this lane fetches (fixed across k). Out-of-range rows are clamped
+    // to the last valid row: they only feed output rows / columns that are never stored.
+    const int lrow = lane / LPR;
+    const uint16_t* src[CPW];
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+        const int chunk = wave * CPW + c;
+        const int trow = (chunk < CA ? chunk : chunk - CA) * RPC + lrow;
+        const int lkc = swz<BK>(lane % LPR, trow);  // the logical chunk landing at lane % LPR
+        if (chunk < CA) {
+            const int64_t r = m0 + trow < T ? m0 + trow : T - 1;
+            src[c] = x + r * ldx + lkc * 8;
+        } else {
+            const int64_t r = n0 + trow < N ? n0 + trow : N - 1;
+            src[c] = w + r * ldw + lkc * 8;
+        }
+    }
+    auto issue = [&](int slot, int64_t k0) {
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) {
+            const int chunk = wave * CPW + c;
+            char* dst = smem + slot * STAGE + chunk * 1024;
+            dma16((const void*)(src[c] + k0), (uint32_t)(uintptr_t)(lds_void*)dst);
+        }
+    };
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+    float ssq[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) ssq[i] = 0.0f;
+
+    const int nk = (int)(K / BK);
+#pragma unroll
+    for (int s = 0; s < NST - 1; ++s)
+        if (s < nk) issue(s, (int64_t)s * BK);
+
+    const int frow = lane & 31, fk = lane >> 5;
+    for (int kt = 0; kt < nk; ++kt) {
+        // k-tile kt must have landed; up to NST-2 later tiles stay in flight
+        const int later = (nk - 1 - kt) < (NST - 2) ? (nk - 1 - kt) : (NST - 2);
+        if constexpr (NST >= 4) {
+            if (later >= 2) wait_vmcnt<2 * CPW>();
+            else if (later == 1) wait_vmcnt<CPW>();
+            else wait_vmcnt<0>();
+        } else if constexpr (NST == 3) {
+            if (later >= 1) wait_vmcnt<CPW>();
+            else wait_vmcnt<0>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        __syncthreads();  // every wavefront's DMA has landed; slot (kt-1) % NST is free again
+        if (kt + NST - 1 < nk) issue((kt + NST - 1) % NST, (int64_t)(kt + NST - 1) * BK);
+        const char* As = smem + (kt % NST) * STAGE;
+        const char* Bs = As + STAGE_A;
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            u32x4 af[TM], bfr[TN];
+            const int kc = ks * 2 + fk;
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int r = wm * WTM + i * 32 + frow;
+                af[i] = *(const u32x4*)(As + r * ROWB + (swz<BK>(kc, r) << 4));
+            }
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int r = wn * WTN + j * 32 + frow;
+                bfr[j] = *(const u32x4*)(Bs + r * ROWB + (swz<BK>(kc, r) << 4));
+            }
+            if constexpr (NORM) {
+                if (wn == 0) {
+#pragma unroll
+                    for (int i = 0; i < TM; ++i) {
+                        const u32x4 v = af[i];
+                        float s = ssq[i];
+                        s = fmaf(bf16_lo(v.x), bf16_lo(v.x), s); s = fmaf(bf16_hi(v.x), bf16_hi(v.x), s);
+                        s = fmaf(bf16_lo(v.y), bf16_lo(v.y), s); s = fmaf(bf16_hi(v.y), bf16_hi(v.y), s);
+                        s = fmaf(bf16_lo(v.z), bf16_lo(v.z), s); s = fmaf(bf16_hi(v.z), bf16_hi(v.z), s);
+                        s = fmaf(bf16_lo(v.w), bf16_lo(v.w), s); s = fmaf(bf16_hi(v.w), bf16_hi(v.w), s);
+                        ssq[i] = s;
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+        }
+    }
+
+    if constexpr (NORM) {
+        // lanes l and l + 32 summed the two halves of each 16-wide k step of the same row
+        if (wn == 0) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const float s = ssq[i] + __shfl_xor(ssq[i], 32);
+                if (lane < 32) rs_lds[wm * WTM + i * 32 + lane] = rsqrtf(s * inv_k + eps);
+            }
+        }
+    }
+    __syncthreads();  // all DMA consumed (the last k-tile waited for vmcnt 0); 1/rms visible
+
+    // accumulator layout of a 32 x 32 block: lane holds column lane % 32 and, for e in 0..15,
+    // row 8 * (e / 4) + 4 * (lane / 32) + e % 4
+    uint16_t* ct = (uint16_t*)smem;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int r = wm * WTM + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                const int c = wn * WTN + j * 32 + (lane & 31);
+                float v = acc[i][j][e];
+                if constexpr (NORM) v *= rs_lds[r];
+                ct[r * CP + c] = to_bf16(v);
+            }
+    __syncthreads();
+    constexpr int C8 = BN / 8;
+    for (int idx = tid; idx < BM * C8; idx += NT) {
+        const int r = idx / C8, c8 = idx % C8;
+        const int64_t gm = m0 + r, gn = n0 + c8 * 8;
+        if (gm < T && gn < N) *(u32x4*)(y + gm * ldy + gn) = *(const u32x4*)(ct + r * CP + c8 * 8);
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Generic kernel.
 
 template <bool NORM>
 __global__ __launch_bounds__(kThreads) void normproj_mfma_kernel(
@@ -279,6 +488,23 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(char* __restrict__ dst,
     for (int64_t i = done + tid; i < nbytes; i += stride) dst[i] = src[i];
 }
 
+template <int BM, int BN, int WM, int WN, int NST, int BK>
+hipError_t launch_pipe(int64_t T, int64_t K, int64_t N, float eps, float inv_k, bool norm,
+                       const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
+                       uint16_t* y, int64_t ldy, hipStream_t st)
+{
+    const int64_t nbm = (T + BM - 1) / BM, nbn = (N + BN - 1) / BN;
+    if (nbm * nbn > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)(nbm * nbn)), block(WM * WN * kWave);
+    if (norm)
+        hipLaunchKernelGGL((normproj_pipe_kernel<BM, BN, WM, WN, NST, BK, true>), grid, block, 0,
+                           st, T, K, N, eps, inv_k, x, ldx, w, ldw, y, ldy, (int)nbm, (int)nbn);
+    else
+        hipLaunchKernelGGL((normproj_pipe_kernel<BM, BN, WM, WN, NST, BK, false>), grid, block, 0,
+                           st, T, K, N, eps, inv_k, x, ldx, w, ldw, y, ldy, (int)nbm, (int)nbn);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_normproj(int64_t T, int64_t K, int64_t N, float eps, bool norm,
@@ -301,6 +527,18 @@ hipError_t launch_normproj(int64_t T, int64_t K, int64_t N, float eps, bool norm
             hipLaunchKernelGGL(normproj_gemv_kernel<false>, dim3((unsigned)nblk), dim3(kThreads), 0,
                                st, (int)T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp, ldy);
         return hipGetLastError();
+    }
+    const bool pipe_ok = N % 8 == 0 && ldy % 8 == 0 && ((uintptr_t)y & 15u) == 0;
+    const int64_t big_tiles = ((T + 255) / 256) * ((N + 255) / 256);
+    if (pipe_ok && K % 32 == 0 && big_tiles >= 512) {
+        // many output tiles: 256 x 256 per workgroup of 8 wavefronts, k-tiles of 32, 4 stages
+        return launch_pipe<256, 256, 4, 2, 4, 32>(T, K, N, eps, inv_k, norm, xp, ldx, wp, ldw, yp,
+                                                  ldy, st);
+    }
+    if (pipe_ok && K % 64 == 0) {
+        // 128 x 128 per workgroup of 4 wavefronts, k-tiles of 64, 2 stages (2 workgroups per CU)
+        return launch_pipe<128, 128, 2, 2, 2, 64>(T, K, N, eps, inv_k, norm, xp, ldx, wp, ldw, yp,
+                                                  ldy, st);
     }
     const int64_t nbm = (T + kBM - 1) / kBM, nbn = (N + kBN - 1) / kBN;
     if (nbm * nbn > 0x7fffffff) return hipErrorInvalidConfiguration;

@@ -184,8 +184,13 @@ def test_normproj_unfused_baseline(Q):
 
 
 @pytest.mark.parametrize("T,K,N", [(5, 256, 130), (16, 1032, 64), (17, 1024, 520),
-                                   (300, 264, 200), (129, 2048, 2048)])
+                                   (300, 264, 200), (129, 2048, 2048), (8200, 1056, 4104),
+                                   (8200, 1024, 4104)])
 def test_normproj_ragged(Q, T, K, N):
+    """Every kernel of the projection: the matrix-vector path (T <= 16), the generic tile
+    kernel (K not a multiple of 32), and both pipelined tilings (128 x 128 and 256 x 256 with
+    k-tiles of 64 and 32), with T and N not multiples of the tile; large cases are checked on a
+    sample of rows."""
     rng = np.random.default_rng(T + K + N)
     x = inputs.random_rows(rng, T, K, "bf16")
     w = inputs.random_rows(rng, K, N, "bf16", scale=0.02)
@@ -196,8 +201,10 @@ def test_normproj_ragged(Q, T, K, N):
     y = Q.normproj_deferred(to_dev(x), wf, eps=1e-6)
     sync()
     assert np.array_equal(to_host(wf), wf_ref.T)
-    check_projection(to_host(y), oracle.normproj(x, wf_ref, 1e-6),
-                     projection_bound(x, wf_ref, 1e-6), f"T={T} K={K} N={N}")
+    rows = sample_rows(T, n=256, seed=T)
+    xs = np.ascontiguousarray(x[rows])
+    check_projection(to_host(y)[rows], oracle.normproj(xs, wf_ref, 1e-6),
+                     projection_bound(xs, wf_ref, 1e-6), f"T={T} K={K} N={N}")
 
 
 def test_normproj_strided_rows(Q):
