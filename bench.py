@@ -232,6 +232,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--tokens", type=int, default=8192)
     ap.add_argument("--cases", default="all", help="'all' or 'none': per-workload timings")
+    ap.add_argument("--only", default="",
+                    help="comma-separated prefixes: time only the cases whose entry point "
+                         "starts with one of them (e.g. 'normproj,qknorm_partial')")
     ap.add_argument("--case-iters", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -282,19 +285,25 @@ def main():
     if args.cases == "all":
         it, wu = args.case_iters, max(5, args.case_iters // 10)
 
+        def want(name):
+            return not args.only or any(name.startswith(p) for p in args.only.split(","))
+
         # empirical copy ceiling over the same bytes (read nbytes/2, write nbytes/2)
         half = (nbytes // 2) // 16 * 16
         n_copy = rotation_count(2 * half)
         bufs = [(torch.empty(half, dtype=torch.uint8, device="cuda"),
                  torch.empty(half, dtype=torch.uint8, device="cuda")) for _ in range(n_copy)]
-        cms = timer.run(lambda i: Q.qkn_device_copy(bufs[i % n_copy][1], bufs[i % n_copy][0]),
-                        it, wu)
-        cases.append({"case": f"device copy {half} B (same traffic as the headline)",
-                      "us_per_call": cms * 1e3, "GB_s": 2 * half / (cms * 1e-3) / 1e9})
+        if want("qkn_device_copy"):
+            cms = timer.run(lambda i: Q.qkn_device_copy(bufs[i % n_copy][1], bufs[i % n_copy][0]),
+                            it, wu)
+            cases.append({"case": f"device copy {half} B (same traffic as the headline)",
+                          "us_per_call": cms * 1e3, "GB_s": 2 * half / (cms * 1e-3) / 1e9})
         del bufs
 
         for cfg, Ts in ((1, (64,)), (2, (1, 16, 256, 4096, 8192)), (3, (1, 512, 8192))):
             for t in Ts:
+                if not want("qknorm_fused"):
+                    continue
                 fn, b = fused_setup(torch, Q, inputs, cfg, t)
                 cms, gms = time_case(timer, fn, it, wu)
                 cases.append({"case": f"qknorm_fused cfg{cfg} {inputs.CONFIGS[cfg]['name']} T={t}",
@@ -306,6 +315,8 @@ def main():
 
         k1, k2, b1, b2 = shard_setup(torch, Q, inputs, 131072)
         for name, fn, b in (("qknorm_partial_sumsq", k1, b1), ("qknorm_apply_with_stats", k2, b2)):
+            if not want(name):
+                continue
             m, gm = time_case(timer, fn, it, wu)
             cases.append({"case": f"{name} cfg4 tp8-shard T=131072", "us_per_call": m * 1e3,
                           "us_per_call_graph": gm * 1e3, "GB_s": b / (gm * 1e-3) / 1e9,
@@ -315,7 +326,8 @@ def main():
 
         for t in (1, 2048, 16384):
             for unfused in (False, True):
-                if unfused and t == 1:
+                if (unfused and t == 1) or not want(
+                        "normproj_unfused" if unfused else "normproj_deferred"):
                     continue
                 fn, flops, b = normproj_setup(torch, Q, inputs, t, unfused)
                 cms, gms = time_case(timer, fn, it, wu)
