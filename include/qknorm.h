@@ -28,7 +28,8 @@
  *   - Misaligned pointers or strides are accepted by the row operations (a scalar-load path
  *     runs instead of the 16-byte one). The norm-then-project calls need 16-byte aligned
  *     rows (QKN_ERR_ALIGN otherwise).
- *   - Results are deterministic: no atomics, fixed reduction order.
+ *   - Results are deterministic: fixed reduction orders, no atomic read-modify-write (the shard
+ *     mailbox flags are device-coherent stores and loads).
  */
 #ifndef QKNORM_H
 #define QKNORM_H
@@ -111,6 +112,59 @@ QKN_API int qknorm_apply_with_stats(int64_t T, float eps, int dtype, int gamma_d
                                     const void* gamma_k, int64_t dk_local, int64_t dk_full,
                                     const float* psq_k, const float* ext_k, int64_t ld_ext_k,
                                     void* stream);
+
+/*
+ * qknorm_shard_fused - the shard stage in ONE pass over this rank's slice.
+ *
+ * ("SwiftQK: ...", abstract: exchange only scalar statistics, overlapping the remaining
+ * peer-to-peer reduction with independent element-wise work in a deadlock-safe persistent
+ * kernel.) Computes exactly what qknorm_partial_sumsq followed by qknorm_apply_with_stats
+ * computes, reading x once: for each block of qknorm_shard_flag_rows() rows it
+ *   1. sums squares of the slice's rows and stores them to psq_*_out [T] (fp32);
+ *   2. if own_ready != NULL, stores `epoch` to own_ready[t * nfb + b] (t = 0 for Q, 1 for K,
+ *      nfb = ceil(T / flag rows)) once the partials of that block are stored device-coherently;
+ *   3. if peer_ready != NULL, waits until peer_ready[(e * 2 + t) * nfb + b] == epoch for every
+ *      peer e < n_ext (device-coherent polls; at most max_spin polls, then sets *timed_out = 1
+ *      and carries on with whatever the mailbox holds), then reads the mailbox coherently;
+ *   4. S = own + ext[0][row] + ... + ext[n_ext-1][row]  (fp32, in this order),
+ *      out = x * gamma * (1 / sqrt(S / d_full + eps)).
+ * ext_* are the mailboxes the peers fill ([n_ext, T] fp32, row stride ld_ext >= T).
+ * With peer_ready != NULL the grid is persistent and occupies at most three quarters of the
+ * device's resident workgroups, so a producer of the flags running on another stream of the
+ * same device always makes progress.
+ *   epoch     non-zero (flags start at zero); n_ext <= 64 when peer_ready != NULL
+ *   timed_out device int (required when peer_ready != NULL), set to 1 on a timeout, never
+ *             cleared by the library
+ *   slices    16-byte aligned, ld * sizeof(dtype) and d_local multiples of 16 bytes
+ *             (QKN_ERR_ALIGN otherwise), d_local <= 2048 bf16 / 1024 fp32 (QKN_ERR_SHAPE)
+ * Other arguments as for qknorm_apply_with_stats; K optional in the same way.
+ */
+QKN_API int qknorm_shard_fused(int64_t T, float eps, int dtype, int gamma_dtype, int64_t n_ext,
+                               const void* q, int64_t ldq, void* q_out, int64_t ldq_out,
+                               const void* gamma_q, int64_t dq_local, int64_t dq_full,
+                               float* psq_q_out, const float* ext_q, int64_t ld_ext_q,
+                               const void* k, int64_t ldk, void* k_out, int64_t ldk_out,
+                               const void* gamma_k, int64_t dk_local, int64_t dk_full,
+                               float* psq_k_out, const float* ext_k, int64_t ld_ext_k,
+                               const uint32_t* peer_ready, uint32_t* own_ready, uint32_t epoch,
+                               int64_t max_spin, int* timed_out, void* stream);
+
+/*
+ * qknorm_shard_publish - a peer's side of the mailbox protocol of qknorm_shard_fused.
+ *
+ * For every peer e < n_ext and row block b: copies part_*[e * ld_part + row] into
+ * ext_*[e * ld_ext + row] for the block's rows with device-coherent stores, waits until they
+ * are acknowledged, then stores `epoch` to ready[(e * 2 + t) * nfb + b]. Under tensor parallelism each rank does
+ * this for its own slot in every peer's mailbox; on one GPU it stands in for the peers.
+ * part_* [n_ext, T] fp32 (row stride ld_part >= T); K optional (part_k == ext_k == NULL).
+ */
+QKN_API int qknorm_shard_publish(int64_t T, int64_t n_ext, const float* part_q, int64_t ld_part_q,
+                                 float* ext_q, int64_t ld_ext_q, const float* part_k,
+                                 int64_t ld_part_k, float* ext_k, int64_t ld_ext_k,
+                                 uint32_t* ready, uint32_t epoch, void* stream);
+
+/* Rows per flag of the shard mailbox protocol (16). */
+QKN_API int64_t qknorm_shard_flag_rows(void);
 
 /*
  * normproj_fold_weight - fold the norm weights into the following projection (once, offline).

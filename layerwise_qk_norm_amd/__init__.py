@@ -6,8 +6,11 @@ include/qknorm.h); this package is its thin Python binding plus the seeded input
 
 from ._lib import (QKN_BF16, QKN_F32, QknError, lib, normproj_deferred, normproj_fold_weight,
                    normproj_unfused, qkn_device_copy, qknorm_apply_with_stats, qknorm_fused,
-                   qknorm_partial_sumsq)
+                   qknorm_partial_sumsq, qknorm_shard_flag_rows, qknorm_shard_fused,
+                   qknorm_shard_publish, shard_flag_blocks)
 
 __all__ = ["QKN_BF16", "QKN_F32", "QknError", "lib", "normproj_deferred",
            "normproj_fold_weight", "normproj_unfused", "qkn_device_copy",
-           "qknorm_apply_with_stats", "qknorm_fused", "qknorm_partial_sumsq"]
+           "qknorm_apply_with_stats", "qknorm_fused", "qknorm_partial_sumsq",
+           "qknorm_shard_flag_rows", "qknorm_shard_fused", "qknorm_shard_publish",
+           "shard_flag_blocks"]

@@ -22,6 +22,7 @@ UNITS = [
     ("rows_inst.hip", ["-DQKN_ROWS_BF=0", "-DQKN_ROWS_GBF=1"], "rows_f32_gbf16"),
     ("rows_inst.hip", ["-DQKN_ROWS_BF=0", "-DQKN_ROWS_GBF=0"], "rows_f32_gf32"),
     ("gemm.hip", [], "gemm"),
+    ("shard.hip", [], "shard"),
 ]
 ARCH = "gfx950"
 

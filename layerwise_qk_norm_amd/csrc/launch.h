@@ -54,4 +54,24 @@ hipError_t launch_normproj(int64_t T, int64_t K, int64_t N, float eps, bool norm
 
 hipError_t launch_copy(void* dst, const void* src, int64_t nbytes, hipStream_t stream);
 
+// Single-launch shard stage (partial sums, publication, wait for peers, aggregation, scale).
+struct ShardArgs {
+    RowSeg seg[2];               // x, y, g, ldx, ldy, d (slice), inv_dfull, ext, ld_ext, psq_out
+    int nseg;
+    int64_t T;
+    float eps;
+    int64_t n_ext;
+    int bf16, gamma_bf16;
+    const uint32_t* peer_ready;  // [n_ext][2][ceil(T / flag rows)] or null
+    uint32_t* own_ready;         // [2][ceil(T / flag rows)] or null
+    uint32_t epoch;
+    int64_t max_spin;
+    int* timed_out;
+};
+hipError_t launch_shard_fused(const ShardArgs& args, hipStream_t stream);
+hipError_t launch_shard_publish(int64_t T, int64_t n_ext, int nseg, const float* const* src,
+                                const int64_t* ld_src, float* const* dst, const int64_t* ld_dst,
+                                uint32_t* ready, uint32_t epoch, hipStream_t stream);
+int64_t shard_flag_rows();
+
 }  // namespace qkn
