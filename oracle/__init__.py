@@ -54,9 +54,21 @@ def lib() -> ctypes.CDLL:
         L.oracle_normproj_unfused.argtypes = [i64, i64, i64, dbl, ci, vp, i64, ci, vp, ci, vp,
                                               i64, vp, i64]
         L.oracle_matmul.argtypes = [i64, i64, i64, ci, vp, i64, ci, vp, i64, vp, i64]
+        L.oracle_qk_chain.argtypes = [i64, i64, i64, i64, dbl, dbl, ci, vp, i64, ci, vp, ci, vp,
+                                      i64, vp, i64, ci, vp, vp, vp, vp, vp]
+        L.oracle_qk_eliminated.argtypes = [i64, i64, i64, i64, dbl, dbl, ci, ci, vp, i64, ci, vp,
+                                           i64, vp, i64, ci, vp, vp, vp, vp, vp]
+        L.oracle_layernorm_rows.argtypes = [i64, i64, dbl, ci, vp, i64, ci, vp, ci, vp, vp, i64]
+        L.oracle_colsum.argtypes = [i64, i64, ci, vp, i64, vp]
+        L.oracle_normproj_layernorm.argtypes = [i64, i64, i64, dbl, ci, vp, i64, ci, vp, i64, ci,
+                                                vp, ci, vp, vp, i64]
+        L.oracle_layernorm_proj_unfused.argtypes = [i64, i64, i64, dbl, ci, vp, i64, ci, vp, ci,
+                                                    vp, ci, vp, i64, vp, i64]
         for f in ("oracle_round_bf16_array", "oracle_rmsnorm_rows", "oracle_partial_sumsq",
                   "oracle_apply_with_stats", "oracle_fold_weight", "oracle_normproj",
-                  "oracle_normproj_unfused", "oracle_matmul"):
+                  "oracle_normproj_unfused", "oracle_matmul", "oracle_qk_chain",
+                  "oracle_qk_eliminated", "oracle_layernorm_rows", "oracle_colsum",
+                  "oracle_normproj_layernorm", "oracle_layernorm_proj_unfused"):
             getattr(L, f).restype = None
         _lib = L
     return _lib
@@ -175,4 +187,95 @@ def matmul(a, b) -> np.ndarray:
     assert K == K2
     y = np.empty((T, N), dtype=np.float64)
     lib().oracle_matmul(T, K, N, _code(a), _ptr(a), K, _code(b), _ptr(b), N, _ptr(y), N)
+    return y
+
+
+def _opt(a):
+    """(storage code, contiguous array or None) of an optional vector."""
+    if a is None:
+        return 0, None
+    a = _c(a)
+    return _code(a), a
+
+
+def qk_chain(x, gamma_pre, wq, wk, gamma_q, gamma_k, eps_pre: float, eps_qk: float):
+    """Pre-attention RMSNorm, Q and K projections (wq [K, nq], wk [K, nk]), then layerwise
+    QK-Norm of each. Returns (yq [T, nq], yk [T, nk])."""
+    x, wq, wk = _c(x), _c(wq), _c(wk)
+    T, K = x.shape
+    nq, nk = wq.shape[1], wk.shape[1]
+    assert wq.shape[0] == K and wk.shape[0] == K and _code(wq) == _code(wk)
+    g1dt, g1 = _opt(gamma_pre)
+    gq, gk = _c(gamma_q), _c(gamma_k)
+    assert _code(gq) == _code(gk)
+    work = np.empty(K + nq + nk, dtype=np.float64)
+    yq = np.empty((T, nq), dtype=np.float64)
+    yk = np.empty((T, nk), dtype=np.float64)
+    lib().oracle_qk_chain(T, K, nq, nk, float(eps_pre), float(eps_qk), _code(x), _ptr(x), K,
+                          g1dt, _ptr(g1), _code(wq), _ptr(wq), nq, _ptr(wk), nk, _code(gq),
+                          _ptr(gq), _ptr(gk), _ptr(work), _ptr(yq), _ptr(yk))
+    return yq, yk
+
+
+def qk_eliminated(x, wqf, wkf, gamma_q, gamma_k, eps_qk: float, eps_pre: float = 0.0,
+                  exact: bool = False):
+    """Projection with the pre-norm weight folded in and no pre-norm (wqf [K, nq], wkf
+    [K, nk]), then layerwise QK-Norm; exact=True uses eps_qk * (mean(x^2) + eps_pre)."""
+    x, wqf, wkf = _c(x), _c(wqf), _c(wkf)
+    T, K = x.shape
+    nq, nk = wqf.shape[1], wkf.shape[1]
+    assert wqf.shape[0] == K and wkf.shape[0] == K and _code(wqf) == _code(wkf)
+    gq, gk = _c(gamma_q), _c(gamma_k)
+    assert _code(gq) == _code(gk)
+    work = np.empty(nq + nk, dtype=np.float64)
+    yq = np.empty((T, nq), dtype=np.float64)
+    yk = np.empty((T, nk), dtype=np.float64)
+    lib().oracle_qk_eliminated(T, K, nq, nk, float(eps_qk), float(eps_pre), int(bool(exact)),
+                               _code(x), _ptr(x), K, _code(wqf), _ptr(wqf), nq, _ptr(wkf), nk,
+                               _code(gq), _ptr(gq), _ptr(gk), _ptr(work), _ptr(yq), _ptr(yk))
+    return yq, yk
+
+
+def layernorm_rows(x, gamma, beta, eps: float, d: int | None = None) -> np.ndarray:
+    x, T, ld, d = _rows(x, d)
+    gdt, g = _opt(gamma)
+    bdt, b = _opt(beta)
+    y = np.empty((T, d), dtype=np.float64)
+    lib().oracle_layernorm_rows(T, d, float(eps), _code(x), _ptr(x), ld, gdt, _ptr(g), bdt,
+                                _ptr(b), _ptr(y), d)
+    return y
+
+
+def colsum(w) -> np.ndarray:
+    """c[n] = sum_k w[k][n] for w [K, N]."""
+    w = _c(w)
+    K, N = w.shape
+    c = np.empty((N,), dtype=np.float64)
+    lib().oracle_colsum(K, N, _code(w), _ptr(w), N, _ptr(c))
+    return c
+
+
+def normproj_layernorm(x, wf, csum, bias, eps: float) -> np.ndarray:
+    """y = r * (x @ W' - mu * colsum) + bias; x [T, K], wf [K, N], colsum / bias [N]."""
+    x, wf, cs = _c(x), _c(wf), _c(csum)
+    T, K = x.shape
+    K2, N = wf.shape
+    assert K == K2 and cs.shape == (N,)
+    bdt, b = _opt(bias)
+    y = np.empty((T, N), dtype=np.float64)
+    lib().oracle_normproj_layernorm(T, K, N, float(eps), _code(x), _ptr(x), K, _code(wf),
+                                    _ptr(wf), N, _code(cs), _ptr(cs), bdt, _ptr(b), _ptr(y), N)
+    return y
+
+
+def layernorm_proj_unfused(x, gamma, beta, w, eps: float) -> np.ndarray:
+    x, w = _c(x), _c(w)
+    T, K = x.shape
+    K2, N = w.shape
+    assert K == K2
+    gdt, g = _opt(gamma)
+    bdt, b = _opt(beta)
+    y = np.empty((T, N), dtype=np.float64)
+    lib().oracle_layernorm_proj_unfused(T, K, N, float(eps), _code(x), _ptr(x), K, gdt, _ptr(g),
+                                        bdt, _ptr(b), _code(w), _ptr(w), N, _ptr(y), N)
     return y

@@ -268,7 +268,181 @@ def pin_bf16_rne_library(o):
     assert np.array_equal(got, ref), int(np.sum(got != ref))
 
 
+# --------------------------------------------------------------------------- pre-norm elimination
+ELIM_WQ = np.eye(2)
+ELIM_WK = np.array([[1.0], [1.0]])
+
+
+def pin_elimination_worked(o):
+    for b in load_blocks("elimination_worked.txt"):
+        x = _vec(b["x"])[None, :]
+        e1, e2 = _expr(b["eps_pre"]), _expr(b["eps_qk"])
+        ones_q, ones_k = np.ones(2), np.ones(1)
+        yq, yk = o.qk_chain(x, None, ELIM_WQ, ELIM_WK, ones_q, ones_k, e1, e2)
+        _close(yq[0], _vec(b["chain_q"]), rtol=1e-14)
+        _close(yk[0], _vec(b["chain_k"]), rtol=1e-14)
+        for mode in ("plain", "exact"):
+            yq, yk = o.qk_eliminated(x, ELIM_WQ, ELIM_WK, ones_q, ones_k, e2, e1,
+                                     exact=(mode == "exact"))
+            _close(yq[0], _vec(b[mode + "_q"]), rtol=1e-14)
+            _close(yk[0], _vec(b[mode + "_k"]), rtol=1e-14)
+
+
+def _elim_case(seed, scale=1.0):
+    rng = np.random.default_rng(seed)
+    T, K, nq, nk = 5, 48, 40, 24
+    x = rng.normal(0.0, scale, (T, K))
+    g1 = rng.normal(1.0, 0.1, K)
+    wq = rng.normal(0.0, 0.1, (K, nq))
+    wk = rng.normal(0.0, 0.1, (K, nk))
+    gq = rng.normal(1.0, 0.05, nq)
+    gk = rng.normal(1.0, 0.05, nk)
+    return x, g1, wq, wk, gq, gk
+
+
+def pin_elimination_identities(o):
+    """Scale invariance: with eps_qk = 0 the pre-norm cancels; the exact form equals the chain
+    for any epsilons; the plain form equals the chain run with eps_qk / (mean(x^2) + eps_pre)
+    per token; in the small-activation regime the plain form visibly differs."""
+    x, g1, wq, wk, gq, gk = _elim_case(21)
+    wqf, wkf = g1[:, None] * wq, g1[:, None] * wk
+    for e1 in (0.0, 1e-2, 0.7):
+        cq, ck = o.qk_chain(x, g1, wq, wk, gq, gk, e1, 0.0)
+        for exact in (False, True):
+            pq, pk = o.qk_eliminated(x, wqf, wkf, gq, gk, 0.0, e1, exact=exact)
+            _close(pq, cq, rtol=1e-12)
+            _close(pk, ck, rtol=1e-12)
+    e1, e2 = 1e-2, 0.3
+    cq, ck = o.qk_chain(x, g1, wq, wk, gq, gk, e1, e2)
+    pq, pk = o.qk_eliminated(x, wqf, wkf, gq, gk, e2, e1, exact=True)
+    _close(pq, cq, rtol=1e-12)
+    _close(pk, ck, rtol=1e-12)
+    pq, pk = o.qk_eliminated(x, wqf, wkf, gq, gk, e2, e1, exact=False)
+    m1 = (x * x).mean(axis=1)
+    for t in range(x.shape[0]):
+        rq, rk = o.qk_chain(x[t:t + 1], g1, wq, wk, gq, gk, e1, e2 / (m1[t] + e1))
+        _close(pq[t], rq[0], rtol=1e-12)
+        _close(pk[t], rk[0], rtol=1e-12)
+    xs = x * 1e-3
+    cq, _ = o.qk_chain(xs, g1, wq, wk, gq, gk, 1e-6, 1e-6)
+    pq, _ = o.qk_eliminated(xs, wqf, wkf, gq, gk, 1e-6, 1e-6, exact=False)
+    assert np.max(np.abs(pq - cq) / np.abs(cq)) > 1e-2
+
+
+def pin_elimination_library(o):
+    """The chain and the eliminated form against torch's fp64 rms_norm and matmul."""
+    import torch
+
+    F = torch.nn.functional
+    x, g1, wq, wk, gq, gk = _elim_case(22)
+    X, G1, WQ, WK = (torch.from_numpy(a) for a in (x, g1, wq, wk))
+    GQ, GK = torch.from_numpy(gq), torch.from_numpy(gk)
+    e1, e2 = 1e-3, 0.05
+    h = F.rms_norm(X, (x.shape[1],), G1, eps=e1)
+    rq = F.rms_norm(h @ WQ, (wq.shape[1],), GQ, eps=e2).numpy()
+    rk = F.rms_norm(h @ WK, (wk.shape[1],), GK, eps=e2).numpy()
+    cq, ck = o.qk_chain(x, g1, wq, wk, gq, gk, e1, e2)
+    _close(cq, rq, rtol=1e-12)
+    _close(ck, rk, rtol=1e-12)
+    wqf, wkf = g1[:, None] * wq, g1[:, None] * wk
+    rq = F.rms_norm(X @ torch.from_numpy(wqf), (wq.shape[1],), GQ, eps=e2).numpy()
+    rk = F.rms_norm(X @ torch.from_numpy(wkf), (wk.shape[1],), GK, eps=e2).numpy()
+    pq, pk = o.qk_eliminated(x, wqf, wkf, gq, gk, e2, e1, exact=False)
+    _close(pq, rq, rtol=1e-12)
+    _close(pk, rk, rtol=1e-12)
+
+
+# --------------------------------------------------------------------------- LayerNorm
+def pin_layernorm_worked(o):
+    for b in load_blocks("layernorm_worked.txt"):
+        x, g, be, eps = _vec(b["x"]), _vec(b["gamma"]), _vec(b["beta"]), _expr(b["eps"])
+        w, wf = _mat(b["w"]), _mat(b["wfold"])
+        _close(o.layernorm_rows(x[None, :], g, be, eps)[0], _vec(b["ln"]), rtol=1e-14,
+               atol=1e-15)
+        _close(o.fold_weight(w, g), wf, atol=0)
+        _close(o.colsum(wf), _vec(b["colsum"]), atol=0)
+        _close(o.matmul(be[None, :], w)[0], _vec(b["bias"]), atol=0)
+        y = _vec(b["y"])
+        _close(o.normproj_layernorm(x[None, :], wf, _vec(b["colsum"]), _vec(b["bias"]), eps)[0],
+               y, rtol=1e-14, atol=1e-15)
+        _close(o.layernorm_proj_unfused(x[None, :], g, be, w, eps)[0], y, rtol=1e-14,
+               atol=1e-15)
+
+
+def pin_layernorm_library(o):
+    """LayerNorm, LayerNorm-then-project and its deferred form against torch's fp64
+    layer_norm and matmul, with K != N (a transposed operand cannot pass)."""
+    import torch
+
+    F = torch.nn.functional
+    rng = np.random.default_rng(23)
+    T, K, N = 6, 56, 40
+    x = rng.normal(0.7, 2.0, (T, K))
+    g = rng.normal(1.0, 0.1, K)
+    be = rng.normal(0.0, 0.5, K)
+    w = rng.normal(0.0, 0.05, (K, N))
+    for eps in (0.0, 1e-5, 0.4):
+        ln = F.layer_norm(torch.from_numpy(x), (K,), torch.from_numpy(g), torch.from_numpy(be),
+                          eps=eps)
+        _close(o.layernorm_rows(x, g, be, eps), ln.numpy(), rtol=1e-12, atol=1e-14)
+        ref = (ln @ torch.from_numpy(w)).numpy()
+        _close(o.layernorm_proj_unfused(x, g, be, w, eps), ref, rtol=1e-11, atol=1e-13)
+        wf = o.fold_weight(w, g)
+        y = o.normproj_layernorm(x, wf, o.colsum(wf), o.matmul(be[None, :], w)[0], eps)
+        _close(y, ref, rtol=1e-11, atol=1e-13)
+    _close(o.colsum(w), w.sum(axis=0), rtol=1e-13, atol=1e-15)
+    # no beta: the bias is optional and means zero
+    ln = F.layer_norm(torch.from_numpy(x), (K,), torch.from_numpy(g), None, eps=1e-5).numpy()
+    _close(o.layernorm_rows(x, g, None, 1e-5), ln, rtol=1e-12, atol=1e-14)
+    wf = o.fold_weight(w, g)
+    _close(o.normproj_layernorm(x, wf, o.colsum(wf), None, 1e-5), ln @ w, rtol=1e-11,
+           atol=1e-13)
+
+
+def pin_layernorm_invariants(o):
+    rng = np.random.default_rng(24)
+    T, d = 5, 301
+    x = rng.normal(0.0, 1.5, (T, d))
+    g = rng.normal(1.0, 0.3, d)
+    be = rng.normal(0.0, 1.0, d)
+    eps = 0.2
+    y = o.layernorm_rows(x, g, be, eps)
+    # invariant to a per-row shift
+    _close(o.layernorm_rows(x + 3.0, g, be, eps), y, rtol=1e-11, atol=1e-12)
+    # scale invariance at eps = 0: LN(c x) - beta = sign(c) (LN(x) - beta)
+    y0 = o.layernorm_rows(x, g, be, 0.0)
+    for c in (4.0, -0.5):
+        _close(o.layernorm_rows(c * x, g, be, 0.0) - be, math.copysign(1.0, c) * (y0 - be),
+               rtol=1e-11, atol=1e-12)
+    # normalised values have zero mean and mean square var / (var + eps)
+    z = (y - be) / g
+    assert np.all(np.abs(z.sum(axis=1)) <= 1e-11 * d)
+    var = np.array([np.mean((row - row.mean()) ** 2) for row in x])
+    _close((z * z).sum(axis=1), d * var / (var + eps), rtol=1e-12)
+    # a constant row maps to beta
+    _close(o.layernorm_rows(np.full((2, d), -2.5), g, be, 1e-3), np.tile(be, (2, 1)),
+           rtol=1e-15, atol=1e-15)
+
+
+def pin_layernorm_brute_force_tiny(o):
+    """d in 2..4, integer rows in {-2..2}^d that are not constant, eps = 0, gamma = 1,
+    beta = 0: y_i^2 = (x_i - mu)^2 d / sum (x - mu)^2 exactly (rational arithmetic)."""
+    for d in range(2, 5):
+        xs = np.array([v for v in product(range(-2, 3), repeat=d) if len(set(v)) > 1],
+                      dtype=np.float64)
+        y = o.layernorm_rows(xs, None, None, 0.0)
+        for row, yr in zip(xs, y):
+            mu = sum(Fraction(int(v)) for v in row) / d
+            ss = sum((Fraction(int(v)) - mu) ** 2 for v in row)
+            for v, yv in zip(row, yr):
+                exact = (Fraction(int(v)) - mu) ** 2 * d / ss
+                assert abs(yv * yv - float(exact)) <= 4e-15 * max(1.0, float(exact)), (row, d)
+
+
 ALL_PINS = [pin_rmsnorm_worked, pin_decomposition_worked, pin_flashnorm_worked,
             pin_bf16_rounding, pin_constant_vector, pin_eps_small_rows, pin_invariants,
             pin_sumsq_exact, pin_brute_force_tiny, pin_decomposition_random,
-            pin_torch_rms_norm, pin_normproj_library, pin_bf16_widening, pin_bf16_rne_library]
+            pin_torch_rms_norm, pin_normproj_library, pin_bf16_widening, pin_bf16_rne_library,
+            pin_elimination_worked, pin_elimination_identities, pin_elimination_library,
+            pin_layernorm_worked, pin_layernorm_library, pin_layernorm_invariants,
+            pin_layernorm_brute_force_tiny]

@@ -42,6 +42,24 @@ MUTANTS = {
     "bf16-low-half": ("<< 16;\n    float f;", "<< 15;\n    float f;"),
     "unfused-no-r": ("double xn = oracle_elem(xdt, x, t * ldx + k) * g * r;",
                      "double xn = oracle_elem(xdt, x, t * ldx + k) * g;"),
+    "elim-eps-no-pre": ("(row_sumsq(xdt, x, t * ldx, K) / (double)K + eps_pre)",
+                        "(row_sumsq(xdt, x, t * ldx, K) / (double)K + 0.0 * eps_pre)"),
+    "elim-eps-inverted": ("eps = eps_qk * (row_sumsq", "eps = eps_qk / (row_sumsq"),
+    "chain-no-prenorm": ("h[i] = oracle_elem(xdt, x, t * ldx + i) * g * r1;",
+                         "h[i] = oracle_elem(xdt, x, t * ldx + i) * g + 0.0 * r1;"),
+    "qk-partial-width": ("for (int64_t i = 0; i < d; ++i) s += v[i] * v[i];",
+                         "for (int64_t i = 0; i < d / 2 + 1; ++i) s += v[i] * v[i];"),
+    "ln-no-mean": ("double c = oracle_elem(dtype, x, off + i) - m;",
+                   "double c = oracle_elem(dtype, x, off + i) - 0.0 * m;"),
+    "ln-sample-variance": ("*var = v / (double)d;", "*var = v / (double)(d - 1);"),
+    "ln-beta-dropped": ("double b = beta ? oracle_elem(bdt, beta, i) : 0.0;\n            y[t * ldy + i]",
+                        "double b = 0.0; (void)bdt;\n            y[t * ldy + i]"),
+    "deferred-no-mean-term": ("r * (acc - mu * oracle_elem(cdt, colsum, n)) + b",
+                              "r * (acc - 0.0 * mu * oracle_elem(cdt, colsum, n)) + b"),
+    "deferred-bias-scaled": ("r * (acc - mu * oracle_elem(cdt, colsum, n)) + b",
+                             "r * (acc - mu * oracle_elem(cdt, colsum, n) + b)"),
+    "colsum-transposed": ("s += oracle_elem(wdt, w, k * ldw + n);",
+                          "s += oracle_elem(wdt, w, (n * K + k) % (K * N));"),
 }
 
 
