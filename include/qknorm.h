@@ -217,6 +217,81 @@ QKN_API int normproj_unfused(int64_t T, int64_t K, int64_t N, float eps, int dty
                              void* y, int64_t ldy, void* stream);
 
 /*
+ * normproj_fold_layernorm - the fold for LayerNorm followed by the projection (once, offline).
+ *
+ * ("FlashNorm: ...", abstract: the same techniques extend to LayerNorm. The pages give no
+ * formulas; the ones used follow from LN(x) W = r (x W' - mu c) + beta W.)
+ *   w_fold      as normproj_fold_weight: W' = diag(gamma) W, bf16, written transposed [N, K]
+ *   colsum[n] = sum_k W'[k, n]  over the bf16 values of w_fold exactly as stored (fp64 sum,
+ *               rounded once to fp32), [N] fp32
+ *   bias[n]   = sum_k beta[k] W[k, n]  (fp64 sum, rounded once), [N] fp32; may be NULL
+ * gamma / beta may be NULL (1 / 0); both use gamma_dtype. Outputs must not overlap each other
+ * or the inputs. Alignment rules of normproj_fold_weight.
+ */
+QKN_API int normproj_fold_layernorm(int64_t K, int64_t N, int dtype, int gamma_dtype,
+                                    const void* w, int64_t ldw, const void* gamma,
+                                    const void* beta, void* w_fold, int64_t ldw_fold,
+                                    float* colsum, float* bias, void* stream);
+
+/*
+ * normproj_deferred_layernorm - LayerNorm followed by the projection, normalisation deferred.
+ *
+ * (Same passage.) For t < T, n < N, with the row statistics taken from the same x tiles that
+ * feed the matrix cores (fp32, sums of x - x[t,0] and of its square):
+ *   mu_t    = (1/K) sum_k x[t,k]
+ *   r_t     = 1 / sqrt( (1/K) sum_k (x[t,k] - mu_t)^2 + eps )
+ *   y[t,n]  = bf16( r_t * (sum_k x[t,k] w_fold[n,k] - mu_t colsum[n]) + bias[n] )
+ *   colsum, bias  [N] fp32 from normproj_fold_layernorm; bias may be NULL (zero)
+ * Other arguments, dtype and alignment rules as normproj_deferred.
+ */
+QKN_API int normproj_deferred_layernorm(int64_t T, int64_t K, int64_t N, float eps, int dtype,
+                                        const void* x, int64_t ldx, const void* w_fold,
+                                        int64_t ldw, const float* colsum, const float* bias,
+                                        void* y, int64_t ldy, void* stream);
+
+/*
+ * normproj_layernorm_unfused - LayerNorm launch then plain projection (measured baseline).
+ *   xn[t,k] = bf16( (x[t,k] - mu_t) r_t gamma[k] + beta[k] )   (caller's scratch xn [T, K])
+ *   y[t,n]  = bf16( sum_k xn[t,k] w_packed[n,k] )
+ * w_packed is the unfolded weight re-laid out by normproj_fold_weight with gamma == NULL.
+ * gamma / beta (gamma_dtype, may be NULL) and xn must be 16-byte aligned. Other rules as
+ * normproj_unfused.
+ */
+QKN_API int normproj_layernorm_unfused(int64_t T, int64_t K, int64_t N, float eps, int dtype,
+                                       int gamma_dtype, const void* x, int64_t ldx,
+                                       const void* gamma, const void* beta,
+                                       const void* w_packed, int64_t ldw, void* xn,
+                                       int64_t ldxn, void* y, int64_t ldy, void* stream);
+
+/*
+ * qknorm_project_eliminated - Q/K projection and layerwise QK-Norm with the pre-attention
+ * RMSNorm removed.
+ *
+ * ("FlashNorm: ...", abstract: by the scale invariance of RMS, an RMSNorm followed by a linear
+ * layer and another RMSNorm lets the first RMSNorm be eliminated, e.g. ahead of attention with
+ * Q/K normalisation.) The pre-norm weight is folded into the stacked projection
+ * w_qk = [W'q ; W'k] ([nq + nk, K] bf16, normproj_fold_weight of the [K, nq + nk] weight):
+ *   p[t,:]       = x[t,:] W'^T                  exact == 0: no pre-norm at all
+ *                = r1_t x[t,:] W'^T             exact == 1: r1_t = 1/sqrt(mean(x_t^2) + eps_pre)
+ *   y[t, 0:nq]   = p[t,0:nq] gamma_q / sqrt(mean(p[t,0:nq]^2) + eps_qk)
+ *   y[t, nq:]    = p[t,nq:] gamma_k / sqrt(mean(p[t,nq:]^2) + eps_qk)
+ * With exact == 0 the result equals the pre-norm -> projection -> QK-Norm chain with eps_qk
+ * replaced per token by eps_qk / (mean(x_t^2) + eps_pre): identical when eps_qk == 0, and for
+ * eps_qk > 0 the two differ by that epsilon alone (negligible once mean(p^2) >> eps_qk * mean(x^2)).
+ * exact == 1 keeps the pre-norm's scale (deferred to the product's output) and equals the
+ * chain for every epsilon.
+ *   x    [T, K] bf16 (stride ldx)     y  [T, nq + nk] bf16 (stride ldy), also holds p (bf16)
+ *   gamma_q [nq], gamma_k [nk] in gamma_dtype; nk == 0 normalises Q only (gamma_k unused)
+ * Two launches: the matrix-core product, then the fused Q+K row kernel in place on y.
+ * Alignment rules of normproj_deferred; y must not overlap x, w_qk or the gammas.
+ */
+QKN_API int qknorm_project_eliminated(int64_t T, int64_t K, int64_t nq, int64_t nk,
+                                      float eps_qk, float eps_pre, int exact, int gamma_dtype,
+                                      const void* x, int64_t ldx, const void* w_qk, int64_t ldw,
+                                      const void* gamma_q, const void* gamma_k, void* y,
+                                      int64_t ldy, void* stream);
+
+/*
  * qkn_device_copy - plain streaming copy of nbytes (16-byte vectors where aligned).
  * Used to calibrate measured bandwidth and memory counters against a kernel of known traffic.
  * dst and src must not overlap.

@@ -4,13 +4,16 @@ The computation lives in libqknorm.so (hand-written HIP kernels behind a C ABI d
 include/qknorm.h); this package is its thin Python binding plus the seeded input generator.
 """
 
-from ._lib import (QKN_BF16, QKN_F32, QknError, lib, normproj_deferred, normproj_fold_weight,
-                   normproj_unfused, qkn_device_copy, qknorm_apply_with_stats, qknorm_fused,
-                   qknorm_partial_sumsq, qknorm_shard_flag_rows, qknorm_shard_fused,
+from ._lib import (QKN_BF16, QKN_F32, QknError, lib, normproj_deferred,
+                   normproj_deferred_layernorm, normproj_fold_layernorm, normproj_fold_weight,
+                   normproj_layernorm_unfused, normproj_unfused, qkn_device_copy,
+                   qknorm_apply_with_stats, qknorm_fused, qknorm_partial_sumsq,
+                   qknorm_project_eliminated, qknorm_shard_flag_rows, qknorm_shard_fused,
                    qknorm_shard_publish, shard_flag_blocks)
 
 __all__ = ["QKN_BF16", "QKN_F32", "QknError", "lib", "normproj_deferred",
-           "normproj_fold_weight", "normproj_unfused", "qkn_device_copy",
+           "normproj_deferred_layernorm", "normproj_fold_layernorm", "normproj_fold_weight",
+           "normproj_layernorm_unfused", "normproj_unfused", "qkn_device_copy",
            "qknorm_apply_with_stats", "qknorm_fused", "qknorm_partial_sumsq",
-           "qknorm_shard_flag_rows", "qknorm_shard_fused", "qknorm_shard_publish",
-           "shard_flag_blocks"]
+           "qknorm_project_eliminated", "qknorm_shard_flag_rows", "qknorm_shard_fused",
+           "qknorm_shard_publish", "shard_flag_blocks"]

@@ -42,6 +42,14 @@ _PROTOS = {
     "normproj_deferred": [_i64, _i64, _i64, _f32, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp],
     "normproj_unfused": [_i64, _i64, _i64, _f32, _int, _int, _vp, _i64, _vp, _vp, _i64, _vp,
                          _i64, _vp, _i64, _vp],
+    "normproj_fold_layernorm": [_i64, _i64, _int, _int, _vp, _i64, _vp, _vp, _vp, _i64, _vp, _vp,
+                                _vp],
+    "normproj_deferred_layernorm": [_i64, _i64, _i64, _f32, _int, _vp, _i64, _vp, _i64, _vp, _vp,
+                                    _vp, _i64, _vp],
+    "normproj_layernorm_unfused": [_i64, _i64, _i64, _f32, _int, _int, _vp, _i64, _vp, _vp, _vp,
+                                   _i64, _vp, _i64, _vp, _i64, _vp],
+    "qknorm_project_eliminated": [_i64, _i64, _i64, _i64, _f32, _f32, _int, _int, _vp, _i64, _vp,
+                                  _i64, _vp, _vp, _vp, _i64, _vp],
     "qkn_device_copy": [_vp, _vp, _i64, _vp],
     "qknorm_shard_fused": [_i64, _f32, _int, _int, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64,
                            _vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _vp, _i64,
@@ -291,6 +299,76 @@ def normproj_unfused(x, gamma, w_packed, eps: float = 1e-6, xn=None, y=None):
         T, K, N, float(eps), _dtype_code(x), _dtype_code(gamma), _ptr(x), _ld(x), _ptr(gamma),
         _ptr(w_packed), _ld(w_packed), _ptr(xn), _ld(xn), _ptr(y), _ld(y), _stream(x)))
     return xn, y
+
+
+def normproj_fold_layernorm(w, gamma=None, beta=None, w_fold=None, colsum=None, bias=None):
+    """W [K, N] bf16 -> (W' = diag(gamma) W transposed [N, K] bf16, colsum [N] fp32 of the
+    stored W', bias = beta W [N] fp32 or None when beta is None)."""
+    torch = _torch()
+    _check_device(w, gamma, beta)
+    K, N = w.shape
+    if w_fold is None:
+        w_fold = torch.empty((N, K), dtype=torch.bfloat16, device=w.device)
+    if colsum is None:
+        colsum = torch.empty((N,), dtype=torch.float32, device=w.device)
+    if bias is None and beta is not None:
+        bias = torch.empty((N,), dtype=torch.float32, device=w.device)
+    gdt = _dtype_code(gamma) if gamma is not None else (
+        _dtype_code(beta) if beta is not None else QKN_BF16)
+    _check("normproj_fold_layernorm", lib().normproj_fold_layernorm(
+        K, N, _dtype_code(w), gdt, _ptr(w), _ld(w), _ptr(gamma), _ptr(beta), _ptr(w_fold),
+        _ld(w_fold), _ptr(colsum), _ptr(bias), _stream(w)))
+    return w_fold, colsum, bias
+
+
+def normproj_deferred_layernorm(x, w_fold, colsum, bias=None, eps: float = 1e-5, y=None):
+    """y [T, N] = r * (x @ W' - mu * colsum) + bias (LayerNorm then project, deferred)."""
+    torch = _torch()
+    _check_device(x, w_fold, colsum, bias)
+    T, K = x.shape
+    N = w_fold.shape[0]
+    if y is None:
+        y = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    _check("normproj_deferred_layernorm", lib().normproj_deferred_layernorm(
+        T, K, N, float(eps), _dtype_code(x), _ptr(x), _ld(x), _ptr(w_fold), _ld(w_fold),
+        _ptr(colsum), _ptr(bias), _ptr(y), _ld(y), _stream(x)))
+    return y
+
+
+def normproj_layernorm_unfused(x, gamma, beta, w_packed, eps: float = 1e-5, xn=None, y=None):
+    """LayerNorm launch into xn, then a plain product with the packed unfolded weight."""
+    torch = _torch()
+    _check_device(x, gamma, beta, w_packed)
+    T, K = x.shape
+    N = w_packed.shape[0]
+    if xn is None:
+        xn = torch.empty((T, K), dtype=torch.bfloat16, device=x.device)
+    if y is None:
+        y = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    g = gamma if gamma is not None else beta
+    _check("normproj_layernorm_unfused", lib().normproj_layernorm_unfused(
+        T, K, N, float(eps), _dtype_code(x), _dtype_code(g) if g is not None else QKN_BF16,
+        _ptr(x), _ld(x), _ptr(gamma), _ptr(beta), _ptr(w_packed), _ld(w_packed), _ptr(xn),
+        _ld(xn), _ptr(y), _ld(y), _stream(x)))
+    return xn, y
+
+
+def qknorm_project_eliminated(x, w_qk, nq: int, gamma_q, gamma_k=None, eps_qk: float = 1e-6,
+                              eps_pre: float = 1e-6, exact: bool = False, y=None):
+    """y [T, nq + nk] = layerwise QK-Norm of x @ W'^T (pre-norm eliminated; exact=True keeps
+    its deferred scale). w_qk [nq + nk, K] is the folded, transposed stacked weight."""
+    torch = _torch()
+    _check_device(x, w_qk, gamma_q, gamma_k)
+    T, K = x.shape
+    N = w_qk.shape[0]
+    nk = N - nq
+    if y is None:
+        y = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    _check("qknorm_project_eliminated", lib().qknorm_project_eliminated(
+        T, K, nq, nk, float(eps_qk), float(eps_pre), int(bool(exact)), _dtype_code(gamma_q),
+        _ptr(x), _ld(x), _ptr(w_qk), _ld(w_qk), _ptr(gamma_q), _ptr(gamma_k), _ptr(y), _ld(y),
+        _stream(x)))
+    return y
 
 
 def qkn_device_copy(dst, src, nbytes: int | None = None):

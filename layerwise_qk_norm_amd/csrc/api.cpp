@@ -399,8 +399,8 @@ QKN_API int normproj_deferred(int64_t T, int64_t K, int64_t N, float eps, int dt
 {
     const int st = check_normproj(T, K, N, eps, dtype, x, ldx, w_fold, ldw, y, ldy);
     if (st != QKN_OK || T == 0 || N == 0) return st;
-    return hip_status(qkn::launch_normproj(T, K, N, eps, true, x, ldx, w_fold, ldw, y, ldy,
-                                           (hipStream_t)stream));
+    return hip_status(qkn::launch_normproj(T, K, N, eps, qkn::kEpiRms, x, ldx, w_fold, ldw, y,
+                                           ldy, nullptr, nullptr, (hipStream_t)stream));
 }
 
 QKN_API int normproj_unfused(int64_t T, int64_t K, int64_t N, float eps, int dtype,
@@ -432,8 +432,120 @@ QKN_API int normproj_unfused(int64_t T, int64_t K, int64_t N, float eps, int dty
                   nullptr};
     hipError_t e = qkn::launch_rows(job, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e);
-    return hip_status(qkn::launch_normproj(T, K, N, eps, false, xn, ldxn, w_packed, ldw, y, ldy,
-                                           (hipStream_t)stream));
+    return hip_status(qkn::launch_normproj(T, K, N, eps, qkn::kEpiPlain, xn, ldxn, w_packed, ldw,
+                                           y, ldy, nullptr, nullptr, (hipStream_t)stream));
+}
+
+QKN_API int normproj_fold_layernorm(int64_t K, int64_t N, int dtype, int gamma_dtype,
+                                    const void* w, int64_t ldw, const void* gamma,
+                                    const void* beta, void* w_fold, int64_t ldw_fold,
+                                    float* colsum, float* bias, void* stream)
+{
+    if (K < 0 || N < 0 || ldw < N || ldw_fold < K) return QKN_ERR_SHAPE;
+    if (dtype != QKN_BF16 || !valid_dtype(gamma_dtype)) return QKN_ERR_DTYPE;
+    if (K == 0 || N == 0) return QKN_OK;
+    if (w == nullptr || w_fold == nullptr || colsum == nullptr) return QKN_ERR_NULL;
+    if (((uintptr_t)w_fold & 15u) != 0 || ldw_fold % 8 != 0) return QKN_ERR_ALIGN;
+    const int64_t gs = elem_size(gamma_dtype);
+    const Range rw = span(w, K, N, ldw, 2), rf = span(w_fold, N, K, ldw_fold, 2);
+    const Range rg = gamma ? span(gamma, 1, K, K, gs) : Range();
+    const Range rb = beta ? span(beta, 1, K, K, gs) : Range();
+    const Range rc = span(colsum, 1, N, N, 4), ro = bias ? span(bias, 1, N, N, 4) : Range();
+    const Range ins[] = {rw, rg, rb};
+    for (const Range& r : ins)
+        if (overlap(rf, r) || overlap(rc, r) || overlap(ro, r)) return QKN_ERR_ALIAS;
+    if (overlap(rf, rc) || overlap(rf, ro) || overlap(rc, ro)) return QKN_ERR_ALIAS;
+    hipError_t e = qkn::launch_fold(K, N, w, ldw, gamma, gamma_dtype == QKN_BF16, w_fold,
+                                    ldw_fold, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(qkn::launch_fold_stats(K, N, w, ldw, gamma, beta, gamma_dtype == QKN_BF16,
+                                             colsum, bias, (hipStream_t)stream));
+}
+
+QKN_API int normproj_deferred_layernorm(int64_t T, int64_t K, int64_t N, float eps, int dtype,
+                                        const void* x, int64_t ldx, const void* w_fold,
+                                        int64_t ldw, const float* colsum, const float* bias,
+                                        void* y, int64_t ldy, void* stream)
+{
+    const int st = check_normproj(T, K, N, eps, dtype, x, ldx, w_fold, ldw, y, ldy);
+    if (st != QKN_OK || T == 0 || N == 0) return st;
+    if (colsum == nullptr) return QKN_ERR_NULL;
+    const Range ry = span(y, T, N, ldy, 2);
+    if (overlap(ry, span(colsum, 1, N, N, 4)) || (bias && overlap(ry, span(bias, 1, N, N, 4))))
+        return QKN_ERR_ALIAS;
+    return hip_status(qkn::launch_normproj(T, K, N, eps, qkn::kEpiLayerNorm, x, ldx, w_fold, ldw,
+                                           y, ldy, colsum, bias, (hipStream_t)stream));
+}
+
+QKN_API int normproj_layernorm_unfused(int64_t T, int64_t K, int64_t N, float eps, int dtype,
+                                       int gamma_dtype, const void* x, int64_t ldx,
+                                       const void* gamma, const void* beta,
+                                       const void* w_packed, int64_t ldw, void* xn,
+                                       int64_t ldxn, void* y, int64_t ldy, void* stream)
+{
+    int st = check_normproj(T, K, N, eps, dtype, x, ldx, w_packed, ldw, y, ldy);
+    if (st != QKN_OK) return st;
+    if (!valid_dtype(gamma_dtype)) return QKN_ERR_DTYPE;
+    if (ldxn < K) return QKN_ERR_SHAPE;
+    if (T == 0 || N == 0) return QKN_OK;
+    if (xn == nullptr) return QKN_ERR_NULL;
+    if (((uintptr_t)xn & 15u) != 0 || ldxn % 8 != 0 || ((uintptr_t)gamma & 15u) != 0 ||
+        ((uintptr_t)beta & 15u) != 0)
+        return QKN_ERR_ALIGN;
+    const int64_t gs = elem_size(gamma_dtype);
+    const Range rxn = span(xn, T, K, ldxn, 2);
+    if (overlap(rxn, span(x, T, K, ldx, 2)) || overlap(rxn, span(w_packed, N, K, ldw, 2)) ||
+        overlap(rxn, span(y, T, N, ldy, 2)) || (gamma && overlap(rxn, span(gamma, 1, K, K, gs))) ||
+        (beta && overlap(rxn, span(beta, 1, K, K, gs))))
+        return QKN_ERR_ALIAS;
+    hipError_t e = qkn::launch_layernorm_rows(T, K, eps, x, ldx, gamma, beta,
+                                              gamma_dtype == QKN_BF16, xn, ldxn,
+                                              (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(qkn::launch_normproj(T, K, N, eps, qkn::kEpiPlain, xn, ldxn, w_packed, ldw,
+                                           y, ldy, nullptr, nullptr, (hipStream_t)stream));
+}
+
+QKN_API int qknorm_project_eliminated(int64_t T, int64_t K, int64_t nq, int64_t nk,
+                                      float eps_qk, float eps_pre, int exact, int gamma_dtype,
+                                      const void* x, int64_t ldx, const void* w_qk, int64_t ldw,
+                                      const void* gamma_q, const void* gamma_k, void* y,
+                                      int64_t ldy, void* stream)
+{
+    if (nq < 1 || nk < 0) return QKN_ERR_SHAPE;
+    if (!valid_eps(eps_pre)) return QKN_ERR_EPS;
+    if (exact != 0 && exact != 1) return QKN_ERR_SHAPE;
+    const int64_t N = nq + nk;
+    int st = check_normproj(T, K, N, eps_qk, QKN_BF16, x, ldx, w_qk, ldw, y, ldy);
+    if (st != QKN_OK) return st;
+    if (!valid_dtype(gamma_dtype)) return QKN_ERR_DTYPE;
+    if (T == 0) return QKN_OK;
+    if (gamma_q == nullptr || (nk > 0 && gamma_k == nullptr)) return QKN_ERR_NULL;
+    const int64_t gs = elem_size(gamma_dtype);
+    const Range ry = span(y, T, N, ldy, 2);
+    if (overlap(ry, span(gamma_q, 1, nq, nq, gs)) ||
+        (nk > 0 && overlap(ry, span(gamma_k, 1, nk, nk, gs))))
+        return QKN_ERR_ALIAS;
+    // p = x W' (scaled by the pre-norm's 1/rms when exact), stored in y in bf16
+    hipError_t e = qkn::launch_normproj(T, K, N, eps_pre, exact ? qkn::kEpiRms : qkn::kEpiPlain,
+                                        x, ldx, w_qk, ldw, y, ldy, nullptr, nullptr,
+                                        (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e);
+    // layerwise QK-Norm of the two column blocks of y, in place
+    qkn::RowJob job = {};
+    job.nseg = nk > 0 ? 2 : 1;
+    job.T = T;
+    job.eps = eps_qk;
+    job.mode = qkn::kFused;
+    job.bf16 = 1;
+    job.gamma_bf16 = gamma_dtype == QKN_BF16;
+    uint16_t* yq = (uint16_t*)y;
+    job.seg[0] = {yq, yq, gamma_q, ldy, ldy, nq, (float)(1.0 / (double)nq), nullptr, nullptr, 0,
+                  0, nullptr};
+    if (nk > 0)
+        job.seg[1] = {yq + nq, yq + nq, gamma_k, ldy, ldy, nk, (float)(1.0 / (double)nk), nullptr,
+                      nullptr, 0, 0, nullptr};
+    return hip_status(qkn::launch_rows(job, (hipStream_t)stream));
 }
 
 QKN_API int qkn_device_copy(void* dst, const void* src, int64_t nbytes, void* stream)

@@ -1,11 +1,18 @@
-// Norm-then-project on gfx950 with the RMS scale deferred to the product's output
-// ("FlashNorm: Fast Normalization for Transformers", abstract, items (i) and (ii)), plus the
-// one-time weight fold and a plain streaming copy used for calibration.
+// Norm-then-project on gfx950 with the normalisation deferred to the product's output
+// ("FlashNorm: Fast Normalization for Transformers", abstract, items (i) and (ii), and its
+// extension to LayerNorm), plus the one-time weight folds, the LayerNorm row kernel of the
+// unfused baseline and a plain streaming copy used for calibration.
 //
-// y[t, n] = r_t * sum_k x[t, k] * w[n, k] with both operands K-contiguous (the fold writes W'
-// transposed), on v_mfma_f32_32x32x16_bf16. The 1/rms factor comes from the same x values that
-// feed the matrix cores, squared and summed on the VALU while the MFMAs run, so no extra pass
-// over x is needed and the reduction proceeds beside the product instead of before it.
+// acc[t, n] = sum_k x[t, k] * w[n, k] with both operands K-contiguous (the fold writes W'
+// transposed), on v_mfma_f32_32x32x16_bf16. The epilogue is one of
+//   plain      y = acc
+//   RMSNorm    y = r_t * acc,                          r_t = 1 / sqrt(mean(x_t^2) + eps)
+//   LayerNorm  y = r_t * (acc - mu_t * c[n]) + b[n],   r_t = 1 / sqrt(var(x_t) + eps)
+// with c the column sums of the folded weight and b = beta W. The row statistics come from the
+// same x values that feed the matrix cores, accumulated on the VALU while the MFMAs run, so no
+// extra pass over x is needed and the reduction proceeds beside the product instead of before
+// it. LayerNorm accumulates sum(x - x0) and sum((x - x0)^2) with x0 the row's first element, so
+// that the one-pass variance does not cancel for rows whose mean is large against their spread.
 //
 // Pipelined kernel (K a multiple of the k-tile, N of 8): a workgroup owns a BM x BN output tile.
 // Its k-tiles of x and W' stream into an NST-deep LDS ring by direct global->LDS DMA
@@ -46,6 +53,54 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+__device__ __forceinline__ float bf16_at(const uint16_t* p, int64_t i)
+{
+    return __uint_as_float((uint32_t)p[i] << 16);
+}
+
+// Row statistics of 8 bf16 values: RMSNorm sums squares; LayerNorm sums the values and their
+// squares after subtracting the row's shift x0.
+template <int EPI>
+__device__ __forceinline__ void accum_stats(const u32x4& v, float x0, float& s1, float& s2)
+{
+    const float e[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                        bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        if constexpr (EPI == kEpiLayerNorm) {
+            const float d = e[j] - x0;
+            s1 += d;
+            s2 = fmaf(d, d, s2);
+        } else {
+            s2 = fmaf(e[j], e[j], s2);
+        }
+    }
+}
+
+// Row scale (and LayerNorm mean) from the row's sums over K columns.
+template <int EPI>
+__device__ __forceinline__ void row_scale(float s1, float s2, float x0, float inv_k, float eps,
+                                          float& rs, float& mu)
+{
+    if constexpr (EPI == kEpiLayerNorm) {
+        const float ms = s1 * inv_k;                          // mean of x - x0
+        const float var = fmaxf(fmaf(-ms, ms, s2 * inv_k), 0.0f);
+        rs = rsqrtf(var + eps);
+        mu = x0 + ms;
+    } else {
+        rs = rsqrtf(s2 * inv_k + eps);
+        mu = 0.0f;
+    }
+}
+
+template <int EPI>
+__device__ __forceinline__ float epilogue(float acc, float rs, float mu, float c, float b)
+{
+    if constexpr (EPI == kEpiRms) return acc * rs;
+    if constexpr (EPI == kEpiLayerNorm) return fmaf(rs, fmaf(-mu, c, acc), b);
+    return acc;
+}
+
 // ------------------------------------------------------------------------------------------
 // Pipelined kernel.
 
@@ -83,11 +138,12 @@ __device__ __forceinline__ int swz(int kc, int r)
     return BK == 64 ? (kc ^ ((r >> 1) & 7)) : (kc ^ ((r >> 2) & 3));
 }
 
-template <int BM, int BN, int WM, int WN, int NST, int BK, bool NORM>
+template <int BM, int BN, int WM, int WN, int NST, int BK, int EPI>
 __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
     int64_t T, int64_t K, int64_t N, float eps, float inv_k, const uint16_t* __restrict__ x,
     int64_t ldx, const uint16_t* __restrict__ w, int64_t ldw, uint16_t* __restrict__ y,
-    int64_t ldy, int nbm, int nbn)
+    int64_t ldy, int nbm, int nbn, const float* __restrict__ colsum,
+    const float* __restrict__ bias)
 {
     constexpr int NW = WM * WN, NT = NW * kWave;
     constexpr int ROWB = BK * 2;            // bytes per tile row
@@ -104,6 +160,7 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
     constexpr int SMEM = PIPE > CTILE ? PIPE : CTILE;
     __shared__ __attribute__((aligned(1024))) char smem[SMEM];
     __shared__ float rs_lds[BM];
+    __shared__ float mu_lds[EPI == kEpiLayerNorm ? BM : 1];
 
     const int tid = (int)threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int wm = wave / WN, wn = wave % WN;
@@ -145,16 +202,22 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
         for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-    float ssq[TM];
+    const int frow = lane & 31, fk = lane >> 5;
+    float s1[TM], s2[TM], x0[TM];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) ssq[i] = 0.0f;
+    for (int i = 0; i < TM; ++i) {
+        s1[i] = s2[i] = x0[i] = 0.0f;
+        if constexpr (EPI == kEpiLayerNorm) {
+            const int64_t r = m0 + wm * WTM + i * 32 + frow;
+            if (wn == 0) x0[i] = bf16_at(x, (r < T ? r : T - 1) * ldx);
+        }
+    }
 
     const int nk = (int)(K / BK);
 #pragma unroll
     for (int s = 0; s < NST - 1; ++s)
         if (s < nk) issue(s, (int64_t)s * BK);
 
-    const int frow = lane & 31, fk = lane >> 5;
     for (int kt = 0; kt < nk; ++kt) {
         // k-tile kt must have landed; up to NST-2 later tiles stay in flight
         const int later = (nk - 1 - kt) < (NST - 2) ? (nk - 1 - kt) : (NST - 2);
@@ -186,18 +249,10 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
                 const int r = wn * WTN + j * 32 + frow;
                 bfr[j] = *(const u32x4*)(Bs + r * ROWB + (swz<BK>(kc, r) << 4));
             }
-            if constexpr (NORM) {
+            if constexpr (EPI != kEpiPlain) {
                 if (wn == 0) {
 #pragma unroll
-                    for (int i = 0; i < TM; ++i) {
-                        const u32x4 v = af[i];
-                        float s = ssq[i];
-                        s = fmaf(bf16_lo(v.x), bf16_lo(v.x), s); s = fmaf(bf16_hi(v.x), bf16_hi(v.x), s);
-                        s = fmaf(bf16_lo(v.y), bf16_lo(v.y), s); s = fmaf(bf16_hi(v.y), bf16_hi(v.y), s);
-                        s = fmaf(bf16_lo(v.z), bf16_lo(v.z), s); s = fmaf(bf16_hi(v.z), bf16_hi(v.z), s);
-                        s = fmaf(bf16_lo(v.w), bf16_lo(v.w), s); s = fmaf(bf16_hi(v.w), bf16_hi(v.w), s);
-                        ssq[i] = s;
-                    }
+                    for (int i = 0; i < TM; ++i) accum_stats<EPI>(af[i], x0[i], s1[i], s2[i]);
                 }
             }
 #pragma unroll
@@ -207,17 +262,35 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
         }
     }
 
-    if constexpr (NORM) {
+    if constexpr (EPI != kEpiPlain) {
         // lanes l and l + 32 summed the two halves of each 16-wide k step of the same row
         if (wn == 0) {
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
-                const float s = ssq[i] + __shfl_xor(ssq[i], 32);
-                if (lane < 32) rs_lds[wm * WTM + i * 32 + lane] = rsqrtf(s * inv_k + eps);
+                const float q2 = s2[i] + __shfl_xor(s2[i], 32);
+                const float q1 = s1[i] + __shfl_xor(s1[i], 32);
+                float rs, mu;
+                row_scale<EPI>(q1, q2, x0[i], inv_k, eps, rs, mu);
+                if (lane < 32) {
+                    rs_lds[wm * WTM + i * 32 + lane] = rs;
+                    if constexpr (EPI == kEpiLayerNorm) mu_lds[wm * WTM + i * 32 + lane] = mu;
+                }
             }
         }
     }
-    __syncthreads();  // all DMA consumed (the last k-tile waited for vmcnt 0); 1/rms visible
+    float cs[TN], bs[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        cs[j] = bs[j] = 0.0f;
+        if constexpr (EPI == kEpiLayerNorm) {
+            const int64_t gn = n0 + wn * WTN + j * 32 + (lane & 31);
+            if (gn < N) {
+                cs[j] = colsum[gn];
+                if (bias) bs[j] = bias[gn];
+            }
+        }
+    }
+    __syncthreads();  // all DMA consumed (the last k-tile waited for vmcnt 0); row scales visible
 
     // accumulator layout of a 32 x 32 block: lane holds column lane % 32 and, for e in 0..15,
     // row 8 * (e / 4) + 4 * (lane / 32) + e % 4
@@ -231,7 +304,8 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
                 const int r = wm * WTM + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
                 const int c = wn * WTN + j * 32 + (lane & 31);
                 float v = acc[i][j][e];
-                if constexpr (NORM) v *= rs_lds[r];
+                if constexpr (EPI == kEpiRms) v *= rs_lds[r];
+                if constexpr (EPI == kEpiLayerNorm) v = epilogue<EPI>(v, rs_lds[r], mu_lds[r], cs[j], bs[j]);
                 ct[r * CP + c] = to_bf16(v);
             }
     __syncthreads();
@@ -246,15 +320,17 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
 // ------------------------------------------------------------------------------------------
 // Generic kernel.
 
-template <bool NORM>
+template <int EPI>
 __global__ __launch_bounds__(kThreads) void normproj_mfma_kernel(
     int64_t T, int64_t K, int64_t N, float eps, float inv_k, const uint16_t* __restrict__ x,
     int64_t ldx, const uint16_t* __restrict__ w, int64_t ldw, uint16_t* __restrict__ y,
-    int64_t ldy, int nbm, int nbn)
+    int64_t ldy, int nbm, int nbn, const float* __restrict__ colsum,
+    const float* __restrict__ bias)
 {
     __shared__ __attribute__((aligned(16))) uint16_t As[kBM * kPitch];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[kBN * kPitch];
     __shared__ float rstd[kBM];
+    __shared__ float mean[EPI == kEpiLayerNorm ? kBM : 1];
 
     // Blocks are handed to the 8 XCDs round-robin; give each XCD a contiguous range of tiles
     // (whole row panels of x) so that panel is fetched into one XCD's L2 only.
@@ -275,7 +351,15 @@ __global__ __launch_bounds__(kThreads) void normproj_mfma_kernel(
     const int ld_row = tid / kChunksPerRow;
     const int ld_kc = tid % kChunksPerRow;
     u32x4 ra[kLoadsPerThread], rb[kLoadsPerThread];
-    float ssq[kLoadsPerThread] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float s1[kLoadsPerThread], s2[kLoadsPerThread], x0[kLoadsPerThread];
+#pragma unroll
+    for (int c = 0; c < kLoadsPerThread; ++c) {
+        s1[c] = s2[c] = x0[c] = 0.0f;
+        if constexpr (EPI == kEpiLayerNorm) {
+            const int64_t gm = m0 + ld_row + c * (kThreads / kChunksPerRow);
+            x0[c] = bf16_at(x, (gm < T ? gm : T - 1) * ldx);
+        }
+    }
 
     auto load_tiles = [&](int64_t k0) {
         const int64_t k = k0 + ld_kc * 8;
@@ -287,20 +371,17 @@ __global__ __launch_bounds__(kThreads) void normproj_mfma_kernel(
             rb[c] = (gn < N && k < K) ? *(const u32x4*)(w + gn * ldw + k) : u32x4{0u, 0u, 0u, 0u};
         }
     };
-    auto store_tiles = [&]() {
+    // k0: first column of the tile just loaded; chunks past K were zero-filled and are left
+    // out of the LayerNorm sums (their shifted values would not be zero)
+    auto store_tiles = [&](int64_t k0) {
+        const bool kin = k0 + ld_kc * 8 < K;
 #pragma unroll
         for (int c = 0; c < kLoadsPerThread; ++c) {
             const int r = ld_row + c * (kThreads / kChunksPerRow);
             *(u32x4*)(As + r * kPitch + ld_kc * 8) = ra[c];
             *(u32x4*)(Bs + r * kPitch + ld_kc * 8) = rb[c];
-            if constexpr (NORM) {
-                const u32x4 v = ra[c];
-                float s = ssq[c];
-                s = fmaf(bf16_lo(v.x), bf16_lo(v.x), s); s = fmaf(bf16_hi(v.x), bf16_hi(v.x), s);
-                s = fmaf(bf16_lo(v.y), bf16_lo(v.y), s); s = fmaf(bf16_hi(v.y), bf16_hi(v.y), s);
-                s = fmaf(bf16_lo(v.z), bf16_lo(v.z), s); s = fmaf(bf16_hi(v.z), bf16_hi(v.z), s);
-                s = fmaf(bf16_lo(v.w), bf16_lo(v.w), s); s = fmaf(bf16_hi(v.w), bf16_hi(v.w), s);
-                ssq[c] = s;
+            if constexpr (EPI != kEpiPlain) {
+                if (kin) accum_stats<EPI>(ra[c], x0[c], s1[c], s2[c]);
             }
         }
     };
@@ -315,7 +396,7 @@ __global__ __launch_bounds__(kThreads) void normproj_mfma_kernel(
 
     const int64_t nk = (K + kBK - 1) / kBK;
     load_tiles(0);
-    store_tiles();
+    store_tiles(0);
     __syncthreads();
 
     // MFMA operand fragments: lane holds row (lane % 32) of a 32-row block, 8 consecutive k
@@ -339,17 +420,23 @@ __global__ __launch_bounds__(kThreads) void normproj_mfma_kernel(
         }
         __syncthreads();
         if (kt + 1 < nk) {
-            store_tiles();
+            store_tiles((kt + 1) * kBK);
             __syncthreads();
         }
     }
 
-    if constexpr (NORM) {
-        // Combine the 8 threads that share each tile row, then 1/rms per row.
+    if constexpr (EPI != kEpiPlain) {
+        // Combine the 8 threads that share each tile row, then the row's scale.
 #pragma unroll
         for (int c = 0; c < kLoadsPerThread; ++c) {
-            const float s = sum8(ssq[c]);
-            if (ld_kc == 0) rstd[ld_row + c * (kThreads / kChunksPerRow)] = rsqrtf(s * inv_k + eps);
+            const float q2 = sum8(s2[c]);
+            const float q1 = sum8(s1[c]);
+            float rs, mu;
+            row_scale<EPI>(q1, q2, x0[c], inv_k, eps, rs, mu);
+            if (ld_kc == 0) {
+                rstd[ld_row + c * (kThreads / kChunksPerRow)] = rs;
+                if constexpr (EPI == kEpiLayerNorm) mean[ld_row + c * (kThreads / kChunksPerRow)] = mu;
+            }
         }
         __syncthreads();
     }
@@ -363,12 +450,20 @@ __global__ __launch_bounds__(kThreads) void normproj_mfma_kernel(
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int64_t gn = n0 + wn * 64 + j * 32 + out_col;
+            float cs = 0.0f, bs = 0.0f;
+            if constexpr (EPI == kEpiLayerNorm) {
+                if (gn < N) {
+                    cs = colsum[gn];
+                    if (bias) bs = bias[gn];
+                }
+            }
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int r = wm * 64 + i * 32 + 8 * (e / 4) + out_row + (e % 4);
                 const int64_t gm = m0 + r;
                 float v = acc[i][j][e];
-                if constexpr (NORM) v *= rstd[r];
+                if constexpr (EPI == kEpiRms) v *= rstd[r];
+                if constexpr (EPI == kEpiLayerNorm) v = epilogue<EPI>(v, rstd[r], mean[r], cs, bs);
                 if (gm < T && gn < N) y[gm * ldy + gn] = to_bf16(v);
             }
         }
@@ -380,21 +475,24 @@ __global__ __launch_bounds__(kThreads) void normproj_mfma_kernel(
 constexpr int kGemvCols = 2;
 constexpr int kGemvMaxT = 16;
 
-template <bool NORM>
+template <int EPI>
 __global__ __launch_bounds__(kThreads) void normproj_gemv_kernel(
     int T, int64_t K, int64_t N, float eps, float inv_k, const uint16_t* __restrict__ x,
     int64_t ldx, const uint16_t* __restrict__ w, int64_t ldw, uint16_t* __restrict__ y,
-    int64_t ldy)
+    int64_t ldy, const float* __restrict__ colsum, const float* __restrict__ bias)
 {
     const int lane = lane_id();
     const int64_t n_base = ((int64_t)blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave) * kGemvCols;
     if (n_base >= N) return;
 
     float acc[kGemvMaxT][kGemvCols];
-    float ssq[kGemvMaxT];
+    float s1[kGemvMaxT], s2[kGemvMaxT], x0[kGemvMaxT];
 #pragma unroll
     for (int t = 0; t < kGemvMaxT; ++t) {
-        ssq[t] = 0.0f;
+        s1[t] = s2[t] = x0[t] = 0.0f;
+        if constexpr (EPI == kEpiLayerNorm) {
+            if (t < T) x0[t] = bf16_at(x, (int64_t)t * ldx);
+        }
 #pragma unroll
         for (int c = 0; c < kGemvCols; ++c) acc[t][c] = 0.0f;
     }
@@ -416,9 +514,9 @@ __global__ __launch_bounds__(kThreads) void normproj_gemv_kernel(
                 const u32x4 v = *(const u32x4*)(x + (int64_t)t * ldx + k);
                 float xf[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
                                bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+                if constexpr (EPI != kEpiPlain) accum_stats<EPI>(v, x0[t], s1[t], s2[t]);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    if constexpr (NORM) ssq[t] = fmaf(xf[e], xf[e], ssq[t]);
 #pragma unroll
                     for (int c = 0; c < kGemvCols; ++c) acc[t][c] = fmaf(xf[e], wf[c][e], acc[t][c]);
                 }
@@ -429,12 +527,21 @@ __global__ __launch_bounds__(kThreads) void normproj_gemv_kernel(
 #pragma unroll
     for (int t = 0; t < kGemvMaxT; ++t) {
         if (t < T) {
-            float rs = 1.0f;
-            if constexpr (NORM) rs = rsqrtf(wave_sum(ssq[t]) * inv_k + eps);
+            float rs = 1.0f, mu = 0.0f;
+            if constexpr (EPI != kEpiPlain)
+                row_scale<EPI>(wave_sum(s1[t]), wave_sum(s2[t]), x0[t], inv_k, eps, rs, mu);
 #pragma unroll
             for (int c = 0; c < kGemvCols; ++c) {
-                const float v = wave_sum(acc[t][c]) * rs;
-                if (lane == c && n_base + c < N) y[(int64_t)t * ldy + n_base + c] = to_bf16(v);
+                const int64_t n = n_base + c;
+                float cs = 0.0f, bs = 0.0f;
+                if constexpr (EPI == kEpiLayerNorm) {
+                    if (n < N) {
+                        cs = colsum[n];
+                        if (bias) bs = bias[n];
+                    }
+                }
+                const float v = epilogue<EPI>(wave_sum(acc[t][c]), rs, mu, cs, bs);
+                if (lane == c && n < N) y[(int64_t)t * ldy + n] = to_bf16(v);
             }
         }
     }
@@ -472,6 +579,100 @@ __global__ __launch_bounds__(kThreads) void fold_kernel(int64_t K, int64_t N,
     }
 }
 
+// Statistics of the LayerNorm fold: c[n] = sum_k W'[k][n] over the folded values exactly as
+// fold_kernel stores them (bf16 of gamma[k] * W[k][n]), and b[n] = sum_k beta[k] * W[k][n].
+// 64 columns per workgroup, the k range split over 4 thread rows, fp64 sums combined in a
+// fixed order and rounded once to fp32.
+__global__ __launch_bounds__(kThreads) void fold_stats_kernel(int64_t K, int64_t N,
+                                                             const uint16_t* __restrict__ w,
+                                                             int64_t ldw, const void* gamma,
+                                                             const void* beta, int gb_bf16,
+                                                             float* __restrict__ colsum,
+                                                             float* __restrict__ bias)
+{
+    __shared__ double red[2][4][64];
+    const int tx = (int)threadIdx.x % 64, ty = (int)threadIdx.x / 64;
+    const int64_t n = (int64_t)blockIdx.x * 64 + tx;
+    double c = 0.0, b = 0.0;
+    if (n < N) {
+        for (int64_t k = ty; k < K; k += 4) {
+            const float wv = bf16_at(w, k * ldw + n);
+            float g = 1.0f, be = 0.0f;
+            if (gamma) g = gb_bf16 ? bf16_at((const uint16_t*)gamma, k) : ((const float*)gamma)[k];
+            if (beta) be = gb_bf16 ? bf16_at((const uint16_t*)beta, k) : ((const float*)beta)[k];
+            c += (double)__uint_as_float((uint32_t)to_bf16(g * wv) << 16);
+            b += (double)be * (double)wv;
+        }
+    }
+    red[0][ty][tx] = c;
+    red[1][ty][tx] = b;
+    __syncthreads();
+    if (ty == 0 && n < N) {
+        colsum[n] = (float)(((red[0][0][tx] + red[0][1][tx]) + red[0][2][tx]) + red[0][3][tx]);
+        if (bias) bias[n] = (float)(((red[1][0][tx] + red[1][1][tx]) + red[1][2][tx]) + red[1][3][tx]);
+    }
+}
+
+// Eight consecutive values from k (a multiple of 8) of a bf16 or fp32 vector, 16-byte loads.
+__device__ __forceinline__ void load8(const void* p, int64_t k, bool bf, float* out)
+{
+    if (bf) {
+        const u32x4 v = *(const u32x4*)((const uint16_t*)p + k);
+        out[0] = bf16_lo(v.x); out[1] = bf16_hi(v.x); out[2] = bf16_lo(v.y); out[3] = bf16_hi(v.y);
+        out[4] = bf16_lo(v.z); out[5] = bf16_hi(v.z); out[6] = bf16_lo(v.w); out[7] = bf16_hi(v.w);
+    } else {
+        const f32x4 a = *(const f32x4*)((const float*)p + k);
+        const f32x4 b = *(const f32x4*)((const float*)p + k + 4);
+        out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+        out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+    }
+}
+
+// LayerNorm rows for the unfused baseline: one workgroup per row, 16-byte accesses (K % 8 == 0,
+// aligned rows, 16-byte aligned gamma and beta). Pass 1 sums x - x0 and its square (x0 = the row's first element), pass 2
+// re-reads the row from cache and writes bf16((x - mu) * r * gamma + beta).
+__global__ __launch_bounds__(kThreads) void layernorm_rows_kernel(
+    int64_t K, float eps, float inv_k, const uint16_t* __restrict__ x, int64_t ldx,
+    const void* gamma, const void* beta, int gb_bf16, uint16_t* __restrict__ y, int64_t ldy)
+{
+    __shared__ float red[2][kThreads / kWave];
+    const int64_t t = blockIdx.x;
+    const uint16_t* xr = x + t * ldx;
+    const float x0 = bf16_at(xr, 0);
+    float s1 = 0.0f, s2 = 0.0f;
+    for (int64_t k = (int64_t)threadIdx.x * 8; k < K; k += kThreads * 8)
+        accum_stats<kEpiLayerNorm>(*(const u32x4*)(xr + k), x0, s1, s2);
+    s1 = wave_sum(s1);
+    s2 = wave_sum(s2);
+    const int wave = (int)threadIdx.x / kWave;
+    if (lane_id() == 0) {
+        red[0][wave] = s1;
+        red[1][wave] = s2;
+    }
+    __syncthreads();
+    float q1 = 0.0f, q2 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kThreads / kWave; ++i) {
+        q1 += red[0][i];
+        q2 += red[1][i];
+    }
+    float rs, mu;
+    row_scale<kEpiLayerNorm>(q1, q2, x0, inv_k, eps, rs, mu);
+    for (int64_t k = (int64_t)threadIdx.x * 8; k < K; k += kThreads * 8) {
+        float e[8], g[8], be[8];
+        load8(xr, k, true, e);
+        if (gamma) load8(gamma, k, gb_bf16, g);
+        if (beta) load8(beta, k, gb_bf16, be);
+        float o[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            o[j] = fmaf((e[j] - mu) * rs, gamma ? g[j] : 1.0f, beta ? be[j] : 0.0f);
+        const u32x4 out = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
+                           pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])};
+        *(u32x4*)(y + t * ldy + k) = out;
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void copy_kernel(char* __restrict__ dst,
                                                         const char* __restrict__ src,
                                                         int64_t nbytes, int vec)
@@ -488,67 +689,98 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(char* __restrict__ dst,
     for (int64_t i = done + tid; i < nbytes; i += stride) dst[i] = src[i];
 }
 
-template <int BM, int BN, int WM, int WN, int NST, int BK>
-hipError_t launch_pipe(int64_t T, int64_t K, int64_t N, float eps, float inv_k, bool norm,
+template <int BM, int BN, int WM, int WN, int NST, int BK, int EPI>
+hipError_t launch_pipe(int64_t T, int64_t K, int64_t N, float eps, float inv_k,
                        const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
-                       uint16_t* y, int64_t ldy, hipStream_t st)
+                       uint16_t* y, int64_t ldy, const float* colsum, const float* bias,
+                       hipStream_t st)
 {
     const int64_t nbm = (T + BM - 1) / BM, nbn = (N + BN - 1) / BN;
     if (nbm * nbn > 0x7fffffff) return hipErrorInvalidConfiguration;
-    const dim3 grid((unsigned)(nbm * nbn)), block(WM * WN * kWave);
-    if (norm)
-        hipLaunchKernelGGL((normproj_pipe_kernel<BM, BN, WM, WN, NST, BK, true>), grid, block, 0,
-                           st, T, K, N, eps, inv_k, x, ldx, w, ldw, y, ldy, (int)nbm, (int)nbn);
-    else
-        hipLaunchKernelGGL((normproj_pipe_kernel<BM, BN, WM, WN, NST, BK, false>), grid, block, 0,
-                           st, T, K, N, eps, inv_k, x, ldx, w, ldw, y, ldy, (int)nbm, (int)nbn);
+    hipLaunchKernelGGL((normproj_pipe_kernel<BM, BN, WM, WN, NST, BK, EPI>),
+                       dim3((unsigned)(nbm * nbn)), dim3(WM * WN * kWave), 0, st, T, K, N, eps,
+                       inv_k, x, ldx, w, ldw, y, ldy, (int)nbm, (int)nbn, colsum, bias);
+    return hipGetLastError();
+}
+
+template <int EPI>
+hipError_t launch_epi(int64_t T, int64_t K, int64_t N, float eps, const uint16_t* xp,
+                      int64_t ldx, const uint16_t* wp, int64_t ldw, uint16_t* yp, int64_t ldy,
+                      const float* colsum, const float* bias, hipStream_t st)
+{
+    const float inv_k = (float)(1.0 / (double)K);
+    if (T <= kGemvMaxT) {
+        const int64_t cols_per_block = (kThreads / kWave) * kGemvCols;
+        const int64_t nblk = (N + cols_per_block - 1) / cols_per_block;
+        if (nblk > 0x7fffffff) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL(normproj_gemv_kernel<EPI>, dim3((unsigned)nblk), dim3(kThreads), 0, st,
+                           (int)T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp, ldy, colsum, bias);
+        return hipGetLastError();
+    }
+    const bool pipe_ok = N % 8 == 0 && ldy % 8 == 0 && ((uintptr_t)yp & 15u) == 0;
+    const int64_t big_tiles = ((T + 255) / 256) * ((N + 255) / 256);
+    if (pipe_ok && K % 32 == 0 && big_tiles >= 512) {
+        // many output tiles: 256 x 256 per workgroup of 8 wavefronts, k-tiles of 32, 4 stages
+        return launch_pipe<256, 256, 4, 2, 4, 32, EPI>(T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp,
+                                                       ldy, colsum, bias, st);
+    }
+    if (pipe_ok && K % 64 == 0) {
+        // 128 x 128 per workgroup of 4 wavefronts, k-tiles of 64, 2 stages (2 workgroups per CU)
+        return launch_pipe<128, 128, 2, 2, 2, 64, EPI>(T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp,
+                                                       ldy, colsum, bias, st);
+    }
+    const int64_t nbm = (T + kBM - 1) / kBM, nbn = (N + kBN - 1) / kBN;
+    if (nbm * nbn > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(normproj_mfma_kernel<EPI>, dim3((unsigned)(nbm * nbn)), dim3(kThreads), 0,
+                       st, T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp, ldy, (int)nbm, (int)nbn,
+                       colsum, bias);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_normproj(int64_t T, int64_t K, int64_t N, float eps, bool norm,
+hipError_t launch_normproj(int64_t T, int64_t K, int64_t N, float eps, int epi,
                            const void* x, int64_t ldx, const void* w, int64_t ldw, void* y,
-                           int64_t ldy, hipStream_t st)
+                           int64_t ldy, const float* colsum, const float* bias, hipStream_t st)
 {
     if (T == 0 || N == 0) return hipSuccess;
-    const float inv_k = (float)(1.0 / (double)K);
     const uint16_t* xp = (const uint16_t*)x;
     const uint16_t* wp = (const uint16_t*)w;
     uint16_t* yp = (uint16_t*)y;
-    if (T <= kGemvMaxT) {
-        const int64_t cols_per_block = (kThreads / kWave) * kGemvCols;
-        const int64_t nblk = (N + cols_per_block - 1) / cols_per_block;
-        if (nblk > 0x7fffffff) return hipErrorInvalidConfiguration;
-        if (norm)
-            hipLaunchKernelGGL(normproj_gemv_kernel<true>, dim3((unsigned)nblk), dim3(kThreads), 0,
-                               st, (int)T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp, ldy);
-        else
-            hipLaunchKernelGGL(normproj_gemv_kernel<false>, dim3((unsigned)nblk), dim3(kThreads), 0,
-                               st, (int)T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp, ldy);
-        return hipGetLastError();
+    switch (epi) {
+    case kEpiPlain:
+        return launch_epi<kEpiPlain>(T, K, N, eps, xp, ldx, wp, ldw, yp, ldy, colsum, bias, st);
+    case kEpiRms:
+        return launch_epi<kEpiRms>(T, K, N, eps, xp, ldx, wp, ldw, yp, ldy, colsum, bias, st);
+    case kEpiLayerNorm:
+        return launch_epi<kEpiLayerNorm>(T, K, N, eps, xp, ldx, wp, ldw, yp, ldy, colsum, bias,
+                                         st);
+    default:
+        return hipErrorInvalidValue;
     }
-    const bool pipe_ok = N % 8 == 0 && ldy % 8 == 0 && ((uintptr_t)y & 15u) == 0;
-    const int64_t big_tiles = ((T + 255) / 256) * ((N + 255) / 256);
-    if (pipe_ok && K % 32 == 0 && big_tiles >= 512) {
-        // many output tiles: 256 x 256 per workgroup of 8 wavefronts, k-tiles of 32, 4 stages
-        return launch_pipe<256, 256, 4, 2, 4, 32>(T, K, N, eps, inv_k, norm, xp, ldx, wp, ldw, yp,
-                                                  ldy, st);
-    }
-    if (pipe_ok && K % 64 == 0) {
-        // 128 x 128 per workgroup of 4 wavefronts, k-tiles of 64, 2 stages (2 workgroups per CU)
-        return launch_pipe<128, 128, 2, 2, 2, 64>(T, K, N, eps, inv_k, norm, xp, ldx, wp, ldw, yp,
-                                                  ldy, st);
-    }
-    const int64_t nbm = (T + kBM - 1) / kBM, nbn = (N + kBN - 1) / kBN;
-    if (nbm * nbn > 0x7fffffff) return hipErrorInvalidConfiguration;
-    const dim3 grid((unsigned)(nbm * nbn));
-    if (norm)
-        hipLaunchKernelGGL(normproj_mfma_kernel<true>, grid, dim3(kThreads), 0, st, T, K, N, eps,
-                           inv_k, xp, ldx, wp, ldw, yp, ldy, (int)nbm, (int)nbn);
-    else
-        hipLaunchKernelGGL(normproj_mfma_kernel<false>, grid, dim3(kThreads), 0, st, T, K, N, eps,
-                           inv_k, xp, ldx, wp, ldw, yp, ldy, (int)nbm, (int)nbn);
+}
+
+hipError_t launch_fold_stats(int64_t K, int64_t N, const void* w, int64_t ldw, const void* gamma,
+                             const void* beta, int gb_bf16, float* colsum, float* bias,
+                             hipStream_t st)
+{
+    if (N == 0) return hipSuccess;
+    const int64_t nblk = (N + 63) / 64;
+    if (nblk > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(fold_stats_kernel, dim3((unsigned)nblk), dim3(kThreads), 0, st, K, N,
+                       (const uint16_t*)w, ldw, gamma, beta, gb_bf16, colsum, bias);
+    return hipGetLastError();
+}
+
+hipError_t launch_layernorm_rows(int64_t T, int64_t K, float eps, const void* x, int64_t ldx,
+                                 const void* gamma, const void* beta, int gb_bf16, void* y,
+                                 int64_t ldy, hipStream_t st)
+{
+    if (T == 0) return hipSuccess;
+    if (T > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(layernorm_rows_kernel, dim3((unsigned)T), dim3(kThreads), 0, st, K, eps,
+                       (float)(1.0 / (double)K), (const uint16_t*)x, ldx, gamma, beta, gb_bf16,
+                       (uint16_t*)y, ldy);
     return hipGetLastError();
 }
 

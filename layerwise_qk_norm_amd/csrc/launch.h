@@ -47,10 +47,27 @@ hipError_t launch_rows(const RowJob& job, hipStream_t stream);
 hipError_t launch_fold(int64_t K, int64_t N, const void* w, int64_t ldw, const void* gamma,
                        int gamma_bf16, void* w_fold, int64_t ldwf, hipStream_t stream);
 
-// y [T, N] = bf16( (x [T, K] . w [N, K]^T) * (norm ? 1/rms(x row) : 1) ).
-hipError_t launch_normproj(int64_t T, int64_t K, int64_t N, float eps, bool norm,
+// Epilogue of the projection acc = x [T, K] . w [N, K]^T.
+enum Epi : int {
+    kEpiPlain = 0,      // y = bf16(acc)
+    kEpiRms = 1,        // y = bf16(acc / rms(x row))
+    kEpiLayerNorm = 2,  // y = bf16(r * (acc - mean(x row) * colsum[n]) + bias[n]), r = 1/std
+};
+hipError_t launch_normproj(int64_t T, int64_t K, int64_t N, float eps, int epi,
                            const void* x, int64_t ldx, const void* w, int64_t ldw, void* y,
-                           int64_t ldy, hipStream_t stream);
+                           int64_t ldy, const float* colsum, const float* bias,
+                           hipStream_t stream);
+
+// colsum[n] = sum_k bf16(gamma[k] * W[k, n]), bias[n] = sum_k beta[k] * W[k, n] (bias may be
+// null; gamma / beta null mean 1 / 0; gamma and beta share one storage type).
+hipError_t launch_fold_stats(int64_t K, int64_t N, const void* w, int64_t ldw, const void* gamma,
+                             const void* beta, int gb_bf16, float* colsum, float* bias,
+                             hipStream_t stream);
+
+// y [T, K] = bf16(LayerNorm(x) * gamma + beta), rows 16-byte aligned, K % 8 == 0.
+hipError_t launch_layernorm_rows(int64_t T, int64_t K, float eps, const void* x, int64_t ldx,
+                                 const void* gamma, const void* beta, int gb_bf16, void* y,
+                                 int64_t ldy, hipStream_t stream);
 
 hipError_t launch_copy(void* dst, const void* src, int64_t nbytes, hipStream_t stream);
 

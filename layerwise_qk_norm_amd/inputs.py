@@ -21,6 +21,15 @@ Transformers", abstract), which are not available here. Shapes and distributions
   5  FlashNorm:     x [T, 2048] ~ N(0, 1), W [2048, 2048] ~ N(0, 0.02), gamma [2048] ~ N(1, 0.05),
                     all bf16
 
+Two further workloads exercise the pre-norm elimination and the LayerNorm fold ("FlashNorm",
+abstract), which the five above do not cover:
+
+  elimination:      x [T, 4096] ~ N(0, 1) (the attention block's input), pre-norm gamma
+                    ~ N(1, 0.05), Wq, Wk [4096, 4096] ~ N(0, 0.02) (OLMo-2-7B widths, 32 heads
+                    x 128), QK-Norm gammas ~ N(1, 0.05), eps 1e-6 for both norms, all bf16
+  layernorm:        as config 5 plus beta [2048] ~ N(0, 0.05), eps 1e-5; x ~ N(mean, 1) with a
+                    selectable per-workload mean (0 by default) to exercise the mean term
+
 N(mu, s) names the standard deviation s. Every (config, T, seed) gets its own PCG64 stream
 (``numpy.random.default_rng(seed)``); draws happen in a fixed order (weights first, then
 activations, then outlier columns or peer partials), so weights are identical across T within
@@ -131,6 +140,44 @@ def make_case(cfg: int, T: int, seed: int = 0) -> dict:
         out.update(x=_store(x, "bf16"), w=_store(w, "bf16"), gamma=_store(g, "bf16"),
                    gamma_dtype="bf16", K=K, N=N)
     return out
+
+
+ELIMINATION = dict(name="qk-proj-olmo2-7b-width", K=4096, nq=4096, nk=4096,
+                   Ts=(16, 2048, 4096))
+LAYERNORM = dict(name="flashnorm-layernorm-2048", K=2048, N=2048, Ts=(1, 2048, 16384))
+
+
+def make_elimination_case(T: int, seed: int = 0, K: int = ELIMINATION["K"],
+                          nq: int = ELIMINATION["nq"], nk: int = ELIMINATION["nk"]) -> dict:
+    """Pre-norm -> Q/K projection -> QK-Norm workload. Keys: x [T, K]; gamma_pre [K];
+    wq [K, nq], wk [K, nk] and their column-wise concatenation w [K, nq + nk]; gamma_q [nq],
+    gamma_k [nk]; eps_pre, eps_qk (all bf16 bits except the epsilons)."""
+    rng = np.random.default_rng(seed)
+    g1 = _normal(rng, 1.0, 0.05, (K,))
+    wq = _normal(rng, 0.0, 0.02, (K, nq))
+    wk = _normal(rng, 0.0, 0.02, (K, nk))
+    gq = _normal(rng, 1.0, 0.05, (nq,))
+    gk = _normal(rng, 1.0, 0.05, (nk,))
+    x = _normal(rng, 0.0, 1.0, (T, K))
+    wq, wk = _store(wq, "bf16"), _store(wk, "bf16")
+    return dict(T=T, seed=seed, name=ELIMINATION["name"], K=K, nq=nq, nk=nk, x=_store(x, "bf16"),
+                gamma_pre=_store(g1, "bf16"), wq=wq, wk=wk,
+                w=np.ascontiguousarray(np.concatenate([wq, wk], axis=1)),
+                gamma_q=_store(gq, "bf16"), gamma_k=_store(gk, "bf16"), eps_pre=EPS_DEFAULT,
+                eps_qk=EPS_DEFAULT)
+
+
+def make_layernorm_case(T: int, seed: int = 0, K: int = LAYERNORM["K"], N: int = LAYERNORM["N"],
+                        x_mean: float = 0.0) -> dict:
+    """LayerNorm -> projection workload. Keys: x [T, K], w [K, N], gamma [K], beta [K] (bf16
+    bits) and eps."""
+    rng = np.random.default_rng(seed)
+    w = _normal(rng, 0.0, 0.02, (K, N))
+    g = _normal(rng, 1.0, 0.05, (K,))
+    b = _normal(rng, 0.0, 0.05, (K,))
+    x = _normal(rng, x_mean, 1.0, (T, K))
+    return dict(T=T, seed=seed, name=LAYERNORM["name"], K=K, N=N, x=_store(x, "bf16"),
+                w=_store(w, "bf16"), gamma=_store(g, "bf16"), beta=_store(b, "bf16"), eps=1e-5)
 
 
 def random_rows(rng: np.random.Generator, T: int, d: int, dtype: str, scale: float = 1.0,

@@ -39,7 +39,9 @@ def test_exports_every_declared_symbol(L):
     assert set(names) >= {"qknorm_fused", "qknorm_partial_sumsq", "qknorm_apply_with_stats",
                           "normproj_fold_weight", "normproj_deferred", "normproj_unfused",
                           "qkn_device_copy", "qkn_status_string", "qkn_last_hip_error",
-                          "qknorm_shard_fused", "qknorm_shard_publish", "qknorm_shard_flag_rows"}
+                          "qknorm_shard_fused", "qknorm_shard_publish", "qknorm_shard_flag_rows",
+                          "normproj_fold_layernorm", "normproj_deferred_layernorm",
+                          "normproj_layernorm_unfused", "qknorm_project_eliminated"}
     for n in names:
         assert hasattr(L, n), n
     nm = shutil.which("nm")
@@ -145,6 +147,54 @@ def test_normproj_validation(L):
     assert L.qkn_device_copy(A, A + 8, 64, None) == ALIAS
     assert L.qkn_device_copy(A, B, -1, None) == SHAPE
     assert L.qkn_device_copy(None, B, 0, None) == OK
+
+
+@no_gpu
+def test_layernorm_projection_validation(L):
+    F = L.normproj_fold_layernorm
+    assert F(16, 16, F32, BF16, A, 16, G1, G2, B, 16, C, D, None) == DTYPE
+    assert F(16, 16, BF16, BF16, A, 8, G1, G2, B, 16, C, D, None) == SHAPE     # ldw < N
+    assert F(16, 16, BF16, BF16, A, 16, G1, G2, B + 2, 16, C, D, None) == ALIGN
+    assert F(16, 16, BF16, BF16, A, 16, G1, G2, B, 16, None, D, None) == NULL  # colsum needed
+    assert F(16, 16, BF16, BF16, A, 16, G1, G2, B, 16, A, D, None) == ALIAS    # colsum on W
+    assert F(16, 16, BF16, BF16, A, 16, G1, G2, B, 16, C, C + 32, None) == ALIAS
+    assert F(16, 16, BF16, BF16, A, 16, G1, G2, B, 16, C, G2, None) == ALIAS   # bias on beta
+    assert F(0, 16, BF16, BF16, None, 16, None, None, None, 0, None, None, None) == OK
+    P = L.normproj_deferred_layernorm
+    assert P(4, 16, 16, 1e-5, F32, A, 16, B, 16, C, D, G1, 16, None) == DTYPE
+    assert P(4, 12, 16, 1e-5, BF16, A, 12, B, 12, C, D, G1, 16, None) == ALIGN
+    assert P(4, 16, 16, -1.0, BF16, A, 16, B, 16, C, D, G1, 16, None) == EPS
+    assert P(4, 16, 16, 1e-5, BF16, A, 16, B, 16, None, D, G1, 16, None) == NULL
+    assert P(4, 16, 16, 1e-5, BF16, A, 16, B, 16, C, D, C, 16, None) == ALIAS  # y over colsum
+    assert P(4, 16, 16, 1e-5, BF16, A, 16, B, 16, C, D, D, 16, None) == ALIAS  # y over bias
+    assert P(0, 16, 16, 1e-5, BF16, None, 16, None, 16, None, None, None, 16, None) == OK
+    U = L.normproj_layernorm_unfused
+    assert U(4, 16, 16, 1e-5, BF16, BF16, A, 16, G1, G2, B, 16, A, 16, C, 16, None) == ALIAS
+    assert U(4, 16, 16, 1e-5, BF16, BF16, A, 16, G1, G2, B, 16, None, 16, C, 16, None) == NULL
+    assert U(4, 16, 16, 1e-5, BF16, BF16, A, 16, G1 + 2, G2, B, 16, D, 16, C, 16, None) == ALIGN
+    assert U(4, 16, 16, 1e-5, BF16, 9, A, 16, G1, G2, B, 16, D, 16, C, 16, None) == DTYPE
+
+
+@no_gpu
+def test_project_eliminated_validation(L):
+    def E(T=4, K=16, nq=8, nk=8, e2=1e-6, e1=1e-6, exact=0, gdt=BF16, x=A, ldx=16, w=B, ldw=16,
+          gq=G1, gk=G2, y=C, ldy=16):
+        return L.qknorm_project_eliminated(T, K, nq, nk, e2, e1, exact, gdt, x, ldx, w, ldw, gq,
+                                           gk, y, ldy, None)
+
+    assert E(nq=0) == SHAPE
+    assert E(nk=-1) == SHAPE
+    assert E(exact=2) == SHAPE
+    assert E(ldy=15) == SHAPE                  # ldy < nq + nk
+    assert E(e2=float("nan")) == EPS
+    assert E(e1=-1.0) == EPS
+    assert E(gdt=3) == DTYPE
+    assert E(K=12, ldx=12, ldw=12) == ALIGN
+    assert E(gq=None) == NULL
+    assert E(gk=None) == NULL
+    assert E(y=A) == ALIAS                     # output over x
+    assert E(y=G1 - 32) == ALIAS               # output running into gamma_q
+    assert E(T=0, x=None, w=None, gq=None, gk=None, y=None) == OK
 
 
 @no_gpu
