@@ -213,6 +213,61 @@ def normproj_setup(torch, Q, inputs, T, unfused=False):
     return (unf if unfused else deferred), flops, nbytes
 
 
+def elimination_setup(torch, Q, inputs, T, mode):
+    """Pre-norm -> Q/K projection -> QK-Norm at OLMo-2-7B widths (x [T, 4096], Wq, Wk
+    [4096, 4096]). mode: 'eliminated' (no pre-norm), 'exact' (pre-norm scale deferred to the
+    product) or 'unfused' (RMSNorm launch, plain product, fused QK-Norm launch in place)."""
+    c = inputs.make_elimination_case(T)
+    x, w = dev(torch, c["x"]), dev(torch, c["w"])
+    g1, gq, gk = dev(torch, c["gamma_pre"]), dev(torch, c["gamma_q"]), dev(torch, c["gamma_k"])
+    K, N, nq = c["K"], c["nq"] + c["nk"], c["nq"]
+    wqk = Q.normproj_fold_weight(w, g1)
+    wp = Q.normproj_fold_weight(w, None) if mode == "unfused" else None
+    del w
+    n = rotation_count(T * (K + N) * 2 + (T * K * 2 if mode == "unfused" else 0))
+    sets = [(x.clone(), torch.empty((T, N), dtype=torch.bfloat16, device="cuda"),
+             torch.empty((T, K), dtype=torch.bfloat16, device="cuda") if mode == "unfused"
+             else None) for _ in range(n)]
+
+    def fn(i):
+        xi, yi, xn = sets[i % n]
+        if mode == "unfused":
+            Q.normproj_unfused(xi, g1, wp, eps=c["eps_pre"], xn=xn, y=yi)
+            Q.qknorm_fused(yi[:, :nq], gq, yi[:, nq:], gk, eps=c["eps_qk"], q_out=yi[:, :nq],
+                           k_out=yi[:, nq:])
+        else:
+            Q.qknorm_project_eliminated(xi, wqk, nq, gq, gk, eps_qk=c["eps_qk"],
+                                        eps_pre=c["eps_pre"], exact=(mode == "exact"), y=yi)
+
+    fn.sets = n
+    return fn, 2.0 * T * K * N
+
+
+def layernorm_setup(torch, Q, inputs, T, unfused):
+    """LayerNorm -> projection at the FlashNorm shape (x [T, 2048], W [2048, 2048]): deferred
+    (one launch) or unfused (LayerNorm launch, then the plain product)."""
+    c = inputs.make_layernorm_case(T)
+    x, w = dev(torch, c["x"]), dev(torch, c["w"])
+    g, be = dev(torch, c["gamma"]), dev(torch, c["beta"])
+    K, N = c["K"], c["N"]
+    wf, cs, b = Q.normproj_fold_layernorm(w, g, be)
+    wp = Q.normproj_fold_weight(w, None)
+    n = rotation_count(T * (K + N) * 2 + (T * K * 2 if unfused else 0))
+    sets = [(x.clone(), torch.empty((T, N), dtype=torch.bfloat16, device="cuda"),
+             torch.empty((T, K), dtype=torch.bfloat16, device="cuda") if unfused else None)
+            for _ in range(n)]
+
+    def fn(i):
+        xi, yi, xn = sets[i % n]
+        if unfused:
+            Q.normproj_layernorm_unfused(xi, g, be, wp, eps=c["eps"], xn=xn, y=yi)
+        else:
+            Q.normproj_deferred_layernorm(xi, wf, cs, b, eps=c["eps"], y=yi)
+
+    fn.sets = n
+    return fn, 2.0 * T * K * N, T * K * 2 + K * N * 2 + T * N * 2
+
+
 def time_case(timer, fn, iters, warmup):
     """(eager ms per call, graph-replay ms per call)."""
     eager = timer.run(fn, iters, warmup)
@@ -355,6 +410,41 @@ def main():
                 name = "normproj_unfused" if unfused else "normproj_deferred"
                 entry = {"case": f"{name} cfg5 flashnorm-2048 T={t}", "us_per_call": cms * 1e3,
                          "us_per_call_graph": gms * 1e3, "TFLOP_s": flops / (gms * 1e-3) / 1e12}
+                if t == 1:
+                    entry["GB_s"] = b / (gms * 1e-3) / 1e9
+                    entry["frac_hbm"] = entry["GB_s"] / PEAK_HBM_GBS
+                else:
+                    entry["frac_mfma_bf16"] = entry["TFLOP_s"] / PEAK_BF16_TFLOPS
+                cases.append(entry)
+                del fn
+                torch.cuda.empty_cache()
+
+        for t in inputs.ELIMINATION["Ts"]:
+            for mode in ("eliminated", "exact", "unfused"):
+                name = {"eliminated": "qknorm_project_eliminated",
+                        "exact": "qknorm_project_eliminated_exact",
+                        "unfused": "unfused_prenorm_chain"}[mode]
+                if (t == 16 and mode != "eliminated") or not want(name):
+                    continue
+                fn, flops = elimination_setup(torch, Q, inputs, t, mode)
+                cms, gms = time_case(timer, fn, it, wu)
+                cases.append({"case": f"{name} {inputs.ELIMINATION['name']} T={t}",
+                              "us_per_call": cms * 1e3, "us_per_call_graph": gms * 1e3,
+                              "TFLOP_s": flops / (gms * 1e-3) / 1e12,
+                              "frac_mfma_bf16": flops / (gms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS})
+                del fn
+                torch.cuda.empty_cache()
+
+        for t in inputs.LAYERNORM["Ts"]:
+            for unfused in (False, True):
+                name = "normproj_layernorm_unfused" if unfused else "normproj_deferred_layernorm"
+                if (unfused and t == 1) or not want(name):
+                    continue
+                fn, flops, b = layernorm_setup(torch, Q, inputs, t, unfused)
+                cms, gms = time_case(timer, fn, it, wu)
+                entry = {"case": f"{name} {inputs.LAYERNORM['name']} T={t}",
+                         "us_per_call": cms * 1e3, "us_per_call_graph": gms * 1e3,
+                         "TFLOP_s": flops / (gms * 1e-3) / 1e12}
                 if t == 1:
                     entry["GB_s"] = b / (gms * 1e-3) / 1e9
                     entry["frac_hbm"] = entry["GB_s"] / PEAK_HBM_GBS

@@ -24,9 +24,11 @@ bool valid_dtype(int dt) { return dt == QKN_F32 || dt == QKN_BF16; }
 int64_t elem_size(int dt) { return dt == QKN_F32 ? 4 : 2; }
 bool valid_eps(float eps) { return std::isfinite(eps) && eps >= 0.0f; }
 
-// Byte range [lo, hi) touched by a [rows, cols] tensor with row stride ld.
+// Bytes touched by a [rows, cols] tensor with row stride ld: the hull [lo, hi) and, per row,
+// `width` bytes every `pitch` bytes (one row: width == pitch == hi - lo).
 struct Range {
     uintptr_t lo = 0, hi = 0;
+    uintptr_t width = 0, pitch = 0;
     bool empty() const { return hi <= lo; }
 };
 
@@ -36,12 +38,26 @@ Range span(const void* p, int64_t rows, int64_t cols, int64_t ld, int64_t es)
     if (p == nullptr || rows <= 0 || cols <= 0) return r;
     r.lo = (uintptr_t)p;
     r.hi = r.lo + (uintptr_t)(((rows - 1) * ld + cols) * es);
+    r.width = (uintptr_t)(cols * es);
+    r.pitch = rows > 1 ? (uintptr_t)(ld * es) : r.hi - r.lo;
     return r;
 }
 
+// Whether two tensors share a byte. Hulls that do not meet never do; two multi-row tensors with
+// the same pitch are disjoint when, within every period of that pitch, one's columns end
+// before the other's begin (e.g. the Q and K column blocks of one [T, nq + nk] matrix);
+// anything else whose hulls meet counts as overlapping.
 bool overlap(const Range& a, const Range& b)
 {
-    return !a.empty() && !b.empty() && a.lo < b.hi && b.lo < a.hi;
+    if (a.empty() || b.empty() || a.hi <= b.lo || b.hi <= a.lo) return false;
+    const bool multi = a.pitch > a.width && b.pitch > b.width;
+    if (multi && a.pitch == b.pitch) {
+        const Range& first = a.lo <= b.lo ? a : b;
+        const Range& second = a.lo <= b.lo ? b : a;
+        const uintptr_t off = (second.lo - first.lo) % first.pitch;
+        if (off >= first.width && off + second.width <= first.pitch) return false;
+    }
+    return true;
 }
 
 // An output may alias its own input exactly (same base, same stride); any other overlap is an

@@ -19,9 +19,11 @@
 // (global_load_lds_dwordx4, 1 KB per wavefront instruction), NST-1 tiles ahead of the one being
 // multiplied; each tile row's 16-byte chunks are XOR-swizzled so the fragment reads of 16
 // consecutive rows fall in 16 distinct bank groups. Wavefronts own WM x WN sub-tiles of 32 x 32
-// MFMA blocks; those in the first column also accumulate the rows' sums of squares from the x
-// fragments they already hold. The epilogue scales by 1/rms, rounds to bf16 and stages the tile
-// through LDS so each lane stores 16 contiguous bytes. Blocks are remapped so that each XCD
+// MFMA blocks; the WN wavefronts that hold the same rows' x fragments take turns over the k
+// steps to accumulate the row statistics (sums of squares through v_dot2c_f32_bf16 for
+// RMSNorm), and their partials are added through LDS in a fixed order. The epilogue applies the
+// row scale, rounds to bf16 and stages the tile through LDS so each lane stores 16 contiguous
+// bytes. Blocks are remapped so that each XCD
 // works on a contiguous range of row panels (one L2 holds each x panel).
 //
 // Generic kernel (any K % 8 == 0, any N): 128 x 128 tiles through padded LDS rows with register
@@ -58,22 +60,35 @@ __device__ __forceinline__ float bf16_at(const uint16_t* p, int64_t i)
     return __uint_as_float((uint32_t)p[i] << 16);
 }
 
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+// s + a.lo * a.lo + a.hi * a.hi for a packed pair of bf16 (v_dot2c_f32_bf16: the products of
+// bf16 values are exact in fp32, one instruction per two elements).
+__device__ __forceinline__ float dot2_sq(uint32_t a, float s)
+{
+    const bf16x2v v = __builtin_bit_cast(bf16x2v, a);
+    return __builtin_amdgcn_fdot2_f32_bf16(v, v, s, false);
+}
+
 // Row statistics of 8 bf16 values: RMSNorm sums squares; LayerNorm sums the values and their
-// squares after subtracting the row's shift x0.
+// squares after subtracting the row's shift x0 (fp32, so that the variance does not cancel).
 template <int EPI>
 __device__ __forceinline__ void accum_stats(const u32x4& v, float x0, float& s1, float& s2)
 {
-    const float e[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                        bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+    if constexpr (EPI == kEpiLayerNorm) {
+        const float e[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                            bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        if constexpr (EPI == kEpiLayerNorm) {
+        for (int j = 0; j < 8; ++j) {
             const float d = e[j] - x0;
             s1 += d;
             s2 = fmaf(d, d, s2);
-        } else {
-            s2 = fmaf(e[j], e[j], s2);
         }
+    } else {
+        s2 = dot2_sq(v.x, s2);
+        s2 = dot2_sq(v.y, s2);
+        s2 = dot2_sq(v.z, s2);
+        s2 = dot2_sq(v.w, s2);
     }
 }
 
@@ -161,6 +176,8 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
     __shared__ __attribute__((aligned(1024))) char smem[SMEM];
     __shared__ float rs_lds[BM];
     __shared__ float mu_lds[EPI == kEpiLayerNorm ? BM : 1];
+    // per wave column: partial row sums over its share of the k steps
+    __shared__ float part_lds[EPI == kEpiPlain ? 1 : 2 * WN * BM];
 
     const int tid = (int)threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int wm = wave / WN, wn = wave % WN;
@@ -209,7 +226,7 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
         s1[i] = s2[i] = x0[i] = 0.0f;
         if constexpr (EPI == kEpiLayerNorm) {
             const int64_t r = m0 + wm * WTM + i * 32 + frow;
-            if (wn == 0) x0[i] = bf16_at(x, (r < T ? r : T - 1) * ldx);
+            x0[i] = bf16_at(x, (r < T ? r : T - 1) * ldx);
         }
     }
 
@@ -250,7 +267,8 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
                 bfr[j] = *(const u32x4*)(Bs + r * ROWB + (swz<BK>(kc, r) << 4));
             }
             if constexpr (EPI != kEpiPlain) {
-                if (wn == 0) {
+                // the WN wavefronts holding the same rows take turns over the k steps
+                if (ks % WN == wn) {
 #pragma unroll
                     for (int i = 0; i < TM; ++i) accum_stats<EPI>(af[i], x0[i], s1[i], s2[i]);
                 }
@@ -264,18 +282,30 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
 
     if constexpr (EPI != kEpiPlain) {
         // lanes l and l + 32 summed the two halves of each 16-wide k step of the same row
-        if (wn == 0) {
 #pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const float q2 = s2[i] + __shfl_xor(s2[i], 32);
-                const float q1 = s1[i] + __shfl_xor(s1[i], 32);
-                float rs, mu;
-                row_scale<EPI>(q1, q2, x0[i], inv_k, eps, rs, mu);
-                if (lane < 32) {
-                    rs_lds[wm * WTM + i * 32 + lane] = rs;
-                    if constexpr (EPI == kEpiLayerNorm) mu_lds[wm * WTM + i * 32 + lane] = mu;
-                }
+        for (int i = 0; i < TM; ++i) {
+            const float q2 = s2[i] + __shfl_xor(s2[i], 32);
+            const float q1 = s1[i] + __shfl_xor(s1[i], 32);
+            if (lane < 32) {
+                part_lds[(0 * WN + wn) * BM + wm * WTM + i * 32 + lane] = q1;
+                part_lds[(1 * WN + wn) * BM + wm * WTM + i * 32 + lane] = q2;
             }
+        }
+        __syncthreads();
+        // one thread per tile row: add the wave columns' partials in a fixed order
+        for (int r = tid; r < BM; r += NT) {
+            float q1 = 0.0f, q2 = 0.0f;
+#pragma unroll
+            for (int c = 0; c < WN; ++c) {
+                q1 += part_lds[(0 * WN + c) * BM + r];
+                q2 += part_lds[(1 * WN + c) * BM + r];
+            }
+            const int64_t gr = m0 + r;
+            const float xr0 = EPI == kEpiLayerNorm ? bf16_at(x, (gr < T ? gr : T - 1) * ldx) : 0.0f;
+            float rs, mu;
+            row_scale<EPI>(q1, q2, xr0, inv_k, eps, rs, mu);
+            rs_lds[r] = rs;
+            if constexpr (EPI == kEpiLayerNorm) mu_lds[r] = mu;
         }
     }
     float cs[TN], bs[TN];

@@ -95,6 +95,14 @@ def test_fused_validation(L):
     assert fused(L, ko=A) == ALIAS
     assert fused(L, qo=G1) == ALIAS
     assert fused(L, qo=A, ldqo=128, ldq=64) == ALIAS     # same base, different stride
+    # Q and K as the two column blocks of one [T, 128] matrix, normalised in place: the blocks
+    # interleave row by row but never share a byte
+    blk = dict(q=A, ldq=128, qo=A, ldqo=128, k=A + 128, ldk=128, ko=A + 128, ldko=128)
+    assert fused(L, **blk) == HIPERR           # accepted; the launch then finds no device
+    # ... while a K block starting one column early runs into Q's last column
+    assert fused(L, **dict(blk, k=A + 126, ko=A + 126)) == ALIAS
+    # and blocks of different strides are judged by their hulls
+    assert fused(L, **dict(blk, ldk=136, ldko=136)) == ALIAS
 
 
 @no_gpu

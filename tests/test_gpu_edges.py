@@ -215,3 +215,20 @@ def test_concurrent_streams(Q):
         ref_q = oracle.rmsnorm_rows(c["q"], c["gamma_q"], 1e-6)
         for j in range(3):
             check_rows(to_host(outs[3 * i + j][0]), ref_q, f"stream {i} rep {j}")
+
+
+def test_fused_column_blocks_in_place(Q):
+    """Q and K as the two column blocks of one [T, nq + nk] matrix (a stacked projection's
+    output), normalised in place: the validation accepts the interleaved blocks and each block
+    is normalised over its own width."""
+    rng = np.random.default_rng(31)
+    T, nq, nk = 257, 640, 128
+    y = inputs.random_rows(rng, T, nq + nk, "bf16")
+    gq, gk = inputs.random_gamma(rng, nq, "bf16"), inputs.random_gamma(rng, nk, "bf16")
+    yd = to_dev(y)
+    Q.qknorm_fused(yd[:, :nq], to_dev(gq), yd[:, nq:], to_dev(gk), eps=1e-6, q_out=yd[:, :nq],
+                   k_out=yd[:, nq:])
+    sync()
+    got = to_host(yd)
+    check_rows(got[:, :nq], oracle.rmsnorm_rows(np.ascontiguousarray(y[:, :nq]), gq, 1e-6), "Q")
+    check_rows(got[:, nq:], oracle.rmsnorm_rows(np.ascontiguousarray(y[:, nq:]), gk, 1e-6), "K")
