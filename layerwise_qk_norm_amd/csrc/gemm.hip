@@ -29,8 +29,8 @@
 // Generic kernel (any K % 8 == 0, any N): 128 x 128 tiles through padded LDS rows with register
 // staging of the next k-tile.
 //
-// Small T (<= 16) is a matrix-vector product bound by streaming W' once: a wavefront per pair
-// of output columns, fp32 dot products reduced across the wave.
+// Small T (<= 16) is a matrix-vector product bound by streaming W' once: 16x16x32 MFMAs with the
+// tokens as rows, K split across a workgroup's wavefronts.
 
 #include "device.h"
 #include "launch.h"
@@ -500,79 +500,127 @@ __global__ __launch_bounds__(kThreads) void normproj_mfma_kernel(
     }
 }
 
-// Matrix-vector form for T <= 16: each wavefront produces kCols adjacent output columns for
-// every token; W' rows are streamed once, x rows come from cache.
-constexpr int kGemvCols = 2;
+// Matrix-vector form for T <= 16 on the matrix cores: v_mfma_f32_16x16x32_bf16 with the (up
+// to 16) tokens as the M dimension. A workgroup owns NTILE 16-column MFMA tiles and splits K
+// over its kMvWaves wavefronts, k steps of 32 interleaved; each lane loads its B fragment (8
+// consecutive k of one W' row, 16 bytes) straight from global memory, kMvUnroll steps ahead,
+// so W' is streamed once with most of it in flight, and x (the A fragments) is read once per
+// workgroup from cache. The wavefronts' partial products and row statistics are added through
+// LDS in a fixed order. Narrow outputs (N <= 4096) use one tile and 16 wavefronts per
+// workgroup so that enough workgroups stream W'.
+//
+// Fragment layout of the 16x16x32 MFMA: lane l supplies A[l % 16][8 (l / 16) .. + 7] and
+// B[8 (l / 16) .. + 7][l % 16]; it receives D[4 (l / 16) + i][l % 16] for i = 0..3.
 constexpr int kGemvMaxT = 16;
+constexpr int kMvUnroll = 8;
 
-template <int EPI>
-__global__ __launch_bounds__(kThreads) void normproj_gemv_kernel(
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4v mfma16(const u32x4& a, const u32x4& b, const f32x4v& c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+template <int EPI, int NTILE, int kMvWaves>
+__global__ __launch_bounds__(kMvWaves * 64) void normproj_mv_kernel(
     int T, int64_t K, int64_t N, float eps, float inv_k, const uint16_t* __restrict__ x,
     int64_t ldx, const uint16_t* __restrict__ w, int64_t ldw, uint16_t* __restrict__ y,
     int64_t ldy, const float* __restrict__ colsum, const float* __restrict__ bias)
 {
-    const int lane = lane_id();
-    const int64_t n_base = ((int64_t)blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave) * kGemvCols;
-    if (n_base >= N) return;
+    constexpr int kMvCols = 16 * NTILE;
+    __shared__ float red_acc[kMvWaves][NTILE][4][kWave];
+    __shared__ float red_st[kMvWaves][2][16];
+    const int lane = lane_id(), wave = (int)threadIdx.x / kWave;
+    const int r16 = lane & 15, g = lane >> 4;
+    const int64_t n0 = (int64_t)blockIdx.x * kMvCols;
+    const bool trow = r16 < T;
 
-    float acc[kGemvMaxT][kGemvCols];
-    float s1[kGemvMaxT], s2[kGemvMaxT], x0[kGemvMaxT];
+    // this lane's W' rows (rows past N are clamped: they feed columns that are never stored)
+    const uint16_t* wrow[NTILE];
 #pragma unroll
-    for (int t = 0; t < kGemvMaxT; ++t) {
-        s1[t] = s2[t] = x0[t] = 0.0f;
-        if constexpr (EPI == kEpiLayerNorm) {
-            if (t < T) x0[t] = bf16_at(x, (int64_t)t * ldx);
+    for (int j = 0; j < NTILE; ++j) {
+        const int64_t n = n0 + j * 16 + r16;
+        wrow[j] = w + (n < N ? n : N - 1) * ldw + g * 8;
+    }
+    const uint16_t* xrow = x + (int64_t)(trow ? r16 : 0) * ldx + g * 8;
+    float x0 = 0.0f;
+    if constexpr (EPI == kEpiLayerNorm) x0 = bf16_at(x, (int64_t)(trow ? r16 : 0) * ldx);
+
+    f32x4v acc[NTILE];
+#pragma unroll
+    for (int j = 0; j < NTILE; ++j) acc[j] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+    float s1 = 0.0f, s2 = 0.0f;
+
+    const int64_t nsteps = (K + 31) / 32;
+    for (int64_t base = wave; base < nsteps; base += (int64_t)kMvWaves * kMvUnroll) {
+        u32x4 a[kMvUnroll], b[NTILE][kMvUnroll];
+        bool ok[kMvUnroll];
+#pragma unroll
+        for (int u = 0; u < kMvUnroll; ++u) {
+            const int64_t st = base + (int64_t)u * kMvWaves;
+            ok[u] = st < nsteps && st * 32 + g * 8 < K;
+            a[u] = (ok[u] && trow) ? *(const u32x4*)(xrow + st * 32) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int j = 0; j < NTILE; ++j)
+                b[j][u] = ok[u] ? load_stream(wrow[j] + st * 32) : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
-        for (int c = 0; c < kGemvCols; ++c) acc[t][c] = 0.0f;
+        for (int u = 0; u < kMvUnroll; ++u) {
+            if constexpr (EPI != kEpiPlain) {
+                if (ok[u] && trow) accum_stats<EPI>(a[u], x0, s1, s2);
+            }
+#pragma unroll
+            for (int j = 0; j < NTILE; ++j) acc[j] = mfma16(a[u], b[j][u], acc[j]);
+        }
     }
 
-    for (int64_t k = (int64_t)lane * 8; k < K; k += kWave * 8) {
-        float wf[kGemvCols][8];
-#pragma unroll
-        for (int c = 0; c < kGemvCols; ++c) {
-            const int64_t n = n_base + c;
-            const u32x4 v = n < N ? load_stream(w + n * ldw + k) : u32x4{0u, 0u, 0u, 0u};
-            wf[c][0] = bf16_lo(v.x); wf[c][1] = bf16_hi(v.x);
-            wf[c][2] = bf16_lo(v.y); wf[c][3] = bf16_hi(v.y);
-            wf[c][4] = bf16_lo(v.z); wf[c][5] = bf16_hi(v.z);
-            wf[c][6] = bf16_lo(v.w); wf[c][7] = bf16_hi(v.w);
-        }
-#pragma unroll
-        for (int t = 0; t < kGemvMaxT; ++t) {
-            if (t < T) {
-                const u32x4 v = *(const u32x4*)(x + (int64_t)t * ldx + k);
-                float xf[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                               bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
-                if constexpr (EPI != kEpiPlain) accum_stats<EPI>(v, x0[t], s1[t], s2[t]);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-#pragma unroll
-                    for (int c = 0; c < kGemvCols; ++c) acc[t][c] = fmaf(xf[e], wf[c][e], acc[t][c]);
-                }
-            }
+    // lanes l, l + 16, l + 32, l + 48 hold the four k groups of row l % 16
+    if constexpr (EPI != kEpiPlain) {
+        s1 += __shfl_xor(s1, 16);
+        s2 += __shfl_xor(s2, 16);
+        s1 += __shfl_xor(s1, 32);
+        s2 += __shfl_xor(s2, 32);
+        if (lane < 16) {
+            red_st[wave][0][lane] = s1;
+            red_st[wave][1][lane] = s2;
         }
     }
+#pragma unroll
+    for (int j = 0; j < NTILE; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red_acc[wave][j][i][lane] = acc[j][i];
+    __syncthreads();
+    if (wave != 0) return;
 
 #pragma unroll
-    for (int t = 0; t < kGemvMaxT; ++t) {
-        if (t < T) {
-            float rs = 1.0f, mu = 0.0f;
-            if constexpr (EPI != kEpiPlain)
-                row_scale<EPI>(wave_sum(s1[t]), wave_sum(s2[t]), x0[t], inv_k, eps, rs, mu);
+    for (int i = 0; i < 4; ++i) {
+        const int t = 4 * g + i;
+        if (t >= T) continue;
+        float rs = 1.0f, mu = 0.0f;
+        if constexpr (EPI != kEpiPlain) {
+            float q1 = 0.0f, q2 = 0.0f;
 #pragma unroll
-            for (int c = 0; c < kGemvCols; ++c) {
-                const int64_t n = n_base + c;
-                float cs = 0.0f, bs = 0.0f;
-                if constexpr (EPI == kEpiLayerNorm) {
-                    if (n < N) {
-                        cs = colsum[n];
-                        if (bias) bs = bias[n];
-                    }
-                }
-                const float v = epilogue<EPI>(wave_sum(acc[t][c]), rs, mu, cs, bs);
-                if (lane == c && n < N) y[(int64_t)t * ldy + n] = to_bf16(v);
+            for (int v = 0; v < kMvWaves; ++v) {
+                q1 += red_st[v][0][t];
+                q2 += red_st[v][1][t];
             }
+            const float xt0 = EPI == kEpiLayerNorm ? bf16_at(x, (int64_t)t * ldx) : 0.0f;
+            row_scale<EPI>(q1, q2, xt0, inv_k, eps, rs, mu);
+        }
+#pragma unroll
+        for (int j = 0; j < NTILE; ++j) {
+            const int64_t n = n0 + j * 16 + r16;
+            if (n >= N) continue;
+            float sum = 0.0f;
+#pragma unroll
+            for (int v = 0; v < kMvWaves; ++v) sum += red_acc[v][j][i][lane];
+            float cs = 0.0f, bs = 0.0f;
+            if constexpr (EPI == kEpiLayerNorm) {
+                cs = colsum[n];
+                if (bias) bs = bias[n];
+            }
+            y[(int64_t)t * ldy + n] = to_bf16(epilogue<EPI>(sum, rs, mu, cs, bs));
         }
     }
 }
@@ -740,11 +788,17 @@ hipError_t launch_epi(int64_t T, int64_t K, int64_t N, float eps, const uint16_t
 {
     const float inv_k = (float)(1.0 / (double)K);
     if (T <= kGemvMaxT) {
-        const int64_t cols_per_block = (kThreads / kWave) * kGemvCols;
-        const int64_t nblk = (N + cols_per_block - 1) / cols_per_block;
+        const bool narrow = N <= 4096;
+        const int64_t nblk = narrow ? (N + 15) / 16 : (N + 31) / 32;
         if (nblk > 0x7fffffff) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL(normproj_gemv_kernel<EPI>, dim3((unsigned)nblk), dim3(kThreads), 0, st,
-                           (int)T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp, ldy, colsum, bias);
+        if (narrow)
+            hipLaunchKernelGGL((normproj_mv_kernel<EPI, 1, 16>), dim3((unsigned)nblk), dim3(16 * kWave),
+                               0, st, (int)T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp, ldy, colsum,
+                               bias);
+        else
+            hipLaunchKernelGGL((normproj_mv_kernel<EPI, 2, 8>), dim3((unsigned)nblk), dim3(8 * kWave),
+                               0, st, (int)T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp, ldy, colsum,
+                               bias);
         return hipGetLastError();
     }
     const bool pipe_ok = N % 8 == 0 && ldy % 8 == 0 && ((uintptr_t)yp & 15u) == 0;
