@@ -809,8 +809,9 @@ hipError_t launch_epi(int64_t T, int64_t K, int64_t N, float eps, const uint16_t
                                                        ldy, colsum, bias, st);
     }
     if (pipe_ok && K % 64 == 0) {
-        // 128 x 128 per workgroup of 4 wavefronts, k-tiles of 64, 2 stages (2 workgroups per CU)
-        return launch_pipe<128, 128, 2, 2, 2, 64, EPI>(T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp,
+        // 128 x 128 per workgroup of 8 wavefronts (32 x 64 each: two wavefronts per SIMD hide
+        // each other's LDS and barrier latency), k-tiles of 64, 2 stages (2 workgroups per CU)
+        return launch_pipe<128, 128, 4, 2, 2, 64, EPI>(T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp,
                                                        ldy, colsum, bias, st);
     }
     const int64_t nbm = (T + kBM - 1) / kBM, nbn = (N + kBN - 1) / kBN;
