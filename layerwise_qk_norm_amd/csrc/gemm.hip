@@ -803,10 +803,15 @@ hipError_t launch_epi(int64_t T, int64_t K, int64_t N, float eps, const uint16_t
     }
     const bool pipe_ok = N % 8 == 0 && ldy % 8 == 0 && ((uintptr_t)yp & 15u) == 0;
     const int64_t big_tiles = ((T + 255) / 256) * ((N + 255) / 256);
-    if (pipe_ok && K % 32 == 0 && big_tiles >= 512) {
-        // many output tiles: 256 x 256 per workgroup of 8 wavefronts, k-tiles of 32, 4 stages
-        return launch_pipe<256, 256, 4, 2, 4, 32, EPI>(T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp,
-                                                       ldy, colsum, bias, st);
+    if (pipe_ok && big_tiles >= 256) {
+        // at least one 256 x 256 tile per CU: 8 wavefronts of 64 x 128, k-tiles of 64 in 2
+        // stages (half the barriers of k-tiles of 32), or of 32 in 4 stages when K needs it
+        if (K % 64 == 0)
+            return launch_pipe<256, 256, 4, 2, 2, 64, EPI>(T, K, N, eps, inv_k, xp, ldx, wp, ldw,
+                                                           yp, ldy, colsum, bias, st);
+        if (K % 32 == 0)
+            return launch_pipe<256, 256, 4, 2, 4, 32, EPI>(T, K, N, eps, inv_k, xp, ldx, wp, ldw,
+                                                           yp, ldy, colsum, bias, st);
     }
     if (pipe_ok && K % 64 == 0) {
         // 128 x 128 per workgroup of 8 wavefronts (32 x 64 each: two wavefronts per SIMD hide
