@@ -164,28 +164,34 @@ def shard_setup(torch, Q, inputs, T):
         Q.qknorm_apply_with_stats(qi, gq, pq, eq, 4096, ki, gk, pk, ek, 4096, eps=c["eps"],
                                   q_out=qo, k_out=ko)
 
-    # single pass with the mailbox protocol: the peers' partials are published once (epoch 1)
-    # before timing, so every pass finds its flags set and measures the one-pass cost
-    nfb = Q.shard_flag_blocks(T)
-    mail_q, mail_k = torch.zeros_like(eq), torch.zeros_like(ek)
-    peer = torch.zeros((7, 2, nfb), dtype=torch.int32, device="cuda")
-    own = torch.zeros((2, nfb), dtype=torch.int32, device="cuda")
+    # single pass with the mailbox: the peers' partials are published once (epoch 1) before
+    # timing, so every pass finds its words tagged and measures the one-pass cost
+    mail_q, mail_k = Q.mailbox_words(7, T), Q.mailbox_words(7, T)
     tout = torch.zeros((1,), dtype=torch.int32, device="cuda")
-    Q.qknorm_shard_publish(eq, mail_q, peer, 1, ek, mail_k)
+    Q.qknorm_shard_publish(eq, mail_q, 1, ek, mail_k)
+    words = [(torch.empty(T, dtype=torch.int64, device="cuda"),
+              torch.empty(T, dtype=torch.int64, device="cuda")) for _ in range(n)]
 
     def k3(i):
-        qi, ki, qo, ko, pq, pk = sets[i % n]
+        qi, ki, qo, ko, _, _ = sets[i % n]
+        wq, wk = words[i % n]
         Q.qknorm_shard_fused(qi, gq, mail_q, 4096, ki, gk, mail_k, 4096, eps=c["eps"], q_out=qo,
-                             k_out=ko, psq_q=pq, psq_k=pk, peer_ready=peer, own_ready=own,
-                             epoch=1, timed_out=tout)
+                             k_out=ko, psq_q=wq, psq_k=wk, epoch=1, timed_out=tout)
 
-    k1.sets = k2.sets = k3.sets = n
-    k3.timed_out = tout
+    def k4(i):  # one workgroup per row block: producers on other devices
+        qi, ki, qo, ko, _, _ = sets[i % n]
+        wq, wk = words[i % n]
+        Q.qknorm_shard_fused(qi, gq, mail_q, 4096, ki, gk, mail_k, 4096, eps=c["eps"], q_out=qo,
+                             k_out=ko, psq_q=wq, psq_k=wk, epoch=1, timed_out=tout,
+                             persistent=False)
+
+    k1.sets = k2.sets = k3.sets = k4.sets = n
+    k3.timed_out = k4.timed_out = tout
 
     b1 = T * 2 * (512 * 2 + 4)
     b2 = T * 2 * (512 * 2 * 2 + 4 + 7 * 4) + 2 * 512 * 2
-    b3 = T * 2 * (512 * 2 * 2 + 4 + 7 * 4) + 2 * 512 * 2 + (7 * 2 + 2) * nfb * 4
-    return k1, k2, k3, b1, b2, b3
+    b3 = T * 2 * (512 * 2 * 2 + 8 + 7 * 8) + 2 * 512 * 2
+    return k1, k2, k3, k4, b1, b2, b3
 
 
 def normproj_setup(torch, Q, inputs, T, unfused=False):
@@ -385,19 +391,22 @@ def main():
                 del fn
                 torch.cuda.empty_cache()
 
-        k1, k2, k3, b1, b2, b3 = shard_setup(torch, Q, inputs, 131072)
-        for name, fn, b in (("qknorm_partial_sumsq", k1, b1), ("qknorm_apply_with_stats", k2, b2),
-                            ("qknorm_shard_fused", k3, b3)):
+        k1, k2, k3, k4, b1, b2, b3 = shard_setup(torch, Q, inputs, 131072)
+        for name, label, fn, b in (
+                ("qknorm_partial_sumsq", "", k1, b1), ("qknorm_apply_with_stats", "", k2, b2),
+                ("qknorm_shard_fused", " persistent", k3, b3),
+                ("qknorm_shard_fused", " one workgroup per row block", k4, b3)):
             if not want(name):
                 continue
             m, gm = time_case(timer, fn, it, wu)
-            cases.append({"case": f"{name} cfg4 tp8-shard T=131072", "us_per_call": m * 1e3,
-                          "us_per_call_graph": gm * 1e3, "GB_s": b / (gm * 1e-3) / 1e9,
+            cases.append({"case": f"{name}{label} cfg4 tp8-shard T=131072",
+                          "us_per_call": m * 1e3, "us_per_call_graph": gm * 1e3,
+                          "GB_s": b / (gm * 1e-3) / 1e9,
                           "frac_hbm": b / (gm * 1e-3) / 1e9 / PEAK_HBM_GBS})
             if name == "qknorm_shard_fused":
                 torch.cuda.synchronize()
                 cases[-1]["timed_out"] = int(fn.timed_out.item())
-        del k1, k2, k3
+        del k1, k2, k3, k4
         torch.cuda.empty_cache()
 
         for t in (1, 2048, 16384):

@@ -29,7 +29,7 @@
  *     runs instead of the 16-byte one). The norm-then-project calls need 16-byte aligned
  *     rows (QKN_ERR_ALIGN otherwise).
  *   - Results are deterministic: fixed reduction orders, no atomic read-modify-write (the shard
- *     mailbox flags are device-coherent stores and loads).
+ *     mailbox words are plain device-coherent 64-bit stores and loads).
  */
 #ifndef QKNORM_H
 #define QKNORM_H
@@ -118,23 +118,30 @@ QKN_API int qknorm_apply_with_stats(int64_t T, float eps, int dtype, int gamma_d
  *
  * ("SwiftQK: ...", abstract: exchange only scalar statistics, overlapping the remaining
  * peer-to-peer reduction with independent element-wise work in a deadlock-safe persistent
- * kernel.) Computes exactly what qknorm_partial_sumsq followed by qknorm_apply_with_stats
- * computes, reading x once: for each block of qknorm_shard_flag_rows() rows it
- *   1. sums squares of the slice's rows and stores them to psq_*_out [T] (fp32);
- *   2. if own_ready != NULL, stores `epoch` to own_ready[t * nfb + b] (t = 0 for Q, 1 for K,
- *      nfb = ceil(T / flag rows)) once the partials of that block are stored device-coherently;
- *   3. if peer_ready != NULL, waits until peer_ready[(e * 2 + t) * nfb + b] == epoch for every
- *      peer e < n_ext (device-coherent polls; at most max_spin polls, then sets *timed_out = 1
- *      and carries on with whatever the mailbox holds), then reads the mailbox coherently;
- *   4. S = own + ext[0][row] + ... + ext[n_ext-1][row]  (fp32, in this order),
+ * kernel.) Computes what qknorm_partial_sumsq followed by qknorm_apply_with_stats computes,
+ * reading x once. Exchanged partials travel as mailbox WORDS: uint64 = (epoch << 32) | the
+ * fp32 bits of the value, each stored and loaded as one aligned 64-bit device-coherent access,
+ * so a word that carries the current epoch carries its value (no separate flags). Per row:
+ *   1. s_own = sum of squares of the slice's row; if psq_*_out != NULL it is published there
+ *      as a word ([T], 8-byte aligned);
+ *   2. if epoch != 0, waits until mail_*[e * ld_mail + row] carries `epoch` for every peer
+ *      e < n_ext (at most max_spin polls per row block, then sets *timed_out = 1 and carries
+ *      on: the rows of that block are then unspecified); with epoch == 0 the mailbox is taken
+ *      as complete and its tags are not looked at;
+ *   3. S = s_own + value(mail[0][row]) + ... + value(mail[n_ext-1][row])  (fp32, this order),
  *      out = x * gamma * (1 / sqrt(S / d_full + eps)).
- * ext_* are the mailboxes the peers fill ([n_ext, T] fp32, row stride ld_ext >= T).
- * With peer_ready != NULL the grid is persistent and occupies at most three quarters of the
- * device's resident workgroups, so a producer of the flags running on another stream of the
- * same device always makes progress.
- *   epoch     non-zero (flags start at zero); n_ext <= 64 when peer_ready != NULL
- *   timed_out device int (required when peer_ready != NULL), set to 1 on a timeout, never
- *             cleared by the library
+ * mail_* are the mailboxes the peers fill ([n_ext, T] words, row stride ld_mail >= T,
+ * 8-byte aligned), for instance by qknorm_shard_publish. A new pass over the same mailbox uses
+ * a new epoch (mailboxes start zeroed, epoch 0 never matches a wait).
+ *   persistent  1: the grid occupies at most three quarters of the device's resident
+ *               workgroups and strides over the row blocks, so a producer of the words running
+ *               on another stream of the SAME device always makes progress (required then);
+ *               0: one workgroup per row block (faster), for producers that do not run on this
+ *               device, such as the peer ranks under tensor parallelism; every rank must then
+ *               launch the same grid so that row blocks are dispatched in the same ascending
+ *               order everywhere. Ignored when epoch == 0 (nothing waits).
+ *   n_ext     0..64
+ *   timed_out device int (required when epoch != 0), set to 1 on a timeout, never cleared
  *   slices    16-byte aligned, ld * sizeof(dtype) and d_local multiples of 16 bytes
  *             (QKN_ERR_ALIGN otherwise), d_local <= 2048 bf16 / 1024 fp32 (QKN_ERR_SHAPE)
  * Other arguments as for qknorm_apply_with_stats; K optional in the same way.
@@ -142,29 +149,27 @@ QKN_API int qknorm_apply_with_stats(int64_t T, float eps, int dtype, int gamma_d
 QKN_API int qknorm_shard_fused(int64_t T, float eps, int dtype, int gamma_dtype, int64_t n_ext,
                                const void* q, int64_t ldq, void* q_out, int64_t ldq_out,
                                const void* gamma_q, int64_t dq_local, int64_t dq_full,
-                               float* psq_q_out, const float* ext_q, int64_t ld_ext_q,
+                               uint64_t* psq_q_out, const uint64_t* mail_q, int64_t ld_mail_q,
                                const void* k, int64_t ldk, void* k_out, int64_t ldk_out,
                                const void* gamma_k, int64_t dk_local, int64_t dk_full,
-                               float* psq_k_out, const float* ext_k, int64_t ld_ext_k,
-                               const uint32_t* peer_ready, uint32_t* own_ready, uint32_t epoch,
-                               int64_t max_spin, int* timed_out, void* stream);
+                               uint64_t* psq_k_out, const uint64_t* mail_k, int64_t ld_mail_k,
+                               uint32_t epoch, int persistent, int64_t max_spin, int* timed_out,
+                               void* stream);
 
 /*
- * qknorm_shard_publish - a peer's side of the mailbox protocol of qknorm_shard_fused.
+ * qknorm_shard_publish - a peer's side of the mailbox of qknorm_shard_fused.
  *
- * For every peer e < n_ext and row block b: copies part_*[e * ld_part + row] into
- * ext_*[e * ld_ext + row] for the block's rows with device-coherent stores, waits until they
- * are acknowledged, then stores `epoch` to ready[(e * 2 + t) * nfb + b]. Under tensor parallelism each rank does
- * this for its own slot in every peer's mailbox; on one GPU it stands in for the peers.
- * part_* [n_ext, T] fp32 (row stride ld_part >= T); K optional (part_k == ext_k == NULL).
+ * For every peer e < n_ext and row t: mail_*[e * ld_mail + t] = (epoch << 32) | bits of
+ * part_*[e * ld_part + t], one device-coherent 64-bit store each. Under tensor parallelism
+ * each rank writes its own slot of every peer's mailbox this way (its psq words); on one GPU
+ * this call stands in for the peers.
+ * part_* [n_ext, T] fp32 (row stride ld_part >= T); mail_* 8-byte aligned words; K optional
+ * (part_k == mail_k == NULL).
  */
 QKN_API int qknorm_shard_publish(int64_t T, int64_t n_ext, const float* part_q, int64_t ld_part_q,
-                                 float* ext_q, int64_t ld_ext_q, const float* part_k,
-                                 int64_t ld_part_k, float* ext_k, int64_t ld_ext_k,
-                                 uint32_t* ready, uint32_t epoch, void* stream);
-
-/* Rows per flag of the shard mailbox protocol (16). */
-QKN_API int64_t qknorm_shard_flag_rows(void);
+                                 uint64_t* mail_q, int64_t ld_mail_q, const float* part_k,
+                                 int64_t ld_part_k, uint64_t* mail_k, int64_t ld_mail_k,
+                                 uint32_t epoch, void* stream);
 
 /*
  * normproj_fold_weight - fold the norm weights into the following projection (once, offline).

@@ -4,16 +4,16 @@ The computation lives in libqknorm.so (hand-written HIP kernels behind a C ABI d
 include/qknorm.h); this package is its thin Python binding plus the seeded input generator.
 """
 
-from ._lib import (QKN_BF16, QKN_F32, QknError, lib, normproj_deferred,
-                   normproj_deferred_layernorm, normproj_fold_layernorm, normproj_fold_weight,
-                   normproj_layernorm_unfused, normproj_unfused, qkn_device_copy,
-                   qknorm_apply_with_stats, qknorm_fused, qknorm_partial_sumsq,
-                   qknorm_project_eliminated, qknorm_shard_flag_rows, qknorm_shard_fused,
-                   qknorm_shard_publish, shard_flag_blocks)
+from ._lib import (QKN_BF16, QKN_F32, QknError, lib, mailbox_epochs, mailbox_values,
+                   mailbox_words, normproj_deferred, normproj_deferred_layernorm,
+                   normproj_fold_layernorm, normproj_fold_weight, normproj_layernorm_unfused,
+                   normproj_unfused, qkn_device_copy, qknorm_apply_with_stats, qknorm_fused,
+                   qknorm_partial_sumsq, qknorm_project_eliminated, qknorm_shard_fused,
+                   qknorm_shard_publish)
 
-__all__ = ["QKN_BF16", "QKN_F32", "QknError", "lib", "normproj_deferred",
-           "normproj_deferred_layernorm", "normproj_fold_layernorm", "normproj_fold_weight",
-           "normproj_layernorm_unfused", "normproj_unfused", "qkn_device_copy",
-           "qknorm_apply_with_stats", "qknorm_fused", "qknorm_partial_sumsq",
-           "qknorm_project_eliminated", "qknorm_shard_flag_rows", "qknorm_shard_fused",
-           "qknorm_shard_publish", "shard_flag_blocks"]
+__all__ = ["QKN_BF16", "QKN_F32", "QknError", "lib", "mailbox_epochs", "mailbox_values",
+           "mailbox_words", "normproj_deferred", "normproj_deferred_layernorm",
+           "normproj_fold_layernorm", "normproj_fold_weight", "normproj_layernorm_unfused",
+           "normproj_unfused", "qkn_device_copy", "qknorm_apply_with_stats", "qknorm_fused",
+           "qknorm_partial_sumsq", "qknorm_project_eliminated", "qknorm_shard_fused",
+           "qknorm_shard_publish"]

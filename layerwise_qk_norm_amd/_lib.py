@@ -53,10 +53,9 @@ _PROTOS = {
     "qkn_device_copy": [_vp, _vp, _i64, _vp],
     "qknorm_shard_fused": [_i64, _f32, _int, _int, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64,
                            _vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _vp, _i64,
-                           _vp, _vp, ctypes.c_uint32, _i64, _vp, _vp],
-    "qknorm_shard_publish": [_i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
+                           ctypes.c_uint32, _int, _i64, _vp, _vp],
+    "qknorm_shard_publish": [_i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
                              ctypes.c_uint32, _vp],
-    "qknorm_shard_flag_rows": [],
     "qkn_status_string": [_int],
     "qkn_last_hip_error": [],
 }
@@ -73,8 +72,7 @@ def lib() -> ctypes.CDLL:
         for name, args in _PROTOS.items():
             f = getattr(L, name)
             f.argtypes = args
-            f.restype = (ctypes.c_char_p if name == "qkn_status_string" else
-                         ctypes.c_int64 if name == "qknorm_shard_flag_rows" else ctypes.c_int)
+            f.restype = ctypes.c_char_p if name == "qkn_status_string" else ctypes.c_int
         _lib = L
     return _lib
 
@@ -205,57 +203,70 @@ def qknorm_apply_with_stats(q, gamma_q, psq_q, ext_q, dq_full: int, k=None, gamm
     return q_out, k_out
 
 
-def qknorm_shard_flag_rows() -> int:
-    return int(lib().qknorm_shard_flag_rows())
+def mailbox_words(n_ext: int, T: int, device="cuda"):
+    """A zeroed shard mailbox: [n_ext, T] 64-bit words (int64 storage of the uint64 words)."""
+    return _torch().zeros((n_ext, T), dtype=_torch().int64, device=device)
 
 
-def shard_flag_blocks(T: int) -> int:
-    r = qknorm_shard_flag_rows()
-    return (T + r - 1) // r
+def mailbox_values(words):
+    """fp32 values held in mailbox words (their low 32 bits), as a float32 tensor view."""
+    torch = _torch()
+    return words.view(torch.int32)[..., 0::2].view(torch.float32)
 
 
-def qknorm_shard_fused(q, gamma_q, ext_q, dq_full: int, k=None, gamma_k=None, ext_k=None,
+def mailbox_epochs(words):
+    """Epoch tags of mailbox words (their high 32 bits)."""
+    return (words >> 32) & 0xFFFFFFFF
+
+
+def qknorm_shard_fused(q, gamma_q, mail_q, dq_full: int, k=None, gamma_k=None, mail_k=None,
                        dk_full: int | None = None, eps: float = 1e-6, q_out=None, k_out=None,
-                       psq_q=None, psq_k=None, peer_ready=None, own_ready=None, epoch: int = 1,
-                       max_spin: int = 1 << 22, timed_out=None):
-    """One-pass shard stage; ext_* [n_ext, T] fp32 mailboxes, flags int32 tensors
-    (peer_ready [n_ext, 2, nfb], own_ready [2, nfb], timed_out [1]).
+                       psq_q=None, psq_k=None, epoch: int = 1, max_spin: int = 1 << 22,
+                       timed_out=None, publish: bool = True, persistent: bool = True):
+    """One-pass shard stage. mail_* [n_ext, T] int64 mailbox words filled by the peers
+    (qknorm_shard_publish); psq_* [T] int64 words receive this rank's own partials (not
+    written when publish is False). epoch == 0: the mailbox is complete, no waiting.
+    persistent=False launches one workgroup per row block (producers on other devices only).
     Returns (q_out, k_out, psq_q, psq_k)."""
     torch = _torch()
-    _check_device(q, k, gamma_q, gamma_k, ext_q, ext_k, peer_ready, own_ready, timed_out)
+    _check_device(q, k, gamma_q, gamma_k, mail_q, mail_k, timed_out)
     T, dq_local = q.shape
-    n_ext = 0 if ext_q is None else ext_q.shape[0]
+    n_ext = 0 if mail_q is None else mail_q.shape[0]
     if q_out is None:
         q_out = torch.empty_like(q)
-    if psq_q is None:
-        psq_q = torch.empty((T,), dtype=torch.float32, device=q.device)
+    if psq_q is None and publish:
+        psq_q = torch.empty((T,), dtype=torch.int64, device=q.device)
     dk_local = 0
     if k is not None:
         dk_local = k.shape[1]
         if k_out is None:
             k_out = torch.empty_like(k)
-        if psq_k is None:
-            psq_k = torch.empty((T,), dtype=torch.float32, device=q.device)
+        if psq_k is None and publish:
+            psq_k = torch.empty((T,), dtype=torch.int64, device=q.device)
+    if not publish:
+        psq_q = psq_k = None
+    if timed_out is None and epoch != 0:
+        timed_out = torch.zeros((1,), dtype=torch.int32, device=q.device)
     _check("qknorm_shard_fused", lib().qknorm_shard_fused(
         T, float(eps), _dtype_code(q), _dtype_code(gamma_q), n_ext,
         _ptr(q), _ld(q), _ptr(q_out), _ld(q_out), _ptr(gamma_q), dq_local, dq_full,
-        _ptr(psq_q), _ptr(ext_q), _ld(ext_q) if n_ext else 0,
+        _ptr(psq_q), _ptr(mail_q), _ld(mail_q) if n_ext else 0,
         _ptr(k), _ld(k) if k is not None else 0, _ptr(k_out), _ld(k_out) if k is not None else 0,
         _ptr(gamma_k), dk_local, dk_full if k is not None else 0, _ptr(psq_k),
-        _ptr(ext_k) if k is not None else None, _ld(ext_k) if (k is not None and n_ext) else 0,
-        _ptr(peer_ready), _ptr(own_ready), int(epoch), int(max_spin), _ptr(timed_out),
-        _stream(q)))
+        _ptr(mail_k) if k is not None else None, _ld(mail_k) if (k is not None and n_ext) else 0,
+        int(epoch), int(bool(persistent)), int(max_spin), _ptr(timed_out), _stream(q)))
     return q_out, k_out, psq_q, psq_k
 
 
-def qknorm_shard_publish(part_q, ext_q, ready, epoch: int, part_k=None, ext_k=None):
-    """Copy peers' partials part_* [n_ext, T] into the mailboxes ext_* and release the flags."""
-    _check_device(part_q, ext_q, ready, part_k, ext_k)
+def qknorm_shard_publish(part_q, mail_q, epoch: int, part_k=None, mail_k=None):
+    """Write peers' partials part_* [n_ext, T] fp32 into the mailboxes mail_* as words tagged
+    with epoch."""
+    _check_device(part_q, mail_q, part_k, mail_k)
     n_ext, T = part_q.shape
     _check("qknorm_shard_publish", lib().qknorm_shard_publish(
-        T, n_ext, _ptr(part_q), _ld(part_q), _ptr(ext_q), _ld(ext_q),
-        _ptr(part_k), _ld(part_k) if part_k is not None else 0, _ptr(ext_k),
-        _ld(ext_k) if ext_k is not None else 0, _ptr(ready), int(epoch), _stream(part_q)))
+        T, n_ext, _ptr(part_q), _ld(part_q), _ptr(mail_q), _ld(mail_q),
+        _ptr(part_k), _ld(part_k) if part_k is not None else 0, _ptr(mail_k),
+        _ld(mail_k) if mail_k is not None else 0, int(epoch), _stream(part_q)))
 
 
 def normproj_fold_weight(w, gamma=None, w_fold=None):

@@ -251,78 +251,70 @@ QKN_API int qknorm_apply_with_stats(int64_t T, float eps, int dtype, int gamma_d
     return hip_status(qkn::launch_rows(job, (hipStream_t)stream));
 }
 
-QKN_API int64_t qknorm_shard_flag_rows(void) { return qkn::shard_flag_rows(); }
-
 QKN_API int qknorm_shard_fused(int64_t T, float eps, int dtype, int gamma_dtype, int64_t n_ext,
                                const void* q, int64_t ldq, void* q_out, int64_t ldq_out,
                                const void* gamma_q, int64_t dq_local, int64_t dq_full,
-                               float* psq_q_out, const float* ext_q, int64_t ld_ext_q,
+                               uint64_t* psq_q_out, const uint64_t* mail_q, int64_t ld_mail_q,
                                const void* k, int64_t ldk, void* k_out, int64_t ldk_out,
                                const void* gamma_k, int64_t dk_local, int64_t dk_full,
-                               float* psq_k_out, const float* ext_k, int64_t ld_ext_k,
-                               const uint32_t* peer_ready, uint32_t* own_ready, uint32_t epoch,
-                               int64_t max_spin, int* timed_out, void* stream)
+                               uint64_t* psq_k_out, const uint64_t* mail_k, int64_t ld_mail_k,
+                               uint32_t epoch, int persistent, int64_t max_spin, int* timed_out,
+                               void* stream)
 {
-    if (T < 0 || n_ext < 0 || max_spin < 0) return QKN_ERR_SHAPE;
+    if (T < 0 || n_ext < 0 || n_ext > 64 || max_spin < 0) return QKN_ERR_SHAPE;
+    if (persistent != 0 && persistent != 1) return QKN_ERR_SHAPE;
     if (!valid_dtype(dtype) || !valid_dtype(gamma_dtype)) return QKN_ERR_DTYPE;
     if (!valid_eps(eps)) return QKN_ERR_EPS;
-    if (epoch == 0 || (peer_ready != nullptr && n_ext > 64)) return QKN_ERR_SHAPE;
     const bool has_k = !(k == nullptr && k_out == nullptr && gamma_k == nullptr &&
-                         psq_k_out == nullptr && ext_k == nullptr && dk_local == 0);
+                         psq_k_out == nullptr && mail_k == nullptr && dk_local == 0);
     const int64_t es = elem_size(dtype), gs = elem_size(gamma_dtype), epv = 16 / es;
     const int64_t dmax = 4 * 64 * epv;
     struct S {
         const void* x; int64_t ldx; void* y; int64_t ldy; const void* g; int64_t dl, df;
-        float* psq; const float* ext; int64_t lde;
-    } segs[2] = {{q, ldq, q_out, ldq_out, gamma_q, dq_local, dq_full, psq_q_out, ext_q, ld_ext_q},
-                 {k, ldk, k_out, ldk_out, gamma_k, dk_local, dk_full, psq_k_out, ext_k, ld_ext_k}};
+        uint64_t* psq; const uint64_t* mail; int64_t ldm;
+    } segs[2] = {{q, ldq, q_out, ldq_out, gamma_q, dq_local, dq_full, psq_q_out, mail_q, ld_mail_q},
+                 {k, ldk, k_out, ldk_out, gamma_k, dk_local, dk_full, psq_k_out, mail_k, ld_mail_k}};
     const int nseg = has_k ? 2 : 1;
     for (int i = 0; i < nseg; ++i) {
         const S& c = segs[i];
         int st = check_rows(T, c.x, c.ldx, c.y, c.ldy, c.dl, true);
         if (st != QKN_OK) return st;
-        if (c.df < c.dl || c.dl > dmax || (n_ext > 0 && c.lde < T)) return QKN_ERR_SHAPE;
-        if (T > 0 && (c.g == nullptr || c.psq == nullptr || (n_ext > 0 && c.ext == nullptr)))
-            return QKN_ERR_NULL;
+        if (c.df < c.dl || c.dl > dmax || (n_ext > 0 && c.ldm < T)) return QKN_ERR_SHAPE;
+        if (T > 0 && (c.g == nullptr || (n_ext > 0 && c.mail == nullptr))) return QKN_ERR_NULL;
         if (((uintptr_t)c.x & 15u) || ((uintptr_t)c.y & 15u) || ((uintptr_t)c.g & 15u) ||
-            (c.ldx * es) % 16 || (c.ldy * es) % 16 || c.dl % epv)
+            (c.ldx * es) % 16 || (c.ldy * es) % 16 || c.dl % epv || ((uintptr_t)c.psq & 7u) ||
+            ((uintptr_t)c.mail & 7u))
             return QKN_ERR_ALIGN;
     }
-    if (T > 0 && peer_ready != nullptr && timed_out == nullptr) return QKN_ERR_NULL;
+    if (T > 0 && epoch != 0 && timed_out == nullptr) return QKN_ERR_NULL;
     if (T == 0) return QKN_OK;
 
-    const int64_t nfb = (T + qkn::shard_flag_rows() - 1) / qkn::shard_flag_rows();
-    Range r_in[2], r_out[2], r_g[2], r_psq[2], r_ext[2];
+    Range r_in[2], r_out[2], r_g[2], r_psq[2], r_mail[2];
     for (int i = 0; i < nseg; ++i) {
         const S& c = segs[i];
         r_in[i] = span(c.x, T, c.dl, c.ldx, es);
         r_out[i] = span(c.y, T, c.dl, c.ldy, es);
         r_g[i] = span(c.g, 1, c.dl, c.dl, gs);
-        r_psq[i] = span(c.psq, 1, T, T, 4);
-        r_ext[i] = n_ext > 0 ? span(c.ext, n_ext, T, c.lde, 4) : Range();
+        r_psq[i] = c.psq ? span(c.psq, 1, T, T, 8) : Range();
+        r_mail[i] = n_ext > 0 ? span(c.mail, n_ext, T, c.ldm, 8) : Range();
     }
-    const Range r_peer = peer_ready ? span(peer_ready, 1, n_ext * 2 * nfb, n_ext * 2 * nfb, 4) : Range();
-    const Range r_own = own_ready ? span(own_ready, 1, 2 * nfb, 2 * nfb, 4) : Range();
     const Range r_to = timed_out ? span(timed_out, 1, 1, 1, 4) : Range();
     for (int i = 0; i < nseg; ++i) {
         // every written range against every other range (exact in-place output allowed)
-        const Range writes[4] = {r_out[i], r_psq[i], r_own, r_to};
-        for (int a = 0; a < 4; ++a) {
+        const Range writes[3] = {r_out[i], r_psq[i], r_to};
+        for (int a = 0; a < 3; ++a) {
             for (int j = 0; j < nseg; ++j) {
                 const bool self_inplace = a == 0 && j == i && segs[i].y == segs[i].x &&
                                           segs[i].ldy == segs[i].ldx;
                 if (!self_inplace && overlap(writes[a], r_in[j])) return QKN_ERR_ALIAS;
-                if (overlap(writes[a], r_g[j]) || overlap(writes[a], r_ext[j])) return QKN_ERR_ALIAS;
+                if (overlap(writes[a], r_g[j]) || overlap(writes[a], r_mail[j])) return QKN_ERR_ALIAS;
                 if (j != i && (overlap(writes[a], r_out[j]) || overlap(writes[a], r_psq[j])))
                     return QKN_ERR_ALIAS;
             }
-            if (overlap(writes[a], r_peer)) return QKN_ERR_ALIAS;
         }
-        if (overlap(r_out[i], r_psq[i]) || overlap(r_out[i], r_own) || overlap(r_out[i], r_to) ||
-            overlap(r_psq[i], r_own) || overlap(r_psq[i], r_to))
+        if (overlap(r_out[i], r_psq[i]) || overlap(r_out[i], r_to) || overlap(r_psq[i], r_to))
             return QKN_ERR_ALIAS;
     }
-    if (overlap(r_own, r_to)) return QKN_ERR_ALIAS;
 
     qkn::ShardArgs a = {};
     a.nseg = nseg;
@@ -331,45 +323,44 @@ QKN_API int qknorm_shard_fused(int64_t T, float eps, int dtype, int gamma_dtype,
     a.n_ext = n_ext;
     a.bf16 = dtype == QKN_BF16;
     a.gamma_bf16 = gamma_dtype == QKN_BF16;
-    a.peer_ready = peer_ready;
-    a.own_ready = own_ready;
     a.epoch = epoch;
+    a.persistent = persistent;
     a.max_spin = max_spin;
     a.timed_out = timed_out;
     for (int i = 0; i < nseg; ++i) {
         const S& c = segs[i];
-        a.seg[i] = {c.x, c.y, c.g, c.ldx, c.ldy, c.dl, (float)(1.0 / (double)c.df), nullptr,
-                    c.ext, c.lde, n_ext, c.psq};
+        a.seg[i] = {c.x, c.y, c.g, c.ldx, c.ldy, c.dl, (float)(1.0 / (double)c.df), c.psq,
+                    c.mail, c.ldm};
     }
     return hip_status(qkn::launch_shard_fused(a, (hipStream_t)stream));
 }
 
 QKN_API int qknorm_shard_publish(int64_t T, int64_t n_ext, const float* part_q, int64_t ld_part_q,
-                                 float* ext_q, int64_t ld_ext_q, const float* part_k,
-                                 int64_t ld_part_k, float* ext_k, int64_t ld_ext_k,
-                                 uint32_t* ready, uint32_t epoch, void* stream)
+                                 uint64_t* mail_q, int64_t ld_mail_q, const float* part_k,
+                                 int64_t ld_part_k, uint64_t* mail_k, int64_t ld_mail_k,
+                                 uint32_t epoch, void* stream)
 {
-    if (T < 0 || n_ext < 0 || epoch == 0) return QKN_ERR_SHAPE;
-    const bool has_k = !(part_k == nullptr && ext_k == nullptr);
+    if (T < 0 || n_ext < 0) return QKN_ERR_SHAPE;
+    const bool has_k = !(part_k == nullptr && mail_k == nullptr);
     if (T == 0 || n_ext == 0) return QKN_OK;
-    if (part_q == nullptr || ext_q == nullptr || ready == nullptr ||
-        (has_k && (part_k == nullptr || ext_k == nullptr)))
+    if (part_q == nullptr || mail_q == nullptr ||
+        (has_k && (part_k == nullptr || mail_k == nullptr)))
         return QKN_ERR_NULL;
-    if (ld_part_q < T || ld_ext_q < T || (has_k && (ld_part_k < T || ld_ext_k < T)))
+    if (ld_part_q < T || ld_mail_q < T || (has_k && (ld_part_k < T || ld_mail_k < T)))
         return QKN_ERR_SHAPE;
-    const int64_t nfb = (T + qkn::shard_flag_rows() - 1) / qkn::shard_flag_rows();
-    const Range rq = span(ext_q, n_ext, T, ld_ext_q, 4), rk = has_k ? span(ext_k, n_ext, T, ld_ext_k, 4) : Range();
-    const Range pq = span(part_q, n_ext, T, ld_part_q, 4), pk = has_k ? span(part_k, n_ext, T, ld_part_k, 4) : Range();
-    const Range rr = span(ready, 1, n_ext * 2 * nfb, n_ext * 2 * nfb, 4);
-    if (overlap(rq, pq) || overlap(rq, pk) || overlap(rq, rk) || overlap(rk, pq) || overlap(rk, pk) ||
-        overlap(rr, rq) || overlap(rr, rk) || overlap(rr, pq) || overlap(rr, pk))
+    if (((uintptr_t)mail_q & 7u) || ((uintptr_t)mail_k & 7u)) return QKN_ERR_ALIGN;
+    const Range rq = span(mail_q, n_ext, T, ld_mail_q, 8);
+    const Range rk = has_k ? span(mail_k, n_ext, T, ld_mail_k, 8) : Range();
+    const Range pq = span(part_q, n_ext, T, ld_part_q, 4);
+    const Range pk = has_k ? span(part_k, n_ext, T, ld_part_k, 4) : Range();
+    if (overlap(rq, pq) || overlap(rq, pk) || overlap(rq, rk) || overlap(rk, pq) || overlap(rk, pk))
         return QKN_ERR_ALIAS;
     const float* src[2] = {part_q, part_k};
     const int64_t lds[2] = {ld_part_q, ld_part_k};
-    float* dst[2] = {ext_q, ext_k};
-    const int64_t ldd[2] = {ld_ext_q, ld_ext_k};
-    return hip_status(qkn::launch_shard_publish(T, n_ext, has_k ? 2 : 1, src, lds, dst, ldd, ready,
-                                                epoch, (hipStream_t)stream));
+    uint64_t* dst[2] = {mail_q, mail_k};
+    const int64_t ldd[2] = {ld_mail_q, ld_mail_k};
+    return hip_status(qkn::launch_shard_publish(T, n_ext, has_k ? 2 : 1, src, lds, dst, ldd, epoch,
+                                                (hipStream_t)stream));
 }
 
 QKN_API int normproj_fold_weight(int64_t K, int64_t N, int dtype, int gamma_dtype,

@@ -71,24 +71,33 @@ hipError_t launch_layernorm_rows(int64_t T, int64_t K, float eps, const void* x,
 
 hipError_t launch_copy(void* dst, const void* src, int64_t nbytes, hipStream_t stream);
 
-// Single-launch shard stage (partial sums, publication, wait for peers, aggregation, scale).
+// Single-launch shard stage (partial sums, publication, wait for peers, aggregation, scale)
+// with an epoch-tagged mailbox: each exchanged partial is one 64-bit word (epoch << 32 | fp32).
+struct ShardSeg {
+    const void* x;
+    void* y;
+    const void* g;
+    int64_t ldx, ldy, d;      // slice width d
+    float inv_dfull;
+    uint64_t* psq_out;        // [T] own partials as words, or null
+    const uint64_t* mail;     // [n_ext][ld_mail] peers' partials as words
+    int64_t ld_mail;
+};
 struct ShardArgs {
-    RowSeg seg[2];               // x, y, g, ldx, ldy, d (slice), inv_dfull, ext, ld_ext, psq_out
+    ShardSeg seg[2];
     int nseg;
     int64_t T;
     float eps;
     int64_t n_ext;
     int bf16, gamma_bf16;
-    const uint32_t* peer_ready;  // [n_ext][2][ceil(T / flag rows)] or null
-    uint32_t* own_ready;         // [2][ceil(T / flag rows)] or null
-    uint32_t epoch;
+    uint32_t epoch;           // 0: mailbox complete before launch, no tag checks, no waiting
+    int persistent;           // 1: persistent three-quarter-capacity grid, 0: one per row block
     int64_t max_spin;
     int* timed_out;
 };
 hipError_t launch_shard_fused(const ShardArgs& args, hipStream_t stream);
 hipError_t launch_shard_publish(int64_t T, int64_t n_ext, int nseg, const float* const* src,
-                                const int64_t* ld_src, float* const* dst, const int64_t* ld_dst,
-                                uint32_t* ready, uint32_t epoch, hipStream_t stream);
-int64_t shard_flag_rows();
+                                const int64_t* ld_src, uint64_t* const* dst,
+                                const int64_t* ld_dst, uint32_t epoch, hipStream_t stream);
 
 }  // namespace qkn

@@ -6,20 +6,28 @@
 // independent element-wise work in a deadlock-safe persistent kernel). Compared with the two
 // launches (partial sums, then aggregation + scale) x is read once instead of twice.
 //
-// Mailbox protocol. Rows are grouped in blocks of kShardFlagRows (16). A peer's partials of
-// one row block (Q or K) are valid in the mailbox once its flag holds the current epoch. The
-// writer stores the values with device-scope coherence (written through the XCD's L2), waits
-// until those stores are acknowledged (s_waitcnt vmcnt(0)), and only then stores the flag; the
-// reader polls the flag and reads the mailbox with device-scope coherent loads. This orders the
-// data before the flag without the device-wide L2 write-back and invalidation that a
-// release/acquire pair costs on a multi-XCD GPU (they made the pass 30x slower). One GPU
-// simulates its peers with shard_publish_kernel.
+// Mailbox. Every exchanged partial travels as one 8-byte word: the epoch of the pass in the
+// upper half, the fp32 value in the lower half, stored and loaded as a single aligned 64-bit
+// access. A reader that sees its epoch in a word has that word's value, so there is no
+// separate flag, no wait for store acknowledgements and no workgroup barrier. Because tag and
+// value can only change together, even a plain, possibly stale cached load is safe to accept
+// when it shows the current epoch: the first look at the mailbox is an ordinary load in flight
+// beside the row loads, and only a word that shows an older epoch is polled again, with
+// device-scope coherent loads that go through to memory across the XCDs (so a stale line can
+// only cost a re-poll, never a wrong value or an endless wait). Words are published with
+// device-scope coherent stores. A release/acquire pair would instead write back and
+// invalidate whole L2 caches. One GPU simulates its peers with shard_publish_kernel, which
+// writes the same words.
 //
-// Deadlock safety. A reader waits only on data that other work produces: when it waits, the
-// grid is persistent and holds at most three quarters of the workgroups the device can keep
-// resident, so a producer launched on another stream of the same device always finds free
-// slots; and every wait is bounded (max_spin polls), after which the kernel records a timeout
-// and finishes, so it never hangs.
+// Deadlock safety. A reader waits only on data that other work produces, and every wait is
+// bounded (max_spin polls, after which the kernel records a timeout and finishes), so it never
+// hangs. Two launch policies: persistent, where the grid holds at most three quarters of the
+// workgroups the device can keep resident and strides over the row blocks (prefetching the
+// next block's rows), so that a producer launched on another stream of the same device always
+// finds free slots; or one workgroup per row block, for producers that do not run on this
+// device (the peers under tensor parallelism). The second streams faster; with it, progress
+// rests on every rank dispatching row blocks in the same ascending order, so that the lowest
+// unfinished block is resident, and has been published, everywhere.
 
 #include <atomic>
 
@@ -29,7 +37,9 @@ namespace qkn {
 namespace {
 
 constexpr int kShardRowsPerWave = 4;
-constexpr int kShardFlagRows = kWavesPerBlock * kShardRowsPerWave;  // one workgroup item
+constexpr int kShardItemRows = kWavesPerBlock * kShardRowsPerWave;  // rows per workgroup item
+constexpr int kPeersPerGroup = kWave / kShardRowsPerWave;           // mailbox words per lane pass
+constexpr int kMaxPeerGroups = 4;                                   // n_ext <= 64
 
 // kernel-argument view of one tensor's slice
 struct ShardTensor {
@@ -38,24 +48,38 @@ struct ShardTensor {
     const void* g;
     int64_t ldx, ldy, d;
     float inv_dfull;
-    float* psq_out;
-    const float* ext;
-    int64_t ld_ext;
+    uint64_t* psq_out;     // [T] tagged words, or null
+    const uint64_t* mail;  // [n_ext][ld_mail] tagged words
+    int64_t ld_mail;
 };
 
 struct ShardJob {
     ShardTensor t[2];
     int nseg;
-    int64_t T, nfb, n_ext;
+    int64_t T, nib, n_ext;  // nib: row blocks per tensor
     float eps;
-    const uint32_t* peer_ready;  // [n_ext][2][nfb] or null: no waiting
-    uint32_t* own_ready;         // [2][nfb] or null: no publication of flags
-    uint32_t epoch;
+    uint32_t epoch;         // 0: the mailbox is complete before launch, tags are not checked
+    int persistent;         // 1: three-quarter-capacity grid striding over the row blocks
     int64_t max_spin;
     int* timed_out;
 };
 
-template <bool BF, bool GBF, int NV>
+__device__ __forceinline__ uint64_t tagged(float v, uint32_t epoch)
+{
+    return ((uint64_t)epoch << 32) | (uint64_t)__float_as_uint(v);
+}
+
+// Registers of one workgroup item in flight: the wavefront's rows and its first look at the
+// mailbox words of those rows.
+template <int NV, int NG>
+struct ShardItem {
+    u32x4 v[kShardRowsPerWave][NV];
+    uint64_t mw[NG];
+    bool mine[NG];
+};
+
+// NG: peer groups of 16 the kernel is built for (1 when n_ext <= 16, else 4).
+template <bool BF, bool GBF, int NV, int NG>
 __global__ __launch_bounds__(kBlock) void shard_fused_kernel(ShardJob job)
 {
     constexpr int EPV = Io<BF>::kEpv;
@@ -64,33 +88,40 @@ __global__ __launch_bounds__(kBlock) void shard_fused_kernel(ShardJob job)
     using G = Gamma<BF, GBF>;
     const int lane = lane_id();
     const int wave = (int)(threadIdx.x / kWave);
-    const int64_t items = job.nfb * job.nseg;
+    const int64_t items = job.nib * job.nseg;
+    const int ngroups = (int)((job.n_ext + kPeersPerGroup - 1) / kPeersPerGroup);
+    const bool check = job.epoch != 0;
+    if ((int64_t)blockIdx.x >= items) return;
 
-    for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
-        const int tsel = item >= job.nfb ? 1 : 0;
-        const int64_t fb = tsel ? item - job.nfb : item;
-        const ShardTensor s = tsel ? job.t[1] : job.t[0];
-        const int64_t row0 = fb * kShardFlagRows + wave * RR;
-
-        // first poll of the peers' flags (lane e: peer e), in flight together with the row loads
-        const bool poll_lane = job.peer_ready != nullptr && lane < job.n_ext;
-        const uint32_t* flag = poll_lane
-            ? job.peer_ready + ((int64_t)lane * 2 + tsel) * job.nfb + fb : nullptr;
-        uint32_t seen = poll_lane
-            ? __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : job.epoch;
-
-        u32x4 graw[NV][G::kGv];
+    // gamma of both tensors, loaded once
+    u32x4 graw[2][NV][G::kGv];
+#pragma unroll
+    for (int ts = 0; ts < 2; ++ts) {
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
             const int64_t col = (int64_t)(j * kWave + lane) * EPV;
-            if (col < s.d) {
-                G::load(s.g, col, graw[j]);
+            if (ts < job.nseg && col < job.t[ts].d) {
+                G::load(job.t[ts].g, col, graw[ts][j]);
             } else {
 #pragma unroll
-                for (int h = 0; h < G::kGv; ++h) graw[j][h] = u32x4{0u, 0u, 0u, 0u};
+                for (int h = 0; h < G::kGv; ++h) graw[ts][j][h] = u32x4{0u, 0u, 0u, 0u};
             }
         }
-        u32x4 v[RR][NV];
+    }
+
+    // issue the loads of one item: the first look at the mailbox words (lane l of group g
+    // watches peer 16 g + l / RR, row row0 + l % RR; plain loads, see above) and the rows
+    auto issue = [&](int64_t item, ShardItem<NV, NG>& it) {
+        const int tsel = item >= job.nib ? 1 : 0;
+        const ShardTensor& s = job.t[tsel];
+        const int64_t row0 = (tsel ? item - job.nib : item) * kShardItemRows + wave * RR;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            const int64_t e = (int64_t)g * kPeersPerGroup + lane / RR;
+            const int64_t t = row0 + lane % RR;
+            it.mine[g] = g < ngroups && e < job.n_ext && t < job.T;
+            it.mw[g] = it.mine[g] ? s.mail[e * s.ld_mail + t] : 0;
+        }
 #pragma unroll
         for (int r = 0; r < RR; ++r) {
             const bool row_ok = row0 + r < job.T;
@@ -98,11 +129,26 @@ __global__ __launch_bounds__(kBlock) void shard_fused_kernel(ShardJob job)
 #pragma unroll
             for (int j = 0; j < NV; ++j) {
                 const int64_t col = (int64_t)(j * kWave + lane) * EPV;
-                v[r][j] = (row_ok && col < s.d) ? load_stream(xr + col * ES) : u32x4{0u, 0u, 0u, 0u};
+                it.v[r][j] = (row_ok && col < s.d) ? load_stream(xr + col * ES)
+                                                   : u32x4{0u, 0u, 0u, 0u};
             }
         }
+    };
 
-        // own partial sums of squares (lane r < RR holds row row0 + r) and their publication
+    ShardItem<NV, NG> cur, nxt;
+    int64_t item = blockIdx.x;
+    issue(item, cur);
+    for (;;) {
+        // the next item's loads are in flight while this one is finished
+        const int64_t next = item + gridDim.x;
+        const bool has_next = next < items;
+        if (has_next) issue(next, nxt);
+
+        const int tsel = item >= job.nib ? 1 : 0;
+        const ShardTensor& s = job.t[tsel];
+        const int64_t row0 = (tsel ? item - job.nib : item) * kShardItemRows + wave * RR;
+
+        // own partial sums of squares (lane r < RR holds row row0 + r), published as words
         float own = 0.0f;
 #pragma unroll
         for (int r = 0; r < RR; ++r) {
@@ -110,7 +156,7 @@ __global__ __launch_bounds__(kBlock) void shard_fused_kernel(ShardJob job)
 #pragma unroll
             for (int j = 0; j < NV; ++j) {
                 float f[EPV];
-                unpack<BF>(v[r][j], f);
+                unpack<BF>(cur.v[r][j], f);
 #pragma unroll
                 for (int e = 0; e < EPV; e += 2) {
                     a0 = fmaf(f[e], f[e], a0);
@@ -121,52 +167,45 @@ __global__ __launch_bounds__(kBlock) void shard_fused_kernel(ShardJob job)
             own = (lane == r) ? t : own;
         }
         const bool stat_lane = lane < RR && row0 + lane < job.T;
-        if (job.own_ready) {
-            if (stat_lane)
-                __hip_atomic_store(s.psq_out + row0 + lane, own, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            __builtin_amdgcn_s_waitcnt(0);  // this wavefront's partials are acknowledged ...
-            __syncthreads();                // ... for all four wavefronts of the row block ...
-            if (threadIdx.x == 0)           // ... before the flag
-                __hip_atomic_store(job.own_ready + tsel * job.nfb + fb, job.epoch,
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        } else if (stat_lane) {
-            s.psq_out[row0 + lane] = own;
-        }
+        if (s.psq_out && stat_lane)
+            __hip_atomic_store(s.psq_out + row0 + lane, tagged(own, job.epoch), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
 
-        // wait for the peers' partials of this row block (usually the first poll already saw them)
-        if (job.peer_ready) {
-            bool done = seen == job.epoch;
-            for (int64_t spin = 0; !__all(done); ++spin) {
+        // wait until every watched word carries this epoch (usually the first look did)
+        if (check) {
+            bool ok = true;
+#pragma unroll
+            for (int g = 0; g < NG; ++g)
+                ok = ok && (!cur.mine[g] || (uint32_t)(cur.mw[g] >> 32) == job.epoch);
+            for (int64_t spin = 0; !__all(ok); ++spin) {
                 if (spin >= job.max_spin) {
                     if (lane == 0) *job.timed_out = 1;
                     break;
                 }
                 __builtin_amdgcn_s_sleep(2);
-                if (!done)
-                    done = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                           job.epoch;
+                ok = true;
+#pragma unroll
+                for (int g = 0; g < NG; ++g) {
+                    if (cur.mine[g] && (uint32_t)(cur.mw[g] >> 32) != job.epoch) {
+                        const int64_t e = (int64_t)g * kPeersPerGroup + lane / RR;
+                        cur.mw[g] = __hip_atomic_load(s.mail + e * s.ld_mail + row0 + lane % RR,
+                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        ok = ok && (uint32_t)(cur.mw[g] >> 32) == job.epoch;
+                    }
+                }
             }
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);  // mailbox reads stay after the polls
         }
 
-        // S = own + peer 0 + peer 1 + ... (fp32, in that order)
+        // S = own + peer 0 + peer 1 + ... (fp32, in that order): lane r < RR gathers the value
+        // of peer e from lane (e % 16) * RR + r of group e / 16
         float S = own;
-        if (stat_lane) {
-            const int64_t t = row0 + lane;
-            for (int64_t e0 = 0; e0 < job.n_ext; e0 += 8) {
-                float p[8];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const float* a = s.ext + (e0 + u) * s.ld_ext + t;
-                    p[u] = e0 + u >= job.n_ext ? 0.0f
-                           : job.peer_ready ? __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                            : *a;
-                }
-#pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    if (e0 + u < job.n_ext) S += p[u];
-            }
+        for (int g = 0; g < NG; ++g) {
+            if (g >= ngroups) break;
+            const float val = __uint_as_float((uint32_t)cur.mw[g]);
+            const int64_t ne = job.n_ext - (int64_t)g * kPeersPerGroup;
+            const int cnt = ne < kPeersPerGroup ? (int)ne : kPeersPerGroup;
+            for (int q = 0; q < cnt; ++q) S += __shfl(val, q * RR + (lane % RR));
         }
         const float rl = rsqrtf(S * s.inv_dfull + job.eps);
 #pragma unroll
@@ -179,47 +218,44 @@ __global__ __launch_bounds__(kBlock) void shard_fused_kernel(ShardJob job)
                     const int64_t col = (int64_t)(j * kWave + lane) * EPV;
                     if (col < s.d) {
                         float f[EPV], o[EPV];
-                        unpack<BF>(v[r][j], f);
+                        unpack<BF>(cur.v[r][j], f);
 #pragma unroll
-                        for (int e = 0; e < EPV; ++e) o[e] = (f[e] * G::at(graw[j], e)) * rs;
+                        for (int e = 0; e < EPV; ++e)
+                            o[e] = (f[e] * G::at(graw[tsel][j], e)) * rs;
                         store_stream(yr + col * ES, pack<BF>(o));
                     }
                 }
             }
         }
-        if (job.own_ready) __syncthreads();  // the next item's flag barrier starts clean
+        if (!has_next) break;
+        cur = nxt;
+        item = next;
     }
 }
 
 struct PublishJob {
     const float* src[2];
     int64_t ld_src[2];
-    float* dst[2];
+    uint64_t* dst[2];
     int64_t ld_dst[2];
     int nseg;
-    int64_t T, nfb, n_ext;
-    uint32_t* ready;
+    int64_t T, n_ext;
     uint32_t epoch;
 };
 
-// One thread per (peer, tensor, row block): copy that block's partials into the mailbox with
-// device-coherent stores, wait for their acknowledgement, then store the flag.
+// One thread per (peer, tensor, row): the peer's partial, tagged with the epoch, as one
+// device-coherent 64-bit store.
 __global__ __launch_bounds__(kBlock) void shard_publish_kernel(PublishJob job)
 {
-    const int64_t total = job.n_ext * job.nseg * job.nfb;
+    const int64_t total = job.n_ext * job.nseg * job.T;
     for (int64_t idx = (int64_t)blockIdx.x * kBlock + threadIdx.x; idx < total;
          idx += (int64_t)gridDim.x * kBlock) {
-        const int64_t fb = idx % job.nfb;
-        const int tsel = (int)((idx / job.nfb) % job.nseg);
-        const int64_t e = idx / (job.nfb * job.nseg);
-        const float* src = job.src[tsel] + e * job.ld_src[tsel];
-        float* dst = job.dst[tsel] + e * job.ld_dst[tsel];
-        const int64_t t1 = (fb + 1) * kShardFlagRows < job.T ? (fb + 1) * kShardFlagRows : job.T;
-        for (int64_t t = fb * kShardFlagRows; t < t1; ++t)
-            __hip_atomic_store(dst + t, src[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __builtin_amdgcn_s_waitcnt(0);
-        __hip_atomic_store(job.ready + (e * 2 + tsel) * job.nfb + fb, job.epoch, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        const int64_t t = idx % job.T;
+        const int tsel = (int)((idx / job.T) % job.nseg);
+        const int64_t e = idx / (job.T * job.nseg);
+        const float v = job.src[tsel][e * job.ld_src[tsel] + t];
+        __hip_atomic_store(job.dst[tsel] + e * job.ld_dst[tsel] + t, tagged(v, job.epoch),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -243,18 +279,20 @@ int device_cus()
 template <bool BF, bool GBF, int NV>
 hipError_t launch_shard_nv(const ShardJob& job, hipStream_t st)
 {
-    auto kernel = shard_fused_kernel<BF, GBF, NV>;
-    const int64_t items = job.nfb * job.nseg;
+    auto kernel = job.n_ext <= kPeersPerGroup ? shard_fused_kernel<BF, GBF, NV, 1>
+                                              : shard_fused_kernel<BF, GBF, NV, kMaxPeerGroups>;
+    const int64_t items = job.nib * job.nseg;
     int64_t grid = items;
-    if (job.peer_ready) {
-        static std::atomic<int> occupancy{0};
-        int occ = occupancy.load(std::memory_order_relaxed);
+    if (job.epoch != 0 && job.persistent) {
+        static std::atomic<int> occupancy[2] = {{0}, {0}};
+        const int which = job.n_ext <= kPeersPerGroup ? 0 : 1;
+        int occ = occupancy[which].load(std::memory_order_relaxed);
         if (occ <= 0) {
             if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, kBlock, 0) !=
                     hipSuccess ||
                 occ <= 0)
                 occ = 1;
-            occupancy.store(occ, std::memory_order_relaxed);
+            occupancy[which].store(occ, std::memory_order_relaxed);
         }
         const int64_t cap = ((int64_t)device_cus() * occ * 3) / 4;
         grid = items < cap ? items : (cap > 0 ? cap : 1);
@@ -276,27 +314,24 @@ hipError_t launch_shard_types(const ShardJob& job, int nv, hipStream_t st)
 
 }  // namespace
 
-int64_t shard_flag_rows() { return kShardFlagRows; }
-
 hipError_t launch_shard_fused(const ShardArgs& a, hipStream_t st)
 {
     if (a.T == 0) return hipSuccess;
     ShardJob job = {};
     job.nseg = a.nseg;
     job.T = a.T;
-    job.nfb = (a.T + kShardFlagRows - 1) / kShardFlagRows;
+    job.nib = (a.T + kShardItemRows - 1) / kShardItemRows;
     job.n_ext = a.n_ext;
     job.eps = a.eps;
-    job.peer_ready = a.peer_ready;
-    job.own_ready = a.own_ready;
     job.epoch = a.epoch;
+    job.persistent = a.persistent;
     job.max_spin = a.max_spin;
     job.timed_out = a.timed_out;
     const int epv = a.bf16 ? 8 : 4;
     int64_t vmax = 0;
     for (int i = 0; i < a.nseg; ++i) {
-        const RowSeg& r = a.seg[i];
-        job.t[i] = {r.x, r.y, r.g, r.ldx, r.ldy, r.d, r.inv_dfull, r.psq_out, r.ext, r.ld_ext};
+        const ShardSeg& r = a.seg[i];
+        job.t[i] = {r.x, r.y, r.g, r.ldx, r.ldy, r.d, r.inv_dfull, r.psq_out, r.mail, r.ld_mail};
         const int64_t v = (r.d + epv - 1) / epv;
         vmax = v > vmax ? v : vmax;
     }
@@ -309,8 +344,8 @@ hipError_t launch_shard_fused(const ShardArgs& a, hipStream_t st)
 }
 
 hipError_t launch_shard_publish(int64_t T, int64_t n_ext, int nseg, const float* const* src,
-                                const int64_t* ld_src, float* const* dst, const int64_t* ld_dst,
-                                uint32_t* ready, uint32_t epoch, hipStream_t st)
+                                const int64_t* ld_src, uint64_t* const* dst,
+                                const int64_t* ld_dst, uint32_t epoch, hipStream_t st)
 {
     if (T == 0 || n_ext == 0) return hipSuccess;
     PublishJob job = {};
@@ -322,13 +357,11 @@ hipError_t launch_shard_publish(int64_t T, int64_t n_ext, int nseg, const float*
     }
     job.nseg = nseg;
     job.T = T;
-    job.nfb = (T + kShardFlagRows - 1) / kShardFlagRows;
     job.n_ext = n_ext;
-    job.ready = ready;
     job.epoch = epoch;
-    const int64_t total = n_ext * nseg * job.nfb;
+    const int64_t total = n_ext * nseg * T;
     int64_t grid = (total + kBlock - 1) / kBlock;
-    if (grid > 1024) grid = 1024;
+    if (grid > 4096) grid = 4096;
     hipLaunchKernelGGL(shard_publish_kernel, dim3((unsigned)grid), dim3(kBlock), 0, st, job);
     return hipGetLastError();
 }

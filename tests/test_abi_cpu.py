@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(L):
     assert set(names) >= {"qknorm_fused", "qknorm_partial_sumsq", "qknorm_apply_with_stats",
                           "normproj_fold_weight", "normproj_deferred", "normproj_unfused",
                           "qkn_device_copy", "qkn_status_string", "qkn_last_hip_error",
-                          "qknorm_shard_fused", "qknorm_shard_publish", "qknorm_shard_flag_rows",
+                          "qknorm_shard_fused", "qknorm_shard_publish",
                           "normproj_fold_layernorm", "normproj_deferred_layernorm",
                           "normproj_layernorm_unfused", "qknorm_project_eliminated"}
     for n in names:
@@ -207,32 +207,38 @@ def test_project_eliminated_validation(L):
 
 @no_gpu
 def test_shard_validation(L):
-    assert L.qknorm_shard_flag_rows() == 16
-
     def shard(T=64, eps=1e-6, dt=BF16, n_ext=7, q=A, ldq=512, qo=B, dl=512, df=4096, psq=D,
-              ext=D + 0x10000, lde=64, peer=G2, own=G2 + 0x10000, epoch=1, spin=100,
-              to=G2 + 0x20000):
+              mail=D + 0x10000, ldm=64, epoch=1, pers=1, spin=100, to=G2 + 0x20000):
         return L.qknorm_shard_fused(T, eps, dt, BF16, n_ext, q, ldq, qo, ldq, G1, dl, df, psq,
-                                    ext, lde, None, 0, None, 0, None, 0, 0, None, None, 0, peer,
-                                    own, epoch, spin, to, None)
+                                    mail, ldm, None, 0, None, 0, None, 0, 0, None, None, 0,
+                                    epoch, pers, spin, to, None)
 
-    assert shard(epoch=0) == SHAPE
     assert shard(n_ext=65) == SHAPE
+    assert shard(n_ext=-1) == SHAPE
     assert shard(spin=-1) == SHAPE
+    assert shard(pers=2) == SHAPE
     assert shard(dl=4096, ldq=4096) == SHAPE       # slice wider than 2048 bf16
     assert shard(df=256) == SHAPE                  # d_full < d_local
+    assert shard(ldm=63) == SHAPE                  # mailbox stride < T
     assert shard(q=A + 2) == ALIGN
     assert shard(dl=500, ldq=512) == ALIGN         # slice width not a multiple of 8
-    assert shard(to=None) == NULL
-    assert shard(psq=None) == NULL
-    assert shard(qo=D) == ALIAS                    # output over the partials
-    assert shard(own=D + 8) == ALIAS               # flags over the partials
-    assert shard(T=0, q=None, qo=None, psq=None, ext=None, peer=None, own=None, to=None) == OK
+    assert shard(mail=D + 0x10004) == ALIGN        # mailbox words not 8-byte aligned
+    assert shard(psq=D + 4) == ALIGN
+    assert shard(to=None) == NULL                  # waiting needs a timeout flag
+    assert shard(mail=None) == NULL
+    assert shard(qo=D) == ALIAS                    # output over the own partials
+    assert shard(psq=D + 0x10000 + 64) == ALIAS    # own partials over the mailbox
+    assert shard(to=D + 0x10000) == ALIAS          # timeout flag over the mailbox
+    assert shard(T=0, q=None, qo=None, psq=None, mail=None, to=None) == OK
+    # epoch 0 (complete mailbox): no timeout flag needed; the own partials are optional
+    assert shard(epoch=0, to=None, psq=None) == HIPERR   # accepted; no device to launch on
     P = L.qknorm_shard_publish
-    assert P(64, 7, A, 64, B, 64, None, 0, None, 0, C, 0, None) == SHAPE   # epoch 0
-    assert P(64, 7, A, 64, B, 63, None, 0, None, 0, C, 1, None) == SHAPE   # ld_ext < T
-    assert P(64, 7, A, 64, A + 64, 64, None, 0, None, 0, C, 1, None) == ALIAS
-    assert P(64, 7, A, 64, B, 64, None, 0, None, 0, None, 1, None) == NULL
+    assert P(64, 7, A, 64, B, 63, None, 0, None, 0, 1, None) == SHAPE      # ld_mail < T
+    assert P(-1, 7, A, 64, B, 64, None, 0, None, 0, 1, None) == SHAPE
+    assert P(64, 7, A, 64, B + 4, 64, None, 0, None, 0, 1, None) == ALIGN
+    assert P(64, 7, A, 64, A + 64, 64, None, 0, None, 0, 1, None) == ALIAS
+    assert P(64, 7, A, 64, None, 64, None, 0, None, 0, 1, None) == NULL
+    assert P(0, 7, None, 0, None, 0, None, 0, None, 0, 1, None) == OK
 
 
 def test_library_has_gfx950_code_object():

@@ -34,12 +34,9 @@ def test_graph_replays_match_eager():
     ln_w, ln_c, ln_b = Q.normproj_fold_layernorm(to_dev(ln[300]["w"]), to_dev(ln[300]["gamma"]),
                                                  to_dev(ln[300]["beta"]))
     # single-launch shard stage: peers published once, before capture
-    nfb = Q.shard_flag_blocks(1000)
-    mail_q, mail_k = torch.zeros_like(eq), torch.zeros_like(ek)
-    peer = torch.zeros((7, 2, nfb), dtype=torch.int32, device="cuda")
-    own = torch.zeros((2, nfb), dtype=torch.int32, device="cuda")
+    mail_q, mail_k = Q.mailbox_words(7, 1000), Q.mailbox_words(7, 1000)
     tout = torch.zeros((1,), dtype=torch.int32, device="cuda")
-    Q.qknorm_shard_publish(eq, mail_q, peer, 1, ek, mail_k)
+    Q.qknorm_shard_publish(eq, mail_q, 1, ek, mail_k)
 
     def outputs():
         return dict(qo=torch.empty_like(q), ko=torch.empty_like(k),
@@ -47,7 +44,8 @@ def test_graph_replays_match_eager():
                     so=torch.empty_like(sq), sko=torch.empty_like(sk),
                     y=torch.empty((300, 2048), dtype=torch.bfloat16, device="cuda"),
                     fo=torch.empty_like(sq), fko=torch.empty_like(sk),
-                    fpq=torch.empty(1000, device="cuda"), fpk=torch.empty(1000, device="cuda"),
+                    fpq=torch.empty(1000, dtype=torch.int64, device="cuda"),
+                    fpk=torch.empty(1000, dtype=torch.int64, device="cuda"),
                     e200=torch.empty((200, 512), dtype=torch.bfloat16, device="cuda"),
                     x200=torch.empty((200, 512), dtype=torch.bfloat16, device="cuda"),
                     e12=torch.empty((12, 512), dtype=torch.bfloat16, device="cuda"),
@@ -62,7 +60,7 @@ def test_graph_replays_match_eager():
         Q.normproj_deferred(x, wf, eps=1e-6, y=o["y"])
         Q.qknorm_shard_fused(sq, sgq, mail_q, 4096, sk, sgk, mail_k, 4096, eps=1e-6,
                              q_out=o["fo"], k_out=o["fko"], psq_q=o["fpq"], psq_k=o["fpk"],
-                             peer_ready=peer, own_ready=own, epoch=1, timed_out=tout)
+                             epoch=1, timed_out=tout)
         Q.qknorm_project_eliminated(el_x[200], el_w, 384, el_gq, el_gk, exact=False, y=o["e200"])
         Q.qknorm_project_eliminated(el_x[200], el_w, 384, el_gq, el_gk, exact=True, y=o["x200"])
         Q.qknorm_project_eliminated(el_x[12], el_w, 384, el_gq, el_gk, exact=True, y=o["e12"])

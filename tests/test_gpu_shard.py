@@ -1,7 +1,7 @@
-"""The single-launch shard stage (partial sums, publication, wait on the peers' flags,
+"""The single-launch shard stage (partial sums, publication, wait on the peers' mailbox words,
 aggregation and scale in one pass) against the fp64 oracle's two-step definition, with the
-mailbox protocol exercised in its normal, concurrent and timed-out forms. Timeouts are forced
-from the host with a tiny spin limit and flags that are never set; every kernel still exits."""
+mailbox exercised in its normal, concurrent and timed-out forms. Timeouts are forced from the
+host with a tiny spin limit and words that never carry the epoch; every kernel still exits."""
 
 import numpy as np
 import pytest
@@ -36,6 +36,18 @@ def zeros_i32(*shape):
     return torch.zeros(shape, dtype=torch.int32, device="cuda")
 
 
+def host_words(values: np.ndarray, epoch: int) -> np.ndarray:
+    """Mailbox words built on the host: epoch in the upper 32 bits, fp32 bits in the lower."""
+    bits = np.ascontiguousarray(values, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((np.uint64(epoch) << np.uint64(32)) | bits).view(np.int64)
+
+
+def words_split(words) -> tuple[np.ndarray, np.ndarray]:
+    """(fp32 values, epochs) of device mailbox words."""
+    w = to_host(words).view(np.uint64)
+    return (w & np.uint64(0xFFFFFFFF)).astype(np.uint32).view(np.float32), (w >> np.uint64(32))
+
+
 def reference(c, d_full, eps):
     pq, pk = oracle.partial_sumsq(c["q"]), oracle.partial_sumsq(c["k"])
     yq = oracle.apply_with_stats(c["q"], c["gamma_q"], pq, c["ext_q"], d_full, eps)
@@ -43,39 +55,42 @@ def reference(c, d_full, eps):
     return pq, pk, yq, yk
 
 
-def check_all(got, ref, what):
+def check_all(got, ref, what, epoch):
     qo, ko, pq, pk = got
     rpq, rpk, ryq, ryk = ref
-    check_rows(to_host(pq), rpq, f"{what} psq_q")
-    check_rows(to_host(pk), rpk, f"{what} psq_k")
+    for words, r, name in ((pq, rpq, "psq_q"), (pk, rpk, "psq_k")):
+        vals, tags = words_split(words)
+        assert np.all(tags == epoch), f"{what} {name}: own partials not tagged with the epoch"
+        check_rows(vals, r, f"{what} {name}")
     check_rows(to_host(qo), ryq, f"{what} Q")
     check_rows(to_host(ko), ryk, f"{what} K")
 
 
-def test_shard_fused_prepublished_tp8(Q):
-    """TP-8 shard at T = 131072: peers' partials published (same stream) before the pass."""
-    import torch
-
+@pytest.mark.parametrize("persistent", [True, False])
+def test_shard_fused_prepublished_tp8(Q, persistent):
+    """TP-8 shard at T = 131072: peers' partials published (same stream) before the pass, with
+    the persistent grid and with one workgroup per row block."""
     c = inputs.make_case(4, 131072)
-    T, nfb = 131072, Q.shard_flag_blocks(131072)
     q, k, gq, gk = (to_dev(c[n]) for n in ("q", "k", "gamma_q", "gamma_k"))
     part_q, part_k = to_dev(c["ext_q"]), to_dev(c["ext_k"])
-    mail_q, mail_k = torch.zeros_like(part_q), torch.zeros_like(part_k)
-    peer, own, to = zeros_i32(7, 2, nfb), zeros_i32(2, nfb), zeros_i32(1)
-    Q.qknorm_shard_publish(part_q, mail_q, peer, 1, part_k, mail_k)
-    got = Q.qknorm_shard_fused(q, gq, mail_q, 4096, k, gk, mail_k, 4096, eps=c["eps"],
-                               peer_ready=peer, own_ready=own, epoch=1, timed_out=to)
+    mail_q, mail_k = Q.mailbox_words(7, 131072), Q.mailbox_words(7, 131072)
+    to = zeros_i32(1)
+    Q.qknorm_shard_publish(part_q, mail_q, 1, part_k, mail_k)
+    got = Q.qknorm_shard_fused(q, gq, mail_q, 4096, k, gk, mail_k, 4096, eps=c["eps"], epoch=1,
+                               timed_out=to, persistent=persistent)
     sync()
     assert int(to.item()) == 0
-    assert np.array_equal(to_host(mail_q), c["ext_q"]) and np.array_equal(to_host(mail_k), c["ext_k"])
-    assert bool((own == 1).all()) and bool((peer == 1).all())
-    check_all(got, reference(c, 4096, c["eps"]), "prepublished")
+    for mail, ext in ((mail_q, c["ext_q"]), (mail_k, c["ext_k"])):
+        vals, tags = words_split(mail)
+        assert np.array_equal(vals.view(np.uint32), ext.view(np.uint32)) and np.all(tags == 1)
+    check_all(got, reference(c, 4096, c["eps"]), "prepublished", 1)
 
 
 @pytest.mark.parametrize("dtype,dl", [("bf16", 512), ("bf16", 520), ("bf16", 2048), ("f32", 8),
                                       ("f32", 1024)])
-def test_shard_fused_without_flags(Q, dtype, dl):
-    """No flags: the mailboxes are already filled. Ragged T, 1, 2 and 4 vectors per lane."""
+def test_shard_fused_complete_mailbox(Q, dtype, dl):
+    """epoch 0: the mailboxes were filled before the launch and their tags are not looked at
+    (here they carry an unrelated tag). Ragged T, 1, 2 and 4 vectors per lane."""
     rng = np.random.default_rng(dl)
     T, n_ext = 1001, 3
     c = dict(q=inputs.random_rows(rng, T, dl, dtype), k=inputs.random_rows(rng, T, dl, dtype),
@@ -83,11 +98,33 @@ def test_shard_fused_without_flags(Q, dtype, dl):
              ext_q=rng.chisquare(dl, size=(n_ext, T)).astype(np.float32),
              ext_k=rng.chisquare(dl, size=(n_ext, T)).astype(np.float32))
     d_full = dl * (n_ext + 1)
-    got = Q.qknorm_shard_fused(to_dev(c["q"]), to_dev(c["gamma_q"]), to_dev(c["ext_q"]), d_full,
-                               to_dev(c["k"]), to_dev(c["gamma_k"]), to_dev(c["ext_k"]), d_full,
-                               eps=1e-6)
+    got = Q.qknorm_shard_fused(to_dev(c["q"]), to_dev(c["gamma_q"]),
+                               to_dev(host_words(c["ext_q"], 77)), d_full, to_dev(c["k"]),
+                               to_dev(c["gamma_k"]), to_dev(host_words(c["ext_k"], 77)), d_full,
+                               eps=1e-6, epoch=0)
     sync()
-    check_all(got, reference(c, d_full, 1e-6), f"no flags d={dl}")
+    check_all(got, reference(c, d_full, 1e-6), f"complete mailbox d={dl}", 0)
+
+
+@pytest.mark.parametrize("n_ext", [1, 16, 17, 64])
+def test_shard_fused_peer_counts(Q, n_ext):
+    """Peer counts that fill one, several and all four 16-peer lane groups of the gather."""
+    rng = np.random.default_rng(n_ext)
+    T, dl = 333, 128
+    c = dict(q=inputs.random_rows(rng, T, dl, "bf16"), k=inputs.random_rows(rng, T, dl, "bf16"),
+             gamma_q=inputs.random_gamma(rng, dl, "bf16"), gamma_k=inputs.random_gamma(rng, dl, "bf16"),
+             ext_q=rng.chisquare(dl, size=(n_ext, T)).astype(np.float32),
+             ext_k=rng.chisquare(dl, size=(n_ext, T)).astype(np.float32))
+    d_full = dl * (n_ext + 1)
+    mail_q, mail_k = Q.mailbox_words(n_ext, T), Q.mailbox_words(n_ext, T)
+    Q.qknorm_shard_publish(to_dev(c["ext_q"]), mail_q, 2, to_dev(c["ext_k"]), mail_k)
+    to = zeros_i32(1)
+    got = Q.qknorm_shard_fused(to_dev(c["q"]), to_dev(c["gamma_q"]), mail_q, d_full,
+                               to_dev(c["k"]), to_dev(c["gamma_k"]), mail_k, d_full, eps=1e-6,
+                               epoch=2, timed_out=to)
+    sync()
+    assert int(to.item()) == 0
+    check_all(got, reference(c, d_full, 1e-6), f"n_ext={n_ext}", 2)
 
 
 def test_shard_fused_concurrent_publisher(Q):
@@ -96,54 +133,55 @@ def test_shard_fused_concurrent_publisher(Q):
     import torch
 
     c = inputs.make_case(4, 65536, seed=9)
-    T, nfb = 65536, Q.shard_flag_blocks(65536)
     q, k, gq, gk = (to_dev(c[n]) for n in ("q", "k", "gamma_q", "gamma_k"))
     part_q, part_k = to_dev(c["ext_q"]), to_dev(c["ext_k"])
-    mail_q, mail_k = torch.zeros_like(part_q), torch.zeros_like(part_k)
-    peer, own, to = zeros_i32(7, 2, nfb), zeros_i32(2, nfb), zeros_i32(1)
+    mail_q, mail_k = Q.mailbox_words(7, 65536), Q.mailbox_words(7, 65536)
+    to = zeros_i32(1)
     sync()
     sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
     with torch.cuda.stream(sa):
         got = Q.qknorm_shard_fused(q, gq, mail_q, 4096, k, gk, mail_k, 4096, eps=c["eps"],
-                                   peer_ready=peer, own_ready=own, epoch=3, timed_out=to)
+                                   epoch=3, timed_out=to)
     with torch.cuda.stream(sb):
-        Q.qknorm_shard_publish(part_q, mail_q, peer, 3, part_k, mail_k)
+        Q.qknorm_shard_publish(part_q, mail_q, 3, part_k, mail_k)
     sync()
     assert int(to.item()) == 0, "the pass timed out waiting for the publisher"
-    check_all(got, reference(c, 4096, c["eps"]), "concurrent")
+    check_all(got, reference(c, 4096, c["eps"]), "concurrent", 3)
 
 
+@pytest.mark.parametrize("persistent", [True, False])
 @pytest.mark.parametrize("stale", [0, 4])
-def test_shard_fused_times_out_without_flags(Q, stale):
-    """Flags never reach the epoch (never set, or left at an older epoch): with a spin limit of
-    8 polls the pass records the timeout and still finishes; its own partials are right."""
+def test_shard_fused_times_out(Q, stale, persistent):
+    """Mailbox words that never carry the epoch (never written, or left at an older epoch):
+    with a spin limit of 8 polls the pass records the timeout and still finishes; its own
+    partials are right."""
     c = inputs.make_case(4, 4096, seed=10)
-    nfb = Q.shard_flag_blocks(4096)
-    peer, to = zeros_i32(7, 2, nfb), zeros_i32(1)
-    peer.fill_(stale)
-    got = Q.qknorm_shard_fused(to_dev(c["q"]), to_dev(c["gamma_q"]), to_dev(c["ext_q"]), 4096,
-                               to_dev(c["k"]), to_dev(c["gamma_k"]), to_dev(c["ext_k"]), 4096,
-                               peer_ready=peer, epoch=5, max_spin=8, timed_out=to)
+    mail_q = to_dev(host_words(c["ext_q"], stale))
+    mail_k = to_dev(host_words(c["ext_k"], stale))
+    to = zeros_i32(1)
+    got = Q.qknorm_shard_fused(to_dev(c["q"]), to_dev(c["gamma_q"]), mail_q, 4096,
+                               to_dev(c["k"]), to_dev(c["gamma_k"]), mail_k, 4096,
+                               epoch=5, max_spin=8, timed_out=to, persistent=persistent)
     sync()
     assert int(to.item()) == 1
-    check_rows(to_host(got[2]), oracle.partial_sumsq(c["q"]), "psq_q after timeout")
+    vals, tags = words_split(got[2])
+    assert np.all(tags == 5)
+    check_rows(vals, oracle.partial_sumsq(c["q"]), "psq_q after timeout")
 
 
-def test_shard_fused_epochs_advance(Q):
+@pytest.mark.parametrize("persistent", [True, False])
+def test_shard_fused_epochs_advance(Q, persistent):
     """Two passes over the same mailboxes with successive epochs."""
-    import torch
-
     c = inputs.make_case(4, 2000, seed=11)
-    nfb = Q.shard_flag_blocks(2000)
     q, k, gq, gk = (to_dev(c[n]) for n in ("q", "k", "gamma_q", "gamma_k"))
     part_q, part_k = to_dev(c["ext_q"]), to_dev(c["ext_k"])
-    mail_q, mail_k = torch.zeros_like(part_q), torch.zeros_like(part_k)
-    peer, own, to = zeros_i32(7, 2, nfb), zeros_i32(2, nfb), zeros_i32(1)
+    mail_q, mail_k = Q.mailbox_words(7, 2000), Q.mailbox_words(7, 2000)
+    to = zeros_i32(1)
     ref = reference(c, 4096, c["eps"])
     for epoch in (1, 2):
-        Q.qknorm_shard_publish(part_q, mail_q, peer, epoch, part_k, mail_k)
+        Q.qknorm_shard_publish(part_q, mail_q, epoch, part_k, mail_k)
         got = Q.qknorm_shard_fused(q, gq, mail_q, 4096, k, gk, mail_k, 4096, eps=c["eps"],
-                                   peer_ready=peer, own_ready=own, epoch=epoch, timed_out=to)
+                                   epoch=epoch, timed_out=to, persistent=persistent)
         sync()
-        assert int(to.item()) == 0 and bool((own == epoch).all())
-        check_all(got, ref, f"epoch {epoch}")
+        assert int(to.item()) == 0
+        check_all(got, ref, f"epoch {epoch}", epoch)
