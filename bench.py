@@ -284,22 +284,38 @@ def time_case(timer, fn, iters, warmup):
 
 # ----------------------------------------------------------------------------- CPU baseline
 def cpu_baseline(inputs, T_full, budget_s=10.0):
-    """The fp64 oracle on the host, single thread, on a bounded sample of the workload: the
-    first 1024 tokens of Q and K, repeated until the budget is spent."""
+    """The fp64 oracle on the host, as it stands, on a bounded sample of the workload: the first
+    1024 tokens of Q and K. Timed once on one thread, then with the sample's rows split over
+    the host cores this process may use (at most 16, the host share of one GPU), each thread
+    calling the unmodified oracle on its rows (the C oracle releases the interpreter lock)."""
     import oracle
+    from concurrent.futures import ThreadPoolExecutor
 
     c = inputs.make_case(2, 1024)
-    done, t0 = 0, time.perf_counter()
-    while True:
-        oracle.rmsnorm_rows(c["q"], c["gamma_q"], c["eps"])
-        oracle.rmsnorm_rows(c["k"], c["gamma_k"], c["eps"])
-        done += 1024
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    return {"value": done / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+
+    def one(rows):
+        oracle.rmsnorm_rows(c["q"][rows], c["gamma_q"], c["eps"])
+        oracle.rmsnorm_rows(c["k"][rows], c["gamma_k"], c["eps"])
+
+    def timed(threads, seconds):
+        chunks = [slice(i * 1024 // threads, (i + 1) * 1024 // threads) for i in range(threads)]
+        done, t0 = 0, time.perf_counter()
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            while True:
+                list(ex.map(one, chunks))
+                done += 1024
+                el = time.perf_counter() - t0
+                if el >= seconds:
+                    return done / el, done // 1024, el
+
+    single, p1, e1 = timed(1, budget_s / 2)
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    multi, pn, en = timed(cores, budget_s / 2)
+    return {"value": multi, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"first 1024 tokens of Q and K [T, 4096] bf16 (of T={T_full}), fp64 "
-                      f"oracle, 1 thread, {done // 1024} passes in {el:.1f} s"}
+                      f"oracle, rows split over {cores} threads, {pn} passes in {en:.1f} s",
+            "single_thread_value": single,
+            "single_thread_sample": f"same sample, 1 thread, {p1} passes in {e1:.1f} s"}
 
 
 # ----------------------------------------------------------------------------- main
