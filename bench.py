@@ -249,9 +249,10 @@ def elimination_setup(torch, Q, inputs, T, mode):
     return fn, 2.0 * T * K * N
 
 
-def layernorm_setup(torch, Q, inputs, T, unfused):
+def layernorm_setup(torch, Q, inputs, T, unfused, in_product=False):
     """LayerNorm -> projection at the FlashNorm shape (x [T, 2048], W [2048, 2048]): deferred
-    (one launch) or unfused (LayerNorm launch, then the plain product)."""
+    (row statistics from a streaming pass into a workspace, or with in_product accumulated
+    inside the product) or unfused (LayerNorm launch, then the plain product)."""
     c = inputs.make_layernorm_case(T)
     x, w = dev(torch, c["x"]), dev(torch, c["w"])
     g, be = dev(torch, c["gamma"]), dev(torch, c["beta"])
@@ -262,13 +263,14 @@ def layernorm_setup(torch, Q, inputs, T, unfused):
     sets = [(x.clone(), torch.empty((T, N), dtype=torch.bfloat16, device="cuda"),
              torch.empty((T, K), dtype=torch.bfloat16, device="cuda") if unfused else None)
             for _ in range(n)]
+    ws = None if in_product else torch.empty((T, 2), dtype=torch.float32, device="cuda")
 
     def fn(i):
         xi, yi, xn = sets[i % n]
         if unfused:
             Q.normproj_layernorm_unfused(xi, g, be, wp, eps=c["eps"], xn=xn, y=yi)
         else:
-            Q.normproj_deferred_layernorm(xi, wf, cs, b, eps=c["eps"], y=yi)
+            Q.normproj_deferred_layernorm(xi, wf, cs, b, eps=c["eps"], y=yi, row_stats=ws)
 
     fn.sets = n
     return fn, 2.0 * T * K * N, T * K * 2 + K * N * 2 + T * N * 2
@@ -461,13 +463,14 @@ def main():
                 torch.cuda.empty_cache()
 
         for t in inputs.LAYERNORM["Ts"]:
-            for unfused in (False, True):
+            for unfused, in_product in ((False, False), (False, True), (True, False)):
                 name = "normproj_layernorm_unfused" if unfused else "normproj_deferred_layernorm"
-                if (unfused and t == 1) or not want(name):
+                if ((unfused or in_product) and t == 1) or not want(name):
                     continue
-                fn, flops, b = layernorm_setup(torch, Q, inputs, t, unfused)
+                fn, flops, b = layernorm_setup(torch, Q, inputs, t, unfused, in_product)
                 cms, gms = time_case(timer, fn, it, wu)
-                entry = {"case": f"{name} {inputs.LAYERNORM['name']} T={t}",
+                label = " (statistics inside the product)" if in_product else ""
+                entry = {"case": f"{name}{label} {inputs.LAYERNORM['name']} T={t}",
                          "us_per_call": cms * 1e3, "us_per_call_graph": gms * 1e3,
                          "TFLOP_s": flops / (gms * 1e-3) / 1e12}
                 if t == 1:

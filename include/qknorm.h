@@ -241,18 +241,26 @@ QKN_API int normproj_fold_layernorm(int64_t K, int64_t N, int dtype, int gamma_d
 /*
  * normproj_deferred_layernorm - LayerNorm followed by the projection, normalisation deferred.
  *
- * (Same passage.) For t < T, n < N, with the row statistics taken from the same x tiles that
- * feed the matrix cores (fp32, sums of x - x[t,0] and of its square):
+ * (Same passage.) For t < T, n < N, with the row statistics in fp32 (sums of x - x[t,0] and of
+ * its square):
  *   mu_t    = (1/K) sum_k x[t,k]
  *   r_t     = 1 / sqrt( (1/K) sum_k (x[t,k] - mu_t)^2 + eps )
  *   y[t,n]  = bf16( r_t * (sum_k x[t,k] w_fold[n,k] - mu_t colsum[n]) + bias[n] )
  *   colsum, bias  [N] fp32 from normproj_fold_layernorm; bias may be NULL (zero)
+ *   row_stats     optional [T, 2] fp32 workspace (8-byte aligned, caller-owned, must not overlap
+ *                 any other argument). When given and the product runs on the matrix-core
+ *                 kernels (T > 16, N and ldy multiples of 8, y 16-byte aligned, K a multiple of
+ *                 64, or of 32 for large shapes), (mu_t, r_t) are computed by one streaming pass
+ *                 over x into row_stats and the product applies them in its epilogue; otherwise
+ *                 (and when NULL) the product accumulates them from the x tiles it multiplies,
+ *                 and row_stats is left untouched. The pass costs one read of x; accumulating
+ *                 inside the product repeats the work once per 128- or 256-column block of y.
  * Other arguments, dtype and alignment rules as normproj_deferred.
  */
 QKN_API int normproj_deferred_layernorm(int64_t T, int64_t K, int64_t N, float eps, int dtype,
                                         const void* x, int64_t ldx, const void* w_fold,
                                         int64_t ldw, const float* colsum, const float* bias,
-                                        void* y, int64_t ldy, void* stream);
+                                        void* y, int64_t ldy, float* row_stats, void* stream);
 
 /*
  * normproj_layernorm_unfused - LayerNorm launch then plain projection (measured baseline).

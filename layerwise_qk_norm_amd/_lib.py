@@ -45,7 +45,7 @@ _PROTOS = {
     "normproj_fold_layernorm": [_i64, _i64, _int, _int, _vp, _i64, _vp, _vp, _vp, _i64, _vp, _vp,
                                 _vp],
     "normproj_deferred_layernorm": [_i64, _i64, _i64, _f32, _int, _vp, _i64, _vp, _i64, _vp, _vp,
-                                    _vp, _i64, _vp],
+                                    _vp, _i64, _vp, _vp],
     "normproj_layernorm_unfused": [_i64, _i64, _i64, _f32, _int, _int, _vp, _i64, _vp, _vp, _vp,
                                    _i64, _vp, _i64, _vp, _i64, _vp],
     "qknorm_project_eliminated": [_i64, _i64, _i64, _i64, _f32, _f32, _int, _int, _vp, _i64, _vp,
@@ -332,17 +332,30 @@ def normproj_fold_layernorm(w, gamma=None, beta=None, w_fold=None, colsum=None, 
     return w_fold, colsum, bias
 
 
-def normproj_deferred_layernorm(x, w_fold, colsum, bias=None, eps: float = 1e-5, y=None):
-    """y [T, N] = r * (x @ W' - mu * colsum) + bias (LayerNorm then project, deferred)."""
+def normproj_deferred_layernorm(x, w_fold, colsum, bias=None, eps: float = 1e-5, y=None,
+                                row_stats="auto"):
+    """y [T, N] = r * (x @ W' - mu * colsum) + bias (LayerNorm then project, deferred).
+
+    row_stats: the [T, 2] fp32 workspace for (mu, r) of each row; "auto" allocates one, None
+    passes none (the statistics are then accumulated inside the product)."""
     torch = _torch()
     _check_device(x, w_fold, colsum, bias)
     T, K = x.shape
     N = w_fold.shape[0]
     if y is None:
         y = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    if isinstance(row_stats, str):
+        if row_stats != "auto":
+            raise ValueError("row_stats must be 'auto', None or a [T, 2] float32 tensor")
+        row_stats = torch.empty((T, 2), dtype=torch.float32, device=x.device)
+    if row_stats is not None:
+        _check_device(row_stats)
+        if tuple(row_stats.shape) != (T, 2) or row_stats.dtype != torch.float32 \
+                or not row_stats.is_contiguous():
+            raise ValueError("row_stats must be a contiguous [T, 2] float32 tensor")
     _check("normproj_deferred_layernorm", lib().normproj_deferred_layernorm(
         T, K, N, float(eps), _dtype_code(x), _ptr(x), _ld(x), _ptr(w_fold), _ld(w_fold),
-        _ptr(colsum), _ptr(bias), _ptr(y), _ld(y), _stream(x)))
+        _ptr(colsum), _ptr(bias), _ptr(y), _ld(y), _ptr(row_stats), _stream(x)))
     return y
 
 

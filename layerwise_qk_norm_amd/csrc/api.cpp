@@ -407,7 +407,7 @@ QKN_API int normproj_deferred(int64_t T, int64_t K, int64_t N, float eps, int dt
     const int st = check_normproj(T, K, N, eps, dtype, x, ldx, w_fold, ldw, y, ldy);
     if (st != QKN_OK || T == 0 || N == 0) return st;
     return hip_status(qkn::launch_normproj(T, K, N, eps, qkn::kEpiRms, x, ldx, w_fold, ldw, y,
-                                           ldy, nullptr, nullptr, (hipStream_t)stream));
+                                           ldy, nullptr, nullptr, nullptr, (hipStream_t)stream));
 }
 
 QKN_API int normproj_unfused(int64_t T, int64_t K, int64_t N, float eps, int dtype,
@@ -440,7 +440,7 @@ QKN_API int normproj_unfused(int64_t T, int64_t K, int64_t N, float eps, int dty
     hipError_t e = qkn::launch_rows(job, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e);
     return hip_status(qkn::launch_normproj(T, K, N, eps, qkn::kEpiPlain, xn, ldxn, w_packed, ldw,
-                                           y, ldy, nullptr, nullptr, (hipStream_t)stream));
+                                           y, ldy, nullptr, nullptr, nullptr, (hipStream_t)stream));
 }
 
 QKN_API int normproj_fold_layernorm(int64_t K, int64_t N, int dtype, int gamma_dtype,
@@ -472,16 +472,33 @@ QKN_API int normproj_fold_layernorm(int64_t K, int64_t N, int dtype, int gamma_d
 QKN_API int normproj_deferred_layernorm(int64_t T, int64_t K, int64_t N, float eps, int dtype,
                                         const void* x, int64_t ldx, const void* w_fold,
                                         int64_t ldw, const float* colsum, const float* bias,
-                                        void* y, int64_t ldy, void* stream)
+                                        void* y, int64_t ldy, float* row_stats, void* stream)
 {
     const int st = check_normproj(T, K, N, eps, dtype, x, ldx, w_fold, ldw, y, ldy);
     if (st != QKN_OK || T == 0 || N == 0) return st;
     if (colsum == nullptr) return QKN_ERR_NULL;
+    if (((uintptr_t)row_stats & 7u) != 0) return QKN_ERR_ALIGN;
     const Range ry = span(y, T, N, ldy, 2);
-    if (overlap(ry, span(colsum, 1, N, N, 4)) || (bias && overlap(ry, span(bias, 1, N, N, 4))))
-        return QKN_ERR_ALIAS;
+    const Range rc = span(colsum, 1, N, N, 4);
+    const Range rb = bias ? span(bias, 1, N, N, 4) : Range{};
+    if (overlap(ry, rc) || (bias && overlap(ry, rb))) return QKN_ERR_ALIAS;
+    if (row_stats) {
+        const Range rs = span(row_stats, 1, 2 * T, 2 * T, 4);
+        if (overlap(rs, ry) || overlap(rs, span(x, T, K, ldx, 2)) ||
+            overlap(rs, span(w_fold, N, K, ldw, 2)) || overlap(rs, rc) ||
+            (bias && overlap(rs, rb)))
+            return QKN_ERR_ALIAS;
+    }
+    const hipStream_t s = (hipStream_t)stream;
+    if (row_stats && qkn::normproj_pipelined(T, K, N, ldy, y)) {
+        // statistics from one streaming pass over x; the product applies them in its epilogue
+        const hipError_t e = qkn::launch_layernorm_stats(T, K, eps, x, ldx, row_stats, s);
+        if (e != hipSuccess) return hip_status(e);
+        return hip_status(qkn::launch_normproj(T, K, N, eps, qkn::kEpiLayerNormStats, x, ldx,
+                                               w_fold, ldw, y, ldy, colsum, bias, row_stats, s));
+    }
     return hip_status(qkn::launch_normproj(T, K, N, eps, qkn::kEpiLayerNorm, x, ldx, w_fold, ldw,
-                                           y, ldy, colsum, bias, (hipStream_t)stream));
+                                           y, ldy, colsum, bias, nullptr, s));
 }
 
 QKN_API int normproj_layernorm_unfused(int64_t T, int64_t K, int64_t N, float eps, int dtype,
@@ -510,7 +527,7 @@ QKN_API int normproj_layernorm_unfused(int64_t T, int64_t K, int64_t N, float ep
                                               (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e);
     return hip_status(qkn::launch_normproj(T, K, N, eps, qkn::kEpiPlain, xn, ldxn, w_packed, ldw,
-                                           y, ldy, nullptr, nullptr, (hipStream_t)stream));
+                                           y, ldy, nullptr, nullptr, nullptr, (hipStream_t)stream));
 }
 
 QKN_API int qknorm_project_eliminated(int64_t T, int64_t K, int64_t nq, int64_t nk,
@@ -535,7 +552,7 @@ QKN_API int qknorm_project_eliminated(int64_t T, int64_t K, int64_t nq, int64_t 
         return QKN_ERR_ALIAS;
     // p = x W' (scaled by the pre-norm's 1/rms when exact), stored in y in bf16
     hipError_t e = qkn::launch_normproj(T, K, N, eps_pre, exact ? qkn::kEpiRms : qkn::kEpiPlain,
-                                        x, ldx, w_qk, ldw, y, ldy, nullptr, nullptr,
+                                        x, ldx, w_qk, ldw, y, ldy, nullptr, nullptr, nullptr,
                                         (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e);
     // layerwise QK-Norm of the two column blocks of y, in place

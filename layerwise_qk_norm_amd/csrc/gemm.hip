@@ -15,15 +15,20 @@
 // that the one-pass variance does not cancel for rows whose mean is large against their spread.
 //
 // Pipelined kernel (K a multiple of the k-tile, N of 8): a workgroup owns a BM x BN output tile.
-// Its k-tiles of x and W' stream into an NST-deep LDS ring by direct global->LDS DMA
-// (global_load_lds_dwordx4, 1 KB per wavefront instruction), NST-1 tiles ahead of the one being
-// multiplied; each tile row's 16-byte chunks are XOR-swizzled so the fragment reads of 16
-// consecutive rows fall in 16 distinct bank groups. Wavefronts own WM x WN sub-tiles of 32 x 32
-// MFMA blocks; the WN wavefronts that hold the same rows' x fragments take turns over the k
-// steps to accumulate the row statistics (sums of squares through v_dot2c_f32_bf16 for
-// RMSNorm), and their partials are added through LDS in a fixed order. The epilogue applies the
-// row scale, rounds to bf16 and stages the tile through LDS so each lane stores 16 contiguous
-// bytes. Blocks are remapped so that each XCD
+// Its k-tiles of x and W' reach LDS by direct global->LDS DMA (global_load_lds_dwordx4, 1 KB per
+// wavefront instruction), either through an NST-deep ring of whole k-tiles or, for 256 x 256
+// tiles with k-tiles of 64 (64 KB each, so only two whole k-tiles fit in LDS), through a ring of
+// five 32 KB parts: the x part of a k-tile is requested two k-tiles ahead and its W' part one
+// ahead, which keeps one and a half k-tiles in flight instead of one, and those requests are
+// spread over the k steps of the current k-tile rather than issued in one burst. Each tile
+// row's 16-byte chunks are XOR-swizzled so the fragment reads of 16 consecutive rows fall in
+// 16 distinct bank groups. Wavefronts own WM x WN sub-tiles of 32 x 32 MFMA blocks, with the W'
+// fragment as the MFMA's first operand so that a lane's accumulator holds one output row and
+// runs of 4 consecutive columns. The WN wavefronts that hold the same rows' x fragments take
+// turns over the k steps to accumulate the row statistics (sums of squares through
+// v_dot2c_f32_bf16 for RMSNorm), and their partials are added through LDS in a fixed order.
+// The epilogue applies the row scale, rounds to bf16, writes the tile to LDS 8 bytes at a time
+// and stores it so each lane writes 16 contiguous bytes. Blocks are remapped so that each XCD
 // works on a contiguous range of row panels (one L2 holds each x panel).
 //
 // Generic kernel (any K % 8 == 0, any N): 128 x 128 tiles through padded LDS rows with register
@@ -108,11 +113,17 @@ __device__ __forceinline__ void row_scale(float s1, float s2, float x0, float in
     }
 }
 
+// Row statistics accumulated inside the product (RMSNorm, LayerNorm) or read from memory.
+template <int EPI>
+constexpr bool kStatsInLoop = EPI == kEpiRms || EPI == kEpiLayerNorm;
+template <int EPI>
+constexpr bool kLayerNormOut = EPI == kEpiLayerNorm || EPI == kEpiLayerNormStats;
+
 template <int EPI>
 __device__ __forceinline__ float epilogue(float acc, float rs, float mu, float c, float b)
 {
     if constexpr (EPI == kEpiRms) return acc * rs;
-    if constexpr (EPI == kEpiLayerNorm) return fmaf(rs, fmaf(-mu, c, acc), b);
+    if constexpr (kLayerNormOut<EPI>) return fmaf(rs, fmaf(-mu, c, acc), b);
     return acc;
 }
 
@@ -153,31 +164,39 @@ __device__ __forceinline__ int swz(int kc, int r)
     return BK == 64 ? (kc ^ ((r >> 1) & 7)) : (kc ^ ((r >> 2) & 3));
 }
 
-template <int BM, int BN, int WM, int WN, int NST, int BK, int EPI>
+template <int BM, int BN, int WM, int WN, int NST, int BK, int EPI, bool RING>
 __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
     int64_t T, int64_t K, int64_t N, float eps, float inv_k, const uint16_t* __restrict__ x,
     int64_t ldx, const uint16_t* __restrict__ w, int64_t ldw, uint16_t* __restrict__ y,
     int64_t ldy, int nbm, int nbn, const float* __restrict__ colsum,
-    const float* __restrict__ bias)
+    const float* __restrict__ bias, const float* __restrict__ rowstats)
 {
     constexpr int NW = WM * WN, NT = NW * kWave;
     constexpr int ROWB = BK * 2;            // bytes per tile row
     constexpr int RPC = 1024 / ROWB;        // tile rows per 1 KB DMA chunk
     constexpr int LPR = ROWB / 16;          // lanes per tile row within a chunk
-    constexpr int STAGE_A = BM * ROWB, STAGE = (BM + BN) * ROWB;
-    constexpr int CA = BM / RPC, CT = (BM + BN) / RPC;
-    static_assert(CT % NW == 0, "DMA chunks must divide among the wavefronts");
-    constexpr int CPW = CT / NW;            // DMA instructions per wavefront per k-tile
+    constexpr int PART_A = BM * ROWB, PART_B = BN * ROWB, STAGE = PART_A + PART_B;
+    constexpr int CA = BM / RPC, CB = BN / RPC;
+    static_assert(CA % NW == 0 && CB % NW == 0, "DMA chunks must divide among the wavefronts");
+    constexpr int CPA = CA / NW, CPB = CB / NW;  // DMA instructions per wavefront per part
+    constexpr int KS = BK / 16;
+    static_assert(!RING || (BM == BN && (CPA + CPB) % KS == 0), "ring: five equal parts");
+    constexpr int PIPE = RING ? 5 * PART_A : NST * STAGE;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int TM = WTM / 32, TN = WTN / 32;
     constexpr int CP = BN + 8;              // epilogue tile pitch (bf16)
-    constexpr int PIPE = NST * STAGE, CTILE = BM * CP * 2;
-    constexpr int SMEM = PIPE > CTILE ? PIPE : CTILE;
+    // after the k loop the pipeline's LDS holds the output tile and the per-row / per-column
+    // epilogue operands
+    constexpr int OFF_RS = BM * CP * 2, OFF_MU = OFF_RS + BM * 4;
+    constexpr int OFF_PART = OFF_MU + BM * 4, OFF_CS = OFF_PART + 2 * WN * BM * 4;
+    constexpr int OFF_BS = OFF_CS + BN * 4, EPI_END = OFF_BS + BN * 4;
+    constexpr int SMEM = PIPE > EPI_END ? PIPE : EPI_END;
     __shared__ __attribute__((aligned(1024))) char smem[SMEM];
-    __shared__ float rs_lds[BM];
-    __shared__ float mu_lds[EPI == kEpiLayerNorm ? BM : 1];
-    // per wave column: partial row sums over its share of the k steps
-    __shared__ float part_lds[EPI == kEpiPlain ? 1 : 2 * WN * BM];
+    float* rs_lds = (float*)(smem + OFF_RS);
+    float* mu_lds = (float*)(smem + OFF_MU);
+    float* part_lds = (float*)(smem + OFF_PART);  // per wave column: partial row sums
+    float* cs_lds = (float*)(smem + OFF_CS);
+    float* bs_lds = (float*)(smem + OFF_BS);
 
     const int tid = (int)threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int wm = wave / WN, wn = wave % WN;
@@ -186,30 +205,38 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
     if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
     const int64_t m0 = (int64_t)(bid / nbn) * BM, n0 = (int64_t)(bid % nbn) * BN;
 
-    // Source of each DMA chunk this lane fetches (fixed across k). Out-of-range rows are clamped
-    // to the last valid row: they only feed output rows / columns that are never stored.
+    // Sources of the DMA chunks this lane fetches (fixed across k): chunks wave * CPA + c of the
+    // x part and wave * CPB + c of the W' part. Out-of-range rows are clamped to the last valid
+    // row: they only feed output rows / columns that are never stored.
     const int lrow = lane / LPR;
-    const uint16_t* src[CPW];
+    const uint16_t* srca[CPA];
+    const uint16_t* srcb[CPB];
 #pragma unroll
-    for (int c = 0; c < CPW; ++c) {
-        const int chunk = wave * CPW + c;
-        const int trow = (chunk < CA ? chunk : chunk - CA) * RPC + lrow;
-        const int lkc = swz<BK>(lane % LPR, trow);  // the logical chunk landing at lane % LPR
-        if (chunk < CA) {
-            const int64_t r = m0 + trow < T ? m0 + trow : T - 1;
-            src[c] = x + r * ldx + lkc * 8;
-        } else {
-            const int64_t r = n0 + trow < N ? n0 + trow : N - 1;
-            src[c] = w + r * ldw + lkc * 8;
-        }
+    for (int c = 0; c < CPA; ++c) {
+        const int trow = (wave * CPA + c) * RPC + lrow;
+        const int64_t r = m0 + trow < T ? m0 + trow : T - 1;
+        srca[c] = x + r * ldx + swz<BK>(lane % LPR, trow) * 8;
     }
-    auto issue = [&](int slot, int64_t k0) {
 #pragma unroll
-        for (int c = 0; c < CPW; ++c) {
-            const int chunk = wave * CPW + c;
-            char* dst = smem + slot * STAGE + chunk * 1024;
-            dma16((const void*)(src[c] + k0), (uint32_t)(uintptr_t)(lds_void*)dst);
-        }
+    for (int c = 0; c < CPB; ++c) {
+        const int trow = (wave * CPB + c) * RPC + lrow;
+        const int64_t r = n0 + trow < N ? n0 + trow : N - 1;
+        srcb[c] = w + r * ldw + swz<BK>(lane % LPR, trow) * 8;
+    }
+    auto dma_a = [&](int c, char* part, int64_t k0) {
+        dma16((const void*)(srca[c] + k0),
+              (uint32_t)(uintptr_t)(lds_void*)(part + (wave * CPA + c) * 1024));
+    };
+    auto dma_b = [&](int c, char* part, int64_t k0) {
+        dma16((const void*)(srcb[c] + k0),
+              (uint32_t)(uintptr_t)(lds_void*)(part + (wave * CPB + c) * 1024));
+    };
+    auto issue_tile = [&](int slot, int64_t k0) {
+        char* base = smem + slot * STAGE;
+#pragma unroll
+        for (int c = 0; c < CPA; ++c) dma_a(c, base, k0);
+#pragma unroll
+        for (int c = 0; c < CPB; ++c) dma_b(c, base + PART_A, k0);
     };
 
     f32x16 acc[TM][TN];
@@ -231,29 +258,52 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
     }
 
     const int nk = (int)(K / BK);
+    if constexpr (RING) {
+        // part p holds the x part of k-tile t when p == 2t mod 5 and its W' part when
+        // p == 2t + 1 mod 5: the x part (streamed from HBM) is requested two k-tiles ahead, the
+        // W' part (shared by every row panel, mostly cache-resident) one ahead
 #pragma unroll
-    for (int s = 0; s < NST - 1; ++s)
-        if (s < nk) issue(s, (int64_t)s * BK);
+        for (int c = 0; c < CPA; ++c) dma_a(c, smem, 0);
+#pragma unroll
+        for (int c = 0; c < CPB; ++c) dma_b(c, smem + PART_A, 0);
+        if (nk > 1) {
+#pragma unroll
+            for (int c = 0; c < CPA; ++c) dma_a(c, smem + 2 * PART_A, BK);
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < NST - 1; ++s)
+            if (s < nk) issue_tile(s, (int64_t)s * BK);
+    }
 
     for (int kt = 0; kt < nk; ++kt) {
-        // k-tile kt must have landed; up to NST-2 later tiles stay in flight
-        const int later = (nk - 1 - kt) < (NST - 2) ? (nk - 1 - kt) : (NST - 2);
-        if constexpr (NST >= 4) {
-            if (later >= 2) wait_vmcnt<2 * CPW>();
-            else if (later == 1) wait_vmcnt<CPW>();
-            else wait_vmcnt<0>();
-        } else if constexpr (NST == 3) {
-            if (later >= 1) wait_vmcnt<CPW>();
+        constexpr int CPT = CPA + CPB;
+        if constexpr (RING) {
+            // k-tile kt must have landed; the x part of k-tile kt + 1 may stay in flight
+            if (kt + 1 < nk) wait_vmcnt<CPA>();
             else wait_vmcnt<0>();
         } else {
-            wait_vmcnt<0>();
+            // k-tile kt must have landed; up to NST-2 later tiles stay in flight
+            const int later = (nk - 1 - kt) < (NST - 2) ? (nk - 1 - kt) : (NST - 2);
+            if constexpr (NST >= 4) {
+                if (later >= 2) wait_vmcnt<2 * CPT>();
+                else if (later == 1) wait_vmcnt<CPT>();
+                else wait_vmcnt<0>();
+            } else if constexpr (NST == 3) {
+                if (later >= 1) wait_vmcnt<CPT>();
+                else wait_vmcnt<0>();
+            } else {
+                wait_vmcnt<0>();
+            }
         }
-        __syncthreads();  // every wavefront's DMA has landed; slot (kt-1) % NST is free again
-        if (kt + NST - 1 < nk) issue((kt + NST - 1) % NST, (int64_t)(kt + NST - 1) * BK);
-        const char* As = smem + (kt % NST) * STAGE;
-        const char* Bs = As + STAGE_A;
+        __syncthreads();  // every wavefront's DMA has landed; the parts of k-tile kt-1 are free
+        if constexpr (!RING) {
+            if (kt + NST - 1 < nk) issue_tile((kt + NST - 1) % NST, (int64_t)(kt + NST - 1) * BK);
+        }
+        const char* As = RING ? smem + ((2 * kt) % 5) * PART_A : smem + (kt % NST) * STAGE;
+        const char* Bs = RING ? smem + ((2 * kt + 1) % 5) * PART_A : As + PART_A;
 #pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
+        for (int ks = 0; ks < KS; ++ks) {
             u32x4 af[TM], bfr[TN];
             const int kc = ks * 2 + fk;
 #pragma unroll
@@ -266,21 +316,58 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
                 const int r = wn * WTN + j * 32 + frow;
                 bfr[j] = *(const u32x4*)(Bs + r * ROWB + (swz<BK>(kc, r) << 4));
             }
-            if constexpr (EPI != kEpiPlain) {
+            if constexpr (kStatsInLoop<EPI>) {
                 // the WN wavefronts holding the same rows take turns over the k steps
                 if (ks % WN == wn) {
 #pragma unroll
                     for (int i = 0; i < TM; ++i) accum_stats<EPI>(af[i], x0[i], s1[i], s2[i]);
                 }
             }
+            // W' fragment as the MFMA's A operand: the accumulator of a 32 x 32 block then holds
+            // output row (token) lane % 32 and 4 consecutive columns per group of 4 values
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+                for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(bfr[j], af[i], acc[i][j]);
+            if constexpr (RING) {
+                // this k step's share of the next DMA requests, spread over the k steps so the
+                // MFMA issue is never held behind a burst of them: the W' part of k-tile kt+1
+                // first, then the x part of k-tile kt+2 (parts freed by the barrier above)
+                constexpr int PER = CPT / KS;
+#pragma unroll
+                for (int h = 0; h < PER; ++h) {
+                    const int c = ks * PER + h;
+                    if (c < CPB) {
+                        if (kt + 1 < nk)
+                            dma_b(c, smem + ((2 * kt + 3) % 5) * PART_A, (int64_t)(kt + 1) * BK);
+                    } else {
+                        if (kt + 2 < nk)
+                            dma_a(c - CPB, smem + ((2 * kt + 4) % 5) * PART_A,
+                                  (int64_t)(kt + 2) * BK);
+                    }
+                }
+            }
         }
     }
+    __syncthreads();  // every wavefront is done with the pipeline's LDS (no DMA is in flight)
 
-    if constexpr (EPI != kEpiPlain) {
+    if constexpr (kLayerNormOut<EPI>) {
+        for (int c = tid; c < BN; c += NT) {
+            const int64_t gn = n0 + c;
+            cs_lds[c] = gn < N ? colsum[gn] : 0.0f;
+            bs_lds[c] = (gn < N && bias) ? bias[gn] : 0.0f;
+        }
+    }
+    if constexpr (EPI == kEpiLayerNormStats) {
+        for (int r = tid; r < BM; r += NT) {
+            const int64_t gr = m0 + r < T ? m0 + r : T - 1;
+            const f32x2 st = *(const f32x2*)(rowstats + 2 * gr);
+            mu_lds[r] = st.x;
+            rs_lds[r] = st.y;
+        }
+        __syncthreads();  // row statistics and column terms visible
+    }
+    if constexpr (kStatsInLoop<EPI>) {
         // lanes l and l + 32 summed the two halves of each 16-wide k step of the same row
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
@@ -307,37 +394,40 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
             rs_lds[r] = rs;
             if constexpr (EPI == kEpiLayerNorm) mu_lds[r] = mu;
         }
+        __syncthreads();  // row scales visible
     }
-    float cs[TN], bs[TN];
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-        cs[j] = bs[j] = 0.0f;
-        if constexpr (EPI == kEpiLayerNorm) {
-            const int64_t gn = n0 + wn * WTN + j * 32 + (lane & 31);
-            if (gn < N) {
-                cs[j] = colsum[gn];
-                if (bias) bs[j] = bias[gn];
-            }
-        }
-    }
-    __syncthreads();  // all DMA consumed (the last k-tile waited for vmcnt 0); row scales visible
 
-    // accumulator layout of a 32 x 32 block: lane holds column lane % 32 and, for e in 0..15,
-    // row 8 * (e / 4) + 4 * (lane / 32) + e % 4
+    // output row wm*WTM + i*32 + lane%32; columns wn*WTN + j*32 + 8g + 4(lane/32) + 0..3 in
+    // accumulator entries 4g .. 4g+3, rounded to bf16 and written 8 bytes at a time
     uint16_t* ct = (uint16_t*)smem;
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TM; ++i) {
+        const int r = wm * WTM + i * 32 + (lane & 31);
+        float rs = 1.0f, mu = 0.0f;
+        if constexpr (EPI != kEpiPlain) rs = rs_lds[r];
+        if constexpr (kLayerNormOut<EPI>) mu = mu_lds[r];
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int r = wm * WTM + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                const int c = wn * WTN + j * 32 + (lane & 31);
-                float v = acc[i][j][e];
-                if constexpr (EPI == kEpiRms) v *= rs_lds[r];
-                if constexpr (EPI == kEpiLayerNorm) v = epilogue<EPI>(v, rs_lds[r], mu_lds[r], cs[j], bs[j]);
-                ct[r * CP + c] = to_bf16(v);
+            for (int g = 0; g < 4; ++g) {
+                const int c = wn * WTN + j * 32 + 8 * g + 4 * (lane >> 5);
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
+                if constexpr (EPI == kEpiRms) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] *= rs;
+                }
+                if constexpr (kLayerNormOut<EPI>) {
+                    const f32x4 cs = *(const f32x4*)(cs_lds + c);
+                    const f32x4 bs = *(const f32x4*)(bs_lds + c);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = epilogue<EPI>(v[e], rs, mu, cs[e], bs[e]);
+                }
+                const u32x2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                *(u32x2*)(ct + r * CP + c) = pk;
             }
+    }
     __syncthreads();
     constexpr int C8 = BN / 8;
     for (int idx = tid; idx < BM * C8; idx += NT) {
@@ -751,6 +841,33 @@ __global__ __launch_bounds__(kThreads) void layernorm_rows_kernel(
     }
 }
 
+// Row statistics of LayerNorm for the product's epilogue: one wavefront per row, the same
+// shifted fp32 sums as the in-product accumulation, (mean, 1/std) per row.
+constexpr int kStatsRowsPerBlock = 4;
+
+__global__ __launch_bounds__(kStatsRowsPerBlock * kWave) void layernorm_stats_kernel(
+    int64_t T, int64_t K, float eps, float inv_k, const uint16_t* __restrict__ x, int64_t ldx,
+    float* __restrict__ rowstats)
+{
+    const int64_t t = (int64_t)blockIdx.x * kStatsRowsPerBlock + threadIdx.x / kWave;
+    if (t >= T) return;
+    const int lane = lane_id();
+    const uint16_t* xr = x + t * ldx;
+    const float x0 = bf16_at(xr, 0);
+    float s1 = 0.0f, s2 = 0.0f;
+#pragma unroll 4
+    for (int64_t k = (int64_t)lane * 8; k < K; k += kWave * 8)
+        accum_stats<kEpiLayerNorm>(*(const u32x4*)(xr + k), x0, s1, s2);
+    s1 = wave_sum(s1);
+    s2 = wave_sum(s2);
+    if (lane == 0) {
+        float rs, mu;
+        row_scale<kEpiLayerNorm>(s1, s2, x0, inv_k, eps, rs, mu);
+        const f32x2 st = {mu, rs};
+        *(f32x2*)(rowstats + 2 * t) = st;
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void copy_kernel(char* __restrict__ dst,
                                                         const char* __restrict__ src,
                                                         int64_t nbytes, int vec)
@@ -767,71 +884,100 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(char* __restrict__ dst,
     for (int64_t i = done + tid; i < nbytes; i += stride) dst[i] = src[i];
 }
 
-template <int BM, int BN, int WM, int WN, int NST, int BK, int EPI>
+template <int BM, int BN, int WM, int WN, int NST, int BK, int EPI, bool RING>
 hipError_t launch_pipe(int64_t T, int64_t K, int64_t N, float eps, float inv_k,
                        const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
                        uint16_t* y, int64_t ldy, const float* colsum, const float* bias,
-                       hipStream_t st)
+                       const float* rowstats, hipStream_t st)
 {
     const int64_t nbm = (T + BM - 1) / BM, nbn = (N + BN - 1) / BN;
     if (nbm * nbn > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((normproj_pipe_kernel<BM, BN, WM, WN, NST, BK, EPI>),
+    hipLaunchKernelGGL((normproj_pipe_kernel<BM, BN, WM, WN, NST, BK, EPI, RING>),
                        dim3((unsigned)(nbm * nbn)), dim3(WM * WN * kWave), 0, st, T, K, N, eps,
-                       inv_k, x, ldx, w, ldw, y, ldy, (int)nbm, (int)nbn, colsum, bias);
+                       inv_k, x, ldx, w, ldw, y, ldy, (int)nbm, (int)nbn, colsum, bias, rowstats);
     return hipGetLastError();
+}
+
+// Kernel choice for a product shape.
+enum Path { kPathMv, kPathBig64, kPathBig32, kPathMid, kPathGeneric };
+
+Path choose_path(int64_t T, int64_t K, int64_t N, int64_t ldy, const void* y)
+{
+    if (T <= kGemvMaxT) return kPathMv;
+    const bool pipe_ok = N % 8 == 0 && ldy % 8 == 0 && ((uintptr_t)y & 15u) == 0;
+    const int64_t big_tiles = ((T + 255) / 256) * ((N + 255) / 256);
+    // at least one 256 x 256 tile per CU: 8 wavefronts of 64 x 128, k-tiles of 64 through the
+    // ring of five parts, or of 32 in 4 whole-tile stages when K needs it
+    if (pipe_ok && big_tiles >= 256 && K % 64 == 0) return kPathBig64;
+    if (pipe_ok && big_tiles >= 256 && K % 32 == 0) return kPathBig32;
+    // 128 x 128 per workgroup of 8 wavefronts (32 x 64 each: two wavefronts per SIMD hide each
+    // other's LDS and barrier latency), k-tiles of 64, 2 stages (2 workgroups per CU)
+    if (pipe_ok && K % 64 == 0) return kPathMid;
+    return kPathGeneric;
 }
 
 template <int EPI>
 hipError_t launch_epi(int64_t T, int64_t K, int64_t N, float eps, const uint16_t* xp,
                       int64_t ldx, const uint16_t* wp, int64_t ldw, uint16_t* yp, int64_t ldy,
-                      const float* colsum, const float* bias, hipStream_t st)
+                      const float* colsum, const float* bias, const float* rowstats,
+                      hipStream_t st)
 {
     const float inv_k = (float)(1.0 / (double)K);
-    if (T <= kGemvMaxT) {
-        const bool narrow = N <= 4096;
-        const int64_t nblk = narrow ? (N + 15) / 16 : (N + 31) / 32;
-        if (nblk > 0x7fffffff) return hipErrorInvalidConfiguration;
-        if (narrow)
-            hipLaunchKernelGGL((normproj_mv_kernel<EPI, 1, 16>), dim3((unsigned)nblk), dim3(16 * kWave),
-                               0, st, (int)T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp, ldy, colsum,
-                               bias);
-        else
-            hipLaunchKernelGGL((normproj_mv_kernel<EPI, 2, 8>), dim3((unsigned)nblk), dim3(8 * kWave),
-                               0, st, (int)T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp, ldy, colsum,
-                               bias);
+    const Path path = choose_path(T, K, N, ldy, yp);
+    switch (path) {
+    case kPathBig64:
+        return launch_pipe<256, 256, 4, 2, 5, 64, EPI, true>(T, K, N, eps, inv_k, xp, ldx, wp,
+                                                             ldw, yp, ldy, colsum, bias,
+                                                             rowstats, st);
+    case kPathBig32:
+        return launch_pipe<256, 256, 4, 2, 4, 32, EPI, false>(T, K, N, eps, inv_k, xp, ldx, wp,
+                                                              ldw, yp, ldy, colsum, bias,
+                                                              rowstats, st);
+    case kPathMid:
+        return launch_pipe<128, 128, 4, 2, 2, 64, EPI, false>(T, K, N, eps, inv_k, xp, ldx, wp,
+                                                              ldw, yp, ldy, colsum, bias,
+                                                              rowstats, st);
+    default:
+        break;
+    }
+    if constexpr (EPI == kEpiLayerNormStats) {
+        return hipErrorInvalidValue;  // statistics from memory: pipelined kernels only
+    } else {
+        if (path == kPathMv) {
+            const bool narrow = N <= 4096;
+            const int64_t nblk = narrow ? (N + 15) / 16 : (N + 31) / 32;
+            if (nblk > 0x7fffffff) return hipErrorInvalidConfiguration;
+            if (narrow)
+                hipLaunchKernelGGL((normproj_mv_kernel<EPI, 1, 16>), dim3((unsigned)nblk),
+                                   dim3(16 * kWave), 0, st, (int)T, K, N, eps, inv_k, xp, ldx, wp,
+                                   ldw, yp, ldy, colsum, bias);
+            else
+                hipLaunchKernelGGL((normproj_mv_kernel<EPI, 2, 8>), dim3((unsigned)nblk),
+                                   dim3(8 * kWave), 0, st, (int)T, K, N, eps, inv_k, xp, ldx, wp,
+                                   ldw, yp, ldy, colsum, bias);
+            return hipGetLastError();
+        }
+        const int64_t nbm = (T + kBM - 1) / kBM, nbn = (N + kBN - 1) / kBN;
+        if (nbm * nbn > 0x7fffffff) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL(normproj_mfma_kernel<EPI>, dim3((unsigned)(nbm * nbn)), dim3(kThreads),
+                           0, st, T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp, ldy, (int)nbm,
+                           (int)nbn, colsum, bias);
         return hipGetLastError();
     }
-    const bool pipe_ok = N % 8 == 0 && ldy % 8 == 0 && ((uintptr_t)yp & 15u) == 0;
-    const int64_t big_tiles = ((T + 255) / 256) * ((N + 255) / 256);
-    if (pipe_ok && big_tiles >= 256) {
-        // at least one 256 x 256 tile per CU: 8 wavefronts of 64 x 128, k-tiles of 64 in 2
-        // stages (half the barriers of k-tiles of 32), or of 32 in 4 stages when K needs it
-        if (K % 64 == 0)
-            return launch_pipe<256, 256, 4, 2, 2, 64, EPI>(T, K, N, eps, inv_k, xp, ldx, wp, ldw,
-                                                           yp, ldy, colsum, bias, st);
-        if (K % 32 == 0)
-            return launch_pipe<256, 256, 4, 2, 4, 32, EPI>(T, K, N, eps, inv_k, xp, ldx, wp, ldw,
-                                                           yp, ldy, colsum, bias, st);
-    }
-    if (pipe_ok && K % 64 == 0) {
-        // 128 x 128 per workgroup of 8 wavefronts (32 x 64 each: two wavefronts per SIMD hide
-        // each other's LDS and barrier latency), k-tiles of 64, 2 stages (2 workgroups per CU)
-        return launch_pipe<128, 128, 4, 2, 2, 64, EPI>(T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp,
-                                                       ldy, colsum, bias, st);
-    }
-    const int64_t nbm = (T + kBM - 1) / kBM, nbn = (N + kBN - 1) / kBN;
-    if (nbm * nbn > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(normproj_mfma_kernel<EPI>, dim3((unsigned)(nbm * nbn)), dim3(kThreads), 0,
-                       st, T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp, ldy, (int)nbm, (int)nbn,
-                       colsum, bias);
-    return hipGetLastError();
 }
 
 }  // namespace
 
+bool normproj_pipelined(int64_t T, int64_t K, int64_t N, int64_t ldy, const void* y)
+{
+    const Path p = choose_path(T, K, N, ldy, y);
+    return p == kPathBig64 || p == kPathBig32 || p == kPathMid;
+}
+
 hipError_t launch_normproj(int64_t T, int64_t K, int64_t N, float eps, int epi,
                            const void* x, int64_t ldx, const void* w, int64_t ldw, void* y,
-                           int64_t ldy, const float* colsum, const float* bias, hipStream_t st)
+                           int64_t ldy, const float* colsum, const float* bias,
+                           const float* rowstats, hipStream_t st)
 {
     if (T == 0 || N == 0) return hipSuccess;
     const uint16_t* xp = (const uint16_t*)x;
@@ -839,15 +985,32 @@ hipError_t launch_normproj(int64_t T, int64_t K, int64_t N, float eps, int epi,
     uint16_t* yp = (uint16_t*)y;
     switch (epi) {
     case kEpiPlain:
-        return launch_epi<kEpiPlain>(T, K, N, eps, xp, ldx, wp, ldw, yp, ldy, colsum, bias, st);
+        return launch_epi<kEpiPlain>(T, K, N, eps, xp, ldx, wp, ldw, yp, ldy, colsum, bias,
+                                     rowstats, st);
     case kEpiRms:
-        return launch_epi<kEpiRms>(T, K, N, eps, xp, ldx, wp, ldw, yp, ldy, colsum, bias, st);
+        return launch_epi<kEpiRms>(T, K, N, eps, xp, ldx, wp, ldw, yp, ldy, colsum, bias,
+                                   rowstats, st);
     case kEpiLayerNorm:
         return launch_epi<kEpiLayerNorm>(T, K, N, eps, xp, ldx, wp, ldw, yp, ldy, colsum, bias,
-                                         st);
+                                         rowstats, st);
+    case kEpiLayerNormStats:
+        return launch_epi<kEpiLayerNormStats>(T, K, N, eps, xp, ldx, wp, ldw, yp, ldy, colsum,
+                                              bias, rowstats, st);
     default:
         return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_layernorm_stats(int64_t T, int64_t K, float eps, const void* x, int64_t ldx,
+                                  float* rowstats, hipStream_t st)
+{
+    if (T == 0) return hipSuccess;
+    const int64_t nblk = (T + kStatsRowsPerBlock - 1) / kStatsRowsPerBlock;
+    if (nblk > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(layernorm_stats_kernel, dim3((unsigned)nblk),
+                       dim3(kStatsRowsPerBlock * kWave), 0, st, T, K, eps,
+                       (float)(1.0 / (double)K), (const uint16_t*)x, ldx, rowstats);
+    return hipGetLastError();
 }
 
 hipError_t launch_fold_stats(int64_t K, int64_t N, const void* w, int64_t ldw, const void* gamma,

@@ -52,11 +52,21 @@ enum Epi : int {
     kEpiPlain = 0,      // y = bf16(acc)
     kEpiRms = 1,        // y = bf16(acc / rms(x row))
     kEpiLayerNorm = 2,  // y = bf16(r * (acc - mean(x row) * colsum[n]) + bias[n]), r = 1/std
+    kEpiLayerNormStats = 3,  // the same with (mean, r) of each row read from rowstats [T, 2]
 };
+// rowstats is read by kEpiLayerNormStats only, which runs on the pipelined kernels alone
+// (normproj_pipelined() must hold).
 hipError_t launch_normproj(int64_t T, int64_t K, int64_t N, float eps, int epi,
                            const void* x, int64_t ldx, const void* w, int64_t ldw, void* y,
                            int64_t ldy, const float* colsum, const float* bias,
-                           hipStream_t stream);
+                           const float* rowstats, hipStream_t stream);
+
+// Whether launch_normproj runs one of the pipelined matrix-core kernels for this shape.
+bool normproj_pipelined(int64_t T, int64_t K, int64_t N, int64_t ldy, const void* y);
+
+// rowstats[t] = (mean of x row t, 1 / sqrt(var + eps)) in fp32, K % 8 == 0, rows 16-byte aligned.
+hipError_t launch_layernorm_stats(int64_t T, int64_t K, float eps, const void* x, int64_t ldx,
+                                  float* rowstats, hipStream_t stream);
 
 // colsum[n] = sum_k bf16(gamma[k] * W[k, n]), bias[n] = sum_k beta[k] * W[k, n] (bias may be
 // null; gamma / beta null mean 1 / 0; gamma and beta share one storage type).

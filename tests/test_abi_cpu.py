@@ -63,7 +63,7 @@ def test_status_strings(L):
 
 
 # Fake, never-dereferenced device addresses (16-byte aligned, far apart).
-A, B, C, D, G1, G2 = (0x7F0000000000 + i * 0x10000000 for i in range(6))
+A, B, C, D, G1, G2, E = (0x7F0000000000 + i * 0x10000000 for i in range(7))
 
 
 def fused(L, T=4, eps=1e-6, dt=BF16, gdt=BF16, q=A, ldq=64, qo=B, ldqo=64, gq=G1, dq=64,
@@ -169,13 +169,20 @@ def test_layernorm_projection_validation(L):
     assert F(16, 16, BF16, BF16, A, 16, G1, G2, B, 16, C, G2, None) == ALIAS   # bias on beta
     assert F(0, 16, BF16, BF16, None, 16, None, None, None, 0, None, None, None) == OK
     P = L.normproj_deferred_layernorm
-    assert P(4, 16, 16, 1e-5, F32, A, 16, B, 16, C, D, G1, 16, None) == DTYPE
-    assert P(4, 12, 16, 1e-5, BF16, A, 12, B, 12, C, D, G1, 16, None) == ALIGN
-    assert P(4, 16, 16, -1.0, BF16, A, 16, B, 16, C, D, G1, 16, None) == EPS
-    assert P(4, 16, 16, 1e-5, BF16, A, 16, B, 16, None, D, G1, 16, None) == NULL
-    assert P(4, 16, 16, 1e-5, BF16, A, 16, B, 16, C, D, C, 16, None) == ALIAS  # y over colsum
-    assert P(4, 16, 16, 1e-5, BF16, A, 16, B, 16, C, D, D, 16, None) == ALIAS  # y over bias
-    assert P(0, 16, 16, 1e-5, BF16, None, 16, None, 16, None, None, None, 16, None) == OK
+    assert P(4, 16, 16, 1e-5, F32, A, 16, B, 16, C, D, G1, 16, None, None) == DTYPE
+    assert P(4, 12, 16, 1e-5, BF16, A, 12, B, 12, C, D, G1, 16, None, None) == ALIGN
+    assert P(4, 16, 16, -1.0, BF16, A, 16, B, 16, C, D, G1, 16, None, None) == EPS
+    assert P(4, 16, 16, 1e-5, BF16, A, 16, B, 16, None, D, G1, 16, None, None) == NULL
+    assert P(4, 16, 16, 1e-5, BF16, A, 16, B, 16, C, D, C, 16, None, None) == ALIAS  # y on colsum
+    assert P(4, 16, 16, 1e-5, BF16, A, 16, B, 16, C, D, D, 16, None, None) == ALIAS  # y on bias
+    # the row-statistics workspace: 8-byte aligned, clear of every other operand
+    assert P(4, 16, 16, 1e-5, BF16, A, 16, B, 16, C, D, G1, 16, E + 4, None) == ALIGN
+    assert P(4, 16, 16, 1e-5, BF16, A, 16, B, 16, C, D, G1, 16, G1 + 8, None) == ALIAS  # on y
+    assert P(4, 16, 16, 1e-5, BF16, A, 16, B, 16, C, D, G1, 16, A + 64, None) == ALIAS  # on x
+    assert P(4, 16, 16, 1e-5, BF16, A, 16, B, 16, C, D, G1, 16, B, None) == ALIAS      # on W'
+    assert P(4, 16, 16, 1e-5, BF16, A, 16, B, 16, C, D, G1, 16, C + 16, None) == ALIAS  # colsum
+    assert P(4, 16, 16, 1e-5, BF16, A, 16, B, 16, C, D, G1, 16, D, None) == ALIAS      # bias
+    assert P(0, 16, 16, 1e-5, BF16, None, 16, None, 16, None, None, None, 16, None, None) == OK
     U = L.normproj_layernorm_unfused
     assert U(4, 16, 16, 1e-5, BF16, BF16, A, 16, G1, G2, B, 16, A, 16, C, 16, None) == ALIAS
     assert U(4, 16, 16, 1e-5, BF16, BF16, A, 16, G1, G2, B, 16, None, 16, C, 16, None) == NULL

@@ -162,13 +162,16 @@ def test_fold_layernorm(Q):
     assert b2 is None and np.array_equal(to_host(cs2), to_host(cs))
 
 
+@pytest.mark.parametrize("stats", ["auto", None])
 @pytest.mark.parametrize("T,x_mean", [(1, 0.0), (2048, 0.0), (16384, 0.0), (2048, 4.0),
                                       (16, 3.0)])
-def test_deferred_layernorm(Q, T, x_mean):
+def test_deferred_layernorm(Q, T, x_mean, stats):
+    """Both sources of the row statistics: a streaming pass into the workspace ("auto") and
+    accumulation inside the product (None)."""
     c = inputs.make_layernorm_case(T, x_mean=x_mean)
     wf_ref, cs_ref, b_ref = ln_reference_parts(c)
     wf, cs, b = Q.normproj_fold_layernorm(to_dev(c["w"]), to_dev(c["gamma"]), to_dev(c["beta"]))
-    y = Q.normproj_deferred_layernorm(to_dev(c["x"]), wf, cs, b, eps=c["eps"])
+    y = Q.normproj_deferred_layernorm(to_dev(c["x"]), wf, cs, b, eps=c["eps"], row_stats=stats)
     sync()
     rows = sample_rows(T, 256, seed=T)
     xs = np.ascontiguousarray(c["x"][rows])
@@ -182,12 +185,14 @@ def test_deferred_layernorm(Q, T, x_mean):
                          "deferred LN vs unfused definition", abs_coeff=2.0 ** -8)
 
 
+@pytest.mark.parametrize("stats", ["auto", None])
 @pytest.mark.parametrize("T,K,N", [(5, 256, 130), (16, 1032, 64), (17, 1024, 520),
                                    (300, 264, 200), (129, 2048, 2048), (8200, 1056, 4104),
                                    (8200, 1024, 4104)])
-def test_deferred_layernorm_ragged(Q, T, K, N):
+def test_deferred_layernorm_ragged(Q, T, K, N, stats):
     """All product kernels with the LayerNorm epilogue, ragged T and N, no beta, x with a mean
-    of 2 (the mean term is exercised everywhere)."""
+    of 2 (the mean term is exercised everywhere), statistics from the workspace pass or from
+    inside the product."""
     rng = np.random.default_rng(T * 7 + K + N)
     x = inputs.f32_to_bf16_bits((widen(inputs.random_rows(rng, T, K, "bf16")) + 2.0)
                                 .astype(np.float32))
@@ -196,13 +201,42 @@ def test_deferred_layernorm_ragged(Q, T, K, N):
     wf_ref = folded(w, g)
     cs_ref = oracle.colsum(wf_ref)
     wf, cs, b = Q.normproj_fold_layernorm(to_dev(w), to_dev(g), None)
-    y = Q.normproj_deferred_layernorm(to_dev(x), wf, cs, None, eps=1e-5)
+    y = Q.normproj_deferred_layernorm(to_dev(x), wf, cs, None, eps=1e-5, row_stats=stats)
     sync()
     assert b is None
     rows = sample_rows(T, 128, seed=T)
     xs = np.ascontiguousarray(x[rows])
     check_projection(to_host(y)[rows], oracle.normproj_layernorm(xs, wf_ref, cs_ref, None, 1e-5),
                      ln_bound(xs, wf_ref, 1e-5), f"LN T={T} K={K} N={N}")
+
+
+@pytest.mark.parametrize("T,K,N,pass_runs", [(4096, 2048, 2048, True), (300, 264, 200, False),
+                                             (12, 2048, 2048, False)])
+def test_deferred_layernorm_row_stats(Q, T, K, N, pass_runs):
+    """The workspace holds (mean, 1/std) of every row when the streaming pass runs (matrix-core
+    shapes) and is left untouched otherwise (K not a multiple of 64 and no 256-tile path; the
+    matrix-vector path for T <= 16)."""
+    import torch
+
+    c = inputs.make_layernorm_case(T, seed=5, K=K, N=N, x_mean=3.0)
+    wf, cs, b = Q.normproj_fold_layernorm(to_dev(c["w"]), to_dev(c["gamma"]), to_dev(c["beta"]))
+    ws = torch.full((T, 2), float("nan"), dtype=torch.float32, device="cuda")
+    Q.normproj_deferred_layernorm(to_dev(c["x"]), wf, cs, b, eps=c["eps"], row_stats=ws)
+    sync()
+    got = to_host(ws).astype(np.float64)
+    if not pass_runs:
+        assert np.all(np.isnan(got)), "row_stats written although the pass does not run"
+        return
+    xw = widen(c["x"])
+    mu = xw.mean(axis=1)
+    var = ((xw - mu[:, None]) ** 2).mean(axis=1)
+    r = 1.0 / np.sqrt(var + c["eps"])
+    # fp32 sums of x - x0 over K terms: the mean within 2^-16 of the mean |x - x0| (plus its own
+    # rounding), r within 2^-14 relative; a dropped term or a wrong shift is off by far more
+    spread = np.abs(xw - xw[:, :1]).mean(axis=1)
+    assert np.all(np.abs(got[:, 0] - mu) <= 2.0 ** -16 * spread + 2.0 ** -22 * np.abs(mu)), \
+        "row means"
+    assert np.all(np.abs(got[:, 1] - r) <= 2.0 ** -14 * r), "row 1/std"
 
 
 def test_layernorm_unfused_baseline(Q):
