@@ -116,9 +116,8 @@ QKN_API int qknorm_apply_with_stats(int64_t T, float eps, int dtype, int gamma_d
 /*
  * qknorm_shard_fused - the shard stage in ONE pass over this rank's slice.
  *
- * ("SwiftQK: ...", abstract: exchange only scalar statistics, overlapping the remaining
- * peer-to-peer reduction with independent element-wise work in a deadlock-safe persistent
- * kernel.) Computes what qknorm_partial_sumsq followed by qknorm_apply_with_stats computes,
+ * ("SwiftQK: ...", abstract: ranks exchange per-row scalars only, and waiting for the peers'
+ * scalars is hidden behind element-wise work in one persistent kernel that cannot deadlock.) Computes what qknorm_partial_sumsq followed by qknorm_apply_with_stats computes,
  * reading x once. Exchanged partials travel as mailbox WORDS: uint64 = (epoch << 32) | the
  * fp32 bits of the value, each stored and loaded as one aligned 64-bit device-coherent access,
  * so a word that carries the current epoch carries its value (no separate flags). Per row:
@@ -224,8 +223,8 @@ QKN_API int normproj_unfused(int64_t T, int64_t K, int64_t N, float eps, int dty
 /*
  * normproj_fold_layernorm - the fold for LayerNorm followed by the projection (once, offline).
  *
- * ("FlashNorm: ...", abstract: the same techniques extend to LayerNorm. The pages give no
- * formulas; the ones used follow from LN(x) W = r (x W' - mu c) + beta W.)
+ * ("FlashNorm: ...", abstract: the folding and deferral carry over to LayerNorm. The pages
+ * give no formulas; the ones used follow from LN(x) W = r (x W' - mu c) + beta W.)
  *   w_fold      as normproj_fold_weight: W' = diag(gamma) W, bf16, written transposed [N, K]
  *   colsum[n] = sum_k W'[k, n]  over the bf16 values of w_fold exactly as stored (fp64 sum,
  *               rounded once to fp32), [N] fp32
@@ -280,9 +279,9 @@ QKN_API int normproj_layernorm_unfused(int64_t T, int64_t K, int64_t N, float ep
  * qknorm_project_eliminated - Q/K projection and layerwise QK-Norm with the pre-attention
  * RMSNorm removed.
  *
- * ("FlashNorm: ...", abstract: by the scale invariance of RMS, an RMSNorm followed by a linear
- * layer and another RMSNorm lets the first RMSNorm be eliminated, e.g. ahead of attention with
- * Q/K normalisation.) The pre-norm weight is folded into the stacked projection
+ * ("FlashNorm: ...", abstract: RMS is unchanged by scaling its input, so with a second RMSNorm
+ * after the linear layer the first one has no effect and can be removed, e.g. ahead of
+ * attention with Q/K normalisation.) The pre-norm weight is folded into the stacked projection
  * w_qk = [W'q ; W'k] ([nq + nk, K] bf16, normproj_fold_weight of the [K, nq + nk] weight):
  *   p[t,:]       = x[t,:] W'^T                  exact == 0: no pre-norm at all
  *                = r1_t x[t,:] W'^T             exact == 1: r1_t = 1/sqrt(mean(x_t^2) + eps_pre)

@@ -2,8 +2,8 @@
 // rank's column slice computes the per-row partial sums of squares, publishes them, waits for
 // the peers' partials, aggregates, and scales the slice it still holds in registers ("SwiftQK:
 // Fast and Communication-Efficient Tensor Parallelism for Query-Key Normalization", abstract:
-// scalar partial-sum aggregation, with the remaining peer-to-peer reduction overlapped with
-// independent element-wise work in a deadlock-safe persistent kernel). Compared with the two
+// ranks exchange per-row scalars only, and the wait for the peers' scalars is hidden behind
+// element-wise work in one persistent kernel that cannot deadlock). Compared with the two
 // launches (partial sums, then aggregation + scale) x is read once instead of twice.
 //
 // Mailbox. Every exchanged partial travels as one 8-byte word: the epoch of the pass in the

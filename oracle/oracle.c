@@ -209,8 +209,8 @@ void oracle_matmul(int64_t T, int64_t K, int64_t N, int adt, const void* a, int6
 
 /* ------------------------------------------------------------------------------------------
  * Eliminating the pre-attention RMSNorm by scale invariance ("FlashNorm: Fast Normalization
- * for Transformers", abstract: an RMSNorm, a linear layer and a second RMSNorm in a row allow
- * the first RMSNorm to be dropped, as in attention with Q/K normalisation).
+ * for Transformers", abstract: when a second RMSNorm follows the linear layer, the first one
+ * changes nothing and can go, as ahead of attention with Q/K normalisation).
  *
  * The chain being simplified, for one token x [K]:
  *     h = x * gamma_pre * r1,  r1 = 1 / sqrt(mean(x^2) + eps_pre)     (pre-attention RMSNorm)
@@ -310,8 +310,8 @@ void oracle_qk_eliminated(int64_t T, int64_t K, int64_t nq, int64_t nk, double e
 }
 
 /* ------------------------------------------------------------------------------------------
- * LayerNorm followed by a linear layer, with the same two steps ("FlashNorm", abstract: the
- * techniques extend to LayerNorm). The pages give no formulas for it; the derivation used:
+ * LayerNorm ahead of a projection, with the same two steps ("FlashNorm", abstract: the method
+ * carries over to LayerNorm). The pages give no formulas for it; the derivation used:
  *
  *     LN(x) = (x - mu) * r * gamma + beta,  mu = mean(x),  r = 1 / sqrt(mean((x - mu)^2) + eps)
  *     LN(x) W = r * (x W' - mu * c) + b,    W' = diag(gamma) W,  c[n] = sum_k W'[k][n],
