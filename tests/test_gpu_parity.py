@@ -185,12 +185,13 @@ def test_normproj_unfused_baseline(Q):
 
 @pytest.mark.parametrize("T,K,N", [(5, 256, 130), (16, 1032, 64), (17, 1024, 520),
                                    (300, 264, 200), (129, 2048, 2048), (8200, 1056, 4104),
-                                   (8200, 1024, 4104)])
+                                   (8200, 1024, 4104), (4096, 64, 4096), (4096, 128, 4096),
+                                   (4100, 192, 4104), (4096, 96, 4096)])
 def test_normproj_ragged(Q, T, K, N):
     """Every kernel of the projection: the matrix-vector path (T <= 16), the generic tile
     kernel (K not a multiple of 32), and both pipelined tilings (128 x 128 and 256 x 256 with
-    k-tiles of 64 and 32), with T and N not multiples of the tile; large cases are checked on a
-    sample of rows."""
+    k-tiles of 64 through the five-part ring, or of 32), with T and N not multiples of the tile
+    and rings of one, two and three k-tiles; large cases are checked on a sample of rows."""
     rng = np.random.default_rng(T + K + N)
     x = inputs.random_rows(rng, T, K, "bf16")
     w = inputs.random_rows(rng, K, N, "bf16", scale=0.02)
@@ -207,11 +208,11 @@ def test_normproj_ragged(Q, T, K, N):
                      projection_bound(xs, wf_ref, 1e-6), f"T={T} K={K} N={N}")
 
 
-def test_normproj_strided_rows(Q):
-    """x and y with row strides above their widths."""
+@pytest.mark.parametrize("T,K,N", [(200, 512, 256), (4096, 256, 4096)])
+def test_normproj_strided_rows(Q, T, K, N):
+    """x and y with row strides above their widths (128 x 128 tiles, and the 256 x 256 ring)."""
     torch = pytest.importorskip("torch")
     rng = np.random.default_rng(7)
-    T, K, N = 200, 512, 256
     xfull = inputs.random_rows(rng, T, K, "bf16", ld=K + 64)
     w = inputs.random_rows(rng, K, N, "bf16", scale=0.02)
     g = inputs.random_gamma(rng, K, "bf16")
@@ -222,6 +223,7 @@ def test_normproj_strided_rows(Q):
     sync()
     yh = to_host(ybuf)
     assert np.all(widen(yh[:, N:]) == 7.0)
-    x = np.ascontiguousarray(xfull[:, :K])
-    check_projection(yh[:, :N], oracle.normproj(x, wf_ref, 1e-6),
-                     projection_bound(x, wf_ref, 1e-6), "strided")
+    rows = sample_rows(T, n=256, seed=T)
+    x = np.ascontiguousarray(xfull[rows, :K])
+    check_projection(yh[rows, :N], oracle.normproj(x, wf_ref, 1e-6),
+                     projection_bound(x, wf_ref, 1e-6), f"strided T={T}")
