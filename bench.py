@@ -19,6 +19,7 @@ import json
 import os
 import re
 import sys
+import statistics
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -68,24 +69,30 @@ class Timer:
     def __init__(self, torch, stream):
         self.torch, self.stream = torch, stream
 
-    def run(self, fn, iters, warmup):
+    def run(self, fn, iters, warmup, reps=1):
+        """ms per call: the median over reps of the mean of iters back-to-back calls."""
         torch = self.torch
+        means = []
         with torch.cuda.stream(self.stream):
             for i in range(warmup):
                 fn(i)
             torch.cuda.synchronize()
-            start = torch.cuda.Event(enable_timing=True)
-            end = torch.cuda.Event(enable_timing=True)
-            start.record(self.stream)
-            for i in range(iters):
-                fn(i)
-            end.record(self.stream)
+            for _ in range(reps):
+                start = torch.cuda.Event(enable_timing=True)
+                end = torch.cuda.Event(enable_timing=True)
+                start.record(self.stream)
+                for i in range(iters):
+                    fn(i)
+                end.record(self.stream)
+                end.synchronize()
+                means.append(start.elapsed_time(end) / iters)
         torch.cuda.synchronize()
-        return start.elapsed_time(end) / iters  # ms per call
+        return statistics.median(means)
 
-    def run_graph(self, fn, per_graph, replays, warmup):
+    def run_graph(self, fn, per_graph, replays, warmup, reps=1):
         """The same launches captured into one HIP graph (per_graph calls, one per rotating
-        buffer set) and replayed: GPU time per call without the host's launch overhead."""
+        buffer set) and replayed: GPU time per call without the host's launch overhead (the
+        median over reps of the mean over replays)."""
         torch = self.torch
         with torch.cuda.stream(self.stream):
             for i in range(per_graph):
@@ -95,19 +102,23 @@ class Timer:
         with torch.cuda.graph(g, stream=self.stream):
             for i in range(per_graph):
                 fn(i)
+        means = []
         with torch.cuda.stream(self.stream):
             for _ in range(warmup):
                 g.replay()
             torch.cuda.synchronize()
-            start = torch.cuda.Event(enable_timing=True)
-            end = torch.cuda.Event(enable_timing=True)
-            start.record(self.stream)
-            for _ in range(replays):
-                g.replay()
-            end.record(self.stream)
+            for _ in range(reps):
+                start = torch.cuda.Event(enable_timing=True)
+                end = torch.cuda.Event(enable_timing=True)
+                start.record(self.stream)
+                for _ in range(replays):
+                    g.replay()
+                end.record(self.stream)
+                end.synchronize()
+                means.append(start.elapsed_time(end) / (replays * per_graph))
         torch.cuda.synchronize()
         del g
-        return start.elapsed_time(end) / (replays * per_graph)
+        return statistics.median(means)
 
 
 def rotation_count(bytes_per_set):
@@ -276,11 +287,14 @@ def layernorm_setup(torch, Q, inputs, T, unfused, in_product=False):
     return fn, 2.0 * T * K * N, T * K * 2 + K * N * 2 + T * N * 2
 
 
+CASE_REPS = 5
+
+
 def time_case(timer, fn, iters, warmup):
-    """(eager ms per call, graph-replay ms per call)."""
-    eager = timer.run(fn, iters, warmup)
+    """(eager ms per call, graph-replay ms per call), each the median of CASE_REPS repeats."""
+    eager = timer.run(fn, iters, warmup, CASE_REPS)
     per_graph = max(fn.sets, 8 if fn.sets == 1 else fn.sets)
-    graph = timer.run_graph(fn, per_graph, max(2, iters // per_graph), 2)
+    graph = timer.run_graph(fn, per_graph, max(2, iters // per_graph), 2, CASE_REPS)
     return eager, graph
 
 
@@ -317,7 +331,37 @@ def cpu_baseline(inputs, T_full, budget_s=10.0):
             "sample": f"first 1024 tokens of Q and K [T, 4096] bf16 (of T={T_full}), fp64 "
                       f"oracle, rows split over {cores} threads, {pn} passes in {en:.1f} s",
             "single_thread_value": single,
-            "single_thread_sample": f"same sample, 1 thread, {p1} passes in {e1:.1f} s"}
+            "single_thread_sample": f"same sample, 1 thread, {p1} passes in {e1:.1f} s",
+            "cpu_model": cpu_model()}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_oracle_projection(inputs, rows=32):
+    """The fp64 oracle of the deferred projection (FlashNorm shape, K = N = 2048) on the first
+    `rows` tokens, one thread, best of 3; per-call times at the benchmarked T are extrapolated
+    per row and labelled so."""
+    import oracle
+
+    c = inputs.make_case(5, rows)
+    wf = oracle.round_bf16(oracle.fold_weight(c["w"], c["gamma"]))
+    best = float("inf")
+    for _ in range(3):
+        t0 = time.perf_counter()
+        oracle.normproj(c["x"], wf, c["eps"])
+        best = min(best, time.perf_counter() - t0)
+    per_row = best / rows
+    return [{"case": f"oracle normproj cfg5 T={t} (extrapolated from {rows} rows, 1 thread)",
+             "us_per_call": per_row * t * 1e6} for t in inputs.CONFIGS[5]["Ts"] if t > 1]
 
 
 # ----------------------------------------------------------------------------- main
@@ -485,6 +529,8 @@ def main():
             print("# " + json.dumps(cs), file=sys.stderr, flush=True)
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(inputs, T, args.cpu_seconds)
+    cpu_cases = (cpu_oracle_projection(inputs) if cpu is not None and args.cases == "all"
+                 and not args.only else [])
 
     out = {
         "metric": METRIC,
@@ -509,6 +555,7 @@ def main():
                      "algorithmic_bytes_per_launch": nbytes,
                      "kernel": "rows_team_kernel<kFused, bf16, bf16, 3, 3> (qknorm_fused)"},
         "cpu_baseline": cpu,
+        "cpu_oracle_cases": cpu_cases,
         "cases": cases,
     }
     print(json.dumps(out), flush=True)
