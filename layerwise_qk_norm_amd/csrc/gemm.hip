@@ -198,12 +198,16 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
     float* cs_lds = (float*)(smem + OFF_CS);
     float* bs_lds = (float*)(smem + OFF_BS);
 
-    const int tid = (int)threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int tid = (int)threadIdx.x, lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wavefront-uniform
     const int wm = wave / WN, wn = wave % WN;
     const int nb = nbm * nbn;
     int bid = (int)blockIdx.x;
     if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
     const int64_t m0 = (int64_t)(bid / nbn) * BM, n0 = (int64_t)(bid % nbn) * BN;
+    // LDS byte address of the pipeline buffer; DMA destinations are offsets from it, kept in
+    // scalar registers
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)smem;
 
     // Sources of the DMA chunks this lane fetches (fixed across k): chunks wave * CPA + c of the
     // x part and wave * CPB + c of the W' part. Out-of-range rows are clamped to the last valid
@@ -223,16 +227,15 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
         const int64_t r = n0 + trow < N ? n0 + trow : N - 1;
         srcb[c] = w + r * ldw + swz<BK>(lane % LPR, trow) * 8;
     }
-    auto dma_a = [&](int c, char* part, int64_t k0) {
-        dma16((const void*)(srca[c] + k0),
-              (uint32_t)(uintptr_t)(lds_void*)(part + (wave * CPA + c) * 1024));
+    // part: byte offset of the destination part within the pipeline buffer
+    auto dma_a = [&](int c, uint32_t part, int64_t k0) {
+        dma16((const void*)(srca[c] + k0), lds0 + part + (uint32_t)(wave * CPA + c) * 1024u);
     };
-    auto dma_b = [&](int c, char* part, int64_t k0) {
-        dma16((const void*)(srcb[c] + k0),
-              (uint32_t)(uintptr_t)(lds_void*)(part + (wave * CPB + c) * 1024));
+    auto dma_b = [&](int c, uint32_t part, int64_t k0) {
+        dma16((const void*)(srcb[c] + k0), lds0 + part + (uint32_t)(wave * CPB + c) * 1024u);
     };
     auto issue_tile = [&](int slot, int64_t k0) {
-        char* base = smem + slot * STAGE;
+        const uint32_t base = (uint32_t)(slot * STAGE);
 #pragma unroll
         for (int c = 0; c < CPA; ++c) dma_a(c, base, k0);
 #pragma unroll
@@ -263,12 +266,12 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
         // p == 2t + 1 mod 5: the x part (streamed from HBM) is requested two k-tiles ahead, the
         // W' part (shared by every row panel, mostly cache-resident) one ahead
 #pragma unroll
-        for (int c = 0; c < CPA; ++c) dma_a(c, smem, 0);
+        for (int c = 0; c < CPA; ++c) dma_a(c, 0u, 0);
 #pragma unroll
-        for (int c = 0; c < CPB; ++c) dma_b(c, smem + PART_A, 0);
+        for (int c = 0; c < CPB; ++c) dma_b(c, (uint32_t)PART_A, 0);
         if (nk > 1) {
 #pragma unroll
-            for (int c = 0; c < CPA; ++c) dma_a(c, smem + 2 * PART_A, BK);
+            for (int c = 0; c < CPA; ++c) dma_a(c, 2u * PART_A, BK);
         }
     } else {
 #pragma unroll
@@ -276,8 +279,12 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
             if (s < nk) issue_tile(s, (int64_t)s * BK);
     }
 
+    int pa = 0;  // ring: part holding the x half of k-tile kt (2 kt mod 5)
     for (int kt = 0; kt < nk; ++kt) {
         constexpr int CPT = CPA + CPB;
+        const int pb = pa == 4 ? 0 : pa + 1;        // W' half of k-tile kt
+        const int pnb = pa >= 2 ? pa - 2 : pa + 3;  // W' half of k-tile kt + 1
+        const int pna = pa >= 1 ? pa - 1 : 4;       // x half of k-tile kt + 2
         if constexpr (RING) {
             // k-tile kt must have landed; the x part of k-tile kt + 1 may stay in flight
             if (kt + 1 < nk) wait_vmcnt<CPA>();
@@ -300,8 +307,8 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
         if constexpr (!RING) {
             if (kt + NST - 1 < nk) issue_tile((kt + NST - 1) % NST, (int64_t)(kt + NST - 1) * BK);
         }
-        const char* As = RING ? smem + ((2 * kt) % 5) * PART_A : smem + (kt % NST) * STAGE;
-        const char* Bs = RING ? smem + ((2 * kt + 1) % 5) * PART_A : As + PART_A;
+        const char* As = RING ? smem + pa * PART_A : smem + (kt % NST) * STAGE;
+        const char* Bs = RING ? smem + pb * PART_A : As + PART_A;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             u32x4 af[TM], bfr[TN];
@@ -339,15 +346,15 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
                     const int c = ks * PER + h;
                     if (c < CPB) {
                         if (kt + 1 < nk)
-                            dma_b(c, smem + ((2 * kt + 3) % 5) * PART_A, (int64_t)(kt + 1) * BK);
+                            dma_b(c, (uint32_t)(pnb * PART_A), (int64_t)(kt + 1) * BK);
                     } else {
                         if (kt + 2 < nk)
-                            dma_a(c - CPB, smem + ((2 * kt + 4) % 5) * PART_A,
-                                  (int64_t)(kt + 2) * BK);
+                            dma_a(c - CPB, (uint32_t)(pna * PART_A), (int64_t)(kt + 2) * BK);
                     }
                 }
             }
         }
+        pa = pa >= 3 ? pa - 3 : pa + 2;
     }
     __syncthreads();  // every wavefront is done with the pipeline's LDS (no DMA is in flight)
 
