@@ -490,7 +490,7 @@ QKN_API int normproj_deferred_layernorm(int64_t T, int64_t K, int64_t N, float e
             return QKN_ERR_ALIAS;
     }
     const hipStream_t s = (hipStream_t)stream;
-    if (row_stats && qkn::normproj_pipelined(T, K, N, ldy, y)) {
+    if (row_stats && qkn::normproj_pipelined(T, K, N, ldx, ldw, ldy, y)) {
         // statistics from one streaming pass over x; the product applies them in its epilogue
         const hipError_t e = qkn::launch_layernorm_stats(T, K, eps, x, ldx, row_stats, s);
         if (e != hipSuccess) return hip_status(e);

@@ -146,6 +146,15 @@ __device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_off)
 }
 #pragma clang diagnostic pop
 
+// The same with a wavefront-uniform 64-bit base in scalar registers and a 32-bit byte offset
+// per lane (the saddr form: no 64-bit address arithmetic per request).
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds_off)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 ::"s"(__builtin_amdgcn_readfirstlane(lds_off)), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt()
 {
@@ -212,27 +221,30 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
     // Sources of the DMA chunks this lane fetches (fixed across k): chunks wave * CPA + c of the
     // x part and wave * CPB + c of the W' part. Out-of-range rows are clamped to the last valid
     // row: they only feed output rows / columns that are never stored.
+    // Each request is a wavefront-uniform base (the tile's first row at column k0) plus a 32-bit
+    // byte offset per lane (row offset, which a 256-row tile keeps below 2^32 for ld < 2^23).
     const int lrow = lane / LPR;
-    const uint16_t* srca[CPA];
-    const uint16_t* srcb[CPB];
+    uint32_t offa[CPA], offb[CPB];
 #pragma unroll
     for (int c = 0; c < CPA; ++c) {
         const int trow = (wave * CPA + c) * RPC + lrow;
         const int64_t r = m0 + trow < T ? m0 + trow : T - 1;
-        srca[c] = x + r * ldx + swz<BK>(lane % LPR, trow) * 8;
+        offa[c] = (uint32_t)(((r - m0) * ldx + swz<BK>(lane % LPR, trow) * 8) * 2);
     }
 #pragma unroll
     for (int c = 0; c < CPB; ++c) {
         const int trow = (wave * CPB + c) * RPC + lrow;
         const int64_t r = n0 + trow < N ? n0 + trow : N - 1;
-        srcb[c] = w + r * ldw + swz<BK>(lane % LPR, trow) * 8;
+        offb[c] = (uint32_t)(((r - n0) * ldw + swz<BK>(lane % LPR, trow) * 8) * 2);
     }
+    const uint16_t* xa = x + m0 * ldx;
+    const uint16_t* wb = w + n0 * ldw;
     // part: byte offset of the destination part within the pipeline buffer
     auto dma_a = [&](int c, uint32_t part, int64_t k0) {
-        dma16((const void*)(srca[c] + k0), lds0 + part + (uint32_t)(wave * CPA + c) * 1024u);
+        dma16s((const void*)(xa + k0), offa[c], lds0 + part + (uint32_t)(wave * CPA + c) * 1024u);
     };
     auto dma_b = [&](int c, uint32_t part, int64_t k0) {
-        dma16((const void*)(srcb[c] + k0), lds0 + part + (uint32_t)(wave * CPB + c) * 1024u);
+        dma16s((const void*)(wb + k0), offb[c], lds0 + part + (uint32_t)(wave * CPB + c) * 1024u);
     };
     auto issue_tile = [&](int slot, int64_t k0) {
         const uint32_t base = (uint32_t)(slot * STAGE);
@@ -908,10 +920,13 @@ hipError_t launch_pipe(int64_t T, int64_t K, int64_t N, float eps, float inv_k,
 // Kernel choice for a product shape.
 enum Path { kPathMv, kPathBig64, kPathBig32, kPathMid, kPathGeneric };
 
-Path choose_path(int64_t T, int64_t K, int64_t N, int64_t ldy, const void* y)
+Path choose_path(int64_t T, int64_t K, int64_t N, int64_t ldx, int64_t ldw, int64_t ldy,
+                 const void* y)
 {
     if (T <= kGemvMaxT) return kPathMv;
-    const bool pipe_ok = N % 8 == 0 && ldy % 8 == 0 && ((uintptr_t)y & 15u) == 0;
+    // the pipelined kernels address a tile's rows with 32-bit byte offsets from its first row
+    const bool pipe_ok = N % 8 == 0 && ldy % 8 == 0 && ((uintptr_t)y & 15u) == 0 &&
+                         ldx < (int64_t(1) << 23) && ldw < (int64_t(1) << 23);
     const int64_t big_tiles = ((T + 255) / 256) * ((N + 255) / 256);
     // at least one 256 x 256 tile per CU: 8 wavefronts of 64 x 128, k-tiles of 64 through the
     // ring of five parts, or of 32 in 4 whole-tile stages when K needs it
@@ -930,7 +945,7 @@ hipError_t launch_epi(int64_t T, int64_t K, int64_t N, float eps, const uint16_t
                       hipStream_t st)
 {
     const float inv_k = (float)(1.0 / (double)K);
-    const Path path = choose_path(T, K, N, ldy, yp);
+    const Path path = choose_path(T, K, N, ldx, ldw, ldy, yp);
     switch (path) {
     case kPathBig64:
         return launch_pipe<256, 256, 4, 2, 5, 64, EPI, true>(T, K, N, eps, inv_k, xp, ldx, wp,
@@ -975,9 +990,10 @@ hipError_t launch_epi(int64_t T, int64_t K, int64_t N, float eps, const uint16_t
 
 }  // namespace
 
-bool normproj_pipelined(int64_t T, int64_t K, int64_t N, int64_t ldy, const void* y)
+bool normproj_pipelined(int64_t T, int64_t K, int64_t N, int64_t ldx, int64_t ldw, int64_t ldy,
+                        const void* y)
 {
-    const Path p = choose_path(T, K, N, ldy, y);
+    const Path p = choose_path(T, K, N, ldx, ldw, ldy, y);
     return p == kPathBig64 || p == kPathBig32 || p == kPathMid;
 }
 

@@ -62,7 +62,8 @@ hipError_t launch_normproj(int64_t T, int64_t K, int64_t N, float eps, int epi,
                            const float* rowstats, hipStream_t stream);
 
 // Whether launch_normproj runs one of the pipelined matrix-core kernels for this shape.
-bool normproj_pipelined(int64_t T, int64_t K, int64_t N, int64_t ldy, const void* y);
+bool normproj_pipelined(int64_t T, int64_t K, int64_t N, int64_t ldx, int64_t ldw, int64_t ldy,
+                        const void* y);
 
 // rowstats[t] = (mean of x row t, 1 / sqrt(var + eps)) in fp32, K % 8 == 0, rows 16-byte aligned.
 hipError_t launch_layernorm_stats(int64_t T, int64_t K, float eps, const void* x, int64_t ldx,
