@@ -448,11 +448,21 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
             }
     }
     __syncthreads();
+    // each thread stores one 16-byte column chunk of every RSTEP-th row: all its LDS reads are
+    // issued before the first global store
     constexpr int C8 = BN / 8;
-    for (int idx = tid; idx < BM * C8; idx += NT) {
-        const int r = idx / C8, c8 = idx % C8;
-        const int64_t gm = m0 + r, gn = n0 + c8 * 8;
-        if (gm < T && gn < N) *(u32x4*)(y + gm * ldy + gn) = *(const u32x4*)(ct + r * CP + c8 * 8);
+    static_assert(NT % C8 == 0 && (BM * C8) % NT == 0, "store loop shape");
+    constexpr int RSTEP = NT / C8, ITER = BM * C8 / NT;
+    const int c8 = tid % C8, r0 = tid / C8;
+    const int64_t gn = n0 + c8 * 8;
+    u32x4 out[ITER];
+#pragma unroll
+    for (int it = 0; it < ITER; ++it)
+        out[it] = *(const u32x4*)(ct + (r0 + it * RSTEP) * CP + c8 * 8);
+    uint16_t* yp = y + (m0 + r0) * ldy + gn;
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+        if (m0 + r0 + it * RSTEP < T && gn < N) *(u32x4*)(yp + (int64_t)it * RSTEP * ldy) = out[it];
     }
 }
 
