@@ -928,7 +928,7 @@ hipError_t launch_pipe(int64_t T, int64_t K, int64_t N, float eps, float inv_k,
 }
 
 // Kernel choice for a product shape.
-enum Path { kPathMv, kPathBig64, kPathBig32, kPathMid, kPathGeneric };
+enum Path { kPathMv, kPathBig64, kPathBig32, kPathMid, kPathMidDeep, kPathGeneric };
 
 Path choose_path(int64_t T, int64_t K, int64_t N, int64_t ldx, int64_t ldw, int64_t ldy,
                  const void* y)
@@ -943,8 +943,11 @@ Path choose_path(int64_t T, int64_t K, int64_t N, int64_t ldx, int64_t ldw, int6
     if (pipe_ok && big_tiles >= 256 && K % 64 == 0) return kPathBig64;
     if (pipe_ok && big_tiles >= 256 && K % 32 == 0) return kPathBig32;
     // 128 x 128 per workgroup of 8 wavefronts (32 x 64 each: two wavefronts per SIMD hide each
-    // other's LDS and barrier latency), k-tiles of 64, 2 stages (2 workgroups per CU)
-    if (pipe_ok && K % 64 == 0) return kPathMid;
+    // other's LDS and barrier latency), k-tiles of 64: with more tiles than CUs, 2 stages and 2
+    // workgroups per CU; with at most one tile per CU, 4 stages (3 k-tiles in flight) in the LDS
+    // the second workgroup would have used
+    const int64_t mid_tiles = ((T + 127) / 128) * ((N + 127) / 128);
+    if (pipe_ok && K % 64 == 0) return mid_tiles <= 256 ? kPathMidDeep : kPathMid;
     return kPathGeneric;
 }
 
@@ -967,6 +970,10 @@ hipError_t launch_epi(int64_t T, int64_t K, int64_t N, float eps, const uint16_t
                                                               rowstats, st);
     case kPathMid:
         return launch_pipe<128, 128, 4, 2, 2, 64, EPI, false>(T, K, N, eps, inv_k, xp, ldx, wp,
+                                                              ldw, yp, ldy, colsum, bias,
+                                                              rowstats, st);
+    case kPathMidDeep:
+        return launch_pipe<128, 128, 4, 2, 4, 64, EPI, false>(T, K, N, eps, inv_k, xp, ldx, wp,
                                                               ldw, yp, ldy, colsum, bias,
                                                               rowstats, st);
     default:
@@ -1004,7 +1011,7 @@ bool normproj_pipelined(int64_t T, int64_t K, int64_t N, int64_t ldx, int64_t ld
                         const void* y)
 {
     const Path p = choose_path(T, K, N, ldx, ldw, ldy, y);
-    return p == kPathBig64 || p == kPathBig32 || p == kPathMid;
+    return p == kPathBig64 || p == kPathBig32 || p == kPathMid || p == kPathMidDeep;
 }
 
 hipError_t launch_normproj(int64_t T, int64_t K, int64_t N, float eps, int epi,

@@ -186,12 +186,14 @@ def test_normproj_unfused_baseline(Q):
 @pytest.mark.parametrize("T,K,N", [(5, 256, 130), (16, 1032, 64), (17, 1024, 520),
                                    (300, 264, 200), (129, 2048, 2048), (8200, 1056, 4104),
                                    (8200, 1024, 4104), (4096, 64, 4096), (4096, 128, 4096),
-                                   (4100, 192, 4104), (4096, 96, 4096)])
+                                   (4100, 192, 4104), (4096, 96, 4096),
+                                   (4100, 512, 2056)])
 def test_normproj_ragged(Q, T, K, N):
     """Every kernel of the projection: the matrix-vector path (T <= 16), the generic tile
-    kernel (K not a multiple of 32), and both pipelined tilings (128 x 128 and 256 x 256 with
-    k-tiles of 64 through the five-part ring, or of 32), with T and N not multiples of the tile
-    and rings of one, two and three k-tiles; large cases are checked on a sample of rows."""
+    kernel (K not a multiple of 32), and the pipelined tilings (128 x 128 with 4 stages when
+    there is at most one tile per CU and 2 otherwise; 256 x 256 with k-tiles of 64 through the
+    five-part ring, or of 32), with T and N not multiples of the tile and rings of one, two and
+    three k-tiles; large cases are checked on a sample of rows."""
     rng = np.random.default_rng(T + K + N)
     x = inputs.random_rows(rng, T, K, "bf16")
     w = inputs.random_rows(rng, K, N, "bf16", scale=0.02)
