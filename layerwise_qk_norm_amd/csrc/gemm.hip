@@ -316,7 +316,10 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
             }
         }
         __syncthreads();  // every wavefront's DMA has landed; the parts of k-tile kt-1 are free
-        if constexpr (!RING) {
+        // whole-tile stages: with NST >= 3 the next k-tile's requests are spread over the k steps
+        // (two later k-tiles are still in flight meanwhile); with 2 stages they go out at once
+        constexpr bool SPREAD = !RING && NST >= 3 && CPT % KS == 0;
+        if constexpr (!RING && !SPREAD) {
             if (kt + NST - 1 < nk) issue_tile((kt + NST - 1) % NST, (int64_t)(kt + NST - 1) * BK);
         }
         const char* As = RING ? smem + pa * PART_A : smem + (kt % NST) * STAGE;
@@ -362,6 +365,19 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
                     } else {
                         if (kt + 2 < nk)
                             dma_a(c - CPB, (uint32_t)(pna * PART_A), (int64_t)(kt + 2) * BK);
+                    }
+                }
+            }
+            if constexpr (SPREAD) {
+                constexpr int PER = CPT / KS;
+                const int nt = kt + NST - 1;
+                const uint32_t base = (uint32_t)((nt % NST) * STAGE);
+#pragma unroll
+                for (int h = 0; h < PER; ++h) {
+                    const int c = ks * PER + h;
+                    if (nt < nk) {
+                        if (c < CPA) dma_a(c, base, (int64_t)nt * BK);
+                        else dma_b(c - CPA, base + PART_A, (int64_t)nt * BK);
                     }
                 }
             }
