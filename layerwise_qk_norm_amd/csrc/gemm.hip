@@ -11,16 +11,20 @@
 // with c the column sums of the folded weight and b = beta W. The row statistics come from the
 // same x values that feed the matrix cores, accumulated on the VALU while the MFMAs run, so no
 // extra pass over x is needed and the reduction proceeds beside the product instead of before
-// it. LayerNorm accumulates sum(x - x0) and sum((x - x0)^2) with x0 the row's first element, so
-// that the one-pass variance does not cancel for rows whose mean is large against their spread.
+// it; for LayerNorm they can instead come from one streaming pass over x (layernorm_stats_kernel)
+// that the product's epilogue reads. LayerNorm accumulates sum(x - x0) and sum((x - x0)^2) with
+// x0 the row's first element, so that the one-pass variance does not cancel for rows whose mean
+// is large against their spread.
 //
 // Pipelined kernel (K a multiple of the k-tile, N of 8): a workgroup owns a BM x BN output tile.
 // Its k-tiles of x and W' reach LDS by direct global->LDS DMA (global_load_lds_dwordx4, 1 KB per
-// wavefront instruction), either through an NST-deep ring of whole k-tiles or, for 256 x 256
-// tiles with k-tiles of 64 (64 KB each, so only two whole k-tiles fit in LDS), through a ring of
-// five 32 KB parts: the x part of a k-tile is requested two k-tiles ahead and its W' part one
-// ahead, which keeps one and a half k-tiles in flight instead of one, and those requests are
-// spread over the k steps of the current k-tile rather than issued in one burst. Each tile
+// wavefront instruction, tile base in scalar registers and a 32-bit offset per lane), either
+// through an NST-deep ring of whole k-tiles or, for 256 x 256 tiles with k-tiles of 64 (64 KB
+// each, so only two whole k-tiles fit in LDS), through a ring of five 32 KB parts: the x part of
+// a k-tile is requested two k-tiles ahead and its W' part one ahead, which keeps one and a half
+// k-tiles in flight instead of one. With five parts or with 3 or more whole-tile stages, the
+// requests are spread over the k steps of the current k-tile rather than issued in one burst.
+// Each tile
 // row's 16-byte chunks are XOR-swizzled so the fragment reads of 16 consecutive rows fall in
 // 16 distinct bank groups. Wavefronts own WM x WN sub-tiles of 32 x 32 MFMA blocks, with the W'
 // fragment as the MFMA's first operand so that a lane's accumulator holds one output row and
