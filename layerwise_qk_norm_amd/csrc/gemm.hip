@@ -645,8 +645,9 @@ __global__ __launch_bounds__(kThreads) void normproj_mfma_kernel(
 // consecutive k of one W' row, 16 bytes) straight from global memory, kMvUnroll steps ahead,
 // so W' is streamed once with most of it in flight, and x (the A fragments) is read once per
 // workgroup from cache. The wavefronts' partial products and row statistics are added through
-// LDS in a fixed order. Narrow outputs (N <= 4096) use one tile and 16 wavefronts per
-// workgroup so that enough workgroups stream W'.
+// LDS in a fixed order. Narrow outputs (N <= 4096) and up to 4 tokens use one tile and 16
+// wavefronts per workgroup so that enough workgroups stream W'; more tokens on wide outputs use
+// two tiles and 12 wavefronts, halving the x fetches.
 //
 // Fragment layout of the 16x16x32 MFMA: lane l supplies A[l % 16][8 (l / 16) .. + 7] and
 // B[8 (l / 16) .. + 7][l % 16]; it receives D[4 (l / 16) + i][l % 16] for i = 0..3.
@@ -1003,7 +1004,10 @@ hipError_t launch_epi(int64_t T, int64_t K, int64_t N, float eps, const uint16_t
         return hipErrorInvalidValue;  // statistics from memory: pipelined kernels only
     } else {
         if (path == kPathMv) {
-            const bool narrow = N <= 4096;
+            // one 16-column tile per workgroup of 16 wavefronts, or, where x is worth sharing
+            // (more than 4 tokens, wide N), two tiles per workgroup of 12: each lane's x
+            // fragment then serves two MFMAs and x is fetched once per 32 columns
+            const bool narrow = N <= 4096 || T <= 4;
             const int64_t nblk = narrow ? (N + 15) / 16 : (N + 31) / 32;
             if (nblk > 0x7fffffff) return hipErrorInvalidConfiguration;
             if (narrow)
@@ -1011,8 +1015,8 @@ hipError_t launch_epi(int64_t T, int64_t K, int64_t N, float eps, const uint16_t
                                    dim3(16 * kWave), 0, st, (int)T, K, N, eps, inv_k, xp, ldx, wp,
                                    ldw, yp, ldy, colsum, bias);
             else
-                hipLaunchKernelGGL((normproj_mv_kernel<EPI, 2, 8>), dim3((unsigned)nblk),
-                                   dim3(8 * kWave), 0, st, (int)T, K, N, eps, inv_k, xp, ldx, wp,
+                hipLaunchKernelGGL((normproj_mv_kernel<EPI, 2, 12>), dim3((unsigned)nblk),
+                                   dim3(12 * kWave), 0, st, (int)T, K, N, eps, inv_k, xp, ldx, wp,
                                    ldw, yp, ldy, colsum, bias);
             return hipGetLastError();
         }

@@ -187,7 +187,7 @@ def test_normproj_unfused_baseline(Q):
                                    (300, 264, 200), (129, 2048, 2048), (8200, 1056, 4104),
                                    (8200, 1024, 4104), (4096, 64, 4096), (4096, 128, 4096),
                                    (4100, 192, 4104), (4096, 96, 4096),
-                                   (4100, 512, 2056)])
+                                   (4100, 512, 2056), (12, 512, 4104)])
 def test_normproj_ragged(Q, T, K, N):
     """Every kernel of the projection: the matrix-vector path (T <= 16), the generic tile
     kernel (K not a multiple of 32), and the pipelined tilings (128 x 128 with 4 stages when
