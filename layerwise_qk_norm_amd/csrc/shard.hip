@@ -294,7 +294,10 @@ hipError_t launch_shard_nv(const ShardJob& job, hipStream_t st)
                 occ = 1;
             occupancy[which].store(occ, std::memory_order_relaxed);
         }
-        const int64_t cap = ((int64_t)device_cus() * occ * 3) / 4;
+        // at most three quarters of the resident capacity, as a whole number of workgroups per
+        // CU so that every CU streams the same share
+        const int cus = device_cus();
+        const int64_t cap = (int64_t)cus * ((occ * 3) / 4 > 0 ? (occ * 3) / 4 : 1);
         grid = items < cap ? items : (cap > 0 ? cap : 1);
     }
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
