@@ -136,28 +136,22 @@ __device__ __forceinline__ float epilogue(float acc, float rs, float mu, float c
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// 16 bytes per lane from global memory straight into LDS at lds_off + 16 * lane. Issued through
-// inline assembly so that the compiler does not wait for it before unrelated LDS reads; the
-// kernel awaits completion with s_waitcnt vmcnt (vector loads complete in issue order). One
-// wait state separates the M0 write from the DMA (a gfx9-family hazard). M0 is declared
-// clobbered; no other instruction in these kernels uses it (checked in the generated code).
+// 16 bytes per lane from global memory straight into LDS at lds_off + 16 * lane, addressed as a
+// wavefront-uniform 64-bit base in scalar registers plus a 32-bit byte offset per lane (no
+// 64-bit address arithmetic per request). Issued through inline assembly so that the compiler
+// does not wait for it before unrelated LDS reads; the kernel awaits completion with s_waitcnt
+// vmcnt (vector loads complete in issue order). One wait state separates the M0 write from the
+// DMA (a gfx9-family hazard). M0 is declared clobbered; no other instruction in these kernels
+// uses it (checked in the generated code).
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_off)
-{
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-                 ::"s"(__builtin_amdgcn_readfirstlane(lds_off)), "v"(gsrc) : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// The same with a wavefront-uniform 64-bit base in scalar registers and a 32-bit byte offset
-// per lane (the saddr form: no 64-bit address arithmetic per request).
 __device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds_off)
 {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                  ::"s"(__builtin_amdgcn_readfirstlane(lds_off)), "v"(voff), "s"(sbase)
                  : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt()
