@@ -209,20 +209,19 @@ def normproj_setup(torch, Q, inputs, T, unfused=False):
     c = inputs.make_case(5, T)
     x, w, g = dev(torch, c["x"]), dev(torch, c["w"]), dev(torch, c["gamma"])
     K, N = w.shape
-    wf = Q.normproj_fold_weight(w, g)
-    wp = Q.normproj_fold_weight(w, None)
-    n = rotation_count(T * (K + N) * 2 + (T * K * 2 if unfused else 0))
+    wm = Q.normproj_fold_weight(w, None) if unfused else Q.normproj_fold_weight(w, g)
+    n = rotation_count(T * (K + N) * 2 + K * N * 2 + (T * K * 2 if unfused else 0))
     sets = [(x.clone(), torch.empty((T, N), dtype=torch.bfloat16, device="cuda"),
-             torch.empty((T, K), dtype=torch.bfloat16, device="cuda") if unfused else None)
-            for _ in range(n)]
+             torch.empty((T, K), dtype=torch.bfloat16, device="cuda") if unfused else None,
+             wm.clone()) for _ in range(n)]
 
     def deferred(i):
-        xi, yi, _ = sets[i % n]
-        Q.normproj_deferred(xi, wf, eps=c["eps"], y=yi)
+        xi, yi, _, wi = sets[i % n]
+        Q.normproj_deferred(xi, wi, eps=c["eps"], y=yi)
 
     def unf(i):
-        xi, yi, xn = sets[i % n]
-        Q.normproj_unfused(xi, g, wp, eps=c["eps"], xn=xn, y=yi)
+        xi, yi, xn, wi = sets[i % n]
+        Q.normproj_unfused(xi, g, wi, eps=c["eps"], xn=xn, y=yi)
 
     flops = 2.0 * T * K * N
     nbytes = T * K * 2 + K * N * 2 + T * N * 2
@@ -238,22 +237,22 @@ def elimination_setup(torch, Q, inputs, T, mode):
     x, w = dev(torch, c["x"]), dev(torch, c["w"])
     g1, gq, gk = dev(torch, c["gamma_pre"]), dev(torch, c["gamma_q"]), dev(torch, c["gamma_k"])
     K, N, nq = c["K"], c["nq"] + c["nk"], c["nq"]
-    wqk = Q.normproj_fold_weight(w, g1)
-    wp = Q.normproj_fold_weight(w, None) if mode == "unfused" else None
+    wm = Q.normproj_fold_weight(w, None if mode == "unfused" else g1)
     del w
-    n = rotation_count(T * (K + N) * 2 + (T * K * 2 if mode == "unfused" else 0))
+    n = rotation_count(T * (K + N) * 2 + K * N * 2 + (T * K * 2 if mode == "unfused" else 0))
     sets = [(x.clone(), torch.empty((T, N), dtype=torch.bfloat16, device="cuda"),
              torch.empty((T, K), dtype=torch.bfloat16, device="cuda") if mode == "unfused"
-             else None) for _ in range(n)]
+             else None, wm.clone()) for _ in range(n)]
+    del wm
 
     def fn(i):
-        xi, yi, xn = sets[i % n]
+        xi, yi, xn, wi = sets[i % n]
         if mode == "unfused":
-            Q.normproj_unfused(xi, g1, wp, eps=c["eps_pre"], xn=xn, y=yi)
+            Q.normproj_unfused(xi, g1, wi, eps=c["eps_pre"], xn=xn, y=yi)
             Q.qknorm_fused(yi[:, :nq], gq, yi[:, nq:], gk, eps=c["eps_qk"], q_out=yi[:, :nq],
                            k_out=yi[:, nq:])
         else:
-            Q.qknorm_project_eliminated(xi, wqk, nq, gq, gk, eps_qk=c["eps_qk"],
+            Q.qknorm_project_eliminated(xi, wi, nq, gq, gk, eps_qk=c["eps_qk"],
                                         eps_pre=c["eps_pre"], exact=(mode == "exact"), y=yi)
 
     fn.sets = n
@@ -268,20 +267,22 @@ def layernorm_setup(torch, Q, inputs, T, unfused, in_product=False):
     x, w = dev(torch, c["x"]), dev(torch, c["w"])
     g, be = dev(torch, c["gamma"]), dev(torch, c["beta"])
     K, N = c["K"], c["N"]
-    wf, cs, b = Q.normproj_fold_layernorm(w, g, be)
-    wp = Q.normproj_fold_weight(w, None)
-    n = rotation_count(T * (K + N) * 2 + (T * K * 2 if unfused else 0))
+    if unfused:
+        wm, cs, b = Q.normproj_fold_weight(w, None), None, None
+    else:
+        wm, cs, b = Q.normproj_fold_layernorm(w, g, be)
+    n = rotation_count(T * (K + N) * 2 + K * N * 2 + (T * K * 2 if unfused else 0))
     sets = [(x.clone(), torch.empty((T, N), dtype=torch.bfloat16, device="cuda"),
-             torch.empty((T, K), dtype=torch.bfloat16, device="cuda") if unfused else None)
-            for _ in range(n)]
+             torch.empty((T, K), dtype=torch.bfloat16, device="cuda") if unfused else None,
+             wm.clone()) for _ in range(n)]
     ws = None if in_product else torch.empty((T, 2), dtype=torch.float32, device="cuda")
 
     def fn(i):
-        xi, yi, xn = sets[i % n]
+        xi, yi, xn, wi = sets[i % n]
         if unfused:
-            Q.normproj_layernorm_unfused(xi, g, be, wp, eps=c["eps"], xn=xn, y=yi)
+            Q.normproj_layernorm_unfused(xi, g, be, wi, eps=c["eps"], xn=xn, y=yi)
         else:
-            Q.normproj_deferred_layernorm(xi, wf, cs, b, eps=c["eps"], y=yi, row_stats=ws)
+            Q.normproj_deferred_layernorm(xi, wi, cs, b, eps=c["eps"], y=yi, row_stats=ws)
 
     fn.sets = n
     return fn, 2.0 * T * K * N, T * K * 2 + K * N * 2 + T * N * 2
