@@ -634,19 +634,29 @@ __global__ __launch_bounds__(kThreads) void normproj_mfma_kernel(
 }
 
 // Matrix-vector form for T <= 16 on the matrix cores: v_mfma_f32_16x16x32_bf16 with the (up
-// to 16) tokens as the M dimension. A workgroup owns NTILE 16-column MFMA tiles and splits K
-// over its kMvWaves wavefronts, k steps of 32 interleaved; each lane loads its B fragment (8
-// consecutive k of one W' row, 16 bytes) straight from global memory, kMvUnroll steps ahead,
-// so W' is streamed once with most of it in flight, and x (the A fragments) is read once per
-// workgroup from cache. The wavefronts' partial products and row statistics are added through
-// LDS in a fixed order. Narrow outputs (N <= 4096) and up to 4 tokens use one tile and 16
-// wavefronts per workgroup so that enough workgroups stream W'; more tokens on wide outputs use
-// two tiles and 12 wavefronts, halving the x fetches.
+// to 16) tokens as the M dimension and 16 W' rows (output columns) as N. Fragment layout: lane
+// l supplies A[l % 16][8 (l / 16) .. + 7] and B[8 (l / 16) .. + 7][l % 16]; it receives
+// D[4 (l / 16) + i][l % 16] for i = 0..3.
 //
-// Fragment layout of the 16x16x32 MFMA: lane l supplies A[l % 16][8 (l / 16) .. + 7] and
-// B[8 (l / 16) .. + 7][l % 16]; it receives D[4 (l / 16) + i][l % 16] for i = 0..3.
+// Loaded straight into registers, those fragments put 16 W' rows x 64 bytes under each load
+// instruction, a shape that streams at about three quarters of the rate of whole 128-byte
+// lines. Instead each wavefront fetches a step of 64 k of its tiles with the LDS DMA, every
+// instruction covering 8 rows x 128 B, into a region of LDS of its own, and reads the fragments
+// back with ds_read_b128. The x rows of the step travel the same way, so every global access of
+// the k loop is a DMA counted by vmcnt alone and the wavefront keeps S steps in flight under
+// its own waits (no barriers: nothing in the loop is shared between wavefronts). A workgroup
+// owns NTILE 16-column tiles; its wavefronts split K into interleaved steps and add their
+// partial products (and row sums) through LDS in a fixed order. Workgroup b starts its walk
+// over K kMvRotate * b steps in: in lockstep, every workgroup would read the same x lines and
+// the same k range of W' at a time, piling the requests onto a few L2 channels.
+//
+// Step layout (16 rows, 2 KB): row r, 16-byte chunk c (8 k values) at byte
+// (r & 1) * 1024 + (r >> 1) * 128 + (c ^ mvl_f(r)) * 16. One DMA instruction fills the even
+// rows and one the odd rows, each lane fetching the chunk its destination slot stands for; a
+// fragment read (16 rows at one chunk per 16-lane phase) then touches 16 distinct 16-byte bank
+// groups of the 256-byte bank row. Steps of up to 8 x rows use r * 128 + (c ^ (r >> 1)) * 16.
 constexpr int kGemvMaxT = 16;
-constexpr int kMvUnroll = 8;
+constexpr int kMvRotate = 7;
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
@@ -656,74 +666,192 @@ __device__ __forceinline__ f32x4v mfma16(const u32x4& a, const u32x4& b, const f
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-template <int EPI, int NTILE, int kMvWaves>
-__global__ __launch_bounds__(kMvWaves * 64) void normproj_mv_kernel(
+__device__ __forceinline__ int mvl_f(int r) { return ((r >> 2) << 1) | (r & 1); }
+__device__ __forceinline__ uint32_t mvl_off16(int r, int c)
+{
+    return (uint32_t)((r & 1) * 1024 + (r >> 1) * 128 + ((c ^ mvl_f(r)) << 4));
+}
+__device__ __forceinline__ uint32_t mvl_off8(int r, int c)
+{
+    return (uint32_t)(r * 128 + ((c ^ (r >> 1)) << 4));
+}
+
+// s_waitcnt vmcnt(N) that the compiler may not move LDS reads above.
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Wait until at most `later` steps of C DMA instructions each remain in flight (0 <= later <= L).
+template <int C, int L>
+__device__ __forceinline__ void wait_steps(int later)
+{
+    if constexpr (L > 0) {
+        if (later >= L) {
+            wait_vm<C * L>();
+            return;
+        }
+        wait_steps<C, L - 1>(later);
+    } else {
+        wait_vm<0>();
+    }
+}
+
+template <int EPI, int NTILE, int XR, int WAVES, int S>
+__global__ __launch_bounds__(WAVES * 64) void normproj_mvl_kernel(
     int T, int64_t K, int64_t N, float eps, float inv_k, const uint16_t* __restrict__ x,
     int64_t ldx, const uint16_t* __restrict__ w, int64_t ldw, uint16_t* __restrict__ y,
     int64_t ldy, const float* __restrict__ colsum, const float* __restrict__ bias)
 {
-    constexpr int kMvCols = 16 * NTILE;
-    __shared__ float red_acc[kMvWaves][NTILE][4][kWave];
-    __shared__ float red_st[kMvWaves][2][16];
-    const int lane = lane_id(), wave = (int)threadIdx.x / kWave;
-    const int r16 = lane & 15, g = lane >> 4;
-    const int64_t n0 = (int64_t)blockIdx.x * kMvCols;
-    const bool trow = r16 < T;
+    constexpr int kCols = 16 * NTILE;
+    static_assert(XR == 1 || XR == 2 || XR == 4 || XR == 8 || XR == 16, "x rows per step");
+    constexpr int XH = XR == 16 ? 2 : 1;          // DMA instructions for the x rows
+    constexpr int XOFF = NTILE * 2048;            // x rows after the W' tiles of a step
+    constexpr int STAGE = XOFF + (XR == 16 ? 2048 : XR * 128);  // one step of one wavefront
+    constexpr int REGION = S * STAGE;             // a wavefront's LDS
+    constexpr int C = 2 * NTILE + XH;             // DMA instructions per step
+    static_assert(S >= 2 && C * (S - 1) < 64, "vmcnt range");
+    static_assert(REGION >= NTILE * 4 * kWave * 4 + 2 * 16 * 4, "partials fit the region");
+    __shared__ __attribute__((aligned(1024))) char smem[WAVES * REGION];
 
-    // this lane's W' rows (rows past N are clamped: they feed columns that are never stored)
-    const uint16_t* wrow[NTILE];
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+    const int r16 = lane & 15, g = lane >> 4;
+    const int64_t n0 = (int64_t)blockIdx.x * kCols;
+    char* region = smem + wave * REGION;
+    const uint32_t lds_region = (uint32_t)(uintptr_t)(lds_void*)region;
+
+    // DMA sources, as a row byte offset (from the tile's first W' row, or from x) and a chunk
+    // byte offset within the step. Rows past N read row N - 1 and token rows past T read row
+    // T - 1: they feed outputs that are never stored. The offsets fit 32 bits for ld < 2^23.
+    const int drow = lane >> 3, dc = lane & 7;
+    uint32_t wrow[NTILE][2], wch[NTILE][2], xrow[XH], xch[XH];
 #pragma unroll
-    for (int j = 0; j < NTILE; ++j) {
-        const int64_t n = n0 + j * 16 + r16;
-        wrow[j] = w + (n < N ? n : N - 1) * ldw + g * 8;
+    for (int j = 0; j < NTILE; ++j)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int r = 2 * drow + h;
+            const int64_t n = n0 + 16 * j + r;
+            wrow[j][h] = (uint32_t)(((n < N ? n : N - 1) - n0) * ldw * 2);
+            wch[j][h] = (uint32_t)((dc ^ mvl_f(r)) << 4);
+        }
+#pragma unroll
+    for (int h = 0; h < XH; ++h) {
+        const int r = XH == 1 ? drow : 2 * drow + h;
+        xrow[h] = (uint32_t)((r < T ? r : T - 1) * ldx * 2);
+        xch[h] = (uint32_t)((XH == 1 ? dc ^ (r >> 1) : dc ^ mvl_f(r)) << 4);
     }
-    const uint16_t* xrow = x + (int64_t)(trow ? r16 : 0) * ldx + g * 8;
+    const uint16_t* wb = w + n0 * ldw;
+    const uint32_t kbytes = (uint32_t)(K * 2);
+
     float x0 = 0.0f;
-    if constexpr (EPI == kEpiLayerNorm) x0 = bf16_at(x, (int64_t)(trow ? r16 : 0) * ldx);
+    if constexpr (EPI == kEpiLayerNorm) {
+        x0 = bf16_at(x, (int64_t)(r16 < T ? r16 : 0) * ldx);
+        asm volatile("" ::"v"(x0));  // its load completes before the first DMA is issued
+    }
+
+    // Step st into slot `slot`: chunks past K read the row's last chunk and are zeroed at use.
+    auto issue = [&](int64_t st, int slot) {
+        const uint32_t kb = (uint32_t)st * 128u;
+        const bool full = kb + 128u <= kbytes;
+        const uint32_t dst = lds_region + (uint32_t)(slot * STAGE);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the slot's fragment reads are done
+#pragma unroll
+        for (int j = 0; j < NTILE; ++j)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t c = full ? kb + wch[j][h] : min(kb + wch[j][h], kbytes - 16u);
+                dma16s(wb, wrow[j][h] + c, dst + (uint32_t)(j * 2048 + h * 1024));
+            }
+#pragma unroll
+        for (int h = 0; h < XH; ++h) {
+            const uint32_t c = full ? kb + xch[h] : min(kb + xch[h], kbytes - 16u);
+            if (XR >= 8 || lane < XR * 8) dma16s(x, xrow[h] + c, dst + (uint32_t)(XOFF + h * 1024));
+        }
+    };
 
     f32x4v acc[NTILE];
 #pragma unroll
     for (int j = 0; j < NTILE; ++j) acc[j] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
     float s1 = 0.0f, s2 = 0.0f;
 
-    const int64_t nsteps = (K + 31) / 32;
-    for (int64_t base = wave; base < nsteps; base += (int64_t)kMvWaves * kMvUnroll) {
-        u32x4 a[kMvUnroll], b[NTILE][kMvUnroll];
-        bool ok[kMvUnroll];
+    auto consume = [&](int64_t st, int slot) {
+        const char* sp = region + slot * STAGE;
+        u32x4 a[2], b[NTILE][2];
 #pragma unroll
-        for (int u = 0; u < kMvUnroll; ++u) {
-            const int64_t st = base + (int64_t)u * kMvWaves;
-            ok[u] = st < nsteps && st * 32 + g * 8 < K;
-            a[u] = (ok[u] && trow) ? *(const u32x4*)(xrow + st * 32) : u32x4{0u, 0u, 0u, 0u};
+        for (int q = 0; q < 2; ++q) {
+            const int c = q * 4 + g;
+            a[q] = *(const u32x4*)(sp + XOFF + (XR == 16 ? mvl_off16(r16, c)
+                                                          : mvl_off8(r16 & (XR - 1), c)));
 #pragma unroll
             for (int j = 0; j < NTILE; ++j)
-                b[j][u] = ok[u] ? load_stream(wrow[j] + st * 32) : u32x4{0u, 0u, 0u, 0u};
+                b[j][q] = *(const u32x4*)(sp + j * 2048 + mvl_off16(r16, c));
+        }
+        bool kin[2] = {true, true};
+        if ((uint32_t)st * 128u + 128u > kbytes) {  // the last, partial step
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                kin[q] = st * 64 + (q * 4 + g) * 8 < K;
+                if (!kin[q]) {
+                    a[q] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+                    for (int j = 0; j < NTILE; ++j) b[j][q] = u32x4{0u, 0u, 0u, 0u};
+                }
+            }
         }
 #pragma unroll
-        for (int u = 0; u < kMvUnroll; ++u) {
+        for (int q = 0; q < 2; ++q) {
+            // chunks past K take no part in the row sums (a zero would add -x0 to LayerNorm's)
             if constexpr (EPI != kEpiPlain) {
-                if (ok[u] && trow) accum_stats<EPI>(a[u], x0, s1, s2);
+                if (kin[q]) accum_stats<EPI>(a[q], x0, s1, s2);
             }
 #pragma unroll
-            for (int j = 0; j < NTILE; ++j) acc[j] = mfma16(a[u], b[j][u], acc[j]);
+            for (int j = 0; j < NTILE; ++j) acc[j] = mfma16(a[q], b[j][q], acc[j]);
+        }
+    };
+
+    const int64_t nsteps = (K + 63) / 64;
+    const int nmine = wave < nsteps ? (int)((nsteps - 1 - wave) / WAVES) + 1 : 0;
+    const int64_t rot = ((int64_t)blockIdx.x * kMvRotate) % nsteps;
+    auto step = [&](int i) {
+        const int64_t st = wave + (int64_t)i * WAVES + rot;
+        return st >= nsteps ? st - nsteps : st;
+    };
+#pragma unroll
+    for (int i = 0; i < S; ++i)
+        if (i < nmine) issue(step(i), i);
+    for (int i0 = 0; i0 < nmine; i0 += S) {
+#pragma unroll
+        for (int u = 0; u < S; ++u) {
+            const int i = i0 + u;
+            if (i >= nmine) break;
+            const int later = nmine - 1 - i;
+            wait_steps<C, S - 1>(later < S - 1 ? later : S - 1);
+            consume(step(i), u);
+            if (i + S < nmine) issue(step(i + S), u);
         }
     }
 
-    // lanes l, l + 16, l + 32, l + 48 hold the four k groups of row l % 16
+    // partial products and row sums into the wavefront's own region (its DMAs are complete)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    float* racc = (float*)region;
+    float* rst = racc + NTILE * 4 * kWave;
+#pragma unroll
+    for (int j = 0; j < NTILE; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) racc[(j * 4 + i) * kWave + lane] = acc[j][i];
     if constexpr (EPI != kEpiPlain) {
         s1 += __shfl_xor(s1, 16);
         s2 += __shfl_xor(s2, 16);
         s1 += __shfl_xor(s1, 32);
         s2 += __shfl_xor(s2, 32);
         if (lane < 16) {
-            red_st[wave][0][lane] = s1;
-            red_st[wave][1][lane] = s2;
+            rst[lane] = s1;
+            rst[16 + lane] = s2;
         }
     }
-#pragma unroll
-    for (int j = 0; j < NTILE; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) red_acc[wave][j][i][lane] = acc[j][i];
     __syncthreads();
     if (wave != 0) return;
 
@@ -735,9 +863,10 @@ __global__ __launch_bounds__(kMvWaves * 64) void normproj_mv_kernel(
         if constexpr (EPI != kEpiPlain) {
             float q1 = 0.0f, q2 = 0.0f;
 #pragma unroll
-            for (int v = 0; v < kMvWaves; ++v) {
-                q1 += red_st[v][0][t];
-                q2 += red_st[v][1][t];
+            for (int v = 0; v < WAVES; ++v) {
+                const float* o = (const float*)(smem + v * REGION) + NTILE * 4 * kWave;
+                q1 += o[t];
+                q2 += o[16 + t];
             }
             const float xt0 = EPI == kEpiLayerNorm ? bf16_at(x, (int64_t)t * ldx) : 0.0f;
             row_scale<EPI>(q1, q2, xt0, inv_k, eps, rs, mu);
@@ -748,7 +877,8 @@ __global__ __launch_bounds__(kMvWaves * 64) void normproj_mv_kernel(
             if (n >= N) continue;
             float sum = 0.0f;
 #pragma unroll
-            for (int v = 0; v < kMvWaves; ++v) sum += red_acc[v][j][i][lane];
+            for (int v = 0; v < WAVES; ++v)
+                sum += ((const float*)(smem + v * REGION))[(j * 4 + i) * kWave + lane];
             float cs = 0.0f, bs = 0.0f;
             if constexpr (EPI == kEpiLayerNorm) {
                 cs = colsum[n];
@@ -942,13 +1072,58 @@ hipError_t launch_pipe(int64_t T, int64_t K, int64_t N, float eps, float inv_k,
     return hipGetLastError();
 }
 
+struct MvJob {
+    int64_t T, K, N;
+    float eps, inv_k;
+    const uint16_t* x;
+    int64_t ldx;
+    const uint16_t* w;
+    int64_t ldw;
+    uint16_t* y;
+    int64_t ldy;
+    const float *colsum, *bias;
+    hipStream_t st;
+};
+
+template <int EPI, int NTILE, int XR, int WAVES, int S>
+hipError_t launch_mvl(const MvJob& j)
+{
+    constexpr int kCols = 16 * NTILE;
+    const int64_t nblk = (j.N + kCols - 1) / kCols;
+    if (nblk > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((normproj_mvl_kernel<EPI, NTILE, XR, WAVES, S>), dim3((unsigned)nblk),
+                       dim3(WAVES * kWave), 0, j.st, (int)j.T, j.K, j.N, j.eps, j.inv_k, j.x,
+                       j.ldx, j.w, j.ldw, j.y, j.ldy, j.colsum, j.bias);
+    return hipGetLastError();
+}
+
+// x rows per step: T rounded up to a power of two. One 16-column tile per workgroup of 8
+// wavefronts (two workgroups per CU) for outputs up to 4096 wide or up to 4 tokens; otherwise
+// two tiles (one workgroup per CU), each x fragment then feeding two MFMAs. The step count
+// fills the LDS the workgroups per CU leave.
+template <int EPI>
+hipError_t launch_mv(const MvJob& j)
+{
+    if (j.N <= 4096 || j.T <= 4) {
+        if (j.T <= 1) return launch_mvl<EPI, 1, 1, 8, 4>(j);
+        if (j.T <= 2) return launch_mvl<EPI, 1, 2, 8, 4>(j);
+        if (j.T <= 4) return launch_mvl<EPI, 1, 4, 8, 4>(j);
+        if (j.T <= 8) return launch_mvl<EPI, 1, 8, 8, 3>(j);
+        return launch_mvl<EPI, 1, 16, 8, 2>(j);
+    }
+    if (j.T <= 8) return launch_mvl<EPI, 2, 8, 8, 4>(j);
+    return launch_mvl<EPI, 2, 16, 8, 3>(j);
+}
+
 // Kernel choice for a product shape.
 enum Path { kPathMv, kPathBig64, kPathBig32, kPathMid, kPathMidDeep, kPathGeneric };
 
 Path choose_path(int64_t T, int64_t K, int64_t N, int64_t ldx, int64_t ldw, int64_t ldy,
                  const void* y)
 {
-    if (T <= kGemvMaxT) return kPathMv;
+    // the matrix-vector kernel addresses W' and x rows with 32-bit byte offsets from the
+    // first row of a tile (at most 32 rows) or of x (at most 16)
+    if (T <= kGemvMaxT && ldx < (int64_t(1) << 26) && ldw < (int64_t(1) << 26)) return kPathMv;
     // the pipelined kernels address a tile's rows with 32-bit byte offsets from its first row
     const bool pipe_ok = N % 8 == 0 && ldy % 8 == 0 && ((uintptr_t)y & 15u) == 0 &&
                          ldx < (int64_t(1) << 23) && ldw < (int64_t(1) << 23);
@@ -997,23 +1172,9 @@ hipError_t launch_epi(int64_t T, int64_t K, int64_t N, float eps, const uint16_t
     if constexpr (EPI == kEpiLayerNormStats) {
         return hipErrorInvalidValue;  // statistics from memory: pipelined kernels only
     } else {
-        if (path == kPathMv) {
-            // one 16-column tile per workgroup of 16 wavefronts, or, where x is worth sharing
-            // (more than 4 tokens, wide N), two tiles per workgroup of 12: each lane's x
-            // fragment then serves two MFMAs and x is fetched once per 32 columns
-            const bool narrow = N <= 4096 || T <= 4;
-            const int64_t nblk = narrow ? (N + 15) / 16 : (N + 31) / 32;
-            if (nblk > 0x7fffffff) return hipErrorInvalidConfiguration;
-            if (narrow)
-                hipLaunchKernelGGL((normproj_mv_kernel<EPI, 1, 16>), dim3((unsigned)nblk),
-                                   dim3(16 * kWave), 0, st, (int)T, K, N, eps, inv_k, xp, ldx, wp,
-                                   ldw, yp, ldy, colsum, bias);
-            else
-                hipLaunchKernelGGL((normproj_mv_kernel<EPI, 2, 12>), dim3((unsigned)nblk),
-                                   dim3(12 * kWave), 0, st, (int)T, K, N, eps, inv_k, xp, ldx, wp,
-                                   ldw, yp, ldy, colsum, bias);
-            return hipGetLastError();
-        }
+        if (path == kPathMv)
+            return launch_mv<EPI>(MvJob{T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp, ldy, colsum,
+                                        bias, st});
         const int64_t nbm = (T + kBM - 1) / kBM, nbn = (N + kBN - 1) / kBN;
         if (nbm * nbn > 0x7fffffff) return hipErrorInvalidConfiguration;
         hipLaunchKernelGGL(normproj_mfma_kernel<EPI>, dim3((unsigned)(nbm * nbn)), dim3(kThreads),

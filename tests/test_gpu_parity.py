@@ -187,7 +187,8 @@ def test_normproj_unfused_baseline(Q):
                                    (300, 264, 200), (129, 2048, 2048), (8200, 1056, 4104),
                                    (8200, 1024, 4104), (4096, 64, 4096), (4096, 128, 4096),
                                    (4100, 192, 4104), (4096, 96, 4096),
-                                   (4100, 512, 2056), (12, 512, 4104)])
+                                   (4100, 512, 2056), (12, 512, 4104), (8, 1000, 4104),
+                                   (1, 8, 24), (3, 64, 40), (16, 4096, 8200)])
 def test_normproj_ragged(Q, T, K, N):
     """Every kernel of the projection: the matrix-vector path (T <= 16), the generic tile
     kernel (K not a multiple of 32), and the pipelined tilings (128 x 128 with 4 stages when
@@ -210,9 +211,10 @@ def test_normproj_ragged(Q, T, K, N):
                      projection_bound(xs, wf_ref, 1e-6), f"T={T} K={K} N={N}")
 
 
-@pytest.mark.parametrize("T,K,N", [(200, 512, 256), (4096, 256, 4096)])
+@pytest.mark.parametrize("T,K,N", [(200, 512, 256), (4096, 256, 4096), (9, 520, 4104)])
 def test_normproj_strided_rows(Q, T, K, N):
-    """x and y with row strides above their widths (128 x 128 tiles, and the 256 x 256 ring)."""
+    """x and y with row strides above their widths (128 x 128 tiles, the 256 x 256 ring, and
+    the matrix-vector form)."""
     torch = pytest.importorskip("torch")
     rng = np.random.default_rng(7)
     xfull = inputs.random_rows(rng, T, K, "bf16", ld=K + 64)
