@@ -190,7 +190,7 @@ def test_deferred_layernorm(Q, T, x_mean, stats):
                                    (300, 264, 200), (129, 2048, 2048), (8200, 1056, 4104),
                                    (8200, 1024, 4104), (4096, 64, 4096), (4100, 192, 4104),
                                    (4100, 512, 2056), (12, 512, 4104), (8, 1000, 4104),
-                                   (1, 8, 24)])
+                                   (1, 8, 24), (3, 520, 4104)])
 def test_deferred_layernorm_ragged(Q, T, K, N, stats):
     """All product kernels with the LayerNorm epilogue, ragged T and N, no beta, x with a mean
     of 2 (the mean term is exercised everywhere), statistics from the workspace pass or from
