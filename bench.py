@@ -376,6 +376,8 @@ def main():
     ap.add_argument("--only", default="",
                     help="comma-separated prefixes: time only the cases whose entry point "
                          "starts with one of them (e.g. 'normproj,qknorm_partial')")
+    ap.add_argument("--ts", default="",
+                    help="comma-separated token counts: per-workload cases at these T only")
     ap.add_argument("--case-iters", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -429,6 +431,11 @@ def main():
         def want(name):
             return not args.only or any(name.startswith(p) for p in args.only.split(","))
 
+        ts_only = {int(v) for v in args.ts.split(",") if v}
+
+        def want_t(t):
+            return not ts_only or t in ts_only
+
         # empirical copy ceiling over the same bytes (read nbytes/2, write nbytes/2)
         half = (nbytes // 2) // 16 * 16
         n_copy = rotation_count(2 * half)
@@ -443,7 +450,7 @@ def main():
 
         for cfg, Ts in ((1, (64,)), (2, (1, 16, 256, 4096, 8192)), (3, (1, 512, 8192))):
             for t in Ts:
-                if not want("qknorm_fused"):
+                if not want("qknorm_fused") or not want_t(t):
                     continue
                 fn, b = fused_setup(torch, Q, inputs, cfg, t)
                 cms, gms = time_case(timer, fn, it, wu)
@@ -474,7 +481,7 @@ def main():
 
         for t in (1, 2048, 16384):
             for unfused in (False, True):
-                if (unfused and t == 1) or not want(
+                if (unfused and t == 1) or not want_t(t) or not want(
                         "normproj_unfused" if unfused else "normproj_deferred"):
                     continue
                 fn, flops, b = normproj_setup(torch, Q, inputs, t, unfused)
@@ -496,7 +503,7 @@ def main():
                 name = {"eliminated": "qknorm_project_eliminated",
                         "exact": "qknorm_project_eliminated_exact",
                         "unfused": "unfused_prenorm_chain"}[mode]
-                if (t == 16 and mode != "eliminated") or not want(name):
+                if (t == 16 and mode != "eliminated") or not want(name) or not want_t(t):
                     continue
                 fn, flops = elimination_setup(torch, Q, inputs, t, mode)
                 cms, gms = time_case(timer, fn, it, wu)
@@ -510,7 +517,7 @@ def main():
         for t in inputs.LAYERNORM["Ts"]:
             for unfused, in_product in ((False, False), (False, True), (True, False)):
                 name = "normproj_layernorm_unfused" if unfused else "normproj_deferred_layernorm"
-                if ((unfused or in_product) and t == 1) or not want(name):
+                if ((unfused or in_product) and t == 1) or not want(name) or not want_t(t):
                     continue
                 fn, flops, b = layernorm_setup(torch, Q, inputs, t, unfused, in_product)
                 cms, gms = time_case(timer, fn, it, wu)
