@@ -551,7 +551,10 @@ QKN_API int qknorm_project_eliminated(int64_t T, int64_t K, int64_t nq, int64_t 
         (nk > 0 && overlap(ry, span(gamma_k, 1, nk, nk, gs))))
         return QKN_ERR_ALIAS;
     // p = x W' (scaled by the pre-norm's 1/rms when exact), stored in y in bf16
-    hipError_t e = qkn::launch_normproj(T, K, N, eps_pre, exact ? qkn::kEpiRms : qkn::kEpiPlain,
+    // (ordinary stores: the row kernel below reads y straight back)
+    hipError_t e = qkn::launch_normproj(T, K, N, eps_pre,
+                                        (exact ? qkn::kEpiRms : qkn::kEpiPlain) |
+                                            qkn::kEpiKeepCached,
                                         x, ldx, w_qk, ldw, y, ldy, nullptr, nullptr, nullptr,
                                         (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e);

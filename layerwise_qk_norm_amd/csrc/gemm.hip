@@ -171,7 +171,8 @@ __device__ __forceinline__ int swz(int kc, int r)
     return BK == 64 ? (kc ^ ((r >> 1) & 7)) : (kc ^ ((r >> 2) & 3));
 }
 
-template <int BM, int BN, int WM, int WN, int NST, int BK, int EPI, bool RING>
+// NTS: non-temporal output stores (the output leaves the library) or ordinary ones.
+template <int BM, int BN, int WM, int WN, int NST, int BK, int EPI, bool RING, bool NTS>
 __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
     int64_t T, int64_t K, int64_t N, float eps, float inv_k, const uint16_t* __restrict__ x,
     int64_t ldx, const uint16_t* __restrict__ w, int64_t ldw, uint16_t* __restrict__ y,
@@ -476,7 +477,11 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
     uint16_t* yp = y + (m0 + r0) * ldy + gn;
 #pragma unroll
     for (int it = 0; it < ITER; ++it) {
-        if (m0 + r0 + it * RSTEP < T && gn < N) *(u32x4*)(yp + (int64_t)it * RSTEP * ldy) = out[it];
+        if (m0 + r0 + it * RSTEP < T && gn < N) {
+            uint16_t* p = yp + (int64_t)it * RSTEP * ldy;
+            if constexpr (NTS) store_stream(p, out[it]);
+            else *(u32x4*)p = out[it];
+        }
     }
 }
 
@@ -1058,18 +1063,35 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(char* __restrict__ dst,
     for (int64_t i = done + tid; i < nbytes; i += stride) dst[i] = src[i];
 }
 
+template <int BM, int BN, int WM, int WN, int NST, int BK, int EPI, bool RING, bool NTS>
+hipError_t launch_pipe_t(int64_t T, int64_t K, int64_t N, float eps, float inv_k,
+                         const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
+                         uint16_t* y, int64_t ldy, const float* colsum, const float* bias,
+                         const float* rowstats, hipStream_t st)
+{
+    const int64_t nbm = (T + BM - 1) / BM, nbn = (N + BN - 1) / BN;
+    if (nbm * nbn > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((normproj_pipe_kernel<BM, BN, WM, WN, NST, BK, EPI, RING, NTS>),
+                       dim3((unsigned)(nbm * nbn)), dim3(WM * WN * kWave), 0, st, T, K, N, eps,
+                       inv_k, x, ldx, w, ldw, y, ldy, (int)nbm, (int)nbn, colsum, bias, rowstats);
+    return hipGetLastError();
+}
+
+// Ordinary output stores exist for the epilogues whose output the library reads back itself
+// (the pre-norm elimination: plain or RMSNorm).
 template <int BM, int BN, int WM, int WN, int NST, int BK, int EPI, bool RING>
 hipError_t launch_pipe(int64_t T, int64_t K, int64_t N, float eps, float inv_k,
                        const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
                        uint16_t* y, int64_t ldy, const float* colsum, const float* bias,
-                       const float* rowstats, hipStream_t st)
+                       const float* rowstats, bool nts, hipStream_t st)
 {
-    const int64_t nbm = (T + BM - 1) / BM, nbn = (N + BN - 1) / BN;
-    if (nbm * nbn > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((normproj_pipe_kernel<BM, BN, WM, WN, NST, BK, EPI, RING>),
-                       dim3((unsigned)(nbm * nbn)), dim3(WM * WN * kWave), 0, st, T, K, N, eps,
-                       inv_k, x, ldx, w, ldw, y, ldy, (int)nbm, (int)nbn, colsum, bias, rowstats);
-    return hipGetLastError();
+    if constexpr (EPI == kEpiPlain || EPI == kEpiRms) {
+        if (!nts)
+            return launch_pipe_t<BM, BN, WM, WN, NST, BK, EPI, RING, false>(
+                T, K, N, eps, inv_k, x, ldx, w, ldw, y, ldy, colsum, bias, rowstats, st);
+    }
+    return launch_pipe_t<BM, BN, WM, WN, NST, BK, EPI, RING, true>(
+        T, K, N, eps, inv_k, x, ldx, w, ldw, y, ldy, colsum, bias, rowstats, st);
 }
 
 struct MvJob {
@@ -1145,7 +1167,7 @@ template <int EPI>
 hipError_t launch_epi(int64_t T, int64_t K, int64_t N, float eps, const uint16_t* xp,
                       int64_t ldx, const uint16_t* wp, int64_t ldw, uint16_t* yp, int64_t ldy,
                       const float* colsum, const float* bias, const float* rowstats,
-                      hipStream_t st)
+                      bool nts, hipStream_t st)
 {
     const float inv_k = (float)(1.0 / (double)K);
     const Path path = choose_path(T, K, N, ldx, ldw, ldy, yp);
@@ -1153,19 +1175,19 @@ hipError_t launch_epi(int64_t T, int64_t K, int64_t N, float eps, const uint16_t
     case kPathBig64:
         return launch_pipe<256, 256, 4, 2, 5, 64, EPI, true>(T, K, N, eps, inv_k, xp, ldx, wp,
                                                              ldw, yp, ldy, colsum, bias,
-                                                             rowstats, st);
+                                                             rowstats, nts, st);
     case kPathBig32:
         return launch_pipe<256, 256, 4, 2, 4, 32, EPI, false>(T, K, N, eps, inv_k, xp, ldx, wp,
                                                               ldw, yp, ldy, colsum, bias,
-                                                              rowstats, st);
+                                                              rowstats, nts, st);
     case kPathMid:
         return launch_pipe<128, 128, 4, 2, 2, 64, EPI, false>(T, K, N, eps, inv_k, xp, ldx, wp,
                                                               ldw, yp, ldy, colsum, bias,
-                                                              rowstats, st);
+                                                              rowstats, nts, st);
     case kPathMidDeep:
         return launch_pipe<128, 128, 4, 2, 4, 64, EPI, false>(T, K, N, eps, inv_k, xp, ldx, wp,
                                                               ldw, yp, ldy, colsum, bias,
-                                                              rowstats, st);
+                                                              rowstats, nts, st);
     default:
         break;
     }
@@ -1199,22 +1221,25 @@ hipError_t launch_normproj(int64_t T, int64_t K, int64_t N, float eps, int epi,
                            const float* rowstats, hipStream_t st)
 {
     if (T == 0 || N == 0) return hipSuccess;
+    // outputs leave the library: non-temporal stores, unless the caller reads them back next
+    const bool nts = (epi & kEpiKeepCached) == 0;
+    epi &= ~kEpiKeepCached;
     const uint16_t* xp = (const uint16_t*)x;
     const uint16_t* wp = (const uint16_t*)w;
     uint16_t* yp = (uint16_t*)y;
     switch (epi) {
     case kEpiPlain:
         return launch_epi<kEpiPlain>(T, K, N, eps, xp, ldx, wp, ldw, yp, ldy, colsum, bias,
-                                     rowstats, st);
+                                     rowstats, nts, st);
     case kEpiRms:
         return launch_epi<kEpiRms>(T, K, N, eps, xp, ldx, wp, ldw, yp, ldy, colsum, bias,
-                                   rowstats, st);
+                                   rowstats, nts, st);
     case kEpiLayerNorm:
         return launch_epi<kEpiLayerNorm>(T, K, N, eps, xp, ldx, wp, ldw, yp, ldy, colsum, bias,
-                                         rowstats, st);
+                                         rowstats, nts, st);
     case kEpiLayerNormStats:
         return launch_epi<kEpiLayerNormStats>(T, K, N, eps, xp, ldx, wp, ldw, yp, ldy, colsum,
-                                              bias, rowstats, st);
+                                              bias, rowstats, nts, st);
     default:
         return hipErrorInvalidValue;
     }

@@ -54,6 +54,9 @@ enum Epi : int {
     kEpiLayerNorm = 2,  // y = bf16(r * (acc - mean(x row) * colsum[n]) + bias[n]), r = 1/std
     kEpiLayerNormStats = 3,  // the same with (mean, r) of each row read from rowstats [T, 2]
 };
+// Flag or-ed into the epilogue: the caller reads y again right away, so the tiled kernels
+// store it with ordinary stores (it stays in the caches) instead of non-temporal ones.
+constexpr int kEpiKeepCached = 16;
 // rowstats is read by kEpiLayerNormStats only, which runs on the pipelined kernels alone
 // (normproj_pipelined() must hold).
 hipError_t launch_normproj(int64_t T, int64_t K, int64_t N, float eps, int epi,
