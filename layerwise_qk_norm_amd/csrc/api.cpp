@@ -435,6 +435,7 @@ QKN_API int normproj_unfused(int64_t T, int64_t K, int64_t N, float eps, int dty
     job.mode = qkn::kFused;
     job.bf16 = 1;
     job.gamma_bf16 = gamma_dtype == QKN_BF16;
+    job.keep_cached = 1;  // the product reads xn straight back
     job.seg[0] = {x, xn, gamma, ldx, ldxn, K, (float)(1.0 / (double)K), nullptr, nullptr, 0, 0,
                   nullptr};
     hipError_t e = qkn::launch_rows(job, (hipStream_t)stream);

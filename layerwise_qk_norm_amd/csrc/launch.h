@@ -36,6 +36,9 @@ struct RowJob {
     int mode;            // RowMode
     int bf16;            // storage of x / y: 1 = bf16, 0 = fp32
     int gamma_bf16;      // storage of gamma: 1 = bf16, 0 = fp32
+    int keep_cached;     // 1: the caller reads y back next, so a one-tensor fused job stores
+                         // it with ordinary stores (kept in the caches) instead of
+                         // non-temporal ones
 };
 
 // Chooses the register-resident kernel (one wavefront per row group, 16-byte accesses) when

@@ -123,8 +123,8 @@ struct Gamma {
     }
 };
 
-// The rows of block `blk` of one tensor under team shape SH.
-template <int MODE, bool BF, bool GBF, int SH>
+// The rows of block `blk` of one tensor under team shape SH; NTS: non-temporal output stores.
+template <int MODE, bool BF, bool GBF, int SH, bool NTS>
 __device__ __forceinline__ void run_team(const RowSeg& s, int64_t T, float eps, int64_t blk,
                                          float* red)
 {
@@ -267,7 +267,8 @@ __device__ __forceinline__ void run_team(const RowSeg& s, int64_t T, float eps, 
                         unpack<BF>(v[r][j], f);
 #pragma unroll
                         for (int e = 0; e < EPV; ++e) o[e] = (f[e] * G::at(graw[j], e)) * rs[r];
-                        store_stream(yr + col * ES, pack<BF>(o));
+                        if constexpr (NTS) store_stream(yr + col * ES, pack<BF>(o));
+                        else *(u32x4*)(yr + col * ES) = pack<BF>(o);
                     }
                 }
             }
@@ -276,13 +277,13 @@ __device__ __forceinline__ void run_team(const RowSeg& s, int64_t T, float eps, 
 }
 
 // Blocks [0, nblk0) serve seg[0] with shape SH0, the rest seg[1] with shape SH1.
-template <int MODE, bool BF, bool GBF, int SH0, int SH1>
+template <int MODE, bool BF, bool GBF, int SH0, int SH1, bool NTS = true>
 __global__ __launch_bounds__(kBlock) void rows_team_kernel(RowJob job, int nblk0)
 {
     __shared__ float red[32];
     const int b = (int)blockIdx.x;
-    if (b < nblk0) run_team<MODE, BF, GBF, SH0>(job.seg[0], job.T, job.eps, b, red);
-    else run_team<MODE, BF, GBF, SH1>(job.seg[1], job.T, job.eps, b - nblk0, red);
+    if (b < nblk0) run_team<MODE, BF, GBF, SH0, NTS>(job.seg[0], job.T, job.eps, b, red);
+    else run_team<MODE, BF, GBF, SH1, NTS>(job.seg[1], job.T, job.eps, b - nblk0, red);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -375,7 +376,7 @@ __global__ __launch_bounds__(kBlock) void rows_generic_kernel(RowJob job)
 
 typedef hipError_t (*RowLaunch)(const RowJob&, hipStream_t);
 
-template <int MODE, bool BF, bool GBF, int SH0, int SH1>
+template <int MODE, bool BF, bool GBF, int SH0, int SH1, bool NTS = true>
 hipError_t launch_team(const RowJob& job, hipStream_t st)
 {
     const int64_t per0 = shape_rows_per_block(MODE, SH0);
@@ -383,7 +384,7 @@ hipError_t launch_team(const RowJob& job, hipStream_t st)
     const int64_t nblk0 = (job.T + per0 - 1) / per0;
     const int64_t nblk1 = job.nseg > 1 ? (job.T + per1 - 1) / per1 : 0;
     if (nblk0 + nblk1 > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((rows_team_kernel<MODE, BF, GBF, SH0, SH1>),
+    hipLaunchKernelGGL((rows_team_kernel<MODE, BF, GBF, SH0, SH1, NTS>),
                        dim3((unsigned)(nblk0 + nblk1)), dim3(kBlock), 0, st, job, (int)nblk0);
     return hipGetLastError();
 }
@@ -410,6 +411,15 @@ RowLaunch pick_team(int i, int j, std::integer_sequence<int, I...>)
     } else {
         ((i == I ? (r = launch_team<MODE, BF, GBF, I, I>, 0) : 0), ...);
     }
+    return r;
+}
+
+// One-tensor fused jobs whose output the caller reads back: ordinary stores.
+template <bool BF, bool GBF, int... I>
+RowLaunch pick_cached(int i, std::integer_sequence<int, I...>)
+{
+    RowLaunch r = nullptr;
+    ((i == I ? (r = launch_team<kFused, BF, GBF, I, I, false>, 0) : 0), ...);
     return r;
 }
 
@@ -463,6 +473,12 @@ hipError_t dispatch_mode(const RowJob& job_in, hipStream_t st)
         cls[1] = c;
     }
     const int i = cls[0], j = MODE == kFused ? cls[1] : cls[0];
+    if constexpr (MODE == kFused) {
+        if (job.nseg == 1 && job.keep_cached) {
+            RowLaunch f = pick_cached<BF, GBF>(i, std::make_integer_sequence<int, kShapeCount>{});
+            return f ? f(job, st) : hipErrorInvalidValue;
+        }
+    }
     RowLaunch f = pick_team<MODE, BF, GBF>(i, j, std::make_integer_sequence<int, kShapeCount>{});
     return f ? f(job, st) : hipErrorInvalidValue;
 }
