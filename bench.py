@@ -232,7 +232,8 @@ def normproj_setup(torch, Q, inputs, T, unfused=False):
 def elimination_setup(torch, Q, inputs, T, mode):
     """Pre-norm -> Q/K projection -> QK-Norm at OLMo-2-7B widths (x [T, 4096], Wq, Wk
     [4096, 4096]). mode: 'eliminated' (no pre-norm), 'exact' (pre-norm scale deferred to the
-    product) or 'unfused' (RMSNorm launch, plain product, fused QK-Norm launch in place)."""
+    product) or 'unfused' (qknorm_project_unfused: RMSNorm launch, plain product, QK-Norm
+    launch in place, the intermediates kept in the caches as in the eliminated form)."""
     c = inputs.make_elimination_case(T)
     x, w = dev(torch, c["x"]), dev(torch, c["w"])
     g1, gq, gk = dev(torch, c["gamma_pre"]), dev(torch, c["gamma_q"]), dev(torch, c["gamma_k"])
@@ -248,9 +249,8 @@ def elimination_setup(torch, Q, inputs, T, mode):
     def fn(i):
         xi, yi, xn, wi = sets[i % n]
         if mode == "unfused":
-            Q.normproj_unfused(xi, g1, wi, eps=c["eps_pre"], xn=xn, y=yi)
-            Q.qknorm_fused(yi[:, :nq], gq, yi[:, nq:], gk, eps=c["eps_qk"], q_out=yi[:, :nq],
-                           k_out=yi[:, nq:])
+            Q.qknorm_project_unfused(xi, g1, wi, nq, gq, gk, eps_qk=c["eps_qk"],
+                                     eps_pre=c["eps_pre"], xn=xn, y=yi)
         else:
             Q.qknorm_project_eliminated(xi, wi, nq, gq, gk, eps_qk=c["eps_qk"],
                                         eps_pre=c["eps_pre"], exact=(mode == "exact"), y=yi)

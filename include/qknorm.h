@@ -304,6 +304,32 @@ QKN_API int qknorm_project_eliminated(int64_t T, int64_t K, int64_t nq, int64_t 
                                       int64_t ldy, void* stream);
 
 /*
+ * qknorm_project_unfused - the chain qknorm_project_eliminated simplifies, in one call
+ * (measured baseline): pre-attention RMSNorm launch, plain product, layerwise QK-Norm launch.
+ *
+ * ("FlashNorm: ...", abstract: the RMSNorm ahead of a linear layer whose output is normalised
+ * again; this is that chain computed as written.)
+ *   xn[t,k]     = bf16( x[t,k] gamma_pre[k] / sqrt(mean(x_t^2) + eps_pre) )   (caller's xn)
+ *   p[t,:]      = bf16( xn[t,:] w_packed^T )                                   (kept in y)
+ *   y[t, 0:nq]  = p[t,0:nq] gamma_q / sqrt(mean(p[t,0:nq]^2) + eps_qk)
+ *   y[t, nq:]   = p[t,nq:] gamma_k / sqrt(mean(p[t,nq:]^2) + eps_qk)
+ * w_packed [nq + nk, K] bf16 is the unfolded stacked weight re-laid out by
+ * normproj_fold_weight with gamma == NULL. The intermediates xn and p are written with
+ * ordinary stores, because the next launch reads them straight back (as p is in
+ * qknorm_project_eliminated), so the two entry points differ by the pre-norm alone.
+ *   x [T, K] bf16 (ldx); xn [T, K] bf16 scratch (ldxn, 16-byte aligned, caller-owned, must not
+ *   overlap any other argument); y [T, nq + nk] bf16 (ldy)
+ *   gamma_pre [K], gamma_q [nq], gamma_k [nk] in gamma_dtype; nk == 0 normalises Q only
+ * Three launches. Alignment rules of normproj_unfused; y must not overlap x, w_packed or the
+ * gammas. Every argument is checked before the first launch.
+ */
+QKN_API int qknorm_project_unfused(int64_t T, int64_t K, int64_t nq, int64_t nk, float eps_qk,
+                                   float eps_pre, int gamma_dtype, const void* x, int64_t ldx,
+                                   const void* gamma_pre, const void* w_packed, int64_t ldw,
+                                   const void* gamma_q, const void* gamma_k, void* xn,
+                                   int64_t ldxn, void* y, int64_t ldy, void* stream);
+
+/*
  * qkn_device_copy - plain streaming copy of nbytes (16-byte vectors where aligned).
  * Used to calibrate measured bandwidth and memory counters against a kernel of known traffic.
  * dst and src must not overlap.

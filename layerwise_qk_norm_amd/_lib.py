@@ -50,6 +50,8 @@ _PROTOS = {
                                    _i64, _vp, _i64, _vp, _i64, _vp],
     "qknorm_project_eliminated": [_i64, _i64, _i64, _i64, _f32, _f32, _int, _int, _vp, _i64, _vp,
                                   _i64, _vp, _vp, _vp, _i64, _vp],
+    "qknorm_project_unfused": [_i64, _i64, _i64, _i64, _f32, _f32, _int, _vp, _i64, _vp, _vp,
+                               _i64, _vp, _vp, _vp, _i64, _vp, _i64, _vp],
     "qkn_device_copy": [_vp, _vp, _i64, _vp],
     "qknorm_shard_fused": [_i64, _f32, _int, _int, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64,
                            _vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _vp, _i64,
@@ -393,6 +395,26 @@ def qknorm_project_eliminated(x, w_qk, nq: int, gamma_q, gamma_k=None, eps_qk: f
         _ptr(x), _ld(x), _ptr(w_qk), _ld(w_qk), _ptr(gamma_q), _ptr(gamma_k), _ptr(y), _ld(y),
         _stream(x)))
     return y
+
+
+def qknorm_project_unfused(x, gamma_pre, w_packed, nq: int, gamma_q, gamma_k=None,
+                           eps_qk: float = 1e-6, eps_pre: float = 1e-6, xn=None, y=None):
+    """The unsimplified chain: RMSNorm launch into xn, plain product with the packed unfolded
+    stacked weight into y, layerwise QK-Norm of y's Q and K blocks in place. Returns (xn, y)."""
+    torch = _torch()
+    _check_device(x, gamma_pre, w_packed, gamma_q, gamma_k)
+    T, K = x.shape
+    N = w_packed.shape[0]
+    nk = N - nq
+    if xn is None:
+        xn = torch.empty((T, K), dtype=torch.bfloat16, device=x.device)
+    if y is None:
+        y = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    _check("qknorm_project_unfused", lib().qknorm_project_unfused(
+        T, K, nq, nk, float(eps_qk), float(eps_pre), _dtype_code(gamma_q), _ptr(x), _ld(x),
+        _ptr(gamma_pre), _ptr(w_packed), _ld(w_packed), _ptr(gamma_q), _ptr(gamma_k), _ptr(xn),
+        _ld(xn), _ptr(y), _ld(y), _stream(x)))
+    return xn, y
 
 
 def qkn_device_copy(dst, src, nbytes: int | None = None):

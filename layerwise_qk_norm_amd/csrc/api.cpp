@@ -410,10 +410,14 @@ QKN_API int normproj_deferred(int64_t T, int64_t K, int64_t N, float eps, int dt
                                            ldy, nullptr, nullptr, nullptr, (hipStream_t)stream));
 }
 
-QKN_API int normproj_unfused(int64_t T, int64_t K, int64_t N, float eps, int dtype,
-                             int gamma_dtype, const void* x, int64_t ldx, const void* gamma,
-                             const void* w_packed, int64_t ldw, void* xn, int64_t ldxn, void* y,
-                             int64_t ldy, void* stream)
+namespace {
+
+// RMSNorm launch into xn (ordinary stores: the product reads xn straight back), then the plain
+// product; keep_y: the caller reads y back next as well.
+int unfused_rms_product(int64_t T, int64_t K, int64_t N, float eps, int dtype, int gamma_dtype,
+                        const void* x, int64_t ldx, const void* gamma, const void* w_packed,
+                        int64_t ldw, void* xn, int64_t ldxn, void* y, int64_t ldy, bool keep_y,
+                        void* stream)
 {
     int st = check_normproj(T, K, N, eps, dtype, x, ldx, w_packed, ldw, y, ldy);
     if (st != QKN_OK) return st;
@@ -435,13 +439,26 @@ QKN_API int normproj_unfused(int64_t T, int64_t K, int64_t N, float eps, int dty
     job.mode = qkn::kFused;
     job.bf16 = 1;
     job.gamma_bf16 = gamma_dtype == QKN_BF16;
-    job.keep_cached = 1;  // the product reads xn straight back
+    job.keep_cached = 1;
     job.seg[0] = {x, xn, gamma, ldx, ldxn, K, (float)(1.0 / (double)K), nullptr, nullptr, 0, 0,
                   nullptr};
     hipError_t e = qkn::launch_rows(job, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e);
-    return hip_status(qkn::launch_normproj(T, K, N, eps, qkn::kEpiPlain, xn, ldxn, w_packed, ldw,
-                                           y, ldy, nullptr, nullptr, nullptr, (hipStream_t)stream));
+    return hip_status(qkn::launch_normproj(T, K, N, eps,
+                                           qkn::kEpiPlain | (keep_y ? qkn::kEpiKeepCached : 0),
+                                           xn, ldxn, w_packed, ldw, y, ldy, nullptr, nullptr,
+                                           nullptr, (hipStream_t)stream));
+}
+
+}  // namespace
+
+QKN_API int normproj_unfused(int64_t T, int64_t K, int64_t N, float eps, int dtype,
+                             int gamma_dtype, const void* x, int64_t ldx, const void* gamma,
+                             const void* w_packed, int64_t ldw, void* xn, int64_t ldxn, void* y,
+                             int64_t ldy, void* stream)
+{
+    return unfused_rms_product(T, K, N, eps, dtype, gamma_dtype, x, ldx, gamma, w_packed, ldw,
+                               xn, ldxn, y, ldy, false, stream);
 }
 
 QKN_API int normproj_fold_layernorm(int64_t K, int64_t N, int dtype, int gamma_dtype,
@@ -531,35 +548,28 @@ QKN_API int normproj_layernorm_unfused(int64_t T, int64_t K, int64_t N, float ep
                                            y, ldy, nullptr, nullptr, nullptr, (hipStream_t)stream));
 }
 
-QKN_API int qknorm_project_eliminated(int64_t T, int64_t K, int64_t nq, int64_t nk,
-                                      float eps_qk, float eps_pre, int exact, int gamma_dtype,
-                                      const void* x, int64_t ldx, const void* w_qk, int64_t ldw,
-                                      const void* gamma_q, const void* gamma_k, void* y,
-                                      int64_t ldy, void* stream)
+namespace {
+
+// Arguments of the layerwise QK-Norm that follows the projection (checked before any launch).
+int check_qk_gammas(int64_t T, int64_t nq, int64_t nk, int gamma_dtype, const void* gamma_q,
+                    const void* gamma_k, const void* y, int64_t ldy)
 {
-    if (nq < 1 || nk < 0) return QKN_ERR_SHAPE;
-    if (!valid_eps(eps_pre)) return QKN_ERR_EPS;
-    if (exact != 0 && exact != 1) return QKN_ERR_SHAPE;
-    const int64_t N = nq + nk;
-    int st = check_normproj(T, K, N, eps_qk, QKN_BF16, x, ldx, w_qk, ldw, y, ldy);
-    if (st != QKN_OK) return st;
     if (!valid_dtype(gamma_dtype)) return QKN_ERR_DTYPE;
     if (T == 0) return QKN_OK;
     if (gamma_q == nullptr || (nk > 0 && gamma_k == nullptr)) return QKN_ERR_NULL;
     const int64_t gs = elem_size(gamma_dtype);
-    const Range ry = span(y, T, N, ldy, 2);
+    const Range ry = span(y, T, nq + nk, ldy, 2);
     if (overlap(ry, span(gamma_q, 1, nq, nq, gs)) ||
         (nk > 0 && overlap(ry, span(gamma_k, 1, nk, nk, gs))))
         return QKN_ERR_ALIAS;
-    // p = x W' (scaled by the pre-norm's 1/rms when exact), stored in y in bf16
-    // (ordinary stores: the row kernel below reads y straight back)
-    hipError_t e = qkn::launch_normproj(T, K, N, eps_pre,
-                                        (exact ? qkn::kEpiRms : qkn::kEpiPlain) |
-                                            qkn::kEpiKeepCached,
-                                        x, ldx, w_qk, ldw, y, ldy, nullptr, nullptr, nullptr,
-                                        (hipStream_t)stream);
-    if (e != hipSuccess) return hip_status(e);
-    // layerwise QK-Norm of the two column blocks of y, in place
+    return QKN_OK;
+}
+
+// Layerwise QK-Norm of the two column blocks of y [T, nq + nk], in place.
+hipError_t qk_norm_in_place(int64_t T, int64_t nq, int64_t nk, float eps_qk, int gamma_dtype,
+                            const void* gamma_q, const void* gamma_k, void* y, int64_t ldy,
+                            void* stream)
+{
     qkn::RowJob job = {};
     job.nseg = nk > 0 ? 2 : 1;
     job.T = T;
@@ -573,7 +583,65 @@ QKN_API int qknorm_project_eliminated(int64_t T, int64_t K, int64_t nq, int64_t 
     if (nk > 0)
         job.seg[1] = {yq + nq, yq + nq, gamma_k, ldy, ldy, nk, (float)(1.0 / (double)nk), nullptr,
                       nullptr, 0, 0, nullptr};
-    return hip_status(qkn::launch_rows(job, (hipStream_t)stream));
+    return qkn::launch_rows(job, (hipStream_t)stream);
+}
+
+}  // namespace
+
+QKN_API int qknorm_project_eliminated(int64_t T, int64_t K, int64_t nq, int64_t nk,
+                                      float eps_qk, float eps_pre, int exact, int gamma_dtype,
+                                      const void* x, int64_t ldx, const void* w_qk, int64_t ldw,
+                                      const void* gamma_q, const void* gamma_k, void* y,
+                                      int64_t ldy, void* stream)
+{
+    if (nq < 1 || nk < 0) return QKN_ERR_SHAPE;
+    if (!valid_eps(eps_pre)) return QKN_ERR_EPS;
+    if (exact != 0 && exact != 1) return QKN_ERR_SHAPE;
+    const int64_t N = nq + nk;
+    int st = check_normproj(T, K, N, eps_qk, QKN_BF16, x, ldx, w_qk, ldw, y, ldy);
+    if (st != QKN_OK) return st;
+    st = check_qk_gammas(T, nq, nk, gamma_dtype, gamma_q, gamma_k, y, ldy);
+    if (st != QKN_OK || T == 0) return st;
+    // p = x W' (scaled by the pre-norm's 1/rms when exact), stored in y in bf16
+    // (ordinary stores: the row kernel below reads y straight back)
+    hipError_t e = qkn::launch_normproj(T, K, N, eps_pre,
+                                        (exact ? qkn::kEpiRms : qkn::kEpiPlain) |
+                                            qkn::kEpiKeepCached,
+                                        x, ldx, w_qk, ldw, y, ldy, nullptr, nullptr, nullptr,
+                                        (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(qk_norm_in_place(T, nq, nk, eps_qk, gamma_dtype, gamma_q, gamma_k, y, ldy,
+                                       stream));
+}
+
+QKN_API int qknorm_project_unfused(int64_t T, int64_t K, int64_t nq, int64_t nk, float eps_qk,
+                                   float eps_pre, int gamma_dtype, const void* x, int64_t ldx,
+                                   const void* gamma_pre, const void* w_packed, int64_t ldw,
+                                   const void* gamma_q, const void* gamma_k, void* xn,
+                                   int64_t ldxn, void* y, int64_t ldy, void* stream)
+{
+    if (nq < 1 || nk < 0) return QKN_ERR_SHAPE;
+    if (!valid_eps(eps_qk)) return QKN_ERR_EPS;
+    const int64_t N = nq + nk;
+    // shapes, pointers and aliasing of the norm and the product are checked by
+    // unfused_rms_product before its first launch; the QK-Norm's arguments here
+    int st = check_normproj(T, K, N, eps_pre, QKN_BF16, x, ldx, w_packed, ldw, y, ldy);
+    if (st != QKN_OK) return st;
+    st = check_qk_gammas(T, nq, nk, gamma_dtype, gamma_q, gamma_k, y, ldy);
+    if (st != QKN_OK) return st;
+    if (T > 0 && xn != nullptr && ldxn >= K) {
+        const Range rxn = span(xn, T, K, ldxn, 2);
+        const int64_t gs = elem_size(gamma_dtype);
+        if (overlap(rxn, span(gamma_q, 1, nq, nq, gs)) ||
+            (nk > 0 && overlap(rxn, span(gamma_k, 1, nk, nk, gs))))
+            return QKN_ERR_ALIAS;
+    }
+    // the pre-norm and the plain product, p kept in the caches for the QK-Norm launch
+    st = unfused_rms_product(T, K, N, eps_pre, QKN_BF16, gamma_dtype, x, ldx, gamma_pre,
+                             w_packed, ldw, xn, ldxn, y, ldy, true, stream);
+    if (st != QKN_OK || T == 0) return st;
+    return hip_status(qk_norm_in_place(T, nq, nk, eps_qk, gamma_dtype, gamma_q, gamma_k, y, ldy,
+                                       stream));
 }
 
 QKN_API int qkn_device_copy(void* dst, const void* src, int64_t nbytes, void* stream)

@@ -41,7 +41,8 @@ def test_exports_every_declared_symbol(L):
                           "qkn_device_copy", "qkn_status_string", "qkn_last_hip_error",
                           "qknorm_shard_fused", "qknorm_shard_publish",
                           "normproj_fold_layernorm", "normproj_deferred_layernorm",
-                          "normproj_layernorm_unfused", "qknorm_project_eliminated"}
+                          "normproj_layernorm_unfused", "qknorm_project_eliminated",
+                          "qknorm_project_unfused"}
     for n in names:
         assert hasattr(L, n), n
     nm = shutil.which("nm")
@@ -210,6 +211,33 @@ def test_project_eliminated_validation(L):
     assert E(y=A) == ALIAS                     # output over x
     assert E(y=G1 - 32) == ALIAS               # output running into gamma_q
     assert E(T=0, x=None, w=None, gq=None, gk=None, y=None) == OK
+
+
+@no_gpu
+def test_project_unfused_validation(L):
+    def U(T=4, K=16, nq=8, nk=8, e2=1e-6, e1=1e-6, gdt=BF16, x=A, ldx=16, g1=G1, w=B, ldw=16,
+          gq=G2, gk=G2 + 64, xn=D, ldxn=16, y=C, ldy=16):
+        return L.qknorm_project_unfused(T, K, nq, nk, e2, e1, gdt, x, ldx, g1, w, ldw, gq, gk,
+                                        xn, ldxn, y, ldy, None)
+
+    assert U(nq=0) == SHAPE
+    assert U(nk=-1) == SHAPE
+    assert U(ldy=15) == SHAPE                  # ldy < nq + nk
+    assert U(ldxn=8) == SHAPE                  # ldxn < K
+    assert U(e2=float("nan")) == EPS
+    assert U(e1=-1.0) == EPS
+    assert U(gdt=3) == DTYPE
+    assert U(K=12, ldx=12, ldw=12, ldxn=12) == ALIGN
+    assert U(xn=D + 2) == ALIGN
+    assert U(gq=None) == NULL
+    assert U(gk=None) == NULL
+    assert U(g1=None) == NULL
+    assert U(xn=None) == NULL
+    assert U(y=A) == ALIAS                     # output over x
+    assert U(y=G2 - 32) == ALIAS               # output running into gamma_q
+    assert U(xn=A) == ALIAS                    # scratch over x
+    assert U(xn=G2 - 32) == ALIAS              # scratch running into gamma_q
+    assert U(T=0, x=None, w=None, g1=None, gq=None, gk=None, xn=None, y=None) == OK
 
 
 @no_gpu

@@ -118,6 +118,37 @@ def test_elimination_full_width(Q, T, exact):
     run_elimination(Q, c, exact, rows, f"T={T} exact={exact}", chain_rows=chain)
 
 
+@pytest.mark.parametrize("T,K,nq,nk", [(300, 512, 384, 136), (16, 256, 256, 64),
+                                       (37, 264, 200, 8), (129, 1024, 1024, 1024),
+                                       (2048, 4096, 4096, 4096)])
+def test_project_unfused_chain(Q, T, K, nq, nk):
+    """The unsimplified chain in one call (RMSNorm launch, plain product with the packed
+    unfolded weight, QK-Norm in place): xn against the oracle's RMSNorm, y against the oracle
+    chain. The GPU rounds xn and p to bf16 on the way: the relative term covers p, and xn's
+    rounding (2^-9 relative per element) enters the product's accumulation bound, hence the
+    2^-8 absolute coefficient (as for the fold's rounding above)."""
+    c = inputs.make_elimination_case(T, seed=T + K + nq + nk, K=K, nq=nq, nk=nk)
+    wp = Q.normproj_fold_weight(to_dev(c["w"]), None)
+    xn, y = Q.qknorm_project_unfused(to_dev(c["x"]), to_dev(c["gamma_pre"]), wp, nq,
+                                     to_dev(c["gamma_q"]), to_dev(c["gamma_k"]),
+                                     eps_qk=c["eps_qk"], eps_pre=c["eps_pre"])
+    sync()
+    rows = sample_rows(T, 64, seed=T)
+    xs = np.ascontiguousarray(c["x"][rows])
+    check_rows(to_host(xn)[rows], oracle.rmsnorm_rows(xs, c["gamma_pre"], c["eps_pre"]),
+               f"unfused chain xn T={T}")
+    cq, ck = oracle.qk_chain(xs, c["gamma_pre"], c["wq"], c["wk"], c["gamma_q"], c["gamma_k"],
+                             c["eps_pre"], c["eps_qk"])
+    wf_ref = folded(c["w"], c["gamma_pre"])
+    got = to_host(y)[rows]
+    args = (c["eps_qk"], c["eps_pre"], True)
+    what = f"unfused chain T={T} K={K} nq={nq} nk={nk}"
+    check_projection(got[:, :nq], cq, elim_bound(xs, wf_ref[:, :nq], c["gamma_q"], *args),
+                     what + " Q", abs_coeff=2.0 ** -8)
+    check_projection(got[:, nq:], ck, elim_bound(xs, wf_ref[:, nq:], c["gamma_k"], *args),
+                     what + " K", abs_coeff=2.0 ** -8)
+
+
 def test_elimination_eps_regime(Q):
     """Small activations (mean(x^2) ~ 1e-6 ~ eps): the plain form follows its own definition
     and visibly departs from the chain, the exact form still equals the chain."""
