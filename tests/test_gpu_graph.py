@@ -24,11 +24,13 @@ def test_graph_replays_match_eager():
     eq, ek = to_dev(c4["ext_q"]), to_dev(c4["ext_k"])
     x = to_dev(c5["x"])
     wf = Q.normproj_fold_weight(to_dev(c5["w"]), to_dev(c5["gamma"]))
-    # pre-norm elimination (matrix-core and matrix-vector paths), deferred LayerNorm
+    # pre-norm elimination (matrix-core and matrix-vector paths) and its unfused chain,
+    # deferred LayerNorm
     el = {T: inputs.make_elimination_case(T, seed=8, K=512, nq=384, nk=128) for T in (200, 12)}
     el_x = {T: to_dev(c["x"]) for T, c in el.items()}
     el_w = Q.normproj_fold_weight(to_dev(el[200]["w"]), to_dev(el[200]["gamma_pre"]))
     el_gq, el_gk = to_dev(el[200]["gamma_q"]), to_dev(el[200]["gamma_k"])
+    el_g1, el_wp = to_dev(el[200]["gamma_pre"]), Q.normproj_fold_weight(to_dev(el[200]["w"]), None)
     ln = {T: inputs.make_layernorm_case(T, seed=8, K=512, N=256, x_mean=1.0) for T in (300, 5)}
     ln_x = {T: to_dev(c["x"]) for T, c in ln.items()}
     ln_w, ln_c, ln_b = Q.normproj_fold_layernorm(to_dev(ln[300]["w"]), to_dev(ln[300]["gamma"]),
@@ -49,6 +51,8 @@ def test_graph_replays_match_eager():
                     e200=torch.empty((200, 512), dtype=torch.bfloat16, device="cuda"),
                     x200=torch.empty((200, 512), dtype=torch.bfloat16, device="cuda"),
                     e12=torch.empty((12, 512), dtype=torch.bfloat16, device="cuda"),
+                    u200=torch.empty((200, 512), dtype=torch.bfloat16, device="cuda"),
+                    un200=torch.empty((200, 512), dtype=torch.bfloat16, device="cuda"),
                     l300=torch.empty((300, 256), dtype=torch.bfloat16, device="cuda"),
                     l5=torch.empty((5, 256), dtype=torch.bfloat16, device="cuda"))
 
@@ -64,6 +68,8 @@ def test_graph_replays_match_eager():
         Q.qknorm_project_eliminated(el_x[200], el_w, 384, el_gq, el_gk, exact=False, y=o["e200"])
         Q.qknorm_project_eliminated(el_x[200], el_w, 384, el_gq, el_gk, exact=True, y=o["x200"])
         Q.qknorm_project_eliminated(el_x[12], el_w, 384, el_gq, el_gk, exact=True, y=o["e12"])
+        Q.qknorm_project_unfused(el_x[200], el_g1, el_wp, 384, el_gq, el_gk, xn=o["un200"],
+                                 y=o["u200"])
         Q.normproj_deferred_layernorm(ln_x[300], ln_w, ln_c, ln_b, eps=1e-5, y=o["l300"])
         Q.normproj_deferred_layernorm(ln_x[5], ln_w, ln_c, ln_b, eps=1e-5, y=o["l5"])
 

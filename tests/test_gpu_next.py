@@ -98,11 +98,14 @@ def run_elimination(Q, c, exact, rows, what, chain_rows=None):
 @pytest.mark.parametrize("exact", [False, True])
 @pytest.mark.parametrize("T,K,nq,nk", [(300, 512, 384, 136), (300, 512, 384, 130),
                                        (16, 256, 256, 64), (37, 264, 200, 0),
-                                       (129, 1024, 1024, 1024), (1, 520, 256, 264)])
+                                       (129, 1024, 1024, 1024), (1, 520, 256, 264),
+                                       (4096, 96, 4096, 4096), (2100, 256, 2048, 8)])
 def test_elimination_shapes(Q, T, K, nq, nk, exact):
     """Every product kernel (matrix-vector T <= 16, generic tiles for K % 32 != 0 or N % 8 != 0,
-    pipelined tiles) followed by the row kernel on the two column blocks in place (16-byte team
-    kernel, or the generic one when the K block is misaligned), Q only included."""
+    pipelined tiles: 128 x 128 with 4 and with 2 stages, 256 x 256 with k-tiles of 64 and of 32,
+    all with the ordinary output stores this entry point uses) followed by the row kernel on
+    the two column blocks in place (16-byte team kernel, or the generic one when the K block is
+    misaligned), Q only included."""
     c = inputs.make_elimination_case(T, seed=T + K + nq + nk, K=K, nq=nq, nk=nk)
     run_elimination(Q, c, exact, np.arange(T), f"T={T} K={K} nq={nq} nk={nk} exact={exact}")
 
