@@ -189,7 +189,8 @@ def test_normproj_unfused_baseline(Q):
                                    (4100, 192, 4104), (4096, 96, 4096),
                                    (4100, 512, 2056), (12, 512, 4104), (8, 1000, 4104),
                                    (1, 8, 24), (3, 64, 40), (16, 4096, 8200), (3, 520, 4104),
-                                   (12, 264, 3000), (2, 2048, 2056)])
+                                   (12, 264, 3000), (2, 2048, 2056), (2, 16, 1),
+                                   (4, 16392, 520), (16, 8200, 4200)])
 def test_normproj_ragged(Q, T, K, N):
     """Every kernel of the projection: the matrix-vector path (T <= 16), the generic tile
     kernel (K not a multiple of 32), and the pipelined tilings (128 x 128 with 4 stages when
