@@ -819,7 +819,9 @@ __global__ __launch_bounds__(WAVES * 64) void normproj_mvl_kernel(
 
     const int64_t nsteps = (K + 63) / 64;
     const int nmine = wave < nsteps ? (int)((nsteps - 1 - wave) / WAVES) + 1 : 0;
-    const int64_t rot = ((int64_t)blockIdx.x * kMvRotate) % nsteps;
+    // (32-bit: nsteps < 2^20 for the strides this kernel accepts)
+    const uint32_t ns32 = (uint32_t)nsteps;
+    const int64_t rot = ns32 ? (int64_t)(((blockIdx.x % ns32) * kMvRotate) % ns32) : 0;
     auto step = [&](int i) {
         const int64_t st = wave + (int64_t)i * WAVES + rot;
         return st >= nsteps ? st - nsteps : st;
