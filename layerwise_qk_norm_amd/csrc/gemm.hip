@@ -32,14 +32,16 @@
 // turns over the k steps to accumulate the row statistics (sums of squares through
 // v_dot2c_f32_bf16 for RMSNorm), and their partials are added through LDS in a fixed order.
 // The epilogue applies the row scale, rounds to bf16, writes the tile to LDS 8 bytes at a time
-// and stores it so each lane writes 16 contiguous bytes. Blocks are remapped so that each XCD
-// works on a contiguous range of row panels (one L2 holds each x panel).
+// and stores it so each lane writes 16 contiguous bytes, non-temporally unless the caller reads
+// the output straight back. Blocks are remapped so that each XCD works on a contiguous range of
+// row panels (one L2 holds each x panel).
 //
 // Generic kernel (any K % 8 == 0, any N): 128 x 128 tiles through padded LDS rows with register
 // staging of the next k-tile.
 //
 // Small T (<= 16) is a matrix-vector product bound by streaming W' once: 16x16x32 MFMAs with the
-// tokens as rows, K split across a workgroup's wavefronts.
+// tokens as rows, W' and x staged through per-wavefront LDS by whole-line DMA, K split across a
+// workgroup's wavefronts in an order rotated per workgroup (normproj_mvl_kernel).
 
 #include "device.h"
 #include "launch.h"
