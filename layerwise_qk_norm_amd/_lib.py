@@ -118,6 +118,13 @@ def _ld(t) -> int:
     return ld if t.shape[0] > 1 else max(ld, t.shape[1])
 
 
+def _vec(t, n: int, what: str):
+    """A 1-D operand passed as a bare pointer (gamma, column sums, per-row partials): it must be
+    contiguous and hold at least n elements, or be None."""
+    if t is not None and (not t.is_contiguous() or t.numel() < n):
+        raise ValueError(f"{what} must be a contiguous tensor of at least {n} elements")
+
+
 def _stream(t):
     torch = _torch()
     return torch.cuda.current_stream(t.device).cuda_stream
@@ -144,6 +151,9 @@ def qknorm_fused(q, gamma_q, k=None, gamma_k=None, eps: float = 1e-6, q_out=None
         dk = k.shape[1] if dk is None else dk
         if k_out is None:
             k_out = torch.empty((T, dk), dtype=k.dtype, device=k.device)
+    _vec(gamma_q, dq, "gamma_q")
+    if k is not None:
+        _vec(gamma_k, dk, "gamma_k")
     gdt = _dtype_code(gamma_q)
     _check("qknorm_fused", lib().qknorm_fused(
         T, float(eps), _dtype_code(q), gdt,
@@ -167,6 +177,8 @@ def qknorm_partial_sumsq(q, k=None, psq_q=None, psq_k=None, dq_local: int | None
         dk_local = k.shape[1] if dk_local is None else dk_local
         if psq_k is None:
             psq_k = torch.empty((T,), dtype=torch.float32, device=q.device)
+    _vec(psq_q, T, "psq_q")
+    _vec(psq_k, T, "psq_k")
     _check("qknorm_partial_sumsq", lib().qknorm_partial_sumsq(
         T, _dtype_code(q), _ptr(q), _ld(q), dq_local, _ptr(psq_q),
         _ptr(k), _ld(k) if k is not None else 0, dk_local if k is not None else 0,
@@ -193,6 +205,11 @@ def qknorm_apply_with_stats(q, gamma_q, psq_q, ext_q, dq_full: int, k=None, gamm
         n_ext_k = 0 if ext_k is None else ext_k.shape[0]
         if n_ext_k != n_ext:
             raise ValueError("ext_q and ext_k must hold the same number of peers")
+    _vec(gamma_q, dq_local, "gamma_q")
+    _vec(psq_q, T, "psq_q")
+    if k is not None:
+        _vec(gamma_k, dk_local, "gamma_k")
+        _vec(psq_k, T, "psq_k")
     gdt = _dtype_code(gamma_q)
     _check("qknorm_apply_with_stats", lib().qknorm_apply_with_stats(
         T, float(eps), _dtype_code(q), gdt, n_ext,
@@ -249,6 +266,11 @@ def qknorm_shard_fused(q, gamma_q, mail_q, dq_full: int, k=None, gamma_k=None, m
         psq_q = psq_k = None
     if timed_out is None and epoch != 0:
         timed_out = torch.zeros((1,), dtype=torch.int32, device=q.device)
+    _vec(gamma_q, dq_local, "gamma_q")
+    _vec(gamma_k, dk_local, "gamma_k")
+    _vec(psq_q, T, "psq_q")
+    _vec(psq_k, T, "psq_k")
+    _vec(timed_out, 1, "timed_out")
     _check("qknorm_shard_fused", lib().qknorm_shard_fused(
         T, float(eps), _dtype_code(q), _dtype_code(gamma_q), n_ext,
         _ptr(q), _ld(q), _ptr(q_out), _ld(q_out), _ptr(gamma_q), dq_local, dq_full,
@@ -278,6 +300,7 @@ def normproj_fold_weight(w, gamma=None, w_fold=None):
     K, N = w.shape
     if w_fold is None:
         w_fold = torch.empty((N, K), dtype=torch.bfloat16, device=w.device)
+    _vec(gamma, K, "gamma")
     _check("normproj_fold_weight", lib().normproj_fold_weight(
         K, N, _dtype_code(w), _dtype_code(gamma) if gamma is not None else QKN_BF16,
         _ptr(w), _ld(w), _ptr(gamma), _ptr(w_fold), _ld(w_fold), _stream(w)))
@@ -308,6 +331,7 @@ def normproj_unfused(x, gamma, w_packed, eps: float = 1e-6, xn=None, y=None):
         xn = torch.empty((T, K), dtype=torch.bfloat16, device=x.device)
     if y is None:
         y = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    _vec(gamma, K, "gamma")
     _check("normproj_unfused", lib().normproj_unfused(
         T, K, N, float(eps), _dtype_code(x), _dtype_code(gamma), _ptr(x), _ld(x), _ptr(gamma),
         _ptr(w_packed), _ld(w_packed), _ptr(xn), _ld(xn), _ptr(y), _ld(y), _stream(x)))
@@ -326,6 +350,10 @@ def normproj_fold_layernorm(w, gamma=None, beta=None, w_fold=None, colsum=None, 
         colsum = torch.empty((N,), dtype=torch.float32, device=w.device)
     if bias is None and beta is not None:
         bias = torch.empty((N,), dtype=torch.float32, device=w.device)
+    _vec(gamma, K, "gamma")
+    _vec(beta, K, "beta")
+    _vec(colsum, N, "colsum")
+    _vec(bias, N, "bias")
     gdt = _dtype_code(gamma) if gamma is not None else (
         _dtype_code(beta) if beta is not None else QKN_BF16)
     _check("normproj_fold_layernorm", lib().normproj_fold_layernorm(
@@ -355,6 +383,8 @@ def normproj_deferred_layernorm(x, w_fold, colsum, bias=None, eps: float = 1e-5,
         if tuple(row_stats.shape) != (T, 2) or row_stats.dtype != torch.float32 \
                 or not row_stats.is_contiguous():
             raise ValueError("row_stats must be a contiguous [T, 2] float32 tensor")
+    _vec(colsum, N, "colsum")
+    _vec(bias, N, "bias")
     _check("normproj_deferred_layernorm", lib().normproj_deferred_layernorm(
         T, K, N, float(eps), _dtype_code(x), _ptr(x), _ld(x), _ptr(w_fold), _ld(w_fold),
         _ptr(colsum), _ptr(bias), _ptr(y), _ld(y), _ptr(row_stats), _stream(x)))
@@ -372,6 +402,8 @@ def normproj_layernorm_unfused(x, gamma, beta, w_packed, eps: float = 1e-5, xn=N
     if y is None:
         y = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
     g = gamma if gamma is not None else beta
+    _vec(gamma, K, "gamma")
+    _vec(beta, K, "beta")
     _check("normproj_layernorm_unfused", lib().normproj_layernorm_unfused(
         T, K, N, float(eps), _dtype_code(x), _dtype_code(g) if g is not None else QKN_BF16,
         _ptr(x), _ld(x), _ptr(gamma), _ptr(beta), _ptr(w_packed), _ld(w_packed), _ptr(xn),
@@ -390,6 +422,8 @@ def qknorm_project_eliminated(x, w_qk, nq: int, gamma_q, gamma_k=None, eps_qk: f
     nk = N - nq
     if y is None:
         y = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    _vec(gamma_q, nq, "gamma_q")
+    _vec(gamma_k, nk, "gamma_k")
     _check("qknorm_project_eliminated", lib().qknorm_project_eliminated(
         T, K, nq, nk, float(eps_qk), float(eps_pre), int(bool(exact)), _dtype_code(gamma_q),
         _ptr(x), _ld(x), _ptr(w_qk), _ld(w_qk), _ptr(gamma_q), _ptr(gamma_k), _ptr(y), _ld(y),
@@ -410,6 +444,9 @@ def qknorm_project_unfused(x, gamma_pre, w_packed, nq: int, gamma_q, gamma_k=Non
         xn = torch.empty((T, K), dtype=torch.bfloat16, device=x.device)
     if y is None:
         y = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    _vec(gamma_pre, K, "gamma_pre")
+    _vec(gamma_q, nq, "gamma_q")
+    _vec(gamma_k, nk, "gamma_k")
     _check("qknorm_project_unfused", lib().qknorm_project_unfused(
         T, K, nq, nk, float(eps_qk), float(eps_pre), _dtype_code(gamma_q), _ptr(x), _ld(x),
         _ptr(gamma_pre), _ptr(w_packed), _ld(w_packed), _ptr(gamma_q), _ptr(gamma_k), _ptr(xn),

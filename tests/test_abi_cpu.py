@@ -292,6 +292,17 @@ def test_python_binding_refuses_host_tensors():
         q.qknorm_fused(x, torch.ones(8, dtype=torch.bfloat16))
 
 
+def test_python_binding_refuses_strided_or_short_vectors():
+    """Vectors travel as bare pointers: a strided view or a short tensor would be misread."""
+    torch = pytest.importorskip("torch")
+    _lib._vec(None, 8, "gamma")
+    _lib._vec(torch.zeros(8), 8, "gamma")
+    with pytest.raises(ValueError):
+        _lib._vec(torch.zeros(16)[::2], 8, "gamma")
+    with pytest.raises(ValueError):
+        _lib._vec(torch.zeros(7), 8, "gamma")
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "absent.so"))
     monkeypatch.setattr(_lib, "_lib", None)
