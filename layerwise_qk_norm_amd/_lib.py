@@ -125,6 +125,13 @@ def _vec(t, n: int, what: str):
         raise ValueError(f"{what} must be a contiguous tensor of at least {n} elements")
 
 
+def _dtypes(dtype, what: str, *ts):
+    """Companion tensors share the one dtype code the C call receives for them."""
+    for t in ts:
+        if t is not None and t.dtype != dtype:
+            raise TypeError(f"{what}: expected {dtype}, got {t.dtype}")
+
+
 def _stream(t):
     torch = _torch()
     return torch.cuda.current_stream(t.device).cuda_stream
@@ -155,6 +162,8 @@ def qknorm_fused(q, gamma_q, k=None, gamma_k=None, eps: float = 1e-6, q_out=None
     if k is not None:
         _vec(gamma_k, dk, "gamma_k")
     gdt = _dtype_code(gamma_q)
+    _dtypes(q.dtype, "k, q_out and k_out must match q", k, q_out, k_out)
+    _dtypes(gamma_q.dtype, "gamma_k must match gamma_q", gamma_k)
     _check("qknorm_fused", lib().qknorm_fused(
         T, float(eps), _dtype_code(q), gdt,
         _ptr(q), _ld(q), _ptr(q_out), _ld(q_out), _ptr(gamma_q), dq,
@@ -179,6 +188,8 @@ def qknorm_partial_sumsq(q, k=None, psq_q=None, psq_k=None, dq_local: int | None
             psq_k = torch.empty((T,), dtype=torch.float32, device=q.device)
     _vec(psq_q, T, "psq_q")
     _vec(psq_k, T, "psq_k")
+    _dtypes(q.dtype, "k must match q", k)
+    _dtypes(torch.float32, "psq_q / psq_k", psq_q, psq_k)
     _check("qknorm_partial_sumsq", lib().qknorm_partial_sumsq(
         T, _dtype_code(q), _ptr(q), _ld(q), dq_local, _ptr(psq_q),
         _ptr(k), _ld(k) if k is not None else 0, dk_local if k is not None else 0,
@@ -211,6 +222,9 @@ def qknorm_apply_with_stats(q, gamma_q, psq_q, ext_q, dq_full: int, k=None, gamm
         _vec(gamma_k, dk_local, "gamma_k")
         _vec(psq_k, T, "psq_k")
     gdt = _dtype_code(gamma_q)
+    _dtypes(q.dtype, "k, q_out and k_out must match q", k, q_out, k_out)
+    _dtypes(gamma_q.dtype, "gamma_k must match gamma_q", gamma_k)
+    _dtypes(torch.float32, "psq_* / ext_*", psq_q, psq_k, ext_q, ext_k)
     _check("qknorm_apply_with_stats", lib().qknorm_apply_with_stats(
         T, float(eps), _dtype_code(q), gdt, n_ext,
         _ptr(q), _ld(q), _ptr(q_out), _ld(q_out), _ptr(gamma_q), dq_local, dq_full,
@@ -271,6 +285,10 @@ def qknorm_shard_fused(q, gamma_q, mail_q, dq_full: int, k=None, gamma_k=None, m
     _vec(psq_q, T, "psq_q")
     _vec(psq_k, T, "psq_k")
     _vec(timed_out, 1, "timed_out")
+    _dtypes(q.dtype, "k, q_out and k_out must match q", k, q_out, k_out)
+    _dtypes(gamma_q.dtype, "gamma_k must match gamma_q", gamma_k)
+    _dtypes(torch.int64, "mailbox and psq words", mail_q, mail_k, psq_q, psq_k)
+    _dtypes(torch.int32, "timed_out", timed_out)
     _check("qknorm_shard_fused", lib().qknorm_shard_fused(
         T, float(eps), _dtype_code(q), _dtype_code(gamma_q), n_ext,
         _ptr(q), _ld(q), _ptr(q_out), _ld(q_out), _ptr(gamma_q), dq_local, dq_full,
@@ -287,6 +305,8 @@ def qknorm_shard_publish(part_q, mail_q, epoch: int, part_k=None, mail_k=None):
     with epoch."""
     _check_device(part_q, mail_q, part_k, mail_k)
     n_ext, T = part_q.shape
+    _dtypes(_torch().float32, "part_q / part_k", part_q, part_k)
+    _dtypes(_torch().int64, "mailbox words", mail_q, mail_k)
     _check("qknorm_shard_publish", lib().qknorm_shard_publish(
         T, n_ext, _ptr(part_q), _ld(part_q), _ptr(mail_q), _ld(mail_q),
         _ptr(part_k), _ld(part_k) if part_k is not None else 0, _ptr(mail_k),
@@ -301,6 +321,7 @@ def normproj_fold_weight(w, gamma=None, w_fold=None):
     if w_fold is None:
         w_fold = torch.empty((N, K), dtype=torch.bfloat16, device=w.device)
     _vec(gamma, K, "gamma")
+    _dtypes(torch.bfloat16, "w_fold", w_fold)
     _check("normproj_fold_weight", lib().normproj_fold_weight(
         K, N, _dtype_code(w), _dtype_code(gamma) if gamma is not None else QKN_BF16,
         _ptr(w), _ld(w), _ptr(gamma), _ptr(w_fold), _ld(w_fold), _stream(w)))
@@ -315,6 +336,7 @@ def normproj_deferred(x, w_fold, eps: float = 1e-6, y=None):
     N = w_fold.shape[0]
     if y is None:
         y = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    _dtypes(torch.bfloat16, "w_fold and y", w_fold, y)
     _check("normproj_deferred", lib().normproj_deferred(
         T, K, N, float(eps), _dtype_code(x), _ptr(x), _ld(x), _ptr(w_fold), _ld(w_fold),
         _ptr(y), _ld(y), _stream(x)))
@@ -332,6 +354,7 @@ def normproj_unfused(x, gamma, w_packed, eps: float = 1e-6, xn=None, y=None):
     if y is None:
         y = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
     _vec(gamma, K, "gamma")
+    _dtypes(torch.bfloat16, "w_packed, xn and y", w_packed, xn, y)
     _check("normproj_unfused", lib().normproj_unfused(
         T, K, N, float(eps), _dtype_code(x), _dtype_code(gamma), _ptr(x), _ld(x), _ptr(gamma),
         _ptr(w_packed), _ld(w_packed), _ptr(xn), _ld(xn), _ptr(y), _ld(y), _stream(x)))
@@ -356,6 +379,10 @@ def normproj_fold_layernorm(w, gamma=None, beta=None, w_fold=None, colsum=None, 
     _vec(bias, N, "bias")
     gdt = _dtype_code(gamma) if gamma is not None else (
         _dtype_code(beta) if beta is not None else QKN_BF16)
+    _dtypes(torch.bfloat16, "w_fold", w_fold)
+    _dtypes(torch.float32, "colsum and bias", colsum, bias)
+    if gamma is not None:
+        _dtypes(gamma.dtype, "beta must match gamma", beta)
     _check("normproj_fold_layernorm", lib().normproj_fold_layernorm(
         K, N, _dtype_code(w), gdt, _ptr(w), _ld(w), _ptr(gamma), _ptr(beta), _ptr(w_fold),
         _ld(w_fold), _ptr(colsum), _ptr(bias), _stream(w)))
@@ -385,6 +412,8 @@ def normproj_deferred_layernorm(x, w_fold, colsum, bias=None, eps: float = 1e-5,
             raise ValueError("row_stats must be a contiguous [T, 2] float32 tensor")
     _vec(colsum, N, "colsum")
     _vec(bias, N, "bias")
+    _dtypes(torch.bfloat16, "w_fold and y", w_fold, y)
+    _dtypes(torch.float32, "colsum and bias", colsum, bias)
     _check("normproj_deferred_layernorm", lib().normproj_deferred_layernorm(
         T, K, N, float(eps), _dtype_code(x), _ptr(x), _ld(x), _ptr(w_fold), _ld(w_fold),
         _ptr(colsum), _ptr(bias), _ptr(y), _ld(y), _ptr(row_stats), _stream(x)))
@@ -404,6 +433,9 @@ def normproj_layernorm_unfused(x, gamma, beta, w_packed, eps: float = 1e-5, xn=N
     g = gamma if gamma is not None else beta
     _vec(gamma, K, "gamma")
     _vec(beta, K, "beta")
+    _dtypes(torch.bfloat16, "w_packed, xn and y", w_packed, xn, y)
+    if gamma is not None:
+        _dtypes(gamma.dtype, "beta must match gamma", beta)
     _check("normproj_layernorm_unfused", lib().normproj_layernorm_unfused(
         T, K, N, float(eps), _dtype_code(x), _dtype_code(g) if g is not None else QKN_BF16,
         _ptr(x), _ld(x), _ptr(gamma), _ptr(beta), _ptr(w_packed), _ld(w_packed), _ptr(xn),
@@ -424,6 +456,8 @@ def qknorm_project_eliminated(x, w_qk, nq: int, gamma_q, gamma_k=None, eps_qk: f
         y = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
     _vec(gamma_q, nq, "gamma_q")
     _vec(gamma_k, nk, "gamma_k")
+    _dtypes(torch.bfloat16, "w_qk and y", w_qk, y)
+    _dtypes(gamma_q.dtype, "gamma_k must match gamma_q", gamma_k)
     _check("qknorm_project_eliminated", lib().qknorm_project_eliminated(
         T, K, nq, nk, float(eps_qk), float(eps_pre), int(bool(exact)), _dtype_code(gamma_q),
         _ptr(x), _ld(x), _ptr(w_qk), _ld(w_qk), _ptr(gamma_q), _ptr(gamma_k), _ptr(y), _ld(y),
@@ -447,6 +481,8 @@ def qknorm_project_unfused(x, gamma_pre, w_packed, nq: int, gamma_q, gamma_k=Non
     _vec(gamma_pre, K, "gamma_pre")
     _vec(gamma_q, nq, "gamma_q")
     _vec(gamma_k, nk, "gamma_k")
+    _dtypes(torch.bfloat16, "w_packed, xn and y", w_packed, xn, y)
+    _dtypes(gamma_q.dtype, "gamma_pre and gamma_k must match gamma_q", gamma_pre, gamma_k)
     _check("qknorm_project_unfused", lib().qknorm_project_unfused(
         T, K, nq, nk, float(eps_qk), float(eps_pre), _dtype_code(gamma_q), _ptr(x), _ld(x),
         _ptr(gamma_pre), _ptr(w_packed), _ld(w_packed), _ptr(gamma_q), _ptr(gamma_k), _ptr(xn),

@@ -303,6 +303,14 @@ def test_python_binding_refuses_strided_or_short_vectors():
         _lib._vec(torch.zeros(7), 8, "gamma")
 
 
+def test_python_binding_refuses_mismatched_dtypes():
+    """One dtype code travels per group of operands: a companion of another dtype is refused."""
+    torch = pytest.importorskip("torch")
+    _lib._dtypes(torch.bfloat16, "w_fold", None, torch.zeros(2, dtype=torch.bfloat16))
+    with pytest.raises(TypeError):
+        _lib._dtypes(torch.bfloat16, "w_fold", torch.zeros(2, dtype=torch.float32))
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "absent.so"))
     monkeypatch.setattr(_lib, "_lib", None)
