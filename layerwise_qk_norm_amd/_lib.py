@@ -125,6 +125,14 @@ def _vec(t, n: int, what: str):
         raise ValueError(f"{what} must be a contiguous tensor of at least {n} elements")
 
 
+def _mat(t, rows: int, cols: int, what: str):
+    """A 2-D operand the kernels address as rows x cols from its pointer and row stride: it
+    must be at least that large (an undersized buffer would be read or written past its end)."""
+    if t is not None and (t.dim() != 2 or t.shape[0] < rows or t.shape[1] < cols):
+        raise ValueError(f"{what} must be a 2-D tensor of at least [{rows}, {cols}], "
+                         f"got {list(t.shape)}")
+
+
 def _dtypes(dtype, what: str, *ts):
     """Companion tensors share the one dtype code the C call receives for them."""
     for t in ts:
@@ -164,6 +172,11 @@ def qknorm_fused(q, gamma_q, k=None, gamma_k=None, eps: float = 1e-6, q_out=None
     gdt = _dtype_code(gamma_q)
     _dtypes(q.dtype, "k, q_out and k_out must match q", k, q_out, k_out)
     _dtypes(gamma_q.dtype, "gamma_k must match gamma_q", gamma_k)
+    _mat(q, T, dq, "q")
+    _mat(q_out, T, dq, "q_out")
+    if k is not None:
+        _mat(k, T, dk, "k")
+        _mat(k_out, T, dk, "k_out")
     _check("qknorm_fused", lib().qknorm_fused(
         T, float(eps), _dtype_code(q), gdt,
         _ptr(q), _ld(q), _ptr(q_out), _ld(q_out), _ptr(gamma_q), dq,
@@ -190,6 +203,9 @@ def qknorm_partial_sumsq(q, k=None, psq_q=None, psq_k=None, dq_local: int | None
     _vec(psq_k, T, "psq_k")
     _dtypes(q.dtype, "k must match q", k)
     _dtypes(torch.float32, "psq_q / psq_k", psq_q, psq_k)
+    _mat(q, T, dq_local, "q")
+    if k is not None:
+        _mat(k, T, dk_local, "k")
     _check("qknorm_partial_sumsq", lib().qknorm_partial_sumsq(
         T, _dtype_code(q), _ptr(q), _ld(q), dq_local, _ptr(psq_q),
         _ptr(k), _ld(k) if k is not None else 0, dk_local if k is not None else 0,
@@ -225,6 +241,13 @@ def qknorm_apply_with_stats(q, gamma_q, psq_q, ext_q, dq_full: int, k=None, gamm
     _dtypes(q.dtype, "k, q_out and k_out must match q", k, q_out, k_out)
     _dtypes(gamma_q.dtype, "gamma_k must match gamma_q", gamma_k)
     _dtypes(torch.float32, "psq_* / ext_*", psq_q, psq_k, ext_q, ext_k)
+    _mat(q, T, dq_local, "q")
+    _mat(q_out, T, dq_local, "q_out")
+    _mat(ext_q, n_ext, T, "ext_q")
+    if k is not None:
+        _mat(k, T, dk_local, "k")
+        _mat(k_out, T, dk_local, "k_out")
+        _mat(ext_k, n_ext, T, "ext_k")
     _check("qknorm_apply_with_stats", lib().qknorm_apply_with_stats(
         T, float(eps), _dtype_code(q), gdt, n_ext,
         _ptr(q), _ld(q), _ptr(q_out), _ld(q_out), _ptr(gamma_q), dq_local, dq_full,
@@ -289,6 +312,12 @@ def qknorm_shard_fused(q, gamma_q, mail_q, dq_full: int, k=None, gamma_k=None, m
     _dtypes(gamma_q.dtype, "gamma_k must match gamma_q", gamma_k)
     _dtypes(torch.int64, "mailbox and psq words", mail_q, mail_k, psq_q, psq_k)
     _dtypes(torch.int32, "timed_out", timed_out)
+    _mat(q_out, T, dq_local, "q_out")
+    _mat(mail_q, n_ext, T, "mail_q")
+    if k is not None:
+        _mat(k, T, 1, "k")
+        _mat(k_out, T, dk_local, "k_out")
+        _mat(mail_k, n_ext, T, "mail_k")
     _check("qknorm_shard_fused", lib().qknorm_shard_fused(
         T, float(eps), _dtype_code(q), _dtype_code(gamma_q), n_ext,
         _ptr(q), _ld(q), _ptr(q_out), _ld(q_out), _ptr(gamma_q), dq_local, dq_full,
@@ -307,6 +336,10 @@ def qknorm_shard_publish(part_q, mail_q, epoch: int, part_k=None, mail_k=None):
     n_ext, T = part_q.shape
     _dtypes(_torch().float32, "part_q / part_k", part_q, part_k)
     _dtypes(_torch().int64, "mailbox words", mail_q, mail_k)
+    _mat(mail_q, n_ext, T, "mail_q")
+    if part_k is not None:
+        _mat(part_k, n_ext, T, "part_k")
+        _mat(mail_k, n_ext, T, "mail_k")
     _check("qknorm_shard_publish", lib().qknorm_shard_publish(
         T, n_ext, _ptr(part_q), _ld(part_q), _ptr(mail_q), _ld(mail_q),
         _ptr(part_k), _ld(part_k) if part_k is not None else 0, _ptr(mail_k),
@@ -322,6 +355,7 @@ def normproj_fold_weight(w, gamma=None, w_fold=None):
         w_fold = torch.empty((N, K), dtype=torch.bfloat16, device=w.device)
     _vec(gamma, K, "gamma")
     _dtypes(torch.bfloat16, "w_fold", w_fold)
+    _mat(w_fold, N, K, "w_fold")
     _check("normproj_fold_weight", lib().normproj_fold_weight(
         K, N, _dtype_code(w), _dtype_code(gamma) if gamma is not None else QKN_BF16,
         _ptr(w), _ld(w), _ptr(gamma), _ptr(w_fold), _ld(w_fold), _stream(w)))
@@ -337,6 +371,8 @@ def normproj_deferred(x, w_fold, eps: float = 1e-6, y=None):
     if y is None:
         y = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
     _dtypes(torch.bfloat16, "w_fold and y", w_fold, y)
+    _mat(w_fold, N, K, "w_fold")
+    _mat(y, T, N, "y")
     _check("normproj_deferred", lib().normproj_deferred(
         T, K, N, float(eps), _dtype_code(x), _ptr(x), _ld(x), _ptr(w_fold), _ld(w_fold),
         _ptr(y), _ld(y), _stream(x)))
@@ -355,6 +391,9 @@ def normproj_unfused(x, gamma, w_packed, eps: float = 1e-6, xn=None, y=None):
         y = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
     _vec(gamma, K, "gamma")
     _dtypes(torch.bfloat16, "w_packed, xn and y", w_packed, xn, y)
+    _mat(w_packed, N, K, "w_packed")
+    _mat(xn, T, K, "xn")
+    _mat(y, T, N, "y")
     _check("normproj_unfused", lib().normproj_unfused(
         T, K, N, float(eps), _dtype_code(x), _dtype_code(gamma), _ptr(x), _ld(x), _ptr(gamma),
         _ptr(w_packed), _ld(w_packed), _ptr(xn), _ld(xn), _ptr(y), _ld(y), _stream(x)))
@@ -383,6 +422,7 @@ def normproj_fold_layernorm(w, gamma=None, beta=None, w_fold=None, colsum=None, 
     _dtypes(torch.float32, "colsum and bias", colsum, bias)
     if gamma is not None:
         _dtypes(gamma.dtype, "beta must match gamma", beta)
+    _mat(w_fold, N, K, "w_fold")
     _check("normproj_fold_layernorm", lib().normproj_fold_layernorm(
         K, N, _dtype_code(w), gdt, _ptr(w), _ld(w), _ptr(gamma), _ptr(beta), _ptr(w_fold),
         _ld(w_fold), _ptr(colsum), _ptr(bias), _stream(w)))
@@ -414,6 +454,8 @@ def normproj_deferred_layernorm(x, w_fold, colsum, bias=None, eps: float = 1e-5,
     _vec(bias, N, "bias")
     _dtypes(torch.bfloat16, "w_fold and y", w_fold, y)
     _dtypes(torch.float32, "colsum and bias", colsum, bias)
+    _mat(w_fold, N, K, "w_fold")
+    _mat(y, T, N, "y")
     _check("normproj_deferred_layernorm", lib().normproj_deferred_layernorm(
         T, K, N, float(eps), _dtype_code(x), _ptr(x), _ld(x), _ptr(w_fold), _ld(w_fold),
         _ptr(colsum), _ptr(bias), _ptr(y), _ld(y), _ptr(row_stats), _stream(x)))
@@ -436,6 +478,9 @@ def normproj_layernorm_unfused(x, gamma, beta, w_packed, eps: float = 1e-5, xn=N
     _dtypes(torch.bfloat16, "w_packed, xn and y", w_packed, xn, y)
     if gamma is not None:
         _dtypes(gamma.dtype, "beta must match gamma", beta)
+    _mat(w_packed, N, K, "w_packed")
+    _mat(xn, T, K, "xn")
+    _mat(y, T, N, "y")
     _check("normproj_layernorm_unfused", lib().normproj_layernorm_unfused(
         T, K, N, float(eps), _dtype_code(x), _dtype_code(g) if g is not None else QKN_BF16,
         _ptr(x), _ld(x), _ptr(gamma), _ptr(beta), _ptr(w_packed), _ld(w_packed), _ptr(xn),
@@ -458,6 +503,8 @@ def qknorm_project_eliminated(x, w_qk, nq: int, gamma_q, gamma_k=None, eps_qk: f
     _vec(gamma_k, nk, "gamma_k")
     _dtypes(torch.bfloat16, "w_qk and y", w_qk, y)
     _dtypes(gamma_q.dtype, "gamma_k must match gamma_q", gamma_k)
+    _mat(w_qk, N, K, "w_qk")
+    _mat(y, T, N, "y")
     _check("qknorm_project_eliminated", lib().qknorm_project_eliminated(
         T, K, nq, nk, float(eps_qk), float(eps_pre), int(bool(exact)), _dtype_code(gamma_q),
         _ptr(x), _ld(x), _ptr(w_qk), _ld(w_qk), _ptr(gamma_q), _ptr(gamma_k), _ptr(y), _ld(y),
@@ -483,6 +530,9 @@ def qknorm_project_unfused(x, gamma_pre, w_packed, nq: int, gamma_q, gamma_k=Non
     _vec(gamma_k, nk, "gamma_k")
     _dtypes(torch.bfloat16, "w_packed, xn and y", w_packed, xn, y)
     _dtypes(gamma_q.dtype, "gamma_pre and gamma_k must match gamma_q", gamma_pre, gamma_k)
+    _mat(w_packed, N, K, "w_packed")
+    _mat(xn, T, K, "xn")
+    _mat(y, T, N, "y")
     _check("qknorm_project_unfused", lib().qknorm_project_unfused(
         T, K, nq, nk, float(eps_qk), float(eps_pre), _dtype_code(gamma_q), _ptr(x), _ld(x),
         _ptr(gamma_pre), _ptr(w_packed), _ld(w_packed), _ptr(gamma_q), _ptr(gamma_k), _ptr(xn),

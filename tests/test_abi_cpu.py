@@ -303,6 +303,17 @@ def test_python_binding_refuses_strided_or_short_vectors():
         _lib._vec(torch.zeros(7), 8, "gamma")
 
 
+def test_python_binding_refuses_undersized_matrices():
+    """2-D operands are addressed from pointer and row stride: too few rows or columns would
+    be read or written past the end of the buffer."""
+    torch = pytest.importorskip("torch")
+    _lib._mat(None, 4, 4, "y")
+    _lib._mat(torch.zeros(4, 8), 4, 8, "y")
+    for bad in (torch.zeros(3, 8), torch.zeros(4, 7), torch.zeros(32)):
+        with pytest.raises(ValueError):
+            _lib._mat(bad, 4, 8, "y")
+
+
 def test_python_binding_refuses_mismatched_dtypes():
     """One dtype code travels per group of operands: a companion of another dtype is refused."""
     torch = pytest.importorskip("torch")
