@@ -33,8 +33,8 @@
 // v_dot2c_f32_bf16 for RMSNorm), and their partials are added through LDS in a fixed order.
 // The epilogue applies the row scale, rounds to bf16, writes the tile to LDS 8 bytes at a time
 // and stores it so each lane writes 16 contiguous bytes, non-temporally unless the caller reads
-// the output straight back. Blocks are remapped so that each XCD works on a contiguous range of
-// row panels (one L2 holds each x panel).
+// the output straight back. Workgroups are remapped so that each XCD works on a block of the
+// tile grid whose row and column panels its L2 can share (the split chosen per grid shape).
 //
 // Generic kernel (any K % 8 == 0, any N): 128 x 128 tiles through padded LDS rows with register
 // staging of the next k-tile.
@@ -213,8 +213,31 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
     const int wm = wave / WN, wn = wave % WN;
     const int nb = nbm * nbn;
     int bid = (int)blockIdx.x;
-    if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
-    const int64_t m0 = (int64_t)(bid / nbn) * BM, n0 = (int64_t)(bid % nbn) * BN;
+    // Workgroup b runs on XCD b % 8. Each XCD takes a block of the tile grid: the row panels
+    // split gx ways and the column panels 8 / gx ways, with gx chosen so that the row and column
+    // panels one XCD's L2 must hold are fewest (ties go to fewer row panels: x streams from
+    // HBM, W' is shared by every row panel); within the block, tiles go row by row. Grids that
+    // do not split evenly keep plain contiguous ranges of tiles per XCD.
+    int64_t m0, n0;
+    int gx = 0;
+    {
+        int best = 0x7fffffff;
+        for (int g = 1; g <= 8; g *= 2)
+            if (nbm % g == 0 && nbn % (8 / g) == 0 && nbm / g + nbn / (8 / g) <= best) {
+                best = nbm / g + nbn / (8 / g);
+                gx = g;
+            }
+    }
+    if (gx) {
+        const int xcd = bid & 7, j = bid >> 3;
+        const int gy = 8 / gx, rpg = nbm / gx, cpg = nbn / gy;
+        m0 = (int64_t)((xcd / gy) * rpg + j / cpg) * BM;
+        n0 = (int64_t)((xcd % gy) * cpg + j % cpg) * BN;
+    } else {
+        if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+        m0 = (int64_t)(bid / nbn) * BM;
+        n0 = (int64_t)(bid % nbn) * BN;
+    }
     // LDS byte address of the pipeline buffer; DMA destinations are offsets from it, kept in
     // scalar registers
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)smem;
