@@ -426,10 +426,10 @@ int unfused_rms_product(int64_t T, int64_t K, int64_t N, float eps, int dtype, i
     if (T == 0 || N == 0) return QKN_OK;
     if (xn == nullptr || gamma == nullptr) return QKN_ERR_NULL;
     if (((uintptr_t)xn & 15u) != 0 || ldxn % 8 != 0) return QKN_ERR_ALIGN;
-    const Range rxn = span(xn, T, K, ldxn, 2);
+    const Range rxn = span(xn, T, K, ldxn, 2), rg = span(gamma, 1, K, K, elem_size(gamma_dtype));
     if (overlap(rxn, span(x, T, K, ldx, 2)) || overlap(rxn, span(w_packed, N, K, ldw, 2)) ||
-        overlap(rxn, span(y, T, N, ldy, 2)) ||
-        overlap(rxn, span(gamma, 1, K, K, elem_size(gamma_dtype))))
+        overlap(rxn, span(y, T, N, ldy, 2)) || overlap(rxn, rg) ||
+        overlap(span(y, T, N, ldy, 2), rg))
         return QKN_ERR_ALIAS;
 
     qkn::RowJob job = {};
@@ -535,10 +535,11 @@ QKN_API int normproj_layernorm_unfused(int64_t T, int64_t K, int64_t N, float ep
         ((uintptr_t)beta & 15u) != 0)
         return QKN_ERR_ALIGN;
     const int64_t gs = elem_size(gamma_dtype);
-    const Range rxn = span(xn, T, K, ldxn, 2);
+    const Range rxn = span(xn, T, K, ldxn, 2), ry = span(y, T, N, ldy, 2);
+    const Range rg = span(gamma, 1, K, K, gs), rb = span(beta, 1, K, K, gs);
     if (overlap(rxn, span(x, T, K, ldx, 2)) || overlap(rxn, span(w_packed, N, K, ldw, 2)) ||
-        overlap(rxn, span(y, T, N, ldy, 2)) || (gamma && overlap(rxn, span(gamma, 1, K, K, gs))) ||
-        (beta && overlap(rxn, span(beta, 1, K, K, gs))))
+        overlap(rxn, ry) || overlap(rxn, rg) || overlap(rxn, rb) || overlap(ry, rg) ||
+        overlap(ry, rb))
         return QKN_ERR_ALIAS;
     hipError_t e = qkn::launch_layernorm_rows(T, K, eps, x, ldx, gamma, beta,
                                               gamma_dtype == QKN_BF16, xn, ldxn,

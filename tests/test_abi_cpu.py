@@ -153,6 +153,7 @@ def test_normproj_validation(L):
     assert U(4, 16, 16, 1e-6, BF16, BF16, A, 16, G1, B, 16, A, 16, C, 16, None) == ALIAS
     assert U(4, 16, 16, 1e-6, BF16, BF16, A, 16, G1, B, 16, None, 16, C, 16, None) == NULL
     assert U(4, 16, 16, 1e-6, BF16, 9, A, 16, G1, B, 16, D, 16, C, 16, None) == DTYPE
+    assert U(4, 16, 16, 1e-6, BF16, BF16, A, 16, G1, B, 16, D, 16, G1 - 32, 16, None) == ALIAS
     assert L.qkn_device_copy(A, A + 8, 64, None) == ALIAS
     assert L.qkn_device_copy(A, B, -1, None) == SHAPE
     assert L.qkn_device_copy(None, B, 0, None) == OK
@@ -189,6 +190,8 @@ def test_layernorm_projection_validation(L):
     assert U(4, 16, 16, 1e-5, BF16, BF16, A, 16, G1, G2, B, 16, None, 16, C, 16, None) == NULL
     assert U(4, 16, 16, 1e-5, BF16, BF16, A, 16, G1 + 2, G2, B, 16, D, 16, C, 16, None) == ALIGN
     assert U(4, 16, 16, 1e-5, BF16, 9, A, 16, G1, G2, B, 16, D, 16, C, 16, None) == DTYPE
+    assert U(4, 16, 16, 1e-5, BF16, BF16, A, 16, G1, G2, B, 16, D, 16, G1 - 32, 16, None) == ALIAS
+    assert U(4, 16, 16, 1e-5, BF16, BF16, A, 16, G1, G2, B, 16, D, 16, G2 - 32, 16, None) == ALIAS
 
 
 @no_gpu
@@ -237,6 +240,7 @@ def test_project_unfused_validation(L):
     assert U(y=G2 - 32) == ALIAS               # output running into gamma_q
     assert U(xn=A) == ALIAS                    # scratch over x
     assert U(xn=G2 - 32) == ALIAS              # scratch running into gamma_q
+    assert U(y=G1 - 32) == ALIAS               # output running into the pre-norm's gamma
     assert U(T=0, x=None, w=None, g1=None, gq=None, gk=None, xn=None, y=None) == OK
 
 
