@@ -99,7 +99,8 @@ def run_elimination(Q, c, exact, rows, what, chain_rows=None):
 @pytest.mark.parametrize("T,K,nq,nk", [(300, 512, 384, 136), (300, 512, 384, 130),
                                        (16, 256, 256, 64), (37, 264, 200, 0),
                                        (129, 1024, 1024, 1024), (1, 520, 256, 264),
-                                       (4096, 96, 4096, 4096), (2100, 256, 2048, 8)])
+                                       (4096, 96, 4096, 4096), (2100, 256, 2048, 8),
+                                       (4352, 64, 4096, 4096)])
 def test_elimination_shapes(Q, T, K, nq, nk, exact):
     """Every product kernel (matrix-vector T <= 16, generic tiles for K % 32 != 0 or N % 8 != 0,
     pipelined tiles: 128 x 128 with 4 and with 2 stages, 256 x 256 with k-tiles of 64 and of 32,
@@ -224,7 +225,8 @@ def test_deferred_layernorm(Q, T, x_mean, stats):
                                    (300, 264, 200), (129, 2048, 2048), (8200, 1056, 4104),
                                    (8200, 1024, 4104), (4096, 64, 4096), (4100, 192, 4104),
                                    (4100, 512, 2056), (12, 512, 4104), (8, 1000, 4104),
-                                   (1, 8, 24), (3, 520, 4104)])
+                                   (1, 8, 24), (3, 520, 4104), (4352, 128, 4096),
+                                   (6000, 256, 6000)])
 def test_deferred_layernorm_ragged(Q, T, K, N, stats):
     """All product kernels with the LayerNorm epilogue, ragged T and N, no beta, x with a mean
     of 2 (the mean term is exercised everywhere), statistics from the workspace pass or from

@@ -190,13 +190,15 @@ def test_normproj_unfused_baseline(Q):
                                    (4100, 512, 2056), (12, 512, 4104), (8, 1000, 4104),
                                    (1, 8, 24), (3, 64, 40), (16, 4096, 8200), (3, 520, 4104),
                                    (12, 264, 3000), (2, 2048, 2056), (2, 16, 1),
-                                   (4, 16392, 520), (16, 8200, 4200)])
+                                   (4, 16392, 520), (16, 8200, 4200), (4352, 64, 4096),
+                                   (4352, 128, 4096), (8192, 128, 8192), (6000, 256, 6000)])
 def test_normproj_ragged(Q, T, K, N):
     """Every kernel of the projection: the matrix-vector path (T <= 16), the generic tile
     kernel (K not a multiple of 32), and the pipelined tilings (128 x 128 with 4 stages when
     there is at most one tile per CU and 2 otherwise; 256 x 256 with k-tiles of 64 through the
     five-part ring, or of 32), with T and N not multiples of the tile and rings of one, two and
-    three k-tiles; large cases are checked on a sample of rows."""
+    three k-tiles, grids of one to four rounds of tiles per CU; large cases are checked on a
+    sample of rows that meets every tile."""
     rng = np.random.default_rng(T + K + N)
     x = inputs.random_rows(rng, T, K, "bf16")
     w = inputs.random_rows(rng, K, N, "bf16", scale=0.02)
