@@ -136,8 +136,8 @@ def dev(torch, a):
 
 
 # ----------------------------------------------------------------------------- workloads
-def fused_setup(torch, Q, inputs, cfg, T):
-    c = inputs.make_case(cfg, T)
+def fused_setup(torch, Q, inputs, workload, T):
+    c = inputs.make_case(workload, T)
     q, k = dev(torch, c["q"]), dev(torch, c["k"])
     gq, gk = dev(torch, c["gamma_q"]), dev(torch, c["gamma_k"])
     es = q.element_size()
@@ -155,7 +155,7 @@ def fused_setup(torch, Q, inputs, cfg, T):
 
 
 def shard_setup(torch, Q, inputs, T):
-    c = inputs.make_case(4, T)
+    c = inputs.make_case("tp8-shard", T)
     q, k = dev(torch, c["q"]), dev(torch, c["k"])
     gq, gk = dev(torch, c["gamma_q"]), dev(torch, c["gamma_k"])
     eq, ek = dev(torch, c["ext_q"]), dev(torch, c["ext_k"])
@@ -206,7 +206,7 @@ def shard_setup(torch, Q, inputs, T):
 
 
 def normproj_setup(torch, Q, inputs, T, unfused=False):
-    c = inputs.make_case(5, T)
+    c = inputs.make_case("flashnorm-2048", T)
     x, w, g = dev(torch, c["x"]), dev(torch, c["w"]), dev(torch, c["gamma"])
     K, N = w.shape
     wm = Q.normproj_fold_weight(w, None) if unfused else Q.normproj_fold_weight(w, g)
@@ -308,7 +308,7 @@ def cpu_baseline(inputs, T_full, budget_s=10.0):
     import oracle
     from concurrent.futures import ThreadPoolExecutor
 
-    c = inputs.make_case(2, 1024)
+    c = inputs.make_case("olmo2-7b", 1024)
 
     def one(rows):
         oracle.rmsnorm_rows(c["q"][rows], c["gamma_q"], c["eps"])
@@ -353,7 +353,7 @@ def cpu_oracle_projection(inputs, rows=32):
     per row and labelled so."""
     import oracle
 
-    c = inputs.make_case(5, rows)
+    c = inputs.make_case("flashnorm-2048", rows)
     wf = oracle.round_bf16(oracle.fold_weight(c["w"], c["gamma"]))
     best = float("inf")
     for _ in range(3):
@@ -361,8 +361,9 @@ def cpu_oracle_projection(inputs, rows=32):
         oracle.normproj(c["x"], wf, c["eps"])
         best = min(best, time.perf_counter() - t0)
     per_row = best / rows
-    return [{"case": f"oracle normproj cfg5 T={t} (extrapolated from {rows} rows, 1 thread)",
-             "us_per_call": per_row * t * 1e6} for t in inputs.CONFIGS[5]["Ts"] if t > 1]
+    return [{"case": f"oracle normproj flashnorm-2048 T={t} (extrapolated from {rows} rows, 1 thread)",
+             "us_per_call": per_row * t * 1e6}
+            for t in inputs.WORKLOADS["flashnorm-2048"]["Ts"] if t > 1]
 
 
 # ----------------------------------------------------------------------------- main
@@ -387,7 +388,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (rows shard with no "
+        print("bench.py measures one GPU: the library has no multi-GPU path (rows shard with no "
               "exchange; the column-sharded exchange is not built). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
@@ -406,7 +407,7 @@ def main():
     timer = Timer(torch, stream)
 
     T = args.tokens
-    step, nbytes = fused_setup(torch, Q, inputs, 2, T)
+    step, nbytes = fused_setup(torch, Q, inputs, "olmo2-7b", T)
     torch.cuda.synchronize()
     ms = timer.run(step, args.steps, args.warmup)
     achieved = nbytes / (ms * 1e-3) / 1e9
@@ -448,13 +449,14 @@ def main():
                           "us_per_call": cms * 1e3, "GB_s": 2 * half / (cms * 1e-3) / 1e9})
         del bufs
 
-        for cfg, Ts in ((1, (64,)), (2, (1, 16, 256, 4096, 8192)), (3, (1, 512, 8192))):
+        for wl, Ts in (("tiny-fp32", (64,)), ("olmo2-7b", (1, 16, 256, 4096, 8192)),
+                       ("gqa-olmo2-32b-like", (1, 512, 8192))):
             for t in Ts:
                 if not want("qknorm_fused") or not want_t(t):
                     continue
-                fn, b = fused_setup(torch, Q, inputs, cfg, t)
+                fn, b = fused_setup(torch, Q, inputs, wl, t)
                 cms, gms = time_case(timer, fn, it, wu)
-                cases.append({"case": f"qknorm_fused cfg{cfg} {inputs.CONFIGS[cfg]['name']} T={t}",
+                cases.append({"case": f"qknorm_fused {wl} T={t}",
                               "us_per_call": cms * 1e3, "us_per_call_graph": gms * 1e3,
                               "GB_s": b / (gms * 1e-3) / 1e9,
                               "frac_hbm": b / (gms * 1e-3) / 1e9 / PEAK_HBM_GBS})
@@ -469,7 +471,7 @@ def main():
             if not want(name):
                 continue
             m, gm = time_case(timer, fn, it, wu)
-            cases.append({"case": f"{name}{label} cfg4 tp8-shard T=131072",
+            cases.append({"case": f"{name}{label} tp8-shard T=131072",
                           "us_per_call": m * 1e3, "us_per_call_graph": gm * 1e3,
                           "GB_s": b / (gm * 1e-3) / 1e9,
                           "frac_hbm": b / (gm * 1e-3) / 1e9 / PEAK_HBM_GBS})
@@ -487,7 +489,7 @@ def main():
                 fn, flops, b = normproj_setup(torch, Q, inputs, t, unfused)
                 cms, gms = time_case(timer, fn, it, wu)
                 name = "normproj_unfused" if unfused else "normproj_deferred"
-                entry = {"case": f"{name} cfg5 flashnorm-2048 T={t}", "us_per_call": cms * 1e3,
+                entry = {"case": f"{name} flashnorm-2048 T={t}", "us_per_call": cms * 1e3,
                          "us_per_call_graph": gms * 1e3, "TFLOP_s": flops / (gms * 1e-3) / 1e12}
                 if t == 1:
                     entry["GB_s"] = b / (gms * 1e-3) / 1e9

@@ -9,17 +9,17 @@ models in "SwiftQK: Fast and Communication-Efficient Tensor Parallelism for Quer
 Normalization", abstract; SmolLM2-135M / Llama-7B scale in "FlashNorm: Fast Normalization for
 Transformers", abstract), which are not available here. Shapes and distributions:
 
-  1  tiny fp32:     Q, K [T, 512] fp32, x ~ N(0, 1), gamma ~ N(1, 0.1), eps 1e-6, T = 64
-  2  OLMo-2-7B:     Q, K [T, 4096] bf16 (32 heads x 128), x ~ N(0, 2), gamma ~ N(1, 0.05)
-  3  GQA, 32B-like: Q [T, 5120] (40 x 128), K [T, 1024] (8 x 128) bf16, x ~ N(0, 1),
-                    1% of the columns of each tensor multiplied by 20 (channel outliers),
-                    independent gammas ~ N(1, 0.05)
-  4  TP shard:      Q, K [T, 512] bf16 (one 4096/8 column slice), x ~ N(0, 1), the shard's own
-                    gamma slices ~ N(1, 0.05), and 7 peers' partial sums of squares per row and
-                    tensor, each a chi-square draw with 512 degrees of freedom (the sum of 512
-                    squared N(0, 1)), fp32, laid out [7, T] peer-major
-  5  FlashNorm:     x [T, 2048] ~ N(0, 1), W [2048, 2048] ~ N(0, 0.02), gamma [2048] ~ N(1, 0.05),
-                    all bf16
+  tiny-fp32:          Q, K [T, 512] fp32, x ~ N(0, 1), gamma ~ N(1, 0.1), eps 1e-6, T = 64
+  olmo2-7b:           Q, K [T, 4096] bf16 (32 heads x 128), x ~ N(0, 2), gamma ~ N(1, 0.05)
+  gqa-olmo2-32b-like: Q [T, 5120] (40 x 128), K [T, 1024] (8 x 128) bf16, x ~ N(0, 1),
+                      1% of the columns of each tensor multiplied by 20 (channel outliers),
+                      independent gammas ~ N(1, 0.05)
+  tp8-shard:          Q, K [T, 512] bf16 (one 4096/8 column slice), x ~ N(0, 1), the shard's
+                      own gamma slices ~ N(1, 0.05), and 7 peers' partial sums of squares per
+                      row and tensor, each a chi-square draw with 512 degrees of freedom (the
+                      sum of 512 squared N(0, 1)), fp32, laid out [7, T] peer-major
+  flashnorm-2048:     x [T, 2048] ~ N(0, 1), W [2048, 2048] ~ N(0, 0.02), gamma [2048]
+                      ~ N(1, 0.05), all bf16
 
 Two further workloads exercise the pre-norm elimination and the LayerNorm fold ("FlashNorm",
 abstract), which the five above do not cover:
@@ -27,13 +27,13 @@ abstract), which the five above do not cover:
   elimination:      x [T, 4096] ~ N(0, 1) (the attention block's input), pre-norm gamma
                     ~ N(1, 0.05), Wq, Wk [4096, 4096] ~ N(0, 0.02) (OLMo-2-7B widths, 32 heads
                     x 128), QK-Norm gammas ~ N(1, 0.05), eps 1e-6 for both norms, all bf16
-  layernorm:        as config 5 plus beta [2048] ~ N(0, 0.05), eps 1e-5; x ~ N(mean, 1) with a
+  layernorm:        as flashnorm-2048 plus beta [2048] ~ N(0, 0.05), eps 1e-5; x ~ N(mean, 1) with a
                     selectable per-workload mean (0 by default) to exercise the mean term
 
-N(mu, s) names the standard deviation s. Every (config, T, seed) gets its own PCG64 stream
+N(mu, s) names the standard deviation s. Every (workload, T, seed) gets its own PCG64 stream
 (``numpy.random.default_rng(seed)``); draws happen in a fixed order (weights first, then
 activations, then outlier columns or peer partials), so weights are identical across T within
-a config. Draws are float32 and are rounded to bf16 with round-to-nearest-even.
+a workload. Draws are float32 and are rounded to bf16 with round-to-nearest-even.
 """
 
 from __future__ import annotations
@@ -42,14 +42,14 @@ import numpy as np
 
 EPS_DEFAULT = 1e-6
 
-# config id -> shapes and token counts the workload is defined for
-CONFIGS = {
-    1: dict(name="tiny-fp32", dq=512, dk=512, dtype="f32", Ts=(64,)),
-    2: dict(name="olmo2-7b", dq=4096, dk=4096, dtype="bf16", Ts=(1, 16, 256, 4096, 8192)),
-    3: dict(name="gqa-olmo2-32b-like", dq=5120, dk=1024, dtype="bf16", Ts=(1, 512, 8192)),
-    4: dict(name="tp8-shard", dq=512, dk=512, dq_full=4096, dk_full=4096, n_ext=7,
-            dtype="bf16", Ts=(131072,)),
-    5: dict(name="flashnorm-2048", K=2048, N=2048, dtype="bf16", Ts=(1, 2048, 16384)),
+# workload name -> shapes and the token counts it is defined for
+WORKLOADS = {
+    "tiny-fp32": dict(dq=512, dk=512, dtype="f32", Ts=(64,)),
+    "olmo2-7b": dict(dq=4096, dk=4096, dtype="bf16", Ts=(1, 16, 256, 4096, 8192)),
+    "gqa-olmo2-32b-like": dict(dq=5120, dk=1024, dtype="bf16", Ts=(1, 512, 8192)),
+    "tp8-shard": dict(dq=512, dk=512, dq_full=4096, dk_full=4096, n_ext=7, dtype="bf16",
+                      Ts=(131072,)),
+    "flashnorm-2048": dict(K=2048, N=2048, dtype="bf16", Ts=(1, 2048, 16384)),
 }
 
 
@@ -82,35 +82,37 @@ def _store(a: np.ndarray, dtype: str) -> np.ndarray:
     return f32_to_bf16_bits(a) if dtype == "bf16" else np.ascontiguousarray(a, np.float32)
 
 
-def make_case(cfg: int, T: int, seed: int = 0) -> dict:
-    """Return the tensors of workload ``cfg`` at ``T`` tokens as host numpy arrays.
+def make_case(workload: str, T: int, seed: int = 0) -> dict:
+    """Return the tensors of ``workload`` (a key of WORKLOADS) at ``T`` tokens as host numpy
+    arrays.
 
     bf16 tensors are uint16 arrays of raw bits; fp32 tensors are float32 arrays. Keys:
-      configs 1-3: q, k [T, d], gamma_q, gamma_k, eps, dtype, gamma_dtype
-      config 4:    the same plus ext_q, ext_k [7, T] fp32, dq_full, dk_full
-      config 5:    x [T, K], w [K, N], gamma [K], eps
+      tiny-fp32, olmo2-7b, gqa-olmo2-32b-like: q, k [T, d], gamma_q, gamma_k, eps, dtype,
+                                               gamma_dtype
+      tp8-shard:      the same plus ext_q, ext_k [7, T] fp32, dq_full, dk_full
+      flashnorm-2048: x [T, K], w [K, N], gamma [K], eps
     """
-    if cfg not in CONFIGS:
-        raise ValueError(f"unknown config {cfg}")
+    if workload not in WORKLOADS:
+        raise ValueError(f"unknown workload {workload!r}")
     if T < 0:
         raise ValueError("T must be >= 0")
-    c = CONFIGS[cfg]
+    c = WORKLOADS[workload]
     rng = np.random.default_rng(seed)
-    out = dict(cfg=cfg, T=T, seed=seed, eps=EPS_DEFAULT, dtype=c["dtype"], name=c["name"])
-    if cfg == 1:
+    out = dict(T=T, seed=seed, eps=EPS_DEFAULT, dtype=c["dtype"], name=workload)
+    if workload == "tiny-fp32":
         gq = _normal(rng, 1.0, 0.1, (c["dq"],))
         gk = _normal(rng, 1.0, 0.1, (c["dk"],))
         xq = _normal(rng, 0.0, 1.0, (T, c["dq"]))
         xk = _normal(rng, 0.0, 1.0, (T, c["dk"]))
         out.update(q=xq, k=xk, gamma_q=gq, gamma_k=gk, gamma_dtype="f32")
-    elif cfg == 2:
+    elif workload == "olmo2-7b":
         gq = _normal(rng, 1.0, 0.05, (c["dq"],))
         gk = _normal(rng, 1.0, 0.05, (c["dk"],))
         xq = _normal(rng, 0.0, 2.0, (T, c["dq"]))
         xk = _normal(rng, 0.0, 2.0, (T, c["dk"]))
         out.update(q=_store(xq, "bf16"), k=_store(xk, "bf16"), gamma_q=_store(gq, "bf16"),
                    gamma_k=_store(gk, "bf16"), gamma_dtype="bf16")
-    elif cfg == 3:
+    elif workload == "gqa-olmo2-32b-like":
         gq = _normal(rng, 1.0, 0.05, (c["dq"],))
         gk = _normal(rng, 1.0, 0.05, (c["dk"],))
         xq = _normal(rng, 0.0, 1.0, (T, c["dq"]))
@@ -122,7 +124,7 @@ def make_case(cfg: int, T: int, seed: int = 0) -> dict:
         out.update(q=_store(xq, "bf16"), k=_store(xk, "bf16"), gamma_q=_store(gq, "bf16"),
                    gamma_k=_store(gk, "bf16"), gamma_dtype="bf16",
                    outlier_cols_q=np.sort(cols_q), outlier_cols_k=np.sort(cols_k))
-    elif cfg == 4:
+    elif workload == "tp8-shard":
         gq = _normal(rng, 1.0, 0.05, (c["dq"],))
         gk = _normal(rng, 1.0, 0.05, (c["dk"],))
         xq = _normal(rng, 0.0, 1.0, (T, c["dq"]))

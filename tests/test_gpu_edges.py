@@ -100,7 +100,7 @@ def test_row_stride_above_width_keeps_padding(Q):
 
 
 def test_in_place(Q):
-    c = inputs.make_case(2, 300, seed=4)
+    c = inputs.make_case("olmo2-7b", 300, seed=4)
     q, k = to_dev(c["q"]), to_dev(c["k"])
     Q.qknorm_fused(q, to_dev(c["gamma_q"]), k, to_dev(c["gamma_k"]), eps=c["eps"], q_out=q,
                    k_out=k)
@@ -108,7 +108,7 @@ def test_in_place(Q):
     check_rows(to_host(q), oracle.rmsnorm_rows(c["q"], c["gamma_q"], c["eps"]), "in-place Q")
     check_rows(to_host(k), oracle.rmsnorm_rows(c["k"], c["gamma_k"], c["eps"]), "in-place K")
     # in-place shard stage
-    c4 = inputs.make_case(4, 200, seed=4)
+    c4 = inputs.make_case("tp8-shard", 200, seed=4)
     q4 = to_dev(c4["q"])
     pq, _ = Q.qknorm_partial_sumsq(q4)
     Q.qknorm_apply_with_stats(q4, to_dev(c4["gamma_q"]), pq, to_dev(c4["ext_q"]), 4096,
@@ -200,7 +200,7 @@ def test_partial_apply_edge_widths(Q):
 def test_concurrent_streams(Q):
     import torch
 
-    cases = [inputs.make_case(2, 2048, seed=s) for s in (31, 32)]
+    cases = [inputs.make_case("olmo2-7b", 2048, seed=s) for s in (31, 32)]
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]
     outs = []
     dev = [(to_dev(c["q"]), to_dev(c["gamma_q"]), to_dev(c["k"]), to_dev(c["gamma_k"]))

@@ -16,9 +16,9 @@ def test_graph_replays_match_eager():
         pytest.skip("no GPU")
     import layerwise_qk_norm_amd as Q
 
-    c2 = inputs.make_case(2, 512, seed=8)
-    c4 = inputs.make_case(4, 1000, seed=8)
-    c5 = inputs.make_case(5, 300, seed=8)
+    c2 = inputs.make_case("olmo2-7b", 512, seed=8)
+    c4 = inputs.make_case("tp8-shard", 1000, seed=8)
+    c5 = inputs.make_case("flashnorm-2048", 300, seed=8)
     q, k, gq, gk = (to_dev(c2[n]) for n in ("q", "k", "gamma_q", "gamma_k"))
     sq, sk, sgq, sgk = (to_dev(c4[n]) for n in ("q", "k", "gamma_q", "gamma_k"))
     eq, ek = to_dev(c4["ext_q"]), to_dev(c4["ext_k"])

@@ -43,21 +43,21 @@ def run_fused(Q, c, check=True):
 
 
 def test_fused_tiny_fp32(Q):
-    run_fused(Q, inputs.make_case(1, 64))
+    run_fused(Q, inputs.make_case("tiny-fp32", 64))
 
 
-@pytest.mark.parametrize("T", inputs.CONFIGS[2]["Ts"])
+@pytest.mark.parametrize("T", inputs.WORKLOADS["olmo2-7b"]["Ts"])
 def test_fused_olmo7b(Q, T):
-    run_fused(Q, inputs.make_case(2, T))
+    run_fused(Q, inputs.make_case("olmo2-7b", T))
 
 
-@pytest.mark.parametrize("T", inputs.CONFIGS[3]["Ts"])
+@pytest.mark.parametrize("T", inputs.WORKLOADS["gqa-olmo2-32b-like"]["Ts"])
 def test_fused_gqa_outliers(Q, T):
-    run_fused(Q, inputs.make_case(3, T))
+    run_fused(Q, inputs.make_case("gqa-olmo2-32b-like", T))
 
 
 def test_fused_deterministic(Q):
-    c = inputs.make_case(2, 1024, seed=5)
+    c = inputs.make_case("olmo2-7b", 1024, seed=5)
     a = run_fused(Q, c, check=False)
     b = run_fused(Q, c, check=False)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
@@ -67,7 +67,7 @@ def test_fused_deterministic(Q):
 def test_shard_stage_tp8(Q):
     """K1 partial sums, then K2 aggregation + scale, at T = 131072 (one 512-column slice of
     4096-wide Q and K, seven peers' partials generated)."""
-    c = inputs.make_case(4, 131072)
+    c = inputs.make_case("tp8-shard", 131072)
     q, k = to_dev(c["q"]), to_dev(c["k"])
     gq, gk = to_dev(c["gamma_q"]), to_dev(c["gamma_k"])
     eq, ek = to_dev(c["ext_q"]), to_dev(c["ext_k"])
@@ -100,7 +100,7 @@ def test_decomposition_matches_fused_on_gpu(Q):
     """Eight column slices of a 4096-wide row (views with ld = 4096): partials, aggregation
     with the other seven slices' partials, scale; equal to the fused launch within rounding."""
     torch = pytest.importorskip("torch")
-    c = inputs.make_case(2, 777, seed=3)
+    c = inputs.make_case("olmo2-7b", 777, seed=3)
     q, gq = to_dev(c["q"]), to_dev(c["gamma_q"])
     fused_q, _ = Q.qknorm_fused(q, gq, eps=c["eps"])
     parts = [Q.qknorm_partial_sumsq(q[:, 512 * s:512 * (s + 1)])[0] for s in range(8)]
@@ -118,7 +118,7 @@ def test_decomposition_matches_fused_on_gpu(Q):
 
 
 def test_apply_without_peers_is_local_norm(Q):
-    c = inputs.make_case(4, 300, seed=2)
+    c = inputs.make_case("tp8-shard", 300, seed=2)
     q, gq = to_dev(c["q"]), to_dev(c["gamma_q"])
     pq, _ = Q.qknorm_partial_sumsq(q)
     qo, _ = Q.qknorm_apply_with_stats(q, gq, pq, None, 512, eps=1e-6)
@@ -146,15 +146,15 @@ def projection_bound(x_bits, wf_bits, eps):
 
 
 def test_fold_weight_bit_exact(Q):
-    c = inputs.make_case(5, 1)
+    c = inputs.make_case("flashnorm-2048", 1)
     wf = Q.normproj_fold_weight(to_dev(c["w"]), to_dev(c["gamma"]))
     sync()
     assert np.array_equal(to_host(wf), folded_reference(c).T)
 
 
-@pytest.mark.parametrize("T", inputs.CONFIGS[5]["Ts"])
+@pytest.mark.parametrize("T", inputs.WORKLOADS["flashnorm-2048"]["Ts"])
 def test_normproj_deferred(Q, T):
-    c = inputs.make_case(5, T)
+    c = inputs.make_case("flashnorm-2048", T)
     wf_ref = folded_reference(c)
     wf = Q.normproj_fold_weight(to_dev(c["w"]), to_dev(c["gamma"]))
     y = Q.normproj_deferred(to_dev(c["x"]), wf, eps=c["eps"])
@@ -167,7 +167,7 @@ def test_normproj_deferred(Q, T):
 
 
 def test_normproj_unfused_baseline(Q):
-    c = inputs.make_case(5, 2048)
+    c = inputs.make_case("flashnorm-2048", 2048)
     x, g = to_dev(c["x"]), to_dev(c["gamma"])
     wp = Q.normproj_fold_weight(to_dev(c["w"]), None)
     sync()

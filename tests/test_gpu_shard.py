@@ -70,7 +70,7 @@ def check_all(got, ref, what, epoch):
 def test_shard_fused_prepublished_tp8(Q, persistent):
     """TP-8 shard at T = 131072: peers' partials published (same stream) before the pass, with
     the persistent grid and with one workgroup per row block."""
-    c = inputs.make_case(4, 131072)
+    c = inputs.make_case("tp8-shard", 131072)
     q, k, gq, gk = (to_dev(c[n]) for n in ("q", "k", "gamma_q", "gamma_k"))
     part_q, part_k = to_dev(c["ext_q"]), to_dev(c["ext_k"])
     mail_q, mail_k = Q.mailbox_words(7, 131072), Q.mailbox_words(7, 131072)
@@ -132,7 +132,7 @@ def test_shard_fused_concurrent_publisher(Q):
     stream of the same GPU while it runs (the pass leaves a quarter of the device free)."""
     import torch
 
-    c = inputs.make_case(4, 65536, seed=9)
+    c = inputs.make_case("tp8-shard", 65536, seed=9)
     q, k, gq, gk = (to_dev(c[n]) for n in ("q", "k", "gamma_q", "gamma_k"))
     part_q, part_k = to_dev(c["ext_q"]), to_dev(c["ext_k"])
     mail_q, mail_k = Q.mailbox_words(7, 65536), Q.mailbox_words(7, 65536)
@@ -155,7 +155,7 @@ def test_shard_fused_times_out(Q, stale, persistent):
     """Mailbox words that never carry the epoch (never written, or left at an older epoch):
     with a spin limit of 8 polls the pass records the timeout and still finishes; its own
     partials are right."""
-    c = inputs.make_case(4, 4096, seed=10)
+    c = inputs.make_case("tp8-shard", 4096, seed=10)
     mail_q = to_dev(host_words(c["ext_q"], stale))
     mail_k = to_dev(host_words(c["ext_k"], stale))
     to = zeros_i32(1)
@@ -172,7 +172,7 @@ def test_shard_fused_times_out(Q, stale, persistent):
 @pytest.mark.parametrize("persistent", [True, False])
 def test_shard_fused_epochs_advance(Q, persistent):
     """Two passes over the same mailboxes with successive epochs."""
-    c = inputs.make_case(4, 2000, seed=11)
+    c = inputs.make_case("tp8-shard", 2000, seed=11)
     q, k, gq, gk = (to_dev(c[n]) for n in ("q", "k", "gamma_q", "gamma_k"))
     part_q, part_k = to_dev(c["ext_q"]), to_dev(c["ext_k"])
     mail_q, mail_k = Q.mailbox_words(7, 2000), Q.mailbox_words(7, 2000)

@@ -7,25 +7,27 @@ from layerwise_qk_norm_amd import inputs
 
 
 def test_same_seed_same_bits():
-    a = inputs.make_case(2, 16, seed=0)
-    b = inputs.make_case(2, 16, seed=0)
-    c = inputs.make_case(2, 16, seed=1)
+    a = inputs.make_case("olmo2-7b", 16, seed=0)
+    b = inputs.make_case("olmo2-7b", 16, seed=0)
+    c = inputs.make_case("olmo2-7b", 16, seed=1)
     for key in ("q", "k", "gamma_q", "gamma_k"):
         assert np.array_equal(a[key], b[key])
     assert not np.array_equal(a["q"], c["q"])
 
 
 def test_weights_identical_across_T():
-    a = inputs.make_case(2, 1)
-    b = inputs.make_case(2, 256)
+    a = inputs.make_case("olmo2-7b", 1)
+    b = inputs.make_case("olmo2-7b", 256)
     assert np.array_equal(a["gamma_q"], b["gamma_q"])
     assert np.array_equal(a["q"][0], b["q"][0])
 
 
-@pytest.mark.parametrize("cfg,T", [(1, 64), (2, 256), (3, 512), (4, 4096), (5, 64)])
-def test_shapes_and_moments(cfg, T):
-    c = inputs.make_case(cfg, T)
-    if cfg == 5:
+@pytest.mark.parametrize("workload,T", [("tiny-fp32", 64), ("olmo2-7b", 256),
+                                        ("gqa-olmo2-32b-like", 512), ("tp8-shard", 4096),
+                                        ("flashnorm-2048", 64)])
+def test_shapes_and_moments(workload, T):
+    c = inputs.make_case(workload, T)
+    if workload == "flashnorm-2048":
         assert c["x"].shape == (T, 2048) and c["w"].shape == (2048, 2048)
         x = inputs.bf16_bits_to_f32(c["x"])
         w = inputs.bf16_bits_to_f32(c["w"])
@@ -33,20 +35,20 @@ def test_shapes_and_moments(cfg, T):
         return
     q = c["q"] if c["dtype"] == "f32" else inputs.bf16_bits_to_f32(c["q"])
     gq = c["gamma_q"] if c["gamma_dtype"] == "f32" else inputs.bf16_bits_to_f32(c["gamma_q"])
-    spec = inputs.CONFIGS[cfg]
+    spec = inputs.WORKLOADS[workload]
     assert q.shape == (T, spec["dq"])
     assert c["k"].shape == (T, spec["dk"])
-    sd = {1: 1.0, 2: 2.0, 3: None, 4: 1.0}[cfg]
+    sd = {"tiny-fp32": 1.0, "olmo2-7b": 2.0, "gqa-olmo2-32b-like": None, "tp8-shard": 1.0}[workload]
     if sd is not None:
         assert abs(q.std() / sd - 1.0) < 0.02
     assert abs(gq.mean() - 1.0) < 0.02
-    if cfg == 4:
+    if workload == "tp8-shard":
         assert c["ext_q"].shape == (7, T) and c["ext_q"].dtype == np.float32
         assert abs(c["ext_q"].mean() / 512.0 - 1.0) < 0.01
 
 
 def test_gqa_outlier_columns():
-    c = inputs.make_case(3, 512)
+    c = inputs.make_case("gqa-olmo2-32b-like", 512)
     q = inputs.bf16_bits_to_f32(c["q"])
     cols = c["outlier_cols_q"]
     assert cols.size == 51 and c["outlier_cols_k"].size == 10
