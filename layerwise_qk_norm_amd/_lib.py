@@ -13,7 +13,9 @@ import os
 import re
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libqknorm.so")
+# QKN_LIBRARY selects another build of the same C ABI (for instance a host-only build under the
+# sanitizers); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("QKN_LIBRARY") or os.path.join(PKG, "libqknorm.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "qknorm.h")
 
 QKN_F32, QKN_BF16 = 0, 1
