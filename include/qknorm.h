@@ -13,10 +13,12 @@
  * Conventions shared by every call:
  *   - Tensors are row-major [T, d] with a row stride ld (in elements, ld >= d).
  *   - Every pointer argument is a DEVICE pointer that the caller allocates and owns; the
- *     library allocates no memory and keeps no workspace between calls.
+ *     library allocates no memory. It keeps no workspace between calls, except the one
+ *     device array per GPU that normproj_deferred_layernorm_noalloc uses.
  *   - `stream` is a hipStream_t passed as void*; NULL selects the null stream. Calls enqueue
  *     work and return; they never synchronise the host. There is no global mutable state
- *     except a thread-local copy of the last HIP error, so calls are thread-safe.
+ *     except a thread-local copy of the last HIP error (and the device addresses of that
+ *     array, looked up once per GPU under a lock), so calls are thread-safe.
  *   - dtype codes: QKN_F32 (float) and QKN_BF16 (bfloat16). Outputs have the input's dtype;
  *     arithmetic is fp32 with one rounding at the output (round to nearest even for bf16).
  *   - Arguments are validated before any HIP call; a non-zero status is returned without
@@ -52,7 +54,8 @@ enum {
     QKN_ERR_EPS = 4,   /* eps is negative, NaN or infinite                               */
     QKN_ERR_ALIAS = 5, /* an output partially overlaps an input or another output        */
     QKN_ERR_ALIGN = 6, /* 16-byte alignment required and not met                         */
-    QKN_ERR_HIP = 7    /* the HIP runtime reported an error; see qkn_last_hip_error()    */
+    QKN_ERR_HIP = 7,   /* the HIP runtime reported an error; see qkn_last_hip_error()    */
+    QKN_ERR_SCRATCH = 8 /* the input exceeds the static workspace of a *_noalloc call     */
 };
 
 /*
@@ -260,6 +263,26 @@ QKN_API int normproj_deferred_layernorm(int64_t T, int64_t K, int64_t N, float e
                                         const void* x, int64_t ldx, const void* w_fold,
                                         int64_t ldw, const float* colsum, const float* bias,
                                         void* y, int64_t ldy, float* row_stats, void* stream);
+
+/*
+ * normproj_deferred_layernorm_noalloc - normproj_deferred_layernorm for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc) and have no workspace of their own to pass.
+ *
+ * Computes exactly what normproj_deferred_layernorm computes with a row_stats workspace (the
+ * same kernels and results), with the workspace taken from a device array the library holds:
+ * 2 * 131072 fp32 (1 MiB) per GPU, kept until the process ends. It calls no allocator.
+ *   T           at most 131072 rows (QKN_ERR_SCRATCH beyond; nothing is launched)
+ * Every call on one GPU shares that GPU's array and overwrites it before reading it, so calls
+ * that overlap in time on one GPU (other streams, other threads) race and must be ordered by
+ * the caller. The first call on a device looks up the array's device address (a HIP call).
+ * Other arguments and rules as normproj_deferred_layernorm.
+ */
+QKN_API int normproj_deferred_layernorm_noalloc(int64_t T, int64_t K, int64_t N, float eps,
+                                                int dtype, const void* x, int64_t ldx,
+                                                const void* w_fold, int64_t ldw,
+                                                const float* colsum, const float* bias, void* y,
+                                                int64_t ldy, void* stream);
 
 /*
  * normproj_layernorm_unfused - LayerNorm launch then plain projection (measured baseline).

@@ -20,7 +20,8 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "qknorm.h")
 
 QKN_F32, QKN_BF16 = 0, 1
 STATUS = {0: "QKN_OK", 1: "QKN_ERR_NULL", 2: "QKN_ERR_SHAPE", 3: "QKN_ERR_DTYPE",
-          4: "QKN_ERR_EPS", 5: "QKN_ERR_ALIAS", 6: "QKN_ERR_ALIGN", 7: "QKN_ERR_HIP"}
+          4: "QKN_ERR_EPS", 5: "QKN_ERR_ALIAS", 6: "QKN_ERR_ALIGN", 7: "QKN_ERR_HIP",
+          8: "QKN_ERR_SCRATCH"}
 
 
 class QknError(RuntimeError):
@@ -48,6 +49,8 @@ _PROTOS = {
                                 _vp],
     "normproj_deferred_layernorm": [_i64, _i64, _i64, _f32, _int, _vp, _i64, _vp, _i64, _vp, _vp,
                                     _vp, _i64, _vp, _vp],
+    "normproj_deferred_layernorm_noalloc": [_i64, _i64, _i64, _f32, _int, _vp, _i64, _vp, _i64,
+                                            _vp, _vp, _vp, _i64, _vp],
     "normproj_layernorm_unfused": [_i64, _i64, _i64, _f32, _int, _int, _vp, _i64, _vp, _vp, _vp,
                                    _i64, _vp, _i64, _vp, _i64, _vp],
     "qknorm_project_eliminated": [_i64, _i64, _i64, _i64, _f32, _f32, _int, _int, _vp, _i64, _vp,
@@ -461,6 +464,28 @@ def normproj_deferred_layernorm(x, w_fold, colsum, bias=None, eps: float = 1e-5,
     _check("normproj_deferred_layernorm", lib().normproj_deferred_layernorm(
         T, K, N, float(eps), _dtype_code(x), _ptr(x), _ld(x), _ptr(w_fold), _ld(w_fold),
         _ptr(colsum), _ptr(bias), _ptr(y), _ld(y), _ptr(row_stats), _stream(x)))
+    return y
+
+
+def normproj_deferred_layernorm_noalloc(x, w_fold, colsum, bias=None, eps: float = 1e-5, y=None):
+    """normproj_deferred_layernorm with the row statistics in the library's own static device
+    workspace (at most 131072 rows); the C call allocates nothing. Pass y to allocate nothing
+    here either."""
+    torch = _torch()
+    _check_device(x, w_fold, colsum, bias, y)
+    T, K = x.shape
+    N = w_fold.shape[0]
+    if y is None:
+        y = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    _vec(colsum, N, "colsum")
+    _vec(bias, N, "bias")
+    _dtypes(torch.bfloat16, "w_fold and y", w_fold, y)
+    _dtypes(torch.float32, "colsum and bias", colsum, bias)
+    _mat(w_fold, N, K, "w_fold")
+    _mat(y, T, N, "y")
+    _check("normproj_deferred_layernorm_noalloc", lib().normproj_deferred_layernorm_noalloc(
+        T, K, N, float(eps), _dtype_code(x), _ptr(x), _ld(x), _ptr(w_fold), _ld(w_fold),
+        _ptr(colsum), _ptr(bias), _ptr(y), _ld(y), _stream(x)))
     return y
 
 

@@ -3,11 +3,20 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/qknorm.h"
 #include "launch.h"
+
+// Workspace of normproj_deferred_layernorm_noalloc: (mean, 1/std) of up to kNoallocRows rows,
+// one copy per GPU for the life of the process. Host code never passes `scratch` itself to a
+// kernel (on the host the name stands for a host-side shadow): it uses the device address
+// hipGetSymbolAddress returns, looked up once per device on the first call made on it.
+constexpr int64_t kNoallocRows = 131072;
+static __device__ __align__(256) float scratch[2 * kNoallocRows];
 
 namespace {
 
@@ -96,6 +105,7 @@ QKN_API const char* qkn_status_string(int status)
     case QKN_ERR_ALIAS: return "an output partially overlaps an input or another output";
     case QKN_ERR_ALIGN: return "16-byte alignment required";
     case QKN_ERR_HIP: return "HIP runtime error (see qkn_last_hip_error)";
+    case QKN_ERR_SCRATCH: return "the input exceeds the library's static workspace";
     default: return "unknown status";
     }
 }
@@ -487,10 +497,13 @@ QKN_API int normproj_fold_layernorm(int64_t K, int64_t N, int dtype, int gamma_d
                                              colsum, bias, (hipStream_t)stream));
 }
 
-QKN_API int normproj_deferred_layernorm(int64_t T, int64_t K, int64_t N, float eps, int dtype,
-                                        const void* x, int64_t ldx, const void* w_fold,
-                                        int64_t ldw, const float* colsum, const float* bias,
-                                        void* y, int64_t ldy, float* row_stats, void* stream)
+namespace {
+
+// Checks of deferred LayerNorm, the optional row-statistics workspace included.
+int check_deferred_layernorm(int64_t T, int64_t K, int64_t N, float eps, int dtype,
+                             const void* x, int64_t ldx, const void* w_fold, int64_t ldw,
+                             const float* colsum, const float* bias, const void* y, int64_t ldy,
+                             const float* row_stats)
 {
     const int st = check_normproj(T, K, N, eps, dtype, x, ldx, w_fold, ldw, y, ldy);
     if (st != QKN_OK || T == 0 || N == 0) return st;
@@ -507,6 +520,16 @@ QKN_API int normproj_deferred_layernorm(int64_t T, int64_t K, int64_t N, float e
             (bias && overlap(rs, rb)))
             return QKN_ERR_ALIAS;
     }
+    return QKN_OK;
+}
+
+// Deferred LayerNorm after its checks: the statistics pass into row_stats and the product that
+// applies them, or (no workspace, or a shape the pass does not serve) the product alone.
+int run_deferred_layernorm(int64_t T, int64_t K, int64_t N, float eps, const void* x,
+                           int64_t ldx, const void* w_fold, int64_t ldw, const float* colsum,
+                           const float* bias, void* y, int64_t ldy, float* row_stats,
+                           void* stream)
+{
     const hipStream_t s = (hipStream_t)stream;
     if (row_stats && qkn::normproj_pipelined(T, K, N, ldx, ldw, ldy, y)) {
         // statistics from one streaming pass over x; the product applies them in its epilogue
@@ -517,6 +540,74 @@ QKN_API int normproj_deferred_layernorm(int64_t T, int64_t K, int64_t N, float e
     }
     return hip_status(qkn::launch_normproj(T, K, N, eps, qkn::kEpiLayerNorm, x, ldx, w_fold, ldw,
                                            y, ldy, colsum, bias, nullptr, s));
+}
+
+constexpr int kMaxDevices = 256;
+std::atomic<float*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the device that owns `stream` (the current device for the
+// null stream).
+int noalloc_scratch(void* stream, float** out)
+{
+    int dev = 0;
+    hipError_t e = stream ? hipStreamGetDevice((hipStream_t)stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (dev < 0 || dev >= kMaxDevices) return hip_status(hipErrorInvalidDevice);
+    float* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            int cur = 0;
+            e = hipGetDevice(&cur);
+            if (e != hipSuccess) return hip_status(e);
+            if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_status(e);
+            void* addr = nullptr;
+            e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+            if (cur != dev) {
+                const hipError_t e2 = hipSetDevice(cur);
+                if (e == hipSuccess) e = e2;
+            }
+            if (e != hipSuccess) return hip_status(e);
+            if (addr == nullptr) return hip_status(hipErrorInvalidSymbol);
+            p = (float*)addr;
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return QKN_OK;
+}
+
+}  // namespace
+
+QKN_API int normproj_deferred_layernorm(int64_t T, int64_t K, int64_t N, float eps, int dtype,
+                                        const void* x, int64_t ldx, const void* w_fold,
+                                        int64_t ldw, const float* colsum, const float* bias,
+                                        void* y, int64_t ldy, float* row_stats, void* stream)
+{
+    const int st = check_deferred_layernorm(T, K, N, eps, dtype, x, ldx, w_fold, ldw, colsum,
+                                            bias, y, ldy, row_stats);
+    if (st != QKN_OK || T == 0 || N == 0) return st;
+    return run_deferred_layernorm(T, K, N, eps, x, ldx, w_fold, ldw, colsum, bias, y, ldy,
+                                  row_stats, stream);
+}
+
+QKN_API int normproj_deferred_layernorm_noalloc(int64_t T, int64_t K, int64_t N, float eps,
+                                                int dtype, const void* x, int64_t ldx,
+                                                const void* w_fold, int64_t ldw,
+                                                const float* colsum, const float* bias, void* y,
+                                                int64_t ldy, void* stream)
+{
+    int st = check_deferred_layernorm(T, K, N, eps, dtype, x, ldx, w_fold, ldw, colsum, bias, y,
+                                      ldy, nullptr);
+    if (st != QKN_OK || T == 0 || N == 0) return st;
+    if (T > kNoallocRows) return QKN_ERR_SCRATCH;
+    float* ws = nullptr;
+    st = noalloc_scratch(stream, &ws);
+    if (st != QKN_OK) return st;
+    return run_deferred_layernorm(T, K, N, eps, x, ldx, w_fold, ldw, colsum, bias, y, ldy, ws,
+                                  stream);
 }
 
 QKN_API int normproj_layernorm_unfused(int64_t T, int64_t K, int64_t N, float eps, int dtype,

@@ -1,7 +1,8 @@
 // Host-only stand-ins for the kernel launchers of libqknorm.so, used to build the C-ABI layer
 // (api.cpp) with the host compiler under AddressSanitizer and UndefinedBehaviorSanitizer. Each
 // launcher answers as the real one does on a machine without a GPU: hipErrorNoDevice. Nothing
-// here runs device code; only argument validation and dispatch in api.cpp are exercised.
+// here runs device code; only argument validation and dispatch in api.cpp are exercised, and the
+// few HIP runtime calls api.cpp makes itself are answered the same way.
 #include "../../layerwise_qk_norm_amd/csrc/launch.h"
 
 namespace qkn {
@@ -46,3 +47,12 @@ hipError_t launch_shard_publish(int64_t, int64_t, int, const float* const*, cons
 }
 
 }  // namespace qkn
+
+// The HIP runtime calls api.cpp makes itself (the static workspace's address lookup), answered
+// as without a device.
+extern "C" {
+hipError_t hipGetDevice(int*) { return hipErrorNoDevice; }
+hipError_t hipSetDevice(int) { return hipErrorNoDevice; }
+hipError_t hipStreamGetDevice(hipStream_t, hipDevice_t*) { return hipErrorNoDevice; }
+hipError_t hipGetSymbolAddress(void**, const void*) { return hipErrorNoDevice; }
+}

@@ -11,7 +11,7 @@ import pytest
 
 from layerwise_qk_norm_amd import _lib
 
-OK, NULL, SHAPE, DTYPE, EPS, ALIAS, ALIGN, HIPERR = range(8)
+OK, NULL, SHAPE, DTYPE, EPS, ALIAS, ALIGN, HIPERR, SCRATCH = range(9)
 F32, BF16 = 0, 1
 
 
@@ -42,6 +42,7 @@ def test_exports_every_declared_symbol(L):
                           "qknorm_shard_fused", "qknorm_shard_publish",
                           "normproj_fold_layernorm", "normproj_deferred_layernorm",
                           "normproj_layernorm_unfused", "qknorm_project_eliminated",
+                          "normproj_deferred_layernorm_noalloc",
                           "qknorm_project_unfused"}
     for n in names:
         assert hasattr(L, n), n
@@ -57,8 +58,8 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for s in range(8):
-        assert L.qkn_status_string(s)
+    for s in range(9):
+        assert L.qkn_status_string(s) != b"unknown status"
     assert L.qkn_status_string(99) == b"unknown status"
     assert L.qkn_last_hip_error() == 0
 
@@ -185,6 +186,16 @@ def test_layernorm_projection_validation(L):
     assert P(4, 16, 16, 1e-5, BF16, A, 16, B, 16, C, D, G1, 16, C + 16, None) == ALIAS  # colsum
     assert P(4, 16, 16, 1e-5, BF16, A, 16, B, 16, C, D, G1, 16, D, None) == ALIAS      # bias
     assert P(0, 16, 16, 1e-5, BF16, None, 16, None, 16, None, None, None, 16, None, None) == OK
+    # the variant with the library's static workspace: the same checks, then its size limit
+    # (131072 rows) before any HIP call; within it, the lookup of the workspace finds no device
+    S = L.normproj_deferred_layernorm_noalloc
+    assert S(4, 16, 16, 1e-5, F32, A, 16, B, 16, C, D, G1, 16, None) == DTYPE
+    assert S(4, 16, 16, -1.0, BF16, A, 16, B, 16, C, D, G1, 16, None) == EPS
+    assert S(4, 16, 16, 1e-5, BF16, A, 16, B, 16, None, D, G1, 16, None) == NULL
+    assert S(4, 16, 16, 1e-5, BF16, A, 16, B, 16, C, D, C, 16, None) == ALIAS
+    assert S(0, 16, 16, 1e-5, BF16, None, 16, None, 16, None, None, None, 16, None) == OK
+    assert S(131073, 16, 16, 1e-5, BF16, A, 16, B, 16, C, D, G1, 16, None) == SCRATCH
+    assert S(131072, 16, 16, 1e-5, BF16, A, 16, B, 16, C, D, G1, 16, None) == HIPERR
     U = L.normproj_layernorm_unfused
     assert U(4, 16, 16, 1e-5, BF16, BF16, A, 16, G1, G2, B, 16, A, 16, C, 16, None) == ALIAS
     assert U(4, 16, 16, 1e-5, BF16, BF16, A, 16, G1, G2, B, 16, None, 16, C, 16, None) == NULL

@@ -32,7 +32,10 @@ def _gpu_present() -> bool:
 def build_sanitized(out_dir: str) -> str:
     """Compile api.cpp and the launcher stand-ins with g++ and the sanitizers; return the .so."""
     rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    # the two spellings hipcc's device-side headers would define: the alignment attribute and
+    # the symbol of a device variable as the host names it
     common = ["g++", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-D__HIP_PLATFORM_AMD__",
+              "-D__align__(n)=__attribute__((aligned(n)))", "-DHIP_SYMBOL(X)=X",
               "-I", os.path.join(rocm, "include"), "-I", os.path.join(ROOT, "include"), *SAN]
     objs = []
     for src, name in ((os.path.join(CSRC, "api.cpp"), "api.o"),
