@@ -209,7 +209,7 @@ def normproj_setup(torch, Q, inputs, T, unfused=False):
     c = inputs.make_case("flashnorm-2048", T)
     x, w, g = dev(torch, c["x"]), dev(torch, c["w"]), dev(torch, c["gamma"])
     K, N = w.shape
-    wm = Q.normproj_fold_weight(w, None) if unfused else Q.normproj_fold_weight(w, g)
+    wm = w if unfused else Q.normproj_fold_weight(w, g)
     n = rotation_count(T * (K + N) * 2 + K * N * 2 + (T * K * 2 if unfused else 0))
     sets = [(x.clone(), torch.empty((T, N), dtype=torch.bfloat16, device="cuda"),
              torch.empty((T, K), dtype=torch.bfloat16, device="cuda") if unfused else None,
@@ -238,7 +238,7 @@ def elimination_setup(torch, Q, inputs, T, mode):
     x, w = dev(torch, c["x"]), dev(torch, c["w"])
     g1, gq, gk = dev(torch, c["gamma_pre"]), dev(torch, c["gamma_q"]), dev(torch, c["gamma_k"])
     K, N, nq = c["K"], c["nq"] + c["nk"], c["nq"]
-    wm = Q.normproj_fold_weight(w, None if mode == "unfused" else g1)
+    wm = w if mode == "unfused" else Q.normproj_fold_weight(w, g1)
     del w
     n = rotation_count(T * (K + N) * 2 + K * N * 2 + (T * K * 2 if mode == "unfused" else 0))
     sets = [(x.clone(), torch.empty((T, N), dtype=torch.bfloat16, device="cuda"),
@@ -268,7 +268,7 @@ def layernorm_setup(torch, Q, inputs, T, unfused, in_product=False):
     g, be = dev(torch, c["gamma"]), dev(torch, c["beta"])
     K, N = c["K"], c["N"]
     if unfused:
-        wm, cs, b = Q.normproj_fold_weight(w, None), None, None
+        wm, cs, b = w, None, None
     else:
         wm, cs, b = Q.normproj_fold_layernorm(w, g, be)
     n = rotation_count(T * (K + N) * 2 + K * N * 2 + (T * K * 2 if unfused else 0))
@@ -300,39 +300,113 @@ def time_case(timer, fn, iters, warmup):
 
 
 # ----------------------------------------------------------------------------- CPU baseline
-def cpu_baseline(inputs, T_full, budget_s=10.0):
-    """The fp64 oracle on the host, as it stands, on a bounded sample of the workload: the first
-    1024 tokens of Q and K. Timed once on one thread, then with the sample's rows split over
-    the host cores this process may use (at most 16, the host share of one GPU), each thread
-    calling the unmodified oracle on its rows (the C oracle releases the interpreter lock)."""
-    import oracle
+def host_cores():
+    """(threads used, cores in this process's affinity mask). The threads are every core of the
+    affinity mask, capped by the host share the machine allots per GPU when it states one in
+    OMP_NUM_THREADS (16 on the GPU machines this runs on)."""
+    affinity = len(os.sched_getaffinity(0))
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    cap = int(share) if share.isdigit() and int(share) > 0 else affinity
+    return max(1, min(affinity, cap)), affinity
+
+
+def oracle_timer(fn, rows_total, threads, min_seconds=0.3, reps=3):
+    """Seconds per pass of fn over rows [0, rows_total), the rows split into `threads` equal
+    chunks run concurrently (the C oracle releases the interpreter lock): the best of `reps`
+    passes, or of as many as fit min_seconds when a pass is short."""
     from concurrent.futures import ThreadPoolExecutor
 
-    c = inputs.make_case("olmo2-7b", 1024)
+    bounds = [(i * rows_total // threads, (i + 1) * rows_total // threads)
+              for i in range(threads)]
+    bounds = [b for b in bounds if b[1] > b[0]]
+    best, t_all, n = float("inf"), time.perf_counter(), 0
+    with ThreadPoolExecutor(max_workers=len(bounds)) as ex:
+        while n < reps or time.perf_counter() - t_all < min_seconds:
+            t0 = time.perf_counter()
+            list(ex.map(lambda b: fn(b[0], b[1]), bounds))
+            best = min(best, time.perf_counter() - t0)
+            n += 1
+            if n >= 50:
+                break
+    return best
 
-    def one(rows):
-        oracle.rmsnorm_rows(c["q"][rows], c["gamma_q"], c["eps"])
-        oracle.rmsnorm_rows(c["k"][rows], c["gamma_k"], c["eps"])
 
-    def timed(threads, seconds):
-        chunks = [slice(i * 1024 // threads, (i + 1) * 1024 // threads) for i in range(threads)]
-        done, t0 = 0, time.perf_counter()
-        with ThreadPoolExecutor(max_workers=threads) as ex:
-            while True:
-                list(ex.map(one, chunks))
-                done += 1024
-                el = time.perf_counter() - t0
-                if el >= seconds:
-                    return done / el, done // 1024, el
+def cpu_oracle_cases(inputs, threads, row_budget_s=1.0):
+    """The fp64 oracle, as it stands, on every workload and token count, on one thread and on
+    `threads` threads. Row operations run on all T rows; the projection's oracle (about
+    2 K N flops per row in naive fp64) runs on a sample of rows sized to about row_budget_s on
+    one thread, and its per-call time is scaled per row to T ("extrapolated")."""
+    import oracle
 
-    single, p1, e1 = timed(1, budget_s / 2)
-    cores = max(1, min(16, len(os.sched_getaffinity(0))))
-    multi, pn, en = timed(cores, budget_s / 2)
-    return {"value": multi, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"first 1024 tokens of Q and K [T, 4096] bf16 (of T={T_full}), fp64 "
-                      f"oracle, rows split over {cores} threads, {pn} passes in {en:.1f} s",
-            "single_thread_value": single,
-            "single_thread_sample": f"same sample, 1 thread, {p1} passes in {e1:.1f} s",
+    out = []
+
+    def add(cfg, T, nthreads, sec, rows_timed, what):
+        rec = {"case": f"oracle {what} {cfg} T={T}", "config": cfg, "T": T, "threads": nthreads,
+               "us_per_call": sec * 1e6, "tokens_per_s": T / sec if sec > 0 else None,
+               "rows_timed": rows_timed}
+        if rows_timed < T:
+            rec["extrapolated"] = f"timed on {rows_timed} of {T} rows, scaled per row"
+        out.append(rec)
+
+    for cfg, Ts in (("tiny-fp32", (64,)), ("olmo2-7b", (1, 16, 256, 4096, 8192)),
+                    ("gqa-olmo2-32b-like", (1, 512, 8192))):
+        for T in Ts:
+            c = inputs.make_case(cfg, T)
+
+            def fused(lo, hi, c=c):
+                oracle.rmsnorm_rows(c["q"][lo:hi], c["gamma_q"], c["eps"])
+                oracle.rmsnorm_rows(c["k"][lo:hi], c["gamma_k"], c["eps"])
+
+            for nt in sorted({1, threads}):
+                add(cfg, T, nt, oracle_timer(fused, T, min(nt, T)), T, "rmsnorm Q+K")
+    c = inputs.make_case("tp8-shard", 131072)
+    T = 131072
+
+    def shard(lo, hi):
+        pq = oracle.partial_sumsq(c["q"][lo:hi])
+        pk = oracle.partial_sumsq(c["k"][lo:hi])
+        oracle.apply_with_stats(c["q"][lo:hi], c["gamma_q"], pq, c["ext_q"][:, lo:hi], 4096,
+                                c["eps"])
+        oracle.apply_with_stats(c["k"][lo:hi], c["gamma_k"], pk, c["ext_k"][:, lo:hi], 4096,
+                                c["eps"])
+
+    for nt in sorted({1, threads}):
+        add("tp8-shard", T, nt, oracle_timer(shard, T, nt, reps=1), T,
+            "partial sums + aggregation and scale")
+    c = inputs.make_case("flashnorm-2048", 64)
+    wf = oracle.round_bf16(oracle.fold_weight(c["w"], c["gamma"]))
+    t0 = time.perf_counter()
+    oracle.normproj(c["x"][:1], wf, c["eps"])
+    per_row = max(time.perf_counter() - t0, 1e-6)
+    for T in inputs.WORKLOADS["flashnorm-2048"]["Ts"]:
+        for nt in sorted({1, threads}):
+            rows = max(1, min(T, nt * max(1, int(row_budget_s / per_row)), 64 * nt))
+            cx = inputs.make_case("flashnorm-2048", rows) if rows > 64 else c
+
+            def proj(lo, hi, cx=cx):
+                oracle.normproj(cx["x"][lo:hi], wf, cx["eps"])
+
+            sec = oracle_timer(proj, rows, min(nt, rows), min_seconds=0.0, reps=1)
+            add("flashnorm-2048", T, nt, sec * T / rows, rows, "deferred projection")
+    return out
+
+
+def cpu_baseline(cases, threads, T_full):
+    """The headline's CPU figure: the oracle of the fused Q+K norm on the whole headline
+    workload on `threads` threads (with the one-thread figure beside it)."""
+    multi = [c for c in cases if c["config"] == "olmo2-7b" and c["T"] == T_full and
+             c["threads"] == threads]
+    single = [c for c in cases if c["config"] == "olmo2-7b" and c["T"] == T_full and
+              c["threads"] == 1]
+    if not multi:
+        return None
+    _, affinity = host_cores()
+    return {"value": multi[0]["tokens_per_s"], "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"all {T_full} tokens of Q and K [{T_full}, 4096] bf16 (the headline "
+                      f"workload), fp64 oracle, rows split over {threads} threads, best pass",
+            "affinity_cores": affinity,
+            "single_thread_value": single[0]["tokens_per_s"] if single else None,
             "cpu_model": cpu_model()}
 
 
@@ -345,25 +419,6 @@ def cpu_model():
     except OSError:
         pass
     return "unknown"
-
-
-def cpu_oracle_projection(inputs, rows=32):
-    """The fp64 oracle of the deferred projection (FlashNorm shape, K = N = 2048) on the first
-    `rows` tokens, one thread, best of 3; per-call times at the benchmarked T are extrapolated
-    per row and labelled so."""
-    import oracle
-
-    c = inputs.make_case("flashnorm-2048", rows)
-    wf = oracle.round_bf16(oracle.fold_weight(c["w"], c["gamma"]))
-    best = float("inf")
-    for _ in range(3):
-        t0 = time.perf_counter()
-        oracle.normproj(c["x"], wf, c["eps"])
-        best = min(best, time.perf_counter() - t0)
-    per_row = best / rows
-    return [{"case": f"oracle normproj flashnorm-2048 T={t} (extrapolated from {rows} rows, 1 thread)",
-             "us_per_call": per_row * t * 1e6}
-            for t in inputs.WORKLOADS["flashnorm-2048"]["Ts"] if t > 1]
 
 
 # ----------------------------------------------------------------------------- main
@@ -381,7 +436,6 @@ def main():
                     help="comma-separated token counts: per-workload cases at these T only")
     ap.add_argument("--case-iters", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calib-copies", type=int, default=0,
                     help="after the timed region, run this many qkn_device_copy launches of "
                          "half the headline's algorithmic bytes (memory-counter calibration)")
@@ -538,9 +592,27 @@ def main():
         for cs in cases:
             print("# " + json.dumps(cs), file=sys.stderr, flush=True)
 
-    cpu = None if args.no_cpu_baseline else cpu_baseline(inputs, T, args.cpu_seconds)
-    cpu_cases = (cpu_oracle_projection(inputs) if cpu is not None and args.cases == "all"
-                 and not args.only else [])
+    cpu, cpu_cases = None, []
+    if not args.no_cpu_baseline:
+        threads, _ = host_cores()
+        if T == 8192:
+            cpu_cases = cpu_oracle_cases(inputs, threads)
+        else:
+            cpu_cases = []
+            c = inputs.make_case("olmo2-7b", T)
+            import oracle
+
+            def fused(lo, hi):
+                oracle.rmsnorm_rows(c["q"][lo:hi], c["gamma_q"], c["eps"])
+                oracle.rmsnorm_rows(c["k"][lo:hi], c["gamma_k"], c["eps"])
+
+            for nt in sorted({1, threads}):
+                sec = oracle_timer(fused, T, min(nt, T))
+                cpu_cases.append({"case": f"oracle rmsnorm Q+K olmo2-7b T={T}",
+                                  "config": "olmo2-7b", "T": T, "threads": nt,
+                                  "us_per_call": sec * 1e6, "tokens_per_s": T / sec,
+                                  "rows_timed": T})
+        cpu = cpu_baseline(cpu_cases, threads, T)
 
     out = {
         "metric": METRIC,

@@ -27,9 +27,12 @@
  *   - An output may alias its own input exactly (same pointer, same ld): the row is read in
  *     full before it is written. Any other overlap between an output and an input or another
  *     output is QKN_ERR_ALIAS.
- *   - Misaligned pointers or strides are accepted by the row operations (a scalar-load path
- *     runs instead of the 16-byte one). The norm-then-project calls need 16-byte aligned
- *     rows (QKN_ERR_ALIGN otherwise).
+ *   - Misaligned pointers and strides are accepted: 16-byte accesses run where every operand
+ *     allows them, element accesses otherwise (the norm-then-project calls only require bf16
+ *     pointers to be 2-byte aligned). The single-launch shard stage (qknorm_shard_fused) is
+ *     the one call that requires 16-byte alignment (QKN_ERR_ALIGN).
+ *   - Projection weights (W, the folded W', the stacked Q/K weights) are row-major [K, N] with
+ *     row stride ldw >= N, the layout y = x W reads them in.
  *   - Results are deterministic: fixed reduction orders, no atomic read-modify-write (the shard
  *     mailbox words are plain device-coherent 64-bit stores and loads).
  */
@@ -53,7 +56,7 @@ enum {
     QKN_ERR_DTYPE = 3, /* unknown dtype code, or a dtype the operation does not support */
     QKN_ERR_EPS = 4,   /* eps is negative, NaN or infinite                               */
     QKN_ERR_ALIAS = 5, /* an output partially overlaps an input or another output        */
-    QKN_ERR_ALIGN = 6, /* 16-byte alignment required and not met                         */
+    QKN_ERR_ALIGN = 6, /* a pointer is not aligned to what the call requires            */
     QKN_ERR_HIP = 7,   /* the HIP runtime reported an error; see qkn_last_hip_error()    */
     QKN_ERR_SCRATCH = 8 /* the input exceeds the static workspace of a *_noalloc call     */
 };
@@ -178,13 +181,12 @@ QKN_API int qknorm_shard_publish(int64_t T, int64_t n_ext, const float* part_q, 
  *
  * ("FlashNorm: Fast Normalization for Transformers", abstract, item (i).)
  * For the projection y = x W with W [K, N] row-major (stride ldw >= N):
- *   w_fold[n * ldw_fold + k] = bf16( gamma[k] * W[k, n] )     (fp32 product, one rounding)
- * i.e. W' = diag(gamma) W is written TRANSPOSED, [N, K] with K contiguous, the layout the
- * matrix-core kernel of normproj_deferred reads. gamma == NULL means gamma = 1 (a plain
- * re-layout, used to pack the unfolded weight of the unfused baseline).
+ *   w_fold[k * ldw_fold + n] = bf16( gamma[k] * W[k, n] )     (fp32 product, one rounding)
+ * i.e. W' = diag(gamma) W in the layout of W, [K, N] row-major (stride ldw_fold >= N), the
+ * operand normproj_deferred takes. gamma == NULL means gamma = 1 (a plain copy). w_fold may be
+ * w itself with the same stride (in place); any other overlap is QKN_ERR_ALIAS.
  *   dtype       storage of W and w_fold: QKN_BF16 only
  *   gamma_dtype QKN_F32 or QKN_BF16
- *   ldw_fold    >= K, a multiple of 8; w_fold 16-byte aligned (QKN_ERR_ALIGN otherwise)
  */
 QKN_API int normproj_fold_weight(int64_t K, int64_t N, int dtype, int gamma_dtype,
                                  const void* w, int64_t ldw, const void* gamma,
@@ -196,13 +198,15 @@ QKN_API int normproj_fold_weight(int64_t K, int64_t N, int dtype, int gamma_dtyp
  * ("FlashNorm: ...", abstract, item (ii): the scalar 1/RMS is applied to the output of the
  * matrix product, so the reduction and the product proceed together.) For t < T, n < N:
  *   r_t     = 1 / sqrt( (1/K) sum_k x[t,k]^2 + eps )         (fp32, from the same x tiles)
- *   y[t,n]  = bf16( r_t * sum_k x[t,k] * w_fold[n,k] )        (bf16 products, fp32 accumulate)
- *   x       [T, K] bf16, stride ldx
- *   w_fold  [N, K] bf16 from normproj_fold_weight, stride ldw
- *   y       [T, N] bf16, stride ldy; must not overlap x or w_fold
+ *   y[t,n]  = bf16( r_t * sum_k x[t,k] * w_fold[k,n] )        (bf16 products, fp32 accumulate)
+ *   x       [T, K] bf16, stride ldx >= K
+ *   w_fold  W' [K, N] bf16 row-major (e.g. from normproj_fold_weight), stride ldw >= N
+ *   y       [T, N] bf16, stride ldy >= N; must not overlap x or w_fold
  *   dtype   QKN_BF16 only
- * K, ldx and ldw must be multiples of 8 and x, w_fold 16-byte aligned (QKN_ERR_ALIGN).
- * T <= 16 runs a streaming matrix-vector kernel; larger T runs the matrix-core (MFMA) kernel.
+ * Any K, strides and 2-byte-aligned pointers. With K, ldx, ldw (and N, for T > 16) multiples
+ * of 8 and x, w_fold 16-byte aligned, T <= 16 runs a streaming matrix-vector kernel and larger
+ * T the pipelined matrix-core (MFMA) kernels; other operands take an element-load
+ * matrix-core kernel.
  */
 QKN_API int normproj_deferred(int64_t T, int64_t K, int64_t N, float eps, int dtype,
                               const void* x, int64_t ldx, const void* w_fold, int64_t ldw,
@@ -213,14 +217,14 @@ QKN_API int normproj_deferred(int64_t T, int64_t K, int64_t N, float eps, int dt
  *
  * ("FlashNorm: ...", abstract: the RMS reduction blocks the following product.)
  *   xn[t,k] = bf16( x[t,k] * gamma[k] * r_t )      (an RMSNorm launch, caller's buffer xn)
- *   y[t,n]  = bf16( sum_k xn[t,k] * w_packed[n,k] ) (a plain matrix-core launch)
- *   w_packed [N, K] bf16 is the UNFOLDED weight re-laid out by normproj_fold_weight with
- *   gamma == NULL. xn [T, K] bf16 (stride ldxn) is scratch owned by the caller.
+ *   y[t,n]  = bf16( sum_k xn[t,k] * w[k,n] )        (a plain matrix-core launch)
+ *   w  the UNFOLDED weight W [K, N] bf16 row-major, stride ldw >= N
+ *   xn [T, K] bf16 (stride ldxn) is scratch owned by the caller.
  * Same dtype and alignment rules as normproj_deferred.
  */
 QKN_API int normproj_unfused(int64_t T, int64_t K, int64_t N, float eps, int dtype,
                              int gamma_dtype, const void* x, int64_t ldx, const void* gamma,
-                             const void* w_packed, int64_t ldw, void* xn, int64_t ldxn,
+                             const void* w, int64_t ldw, void* xn, int64_t ldxn,
                              void* y, int64_t ldy, void* stream);
 
 /*
@@ -228,12 +232,12 @@ QKN_API int normproj_unfused(int64_t T, int64_t K, int64_t N, float eps, int dty
  *
  * ("FlashNorm: ...", abstract: the folding and deferral carry over to LayerNorm. The pages
  * give no formulas; the ones used follow from LN(x) W = r (x W' - mu c) + beta W.)
- *   w_fold      as normproj_fold_weight: W' = diag(gamma) W, bf16, written transposed [N, K]
+ *   w_fold      as normproj_fold_weight: W' = diag(gamma) W, bf16 [K, N] row-major
  *   colsum[n] = sum_k W'[k, n]  over the bf16 values of w_fold exactly as stored (fp64 sum,
  *               rounded once to fp32), [N] fp32
  *   bias[n]   = sum_k beta[k] W[k, n]  (fp64 sum, rounded once), [N] fp32; may be NULL
  * gamma / beta may be NULL (1 / 0); both use gamma_dtype. Outputs must not overlap each other
- * or the inputs. Alignment rules of normproj_fold_weight.
+ * or the inputs. Layout and alignment rules of normproj_fold_weight.
  */
 QKN_API int normproj_fold_layernorm(int64_t K, int64_t N, int dtype, int gamma_dtype,
                                     const void* w, int64_t ldw, const void* gamma,
@@ -247,15 +251,16 @@ QKN_API int normproj_fold_layernorm(int64_t K, int64_t N, int dtype, int gamma_d
  * its square):
  *   mu_t    = (1/K) sum_k x[t,k]
  *   r_t     = 1 / sqrt( (1/K) sum_k (x[t,k] - mu_t)^2 + eps )
- *   y[t,n]  = bf16( r_t * (sum_k x[t,k] w_fold[n,k] - mu_t colsum[n]) + bias[n] )
+ *   y[t,n]  = bf16( r_t * (sum_k x[t,k] w_fold[k,n] - mu_t colsum[n]) + bias[n] )
  *   colsum, bias  [N] fp32 from normproj_fold_layernorm; bias may be NULL (zero)
- *   row_stats     optional [T, 2] fp32 workspace (8-byte aligned, caller-owned, must not overlap
- *                 any other argument). When given and the product runs on the matrix-core
- *                 kernels (T > 16, N and ldy multiples of 8, y 16-byte aligned, K a multiple of
- *                 64, or of 32 for large shapes), (mu_t, r_t) are computed by one streaming pass
- *                 over x into row_stats and the product applies them in its epilogue; otherwise
- *                 (and when NULL) the product accumulates them from the x tiles it multiplies,
- *                 and row_stats is left untouched. The pass costs one read of x; accumulating
+ *   row_stats     optional [T, 2] fp32 workspace (caller-owned, must not overlap any other
+ *                 argument). When given, 8-byte aligned, and the product runs on the pipelined
+ *                 matrix-core kernels (T > 16; N, ldy, K, ldx, ldw multiples of 8; x, w_fold and
+ *                 y 16-byte aligned; K a multiple of 64, or of 32 for large shapes), (mu_t, r_t)
+ *                 are computed by one streaming pass over x into row_stats and the product
+ *                 applies them in its epilogue; otherwise (and when NULL) the product
+ *                 accumulates them from the x tiles it multiplies, and row_stats is left
+ *                 untouched. The pass costs one read of x; accumulating
  *                 inside the product repeats the work once per 128- or 256-column block of y.
  * Other arguments, dtype and alignment rules as normproj_deferred.
  */
@@ -287,15 +292,14 @@ QKN_API int normproj_deferred_layernorm_noalloc(int64_t T, int64_t K, int64_t N,
 /*
  * normproj_layernorm_unfused - LayerNorm launch then plain projection (measured baseline).
  *   xn[t,k] = bf16( (x[t,k] - mu_t) r_t gamma[k] + beta[k] )   (caller's scratch xn [T, K])
- *   y[t,n]  = bf16( sum_k xn[t,k] w_packed[n,k] )
- * w_packed is the unfolded weight re-laid out by normproj_fold_weight with gamma == NULL.
- * gamma / beta (gamma_dtype, may be NULL) and xn must be 16-byte aligned. Other rules as
- * normproj_unfused.
+ *   y[t,n]  = bf16( sum_k xn[t,k] w[k,n] )
+ * w is the unfolded weight W [K, N] row-major. gamma / beta (gamma_dtype, may be NULL) must be
+ * aligned to their element size. Other rules as normproj_unfused.
  */
 QKN_API int normproj_layernorm_unfused(int64_t T, int64_t K, int64_t N, float eps, int dtype,
                                        int gamma_dtype, const void* x, int64_t ldx,
                                        const void* gamma, const void* beta,
-                                       const void* w_packed, int64_t ldw, void* xn,
+                                       const void* w, int64_t ldw, void* xn,
                                        int64_t ldxn, void* y, int64_t ldy, void* stream);
 
 /*
@@ -305,9 +309,10 @@ QKN_API int normproj_layernorm_unfused(int64_t T, int64_t K, int64_t N, float ep
  * ("FlashNorm: ...", abstract: RMS is unchanged by scaling its input, so with a second RMSNorm
  * after the linear layer the first one has no effect and can be removed, e.g. ahead of
  * attention with Q/K normalisation.) The pre-norm weight is folded into the stacked projection
- * w_qk = [W'q ; W'k] ([nq + nk, K] bf16, normproj_fold_weight of the [K, nq + nk] weight):
- *   p[t,:]       = x[t,:] W'^T                  exact == 0: no pre-norm at all
- *                = r1_t x[t,:] W'^T             exact == 1: r1_t = 1/sqrt(mean(x_t^2) + eps_pre)
+ * w_qk = [W'q | W'k] ([K, nq + nk] bf16 row-major, stride ldw >= nq + nk: normproj_fold_weight
+ * of the stacked weight [Wq | Wk] with the pre-norm's gamma):
+ *   p[t,:]       = x[t,:] w_qk                  exact == 0: no pre-norm at all
+ *                = r1_t x[t,:] w_qk             exact == 1: r1_t = 1/sqrt(mean(x_t^2) + eps_pre)
  *   y[t, 0:nq]   = p[t,0:nq] gamma_q / sqrt(mean(p[t,0:nq]^2) + eps_qk)
  *   y[t, nq:]    = p[t,nq:] gamma_k / sqrt(mean(p[t,nq:]^2) + eps_qk)
  * With exact == 0 the result equals the pre-norm -> projection -> QK-Norm chain with eps_qk
@@ -333,22 +338,22 @@ QKN_API int qknorm_project_eliminated(int64_t T, int64_t K, int64_t nq, int64_t 
  * ("FlashNorm: ...", abstract: the RMSNorm ahead of a linear layer whose output is normalised
  * again; this is that chain computed as written.)
  *   xn[t,k]     = bf16( x[t,k] gamma_pre[k] / sqrt(mean(x_t^2) + eps_pre) )   (caller's xn)
- *   p[t,:]      = bf16( xn[t,:] w_packed^T )                                   (kept in y)
+ *   p[t,:]      = bf16( xn[t,:] w )                                            (kept in y)
  *   y[t, 0:nq]  = p[t,0:nq] gamma_q / sqrt(mean(p[t,0:nq]^2) + eps_qk)
  *   y[t, nq:]   = p[t,nq:] gamma_k / sqrt(mean(p[t,nq:]^2) + eps_qk)
- * w_packed [nq + nk, K] bf16 is the unfolded stacked weight re-laid out by
- * normproj_fold_weight with gamma == NULL. The intermediates xn and p are written with
+ * w [K, nq + nk] bf16 row-major is the unfolded stacked weight [Wq | Wk] (stride ldw >= nq + nk).
+ * The intermediates xn and p are written with
  * ordinary stores, because the next launch reads them straight back (as p is in
  * qknorm_project_eliminated), so the two entry points differ by the pre-norm alone.
- *   x [T, K] bf16 (ldx); xn [T, K] bf16 scratch (ldxn, 16-byte aligned, caller-owned, must not
+ *   x [T, K] bf16 (ldx); xn [T, K] bf16 scratch (ldxn, caller-owned, must not
  *   overlap any other argument); y [T, nq + nk] bf16 (ldy)
  *   gamma_pre [K], gamma_q [nq], gamma_k [nk] in gamma_dtype; nk == 0 normalises Q only
- * Three launches. Alignment rules of normproj_unfused; y must not overlap x, w_packed or the
+ * Three launches. Alignment rules of normproj_unfused; y must not overlap x, w or the
  * gammas. Every argument is checked before the first launch.
  */
 QKN_API int qknorm_project_unfused(int64_t T, int64_t K, int64_t nq, int64_t nk, float eps_qk,
                                    float eps_pre, int gamma_dtype, const void* x, int64_t ldx,
-                                   const void* gamma_pre, const void* w_packed, int64_t ldw,
+                                   const void* gamma_pre, const void* w, int64_t ldw,
                                    const void* gamma_q, const void* gamma_k, void* xn,
                                    int64_t ldxn, void* y, int64_t ldy, void* stream);
 

@@ -352,15 +352,16 @@ def qknorm_shard_publish(part_q, mail_q, epoch: int, part_k=None, mail_k=None):
 
 
 def normproj_fold_weight(w, gamma=None, w_fold=None):
-    """W [K, N] bf16 -> W' = diag(gamma) W stored transposed, [N, K] bf16 (K contiguous)."""
+    """W [K, N] bf16 -> W' = diag(gamma) W, [K, N] bf16 (the layout of W; w_fold may be w
+    itself for an in-place fold)."""
     torch = _torch()
     _check_device(w, gamma)
     K, N = w.shape
     if w_fold is None:
-        w_fold = torch.empty((N, K), dtype=torch.bfloat16, device=w.device)
+        w_fold = torch.empty((K, N), dtype=torch.bfloat16, device=w.device)
     _vec(gamma, K, "gamma")
     _dtypes(torch.bfloat16, "w_fold", w_fold)
-    _mat(w_fold, N, K, "w_fold")
+    _mat(w_fold, K, N, "w_fold")
     _check("normproj_fold_weight", lib().normproj_fold_weight(
         K, N, _dtype_code(w), _dtype_code(gamma) if gamma is not None else QKN_BF16,
         _ptr(w), _ld(w), _ptr(gamma), _ptr(w_fold), _ld(w_fold), _stream(w)))
@@ -368,15 +369,15 @@ def normproj_fold_weight(w, gamma=None, w_fold=None):
 
 
 def normproj_deferred(x, w_fold, eps: float = 1e-6, y=None):
-    """y [T, N] = (x @ W') * (1/rms(x)) with w_fold [N, K] from normproj_fold_weight."""
+    """y [T, N] = (x @ W') * (1/rms(x)) with w_fold = W' [K, N] (normproj_fold_weight)."""
     torch = _torch()
     _check_device(x, w_fold)
     T, K = x.shape
-    N = w_fold.shape[0]
+    N = w_fold.shape[1]
     if y is None:
         y = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
     _dtypes(torch.bfloat16, "w_fold and y", w_fold, y)
-    _mat(w_fold, N, K, "w_fold")
+    _mat(w_fold, K, N, "w_fold")
     _mat(y, T, N, "y")
     _check("normproj_deferred", lib().normproj_deferred(
         T, K, N, float(eps), _dtype_code(x), _ptr(x), _ld(x), _ptr(w_fold), _ld(w_fold),
@@ -384,35 +385,35 @@ def normproj_deferred(x, w_fold, eps: float = 1e-6, y=None):
     return y
 
 
-def normproj_unfused(x, gamma, w_packed, eps: float = 1e-6, xn=None, y=None):
-    """RMSNorm launch into xn, then a plain product with the packed unfolded weight."""
+def normproj_unfused(x, gamma, w, eps: float = 1e-6, xn=None, y=None):
+    """RMSNorm launch into xn, then a plain product with the unfolded weight w [K, N]."""
     torch = _torch()
-    _check_device(x, gamma, w_packed)
+    _check_device(x, gamma, w)
     T, K = x.shape
-    N = w_packed.shape[0]
+    N = w.shape[1]
     if xn is None:
         xn = torch.empty((T, K), dtype=torch.bfloat16, device=x.device)
     if y is None:
         y = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
     _vec(gamma, K, "gamma")
-    _dtypes(torch.bfloat16, "w_packed, xn and y", w_packed, xn, y)
-    _mat(w_packed, N, K, "w_packed")
+    _dtypes(torch.bfloat16, "w, xn and y", w, xn, y)
+    _mat(w, K, N, "w")
     _mat(xn, T, K, "xn")
     _mat(y, T, N, "y")
     _check("normproj_unfused", lib().normproj_unfused(
         T, K, N, float(eps), _dtype_code(x), _dtype_code(gamma), _ptr(x), _ld(x), _ptr(gamma),
-        _ptr(w_packed), _ld(w_packed), _ptr(xn), _ld(xn), _ptr(y), _ld(y), _stream(x)))
+        _ptr(w), _ld(w), _ptr(xn), _ld(xn), _ptr(y), _ld(y), _stream(x)))
     return xn, y
 
 
 def normproj_fold_layernorm(w, gamma=None, beta=None, w_fold=None, colsum=None, bias=None):
-    """W [K, N] bf16 -> (W' = diag(gamma) W transposed [N, K] bf16, colsum [N] fp32 of the
+    """W [K, N] bf16 -> (W' = diag(gamma) W [K, N] bf16, colsum [N] fp32 of the
     stored W', bias = beta W [N] fp32 or None when beta is None)."""
     torch = _torch()
     _check_device(w, gamma, beta)
     K, N = w.shape
     if w_fold is None:
-        w_fold = torch.empty((N, K), dtype=torch.bfloat16, device=w.device)
+        w_fold = torch.empty((K, N), dtype=torch.bfloat16, device=w.device)
     if colsum is None:
         colsum = torch.empty((N,), dtype=torch.float32, device=w.device)
     if bias is None and beta is not None:
@@ -427,7 +428,7 @@ def normproj_fold_layernorm(w, gamma=None, beta=None, w_fold=None, colsum=None, 
     _dtypes(torch.float32, "colsum and bias", colsum, bias)
     if gamma is not None:
         _dtypes(gamma.dtype, "beta must match gamma", beta)
-    _mat(w_fold, N, K, "w_fold")
+    _mat(w_fold, K, N, "w_fold")
     _check("normproj_fold_layernorm", lib().normproj_fold_layernorm(
         K, N, _dtype_code(w), gdt, _ptr(w), _ld(w), _ptr(gamma), _ptr(beta), _ptr(w_fold),
         _ld(w_fold), _ptr(colsum), _ptr(bias), _stream(w)))
@@ -443,7 +444,7 @@ def normproj_deferred_layernorm(x, w_fold, colsum, bias=None, eps: float = 1e-5,
     torch = _torch()
     _check_device(x, w_fold, colsum, bias)
     T, K = x.shape
-    N = w_fold.shape[0]
+    N = w_fold.shape[1]
     if y is None:
         y = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
     if isinstance(row_stats, str):
@@ -459,7 +460,7 @@ def normproj_deferred_layernorm(x, w_fold, colsum, bias=None, eps: float = 1e-5,
     _vec(bias, N, "bias")
     _dtypes(torch.bfloat16, "w_fold and y", w_fold, y)
     _dtypes(torch.float32, "colsum and bias", colsum, bias)
-    _mat(w_fold, N, K, "w_fold")
+    _mat(w_fold, K, N, "w_fold")
     _mat(y, T, N, "y")
     _check("normproj_deferred_layernorm", lib().normproj_deferred_layernorm(
         T, K, N, float(eps), _dtype_code(x), _ptr(x), _ld(x), _ptr(w_fold), _ld(w_fold),
@@ -474,14 +475,14 @@ def normproj_deferred_layernorm_noalloc(x, w_fold, colsum, bias=None, eps: float
     torch = _torch()
     _check_device(x, w_fold, colsum, bias, y)
     T, K = x.shape
-    N = w_fold.shape[0]
+    N = w_fold.shape[1]
     if y is None:
         y = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
     _vec(colsum, N, "colsum")
     _vec(bias, N, "bias")
     _dtypes(torch.bfloat16, "w_fold and y", w_fold, y)
     _dtypes(torch.float32, "colsum and bias", colsum, bias)
-    _mat(w_fold, N, K, "w_fold")
+    _mat(w_fold, K, N, "w_fold")
     _mat(y, T, N, "y")
     _check("normproj_deferred_layernorm_noalloc", lib().normproj_deferred_layernorm_noalloc(
         T, K, N, float(eps), _dtype_code(x), _ptr(x), _ld(x), _ptr(w_fold), _ld(w_fold),
@@ -489,12 +490,12 @@ def normproj_deferred_layernorm_noalloc(x, w_fold, colsum, bias=None, eps: float
     return y
 
 
-def normproj_layernorm_unfused(x, gamma, beta, w_packed, eps: float = 1e-5, xn=None, y=None):
-    """LayerNorm launch into xn, then a plain product with the packed unfolded weight."""
+def normproj_layernorm_unfused(x, gamma, beta, w, eps: float = 1e-5, xn=None, y=None):
+    """LayerNorm launch into xn, then a plain product with the unfolded weight w [K, N]."""
     torch = _torch()
-    _check_device(x, gamma, beta, w_packed)
+    _check_device(x, gamma, beta, w)
     T, K = x.shape
-    N = w_packed.shape[0]
+    N = w.shape[1]
     if xn is None:
         xn = torch.empty((T, K), dtype=torch.bfloat16, device=x.device)
     if y is None:
@@ -502,27 +503,28 @@ def normproj_layernorm_unfused(x, gamma, beta, w_packed, eps: float = 1e-5, xn=N
     g = gamma if gamma is not None else beta
     _vec(gamma, K, "gamma")
     _vec(beta, K, "beta")
-    _dtypes(torch.bfloat16, "w_packed, xn and y", w_packed, xn, y)
+    _dtypes(torch.bfloat16, "w, xn and y", w, xn, y)
     if gamma is not None:
         _dtypes(gamma.dtype, "beta must match gamma", beta)
-    _mat(w_packed, N, K, "w_packed")
+    _mat(w, K, N, "w")
     _mat(xn, T, K, "xn")
     _mat(y, T, N, "y")
     _check("normproj_layernorm_unfused", lib().normproj_layernorm_unfused(
         T, K, N, float(eps), _dtype_code(x), _dtype_code(g) if g is not None else QKN_BF16,
-        _ptr(x), _ld(x), _ptr(gamma), _ptr(beta), _ptr(w_packed), _ld(w_packed), _ptr(xn),
+        _ptr(x), _ld(x), _ptr(gamma), _ptr(beta), _ptr(w), _ld(w), _ptr(xn),
         _ld(xn), _ptr(y), _ld(y), _stream(x)))
     return xn, y
 
 
 def qknorm_project_eliminated(x, w_qk, nq: int, gamma_q, gamma_k=None, eps_qk: float = 1e-6,
                               eps_pre: float = 1e-6, exact: bool = False, y=None):
-    """y [T, nq + nk] = layerwise QK-Norm of x @ W'^T (pre-norm eliminated; exact=True keeps
-    its deferred scale). w_qk [nq + nk, K] is the folded, transposed stacked weight."""
+    """y [T, nq + nk] = layerwise QK-Norm of x @ W' (pre-norm eliminated; exact=True keeps
+    its deferred scale). w_qk [K, nq + nk] is the stacked weight [Wq | Wk] with the pre-norm
+    gamma folded in (normproj_fold_weight)."""
     torch = _torch()
     _check_device(x, w_qk, gamma_q, gamma_k)
     T, K = x.shape
-    N = w_qk.shape[0]
+    N = w_qk.shape[1]
     nk = N - nq
     if y is None:
         y = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
@@ -530,7 +532,7 @@ def qknorm_project_eliminated(x, w_qk, nq: int, gamma_q, gamma_k=None, eps_qk: f
     _vec(gamma_k, nk, "gamma_k")
     _dtypes(torch.bfloat16, "w_qk and y", w_qk, y)
     _dtypes(gamma_q.dtype, "gamma_k must match gamma_q", gamma_k)
-    _mat(w_qk, N, K, "w_qk")
+    _mat(w_qk, K, N, "w_qk")
     _mat(y, T, N, "y")
     _check("qknorm_project_eliminated", lib().qknorm_project_eliminated(
         T, K, nq, nk, float(eps_qk), float(eps_pre), int(bool(exact)), _dtype_code(gamma_q),
@@ -539,14 +541,15 @@ def qknorm_project_eliminated(x, w_qk, nq: int, gamma_q, gamma_k=None, eps_qk: f
     return y
 
 
-def qknorm_project_unfused(x, gamma_pre, w_packed, nq: int, gamma_q, gamma_k=None,
+def qknorm_project_unfused(x, gamma_pre, w, nq: int, gamma_q, gamma_k=None,
                            eps_qk: float = 1e-6, eps_pre: float = 1e-6, xn=None, y=None):
-    """The unsimplified chain: RMSNorm launch into xn, plain product with the packed unfolded
-    stacked weight into y, layerwise QK-Norm of y's Q and K blocks in place. Returns (xn, y)."""
+    """The unsimplified chain: RMSNorm launch into xn, plain product with the unfolded stacked
+    weight w [K, nq + nk] into y, layerwise QK-Norm of y's Q and K blocks in place. Returns
+    (xn, y)."""
     torch = _torch()
-    _check_device(x, gamma_pre, w_packed, gamma_q, gamma_k)
+    _check_device(x, gamma_pre, w, gamma_q, gamma_k)
     T, K = x.shape
-    N = w_packed.shape[0]
+    N = w.shape[1]
     nk = N - nq
     if xn is None:
         xn = torch.empty((T, K), dtype=torch.bfloat16, device=x.device)
@@ -555,14 +558,14 @@ def qknorm_project_unfused(x, gamma_pre, w_packed, nq: int, gamma_q, gamma_k=Non
     _vec(gamma_pre, K, "gamma_pre")
     _vec(gamma_q, nq, "gamma_q")
     _vec(gamma_k, nk, "gamma_k")
-    _dtypes(torch.bfloat16, "w_packed, xn and y", w_packed, xn, y)
+    _dtypes(torch.bfloat16, "w, xn and y", w, xn, y)
     _dtypes(gamma_q.dtype, "gamma_pre and gamma_k must match gamma_q", gamma_pre, gamma_k)
-    _mat(w_packed, N, K, "w_packed")
+    _mat(w, K, N, "w")
     _mat(xn, T, K, "xn")
     _mat(y, T, N, "y")
     _check("qknorm_project_unfused", lib().qknorm_project_unfused(
         T, K, nq, nk, float(eps_qk), float(eps_pre), _dtype_code(gamma_q), _ptr(x), _ld(x),
-        _ptr(gamma_pre), _ptr(w_packed), _ld(w_packed), _ptr(gamma_q), _ptr(gamma_k), _ptr(xn),
+        _ptr(gamma_pre), _ptr(w), _ld(w), _ptr(gamma_q), _ptr(gamma_k), _ptr(xn),
         _ld(xn), _ptr(y), _ld(y), _stream(x)))
     return xn, y
 

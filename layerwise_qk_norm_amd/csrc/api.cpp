@@ -103,7 +103,7 @@ QKN_API const char* qkn_status_string(int status)
     case QKN_ERR_DTYPE: return "unsupported dtype code";
     case QKN_ERR_EPS: return "eps must be finite and >= 0";
     case QKN_ERR_ALIAS: return "an output partially overlaps an input or another output";
-    case QKN_ERR_ALIGN: return "16-byte alignment required";
+    case QKN_ERR_ALIGN: return "a pointer is not aligned to what the call requires";
     case QKN_ERR_HIP: return "HIP runtime error (see qkn_last_hip_error)";
     case QKN_ERR_SCRATCH: return "the input exceeds the library's static workspace";
     default: return "unknown status";
@@ -377,33 +377,32 @@ QKN_API int normproj_fold_weight(int64_t K, int64_t N, int dtype, int gamma_dtyp
                                  const void* w, int64_t ldw, const void* gamma, void* w_fold,
                                  int64_t ldw_fold, void* stream)
 {
-    if (K < 0 || N < 0 || ldw < N || ldw_fold < K) return QKN_ERR_SHAPE;
+    if (K < 0 || N < 0 || ldw < N || ldw_fold < N) return QKN_ERR_SHAPE;
     if (dtype != QKN_BF16 || !valid_dtype(gamma_dtype)) return QKN_ERR_DTYPE;
     if (K == 0 || N == 0) return QKN_OK;
     if (w == nullptr || w_fold == nullptr) return QKN_ERR_NULL;
-    if (((uintptr_t)w_fold & 15u) != 0 || ldw_fold % 8 != 0) return QKN_ERR_ALIGN;
-    const Range rw = span(w, K, N, ldw, 2), rf = span(w_fold, N, K, ldw_fold, 2);
+    const Range rw = span(w, K, N, ldw, 2), rf = span(w_fold, K, N, ldw_fold, 2);
     const Range rg = gamma ? span(gamma, 1, K, K, elem_size(gamma_dtype)) : Range();
-    if (overlap(rf, rw) || overlap(rf, rg)) return QKN_ERR_ALIAS;
+    // in place (w_fold == w, same stride) is allowed: each element is read, then written
+    if (!out_ok(w_fold, ldw_fold, w, ldw, rf, rw, &rg, 1)) return QKN_ERR_ALIAS;
     return hip_status(qkn::launch_fold(K, N, w, ldw, gamma, gamma_dtype == QKN_BF16, w_fold,
                                        ldw_fold, (hipStream_t)stream));
 }
 
 namespace {
 
+// x [T, K] (ldx), w [K, N] row-major (ldw), y [T, N] (ldy), all bf16 at any alignment.
 int check_normproj(int64_t T, int64_t K, int64_t N, float eps, int dtype, const void* x,
                    int64_t ldx, const void* w, int64_t ldw, const void* y, int64_t ldy)
 {
-    if (T < 0 || K < 1 || N < 0 || ldx < K || ldw < K || ldy < N) return QKN_ERR_SHAPE;
+    if (T < 0 || K < 1 || N < 0 || ldx < K || ldw < N || ldy < N) return QKN_ERR_SHAPE;
     if (dtype != QKN_BF16) return QKN_ERR_DTYPE;
     if (!valid_eps(eps)) return QKN_ERR_EPS;
     if (T == 0 || N == 0) return QKN_OK;
     if (x == nullptr || w == nullptr || y == nullptr) return QKN_ERR_NULL;
-    if (K % 8 != 0 || ldx % 8 != 0 || ldw % 8 != 0 || ((uintptr_t)x & 15u) != 0 ||
-        ((uintptr_t)w & 15u) != 0)
-        return QKN_ERR_ALIGN;
+    if (((uintptr_t)x & 1u) || ((uintptr_t)w & 1u) || ((uintptr_t)y & 1u)) return QKN_ERR_ALIGN;
     const Range ry = span(y, T, N, ldy, 2);
-    if (overlap(ry, span(x, T, K, ldx, 2)) || overlap(ry, span(w, N, K, ldw, 2)))
+    if (overlap(ry, span(x, T, K, ldx, 2)) || overlap(ry, span(w, K, N, ldw, 2)))
         return QKN_ERR_ALIAS;
     return QKN_OK;
 }
@@ -416,8 +415,9 @@ QKN_API int normproj_deferred(int64_t T, int64_t K, int64_t N, float eps, int dt
 {
     const int st = check_normproj(T, K, N, eps, dtype, x, ldx, w_fold, ldw, y, ldy);
     if (st != QKN_OK || T == 0 || N == 0) return st;
-    return hip_status(qkn::launch_normproj(T, K, N, eps, qkn::kEpiRms, x, ldx, w_fold, ldw, y,
-                                           ldy, nullptr, nullptr, nullptr, (hipStream_t)stream));
+    return hip_status(qkn::launch_normproj(T, K, N, eps, qkn::kEpiRms | qkn::kWeightRowMajor, x,
+                                           ldx, w_fold, ldw, y, ldy, nullptr, nullptr, nullptr,
+                                           (hipStream_t)stream));
 }
 
 namespace {
@@ -425,19 +425,19 @@ namespace {
 // RMSNorm launch into xn (ordinary stores: the product reads xn straight back), then the plain
 // product; keep_y: the caller reads y back next as well.
 int unfused_rms_product(int64_t T, int64_t K, int64_t N, float eps, int dtype, int gamma_dtype,
-                        const void* x, int64_t ldx, const void* gamma, const void* w_packed,
+                        const void* x, int64_t ldx, const void* gamma, const void* w,
                         int64_t ldw, void* xn, int64_t ldxn, void* y, int64_t ldy, bool keep_y,
                         void* stream)
 {
-    int st = check_normproj(T, K, N, eps, dtype, x, ldx, w_packed, ldw, y, ldy);
+    int st = check_normproj(T, K, N, eps, dtype, x, ldx, w, ldw, y, ldy);
     if (st != QKN_OK) return st;
     if (!valid_dtype(gamma_dtype)) return QKN_ERR_DTYPE;
     if (ldxn < K) return QKN_ERR_SHAPE;
     if (T == 0 || N == 0) return QKN_OK;
     if (xn == nullptr || gamma == nullptr) return QKN_ERR_NULL;
-    if (((uintptr_t)xn & 15u) != 0 || ldxn % 8 != 0) return QKN_ERR_ALIGN;
+    if (((uintptr_t)xn & 1u) != 0) return QKN_ERR_ALIGN;
     const Range rxn = span(xn, T, K, ldxn, 2), rg = span(gamma, 1, K, K, elem_size(gamma_dtype));
-    if (overlap(rxn, span(x, T, K, ldx, 2)) || overlap(rxn, span(w_packed, N, K, ldw, 2)) ||
+    if (overlap(rxn, span(x, T, K, ldx, 2)) || overlap(rxn, span(w, K, N, ldw, 2)) ||
         overlap(rxn, span(y, T, N, ldy, 2)) || overlap(rxn, rg) ||
         overlap(span(y, T, N, ldy, 2), rg))
         return QKN_ERR_ALIAS;
@@ -455,20 +455,21 @@ int unfused_rms_product(int64_t T, int64_t K, int64_t N, float eps, int dtype, i
     hipError_t e = qkn::launch_rows(job, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e);
     return hip_status(qkn::launch_normproj(T, K, N, eps,
-                                           qkn::kEpiPlain | (keep_y ? qkn::kEpiKeepCached : 0),
-                                           xn, ldxn, w_packed, ldw, y, ldy, nullptr, nullptr,
-                                           nullptr, (hipStream_t)stream));
+                                           qkn::kEpiPlain | qkn::kWeightRowMajor |
+                                               (keep_y ? qkn::kEpiKeepCached : 0),
+                                           xn, ldxn, w, ldw, y, ldy, nullptr, nullptr, nullptr,
+                                           (hipStream_t)stream));
 }
 
 }  // namespace
 
 QKN_API int normproj_unfused(int64_t T, int64_t K, int64_t N, float eps, int dtype,
                              int gamma_dtype, const void* x, int64_t ldx, const void* gamma,
-                             const void* w_packed, int64_t ldw, void* xn, int64_t ldxn, void* y,
+                             const void* w, int64_t ldw, void* xn, int64_t ldxn, void* y,
                              int64_t ldy, void* stream)
 {
-    return unfused_rms_product(T, K, N, eps, dtype, gamma_dtype, x, ldx, gamma, w_packed, ldw,
-                               xn, ldxn, y, ldy, false, stream);
+    return unfused_rms_product(T, K, N, eps, dtype, gamma_dtype, x, ldx, gamma, w, ldw, xn, ldxn,
+                               y, ldy, false, stream);
 }
 
 QKN_API int normproj_fold_layernorm(int64_t K, int64_t N, int dtype, int gamma_dtype,
@@ -476,13 +477,12 @@ QKN_API int normproj_fold_layernorm(int64_t K, int64_t N, int dtype, int gamma_d
                                     const void* beta, void* w_fold, int64_t ldw_fold,
                                     float* colsum, float* bias, void* stream)
 {
-    if (K < 0 || N < 0 || ldw < N || ldw_fold < K) return QKN_ERR_SHAPE;
+    if (K < 0 || N < 0 || ldw < N || ldw_fold < N) return QKN_ERR_SHAPE;
     if (dtype != QKN_BF16 || !valid_dtype(gamma_dtype)) return QKN_ERR_DTYPE;
     if (K == 0 || N == 0) return QKN_OK;
     if (w == nullptr || w_fold == nullptr || colsum == nullptr) return QKN_ERR_NULL;
-    if (((uintptr_t)w_fold & 15u) != 0 || ldw_fold % 8 != 0) return QKN_ERR_ALIGN;
     const int64_t gs = elem_size(gamma_dtype);
-    const Range rw = span(w, K, N, ldw, 2), rf = span(w_fold, N, K, ldw_fold, 2);
+    const Range rw = span(w, K, N, ldw, 2), rf = span(w_fold, K, N, ldw_fold, 2);
     const Range rg = gamma ? span(gamma, 1, K, K, gs) : Range();
     const Range rb = beta ? span(beta, 1, K, K, gs) : Range();
     const Range rc = span(colsum, 1, N, N, 4), ro = bias ? span(bias, 1, N, N, 4) : Range();
@@ -508,7 +508,6 @@ int check_deferred_layernorm(int64_t T, int64_t K, int64_t N, float eps, int dty
     const int st = check_normproj(T, K, N, eps, dtype, x, ldx, w_fold, ldw, y, ldy);
     if (st != QKN_OK || T == 0 || N == 0) return st;
     if (colsum == nullptr) return QKN_ERR_NULL;
-    if (((uintptr_t)row_stats & 7u) != 0) return QKN_ERR_ALIGN;
     const Range ry = span(y, T, N, ldy, 2);
     const Range rc = span(colsum, 1, N, N, 4);
     const Range rb = bias ? span(bias, 1, N, N, 4) : Range{};
@@ -516,7 +515,7 @@ int check_deferred_layernorm(int64_t T, int64_t K, int64_t N, float eps, int dty
     if (row_stats) {
         const Range rs = span(row_stats, 1, 2 * T, 2 * T, 4);
         if (overlap(rs, ry) || overlap(rs, span(x, T, K, ldx, 2)) ||
-            overlap(rs, span(w_fold, N, K, ldw, 2)) || overlap(rs, rc) ||
+            overlap(rs, span(w_fold, K, N, ldw, 2)) || overlap(rs, rc) ||
             (bias && overlap(rs, rb)))
             return QKN_ERR_ALIAS;
     }
@@ -531,15 +530,20 @@ int run_deferred_layernorm(int64_t T, int64_t K, int64_t N, float eps, const voi
                            void* stream)
 {
     const hipStream_t s = (hipStream_t)stream;
-    if (row_stats && qkn::normproj_pipelined(T, K, N, ldx, ldw, ldy, y)) {
+    const int wl = qkn::kWeightRowMajor;
+    // the workspace holds (mean, 1/std) pairs as 8-byte stores: one that is not 8-byte aligned
+    // is left unused
+    if (row_stats && ((uintptr_t)row_stats & 7u) == 0 &&
+        qkn::normproj_pipelined(T, K, N, x, ldx, w_fold, ldw, ldy, y, wl)) {
         // statistics from one streaming pass over x; the product applies them in its epilogue
         const hipError_t e = qkn::launch_layernorm_stats(T, K, eps, x, ldx, row_stats, s);
         if (e != hipSuccess) return hip_status(e);
-        return hip_status(qkn::launch_normproj(T, K, N, eps, qkn::kEpiLayerNormStats, x, ldx,
-                                               w_fold, ldw, y, ldy, colsum, bias, row_stats, s));
+        return hip_status(qkn::launch_normproj(T, K, N, eps, qkn::kEpiLayerNormStats | wl, x,
+                                               ldx, w_fold, ldw, y, ldy, colsum, bias, row_stats,
+                                               s));
     }
-    return hip_status(qkn::launch_normproj(T, K, N, eps, qkn::kEpiLayerNorm, x, ldx, w_fold, ldw,
-                                           y, ldy, colsum, bias, nullptr, s));
+    return hip_status(qkn::launch_normproj(T, K, N, eps, qkn::kEpiLayerNorm | wl, x, ldx, w_fold,
+                                           ldw, y, ldy, colsum, bias, nullptr, s));
 }
 
 constexpr int kMaxDevices = 256;
@@ -612,23 +616,23 @@ QKN_API int normproj_deferred_layernorm_noalloc(int64_t T, int64_t K, int64_t N,
 
 QKN_API int normproj_layernorm_unfused(int64_t T, int64_t K, int64_t N, float eps, int dtype,
                                        int gamma_dtype, const void* x, int64_t ldx,
-                                       const void* gamma, const void* beta,
-                                       const void* w_packed, int64_t ldw, void* xn,
-                                       int64_t ldxn, void* y, int64_t ldy, void* stream)
+                                       const void* gamma, const void* beta, const void* w,
+                                       int64_t ldw, void* xn, int64_t ldxn, void* y, int64_t ldy,
+                                       void* stream)
 {
-    int st = check_normproj(T, K, N, eps, dtype, x, ldx, w_packed, ldw, y, ldy);
+    int st = check_normproj(T, K, N, eps, dtype, x, ldx, w, ldw, y, ldy);
     if (st != QKN_OK) return st;
     if (!valid_dtype(gamma_dtype)) return QKN_ERR_DTYPE;
     if (ldxn < K) return QKN_ERR_SHAPE;
     if (T == 0 || N == 0) return QKN_OK;
     if (xn == nullptr) return QKN_ERR_NULL;
-    if (((uintptr_t)xn & 15u) != 0 || ldxn % 8 != 0 || ((uintptr_t)gamma & 15u) != 0 ||
-        ((uintptr_t)beta & 15u) != 0)
-        return QKN_ERR_ALIGN;
     const int64_t gs = elem_size(gamma_dtype);
+    if (((uintptr_t)xn & 1u) != 0 || ((uintptr_t)gamma % (uintptr_t)gs) != 0 ||
+        ((uintptr_t)beta % (uintptr_t)gs) != 0)
+        return QKN_ERR_ALIGN;
     const Range rxn = span(xn, T, K, ldxn, 2), ry = span(y, T, N, ldy, 2);
     const Range rg = span(gamma, 1, K, K, gs), rb = span(beta, 1, K, K, gs);
-    if (overlap(rxn, span(x, T, K, ldx, 2)) || overlap(rxn, span(w_packed, N, K, ldw, 2)) ||
+    if (overlap(rxn, span(x, T, K, ldx, 2)) || overlap(rxn, span(w, K, N, ldw, 2)) ||
         overlap(rxn, ry) || overlap(rxn, rg) || overlap(rxn, rb) || overlap(ry, rg) ||
         overlap(ry, rb))
         return QKN_ERR_ALIAS;
@@ -636,8 +640,9 @@ QKN_API int normproj_layernorm_unfused(int64_t T, int64_t K, int64_t N, float ep
                                               gamma_dtype == QKN_BF16, xn, ldxn,
                                               (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e);
-    return hip_status(qkn::launch_normproj(T, K, N, eps, qkn::kEpiPlain, xn, ldxn, w_packed, ldw,
-                                           y, ldy, nullptr, nullptr, nullptr, (hipStream_t)stream));
+    return hip_status(qkn::launch_normproj(T, K, N, eps, qkn::kEpiPlain | qkn::kWeightRowMajor,
+                                           xn, ldxn, w, ldw, y, ldy, nullptr, nullptr, nullptr,
+                                           (hipStream_t)stream));
 }
 
 namespace {
@@ -698,7 +703,7 @@ QKN_API int qknorm_project_eliminated(int64_t T, int64_t K, int64_t nq, int64_t 
     // (ordinary stores: the row kernel below reads y straight back)
     hipError_t e = qkn::launch_normproj(T, K, N, eps_pre,
                                         (exact ? qkn::kEpiRms : qkn::kEpiPlain) |
-                                            qkn::kEpiKeepCached,
+                                            qkn::kEpiKeepCached | qkn::kWeightRowMajor,
                                         x, ldx, w_qk, ldw, y, ldy, nullptr, nullptr, nullptr,
                                         (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e);
@@ -708,7 +713,7 @@ QKN_API int qknorm_project_eliminated(int64_t T, int64_t K, int64_t nq, int64_t 
 
 QKN_API int qknorm_project_unfused(int64_t T, int64_t K, int64_t nq, int64_t nk, float eps_qk,
                                    float eps_pre, int gamma_dtype, const void* x, int64_t ldx,
-                                   const void* gamma_pre, const void* w_packed, int64_t ldw,
+                                   const void* gamma_pre, const void* w, int64_t ldw,
                                    const void* gamma_q, const void* gamma_k, void* xn,
                                    int64_t ldxn, void* y, int64_t ldy, void* stream)
 {
@@ -717,7 +722,7 @@ QKN_API int qknorm_project_unfused(int64_t T, int64_t K, int64_t nq, int64_t nk,
     const int64_t N = nq + nk;
     // shapes, pointers and aliasing of the norm and the product are checked by
     // unfused_rms_product before its first launch; the QK-Norm's arguments here
-    int st = check_normproj(T, K, N, eps_pre, QKN_BF16, x, ldx, w_packed, ldw, y, ldy);
+    int st = check_normproj(T, K, N, eps_pre, QKN_BF16, x, ldx, w, ldw, y, ldy);
     if (st != QKN_OK) return st;
     st = check_qk_gammas(T, nq, nk, gamma_dtype, gamma_q, gamma_k, y, ldy);
     if (st != QKN_OK) return st;
@@ -730,7 +735,7 @@ QKN_API int qknorm_project_unfused(int64_t T, int64_t K, int64_t nq, int64_t nk,
     }
     // the pre-norm and the plain product, p kept in the caches for the QK-Norm launch
     st = unfused_rms_product(T, K, N, eps_pre, QKN_BF16, gamma_dtype, x, ldx, gamma_pre,
-                             w_packed, ldw, xn, ldxn, y, ldy, true, stream);
+                             w, ldw, xn, ldxn, y, ldy, true, stream);
     if (st != QKN_OK || T == 0) return st;
     return hip_status(qk_norm_in_place(T, nq, nk, eps_qk, gamma_dtype, gamma_q, gamma_k, y, ldy,
                                        stream));

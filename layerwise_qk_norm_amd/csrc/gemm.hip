@@ -173,8 +173,29 @@ __device__ __forceinline__ int swz(int kc, int r)
     return BK == 64 ? (kc ^ ((r >> 1) & 7)) : (kc ^ ((r >> 2) & 3));
 }
 
+// Physical 16-byte chunk of logical chunk c in k row r of a row-major W' tile. A transpose
+// load reads 4 consecutive rows at the same 64 bytes per 16-lane group; xoring the 64-byte
+// segment index with r % 4 puts those rows in 4 different 64-byte bank groups.
+__device__ __forceinline__ int swz_kn(int c, int r) { return c ^ ((r & 3) << 2); }
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// ds_read_b64_tr_b16 at LDS address p (8-byte aligned).
+__device__ __forceinline__ u32x2 lds_tr16(const char* p)
+{
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p));
+}
+
 // NTS: non-temporal output stores (the output leaves the library) or ordinary ones.
-template <int BM, int BN, int WM, int WN, int NST, int BK, int EPI, bool RING, bool NTS>
+// WKN: W' is row-major [K, N] (N contiguous) instead of [N, K]; its k-tile lands in LDS as BK
+// rows of BN columns and the MFMA fragments (8 consecutive k of one column per lane) are read
+// with the LDS transpose load ds_read_b64_tr_b16 (gfx950). Within each 16-lane group that
+// instruction hands lane i, element j the 16-bit element i % 4 of the 8 bytes that lane
+// 4 j + i / 4 addressed: when lane 4 r + c of a group addresses columns 4 c .. 4 c + 3 of row
+// r of a 4-row block, lane i receives column i of rows 0..3.
+template <int BM, int BN, int WM, int WN, int NST, int BK, int EPI, bool RING, bool NTS,
+          bool WKN>
 __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
     int64_t T, int64_t K, int64_t N, float eps, float inv_k, const uint16_t* __restrict__ x,
     int64_t ldx, const uint16_t* __restrict__ w, int64_t ldw, uint16_t* __restrict__ y,
@@ -185,8 +206,12 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
     constexpr int ROWB = BK * 2;            // bytes per tile row
     constexpr int RPC = 1024 / ROWB;        // tile rows per 1 KB DMA chunk
     constexpr int LPR = ROWB / 16;          // lanes per tile row within a chunk
+    // W' part: BN rows of BK (k contiguous) or, row-major, BK rows of BN (n contiguous)
+    constexpr int ROWB_B = WKN ? BN * 2 : ROWB;
+    constexpr int RPC_B = 1024 / ROWB_B, LPR_B = ROWB_B / 16;
     constexpr int PART_A = BM * ROWB, PART_B = BN * ROWB, STAGE = PART_A + PART_B;
-    constexpr int CA = BM / RPC, CB = BN / RPC;
+    constexpr int CA = BM / RPC, CB = (WKN ? BK : BN) / RPC_B;
+    static_assert(!WKN || (RPC_B >= 1 && LPR_B <= kWave), "row-major W' tile rows");
     static_assert(CA % NW == 0 && CB % NW == 0, "DMA chunks must divide among the wavefronts");
     constexpr int CPA = CA / NW, CPB = CB / NW;  // DMA instructions per wavefront per part
     constexpr int KS = BK / 16;
@@ -257,18 +282,29 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
     }
 #pragma unroll
     for (int c = 0; c < CPB; ++c) {
-        const int trow = (wave * CPB + c) * RPC + lrow;
-        const int64_t r = n0 + trow < N ? n0 + trow : N - 1;
-        offb[c] = (uint32_t)(((r - n0) * ldw + swz<BK>(lane % LPR, trow) * 8) * 2);
+        if constexpr (WKN) {
+            // k row trow of the tile, 16-byte chunk (8 columns) given by the lane's slot; chunks
+            // past N (a multiple of 8) read the last chunk and feed columns never stored
+            const int trow = (wave * CPB + c) * RPC_B + lane / LPR_B;
+            const int64_t col = n0 + (int64_t)swz_kn(lane % LPR_B, trow) * 8;
+            offb[c] = (uint32_t)((trow * ldw + ((col < N ? col : N - 8) - n0)) * 2);
+        } else {
+            const int trow = (wave * CPB + c) * RPC + lrow;
+            const int64_t r = n0 + trow < N ? n0 + trow : N - 1;
+            offb[c] = (uint32_t)(((r - n0) * ldw + swz<BK>(lane % LPR, trow) * 8) * 2);
+        }
     }
     const uint16_t* xa = x + m0 * ldx;
-    const uint16_t* wb = w + n0 * ldw;
+    const uint16_t* wb = WKN ? w + n0 : w + n0 * ldw;
+    const int64_t wstep = WKN ? ldw : 1;  // elements from one k to the next in W'
+
     // part: byte offset of the destination part within the pipeline buffer
     auto dma_a = [&](int c, uint32_t part, int64_t k0) {
         dma16s((const void*)(xa + k0), offa[c], lds0 + part + (uint32_t)(wave * CPA + c) * 1024u);
     };
     auto dma_b = [&](int c, uint32_t part, int64_t k0) {
-        dma16s((const void*)(wb + k0), offb[c], lds0 + part + (uint32_t)(wave * CPB + c) * 1024u);
+        dma16s((const void*)(wb + k0 * wstep), offb[c],
+               lds0 + part + (uint32_t)(wave * CPB + c) * 1024u);
     };
     auto issue_tile = [&](int slot, int64_t k0) {
         const uint32_t base = (uint32_t)(slot * STAGE);
@@ -286,6 +322,20 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
     const int frow = lane & 31, fk = lane >> 5;
+    // WKN fragment reads: lane 4 r + c of its 16-lane group g addresses row 8 (g / 2) + r (+ 4
+    // for the second half of the 8 k) at columns 16 (g % 2) + 4 c .. + 3 of 32-column block j;
+    // boff[j] is that byte offset within the first k step (later steps add 16 rows, which
+    // keeps the row modulo 4 and so the swizzle)
+    uint32_t boff[TN];
+    if constexpr (WKN) {
+        const int g = lane >> 4, i = lane & 15;
+        const int r = 8 * (g >> 1) + (i >> 2);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int col = wn * WTN + j * 32 + 16 * (g & 1) + 4 * (i & 3);
+            boff[j] = (uint32_t)(r * ROWB_B + (swz_kn(col >> 3, r) << 4) + (col & 7) * 2);
+        }
+    }
     float s1[TM], s2[TM], x0[TM];
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
@@ -359,8 +409,15 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
             }
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
-                const int r = wn * WTN + j * 32 + frow;
-                bfr[j] = *(const u32x4*)(Bs + r * ROWB + (swz<BK>(kc, r) << 4));
+                if constexpr (WKN) {
+                    // rows ks * 16 + ...: the swizzle depends on the row modulo 4 only
+                    const char* p = Bs + ks * 16 * ROWB_B + boff[j];
+                    const u32x2 lo = lds_tr16(p), hi = lds_tr16(p + 4 * ROWB_B);
+                    bfr[j] = u32x4{lo.x, lo.y, hi.x, hi.y};
+                } else {
+                    const int r = wn * WTN + j * 32 + frow;
+                    bfr[j] = *(const u32x4*)(Bs + r * ROWB + (swz<BK>(kc, r) << 4));
+                }
             }
             if constexpr (kStatsInLoop<EPI>) {
                 // the WN wavefronts holding the same rows take turns over the k steps
@@ -663,6 +720,171 @@ __global__ __launch_bounds__(kThreads) void normproj_mfma_kernel(
     }
 }
 
+// Element kernel: any K, any row strides, any 2-byte alignment of x, W' and y, W' in either
+// layout. 128 x 128 tiles, k-tiles of 64; each thread loads 32 elements of x and of W' per
+// k-tile with 2-byte loads (consecutive threads on consecutive elements of a row), which it
+// stores into padded LDS rows k-contiguous for both operands before the matrix-core loop of
+// the generic kernel. Elements past T, N or K are zero. The row statistics are summed from the
+// staged x tile in LDS (two threads per row, 32 columns each), elements past K left out.
+template <int EPI, bool WKN>
+__global__ __launch_bounds__(kThreads) void normproj_elem_kernel(
+    int64_t T, int64_t K, int64_t N, float eps, float inv_k, const uint16_t* __restrict__ x,
+    int64_t ldx, const uint16_t* __restrict__ w, int64_t ldw, uint16_t* __restrict__ y,
+    int64_t ldy, int nbm, int nbn, const float* __restrict__ colsum,
+    const float* __restrict__ bias)
+{
+    constexpr int kPer = kBM * kBK / kThreads;  // 32 elements per thread and operand
+    __shared__ __attribute__((aligned(16))) uint16_t As[kBM * kPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[kBN * kPitch];
+    __shared__ float rstd[kBM];
+    __shared__ float mean[kBM];
+    __shared__ float part[2][2][kBM];
+
+    const int nb = nbm * nbn;
+    int bid = (int)blockIdx.x;
+    if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+    const int64_t m0 = (int64_t)(bid / nbn) * kBM;
+    const int64_t n0 = (int64_t)(bid % nbn) * kBN;
+    const int tid = (int)threadIdx.x;
+    const int lane = lane_id();
+    const int wave = tid / kWave;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    uint16_t ra[kPer], rb[kPer];
+    // element e of this thread: x tile row (e * 256 + tid) / 64, column tid % 64; W' element
+    // (n, k) with n = (e * 256 + tid) % 128 and k = (e * 256 + tid) / 128 when row-major (so
+    // consecutive threads read consecutive columns), else n = (e * 256 + tid) / 64,
+    // k = tid % 64
+    auto load_tiles = [&](int64_t k0) {
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) {
+            const int idx = e * kThreads + tid;
+            const int64_t gm = m0 + idx / kBK, gk = k0 + idx % kBK;
+            ra[e] = (gm < T && gk < K) ? x[gm * ldx + gk] : (uint16_t)0;
+            if constexpr (WKN) {
+                const int64_t gn = n0 + idx % kBN, wk = k0 + idx / kBN;
+                rb[e] = (gn < N && wk < K) ? w[wk * ldw + gn] : (uint16_t)0;
+            } else {
+                const int64_t gn = n0 + idx / kBK;
+                rb[e] = (gn < N && gk < K) ? w[gn * ldw + gk] : (uint16_t)0;
+            }
+        }
+    };
+    auto store_tiles = [&]() {
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) {
+            const int idx = e * kThreads + tid;
+            As[(idx / kBK) * kPitch + idx % kBK] = ra[e];
+            if constexpr (WKN) Bs[(idx % kBN) * kPitch + idx / kBN] = rb[e];
+            else Bs[(idx / kBK) * kPitch + idx % kBK] = rb[e];
+        }
+    };
+
+    // statistics: thread tid sums row tid / 2, columns 32 (tid % 2) .. + 31 of each x tile
+    const int srow = tid >> 1, shalf = tid & 1;
+    float s1 = 0.0f, s2 = 0.0f, x0 = 0.0f;
+    if constexpr (EPI == kEpiLayerNorm) {
+        const int64_t r = m0 + srow;
+        x0 = bf16_at(x, (r < T ? r : T - 1) * ldx);
+    }
+    auto tile_stats = [&](int64_t k0) {
+        if constexpr (EPI != kEpiPlain) {
+#pragma unroll
+            for (int c = 0; c < 32; ++c) {
+                const int col = shalf * 32 + c;
+                if (k0 + col < K) {
+                    const float v = __uint_as_float((uint32_t)As[srow * kPitch + col] << 16);
+                    if constexpr (EPI == kEpiLayerNorm) {
+                        const float d = v - x0;
+                        s1 += d;
+                        s2 = fmaf(d, d, s2);
+                    } else {
+                        s2 = fmaf(v, v, s2);
+                    }
+                }
+            }
+        }
+    };
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    const int64_t nk = (K + kBK - 1) / kBK;
+    load_tiles(0);
+    const int frag_row = lane & 31;
+    const int frag_k = (lane >> 5) * 8;
+    for (int64_t kt = 0; kt < nk; ++kt) {
+        store_tiles();
+        __syncthreads();
+        if (kt + 1 < nk) load_tiles((kt + 1) * kBK);
+        tile_stats(kt * kBK);
+#pragma unroll
+        for (int ks = 0; ks < kBK / 16; ++ks) {
+            u32x4 af[2], bfr[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                af[i] = *(const u32x4*)(As + (wm * 64 + i * 32 + frag_row) * kPitch + ks * 16 + frag_k);
+                bfr[i] = *(const u32x4*)(Bs + (wn * 64 + i * 32 + frag_row) * kPitch + ks * 16 + frag_k);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+
+    if constexpr (EPI != kEpiPlain) {
+        part[0][shalf][srow] = s1;
+        part[1][shalf][srow] = s2;
+        __syncthreads();
+        if (tid < kBM) {
+            const float q1 = part[0][0][tid] + part[0][1][tid];
+            const float q2 = part[1][0][tid] + part[1][1][tid];
+            const int64_t r = m0 + tid;
+            const float xr0 = EPI == kEpiLayerNorm ? bf16_at(x, (r < T ? r : T - 1) * ldx) : 0.0f;
+            float rs, mu;
+            row_scale<EPI>(q1, q2, xr0, inv_k, eps, rs, mu);
+            rstd[tid] = rs;
+            mean[tid] = mu;
+        }
+        __syncthreads();
+    }
+
+    // accumulator of a 32 x 32 block: lane holds column lane % 32 and, for e in 0..15, row
+    // 8 (e / 4) + 4 (lane / 32) + e % 4
+    const int out_col = lane & 31;
+    const int out_row = (lane >> 5) * 4;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int64_t gn = n0 + wn * 64 + j * 32 + out_col;
+            float cs = 0.0f, bs = 0.0f;
+            if constexpr (EPI == kEpiLayerNorm) {
+                if (gn < N) {
+                    cs = colsum[gn];
+                    if (bias) bs = bias[gn];
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int r = wm * 64 + i * 32 + 8 * (e / 4) + out_row + (e % 4);
+                const int64_t gm = m0 + r;
+                float v = acc[i][j][e];
+                if constexpr (EPI == kEpiRms) v *= rstd[r];
+                if constexpr (EPI == kEpiLayerNorm) v = epilogue<EPI>(v, rstd[r], mean[r], cs, bs);
+                if (gm < T && gn < N) y[gm * ldy + gn] = to_bf16(v);
+            }
+        }
+    }
+}
+
 // Matrix-vector form for T <= 16 on the matrix cores: v_mfma_f32_16x16x32_bf16 with the (up
 // to 16) tokens as the M dimension and 16 W' rows (output columns) as N. Fragment layout: lane
 // l supplies A[l % 16][8 (l / 16) .. + 7] and B[8 (l / 16) .. + 7][l % 16]; it receives
@@ -729,7 +951,13 @@ __device__ __forceinline__ void wait_steps(int later)
     }
 }
 
-template <int EPI, int NTILE, int XR, int WAVES, int S>
+// Row-major W' ([K, N], WKN): a tile's step is 64 k rows of 32 bytes (16 columns), row k of
+// the step in slot mvk_slot(k) (slot s at byte 32 s). A fragment is two transpose loads, each
+// 4 rows x 16 columns per 16-lane group; the slot order puts the two groups of a half-wavefront
+// (rows 8 apart) in different halves of the 256-byte bank row.
+__device__ __forceinline__ int mvk_slot(int k) { return k ^ (((k >> 3) & 1) << 2); }
+
+template <int EPI, int NTILE, int XR, int WAVES, int S, bool WKN>
 __global__ __launch_bounds__(WAVES * 64) void normproj_mvl_kernel(
     int T, int64_t K, int64_t N, float eps, float inv_k, const uint16_t* __restrict__ x,
     int64_t ldx, const uint16_t* __restrict__ w, int64_t ldw, uint16_t* __restrict__ y,
@@ -758,14 +986,26 @@ __global__ __launch_bounds__(WAVES * 64) void normproj_mvl_kernel(
     // T - 1: they feed outputs that are never stored. The offsets fit 32 bits for ld < 2^23.
     const int drow = lane >> 3, dc = lane & 7;
     uint32_t wrow[NTILE][2], wch[NTILE][2], xrow[XH], xch[XH];
+    // WKN: instruction h of tile j fills slots 32 h .. 32 h + 31, lane l slot 32 h + l / 2 and
+    // its 16-byte half l % 2: wrow is that slot's k row within the step (scaled by the row
+    // stride later), wch the byte offset of the lane's 8 columns from column n0 (chunks past N,
+    // a multiple of 8, read the last chunk and feed columns never stored)
+    int wk[2] = {0, 0};
 #pragma unroll
     for (int j = 0; j < NTILE; ++j)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const int r = 2 * drow + h;
-            const int64_t n = n0 + 16 * j + r;
-            wrow[j][h] = (uint32_t)(((n < N ? n : N - 1) - n0) * ldw * 2);
-            wch[j][h] = (uint32_t)((dc ^ mvl_f(r)) << 4);
+            if constexpr (WKN) {
+                wk[h] = mvk_slot(32 * h + (lane >> 1));
+                const int64_t n = n0 + 16 * j + 8 * (lane & 1);
+                wrow[j][h] = (uint32_t)(wk[h] * ldw * 2);
+                wch[j][h] = (uint32_t)(((n < N ? n : N - 8) - n0) * 2);
+            } else {
+                const int r = 2 * drow + h;
+                const int64_t n = n0 + 16 * j + r;
+                wrow[j][h] = (uint32_t)(((n < N ? n : N - 1) - n0) * ldw * 2);
+                wch[j][h] = (uint32_t)((dc ^ mvl_f(r)) << 4);
+            }
         }
 #pragma unroll
     for (int h = 0; h < XH; ++h) {
@@ -773,7 +1013,7 @@ __global__ __launch_bounds__(WAVES * 64) void normproj_mvl_kernel(
         xrow[h] = (uint32_t)((r < T ? r : T - 1) * ldx * 2);
         xch[h] = (uint32_t)((XH == 1 ? dc ^ (r >> 1) : dc ^ mvl_f(r)) << 4);
     }
-    const uint16_t* wb = w + n0 * ldw;
+    const uint16_t* wb = WKN ? w + n0 : w + n0 * ldw;
     const uint32_t kbytes = (uint32_t)(K * 2);
 
     float x0 = 0.0f;
@@ -788,13 +1028,27 @@ __global__ __launch_bounds__(WAVES * 64) void normproj_mvl_kernel(
         const bool full = kb + 128u <= kbytes;
         const uint32_t dst = lds_region + (uint32_t)(slot * STAGE);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the slot's fragment reads are done
+        if constexpr (WKN) {
+            // the step's first k row as the scalar base; rows past K read row K - 1 (zeroed at
+            // use like the chunks past K of the other layout)
+            const uint16_t* wst = wb + st * 64 * ldw;
 #pragma unroll
-        for (int j = 0; j < NTILE; ++j)
+            for (int j = 0; j < NTILE; ++j)
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const uint32_t c = full ? kb + wch[j][h] : min(kb + wch[j][h], kbytes - 16u);
-                dma16s(wb, wrow[j][h] + c, dst + (uint32_t)(j * 2048 + h * 1024));
-            }
+                for (int h = 0; h < 2; ++h) {
+                    uint32_t ro = wrow[j][h];
+                    if (!full && st * 64 + wk[h] >= K) ro = (uint32_t)((K - 1 - st * 64) * ldw * 2);
+                    dma16s(wst, ro + wch[j][h], dst + (uint32_t)(j * 2048 + h * 1024));
+                }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NTILE; ++j)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t c = full ? kb + wch[j][h] : min(kb + wch[j][h], kbytes - 16u);
+                    dma16s(wb, wrow[j][h] + c, dst + (uint32_t)(j * 2048 + h * 1024));
+                }
+        }
 #pragma unroll
         for (int h = 0; h < XH; ++h) {
             const uint32_t c = full ? kb + xch[h] : min(kb + xch[h], kbytes - 16u);
@@ -816,8 +1070,18 @@ __global__ __launch_bounds__(WAVES * 64) void normproj_mvl_kernel(
             a[q] = *(const u32x4*)(sp + XOFF + (XR == 16 ? mvl_off16(r16, c)
                                                           : mvl_off8(r16 & (XR - 1), c)));
 #pragma unroll
-            for (int j = 0; j < NTILE; ++j)
-                b[j][q] = *(const u32x4*)(sp + j * 2048 + mvl_off16(r16, c));
+            for (int j = 0; j < NTILE; ++j) {
+                if constexpr (WKN) {
+                    // rows 32 q + 8 g + (r16 >> 2) (+ 4), columns 4 (r16 & 3) .. + 3
+                    const int k0 = 32 * q + 8 * g + (r16 >> 2);
+                    const char* p = sp + j * 2048 + ((r16 & 3) << 3);
+                    const u32x2 lo = lds_tr16(p + (mvk_slot(k0) << 5));
+                    const u32x2 hi = lds_tr16(p + (mvk_slot(k0 + 4) << 5));
+                    b[j][q] = u32x4{lo.x, lo.y, hi.x, hi.y};
+                } else {
+                    b[j][q] = *(const u32x4*)(sp + j * 2048 + mvl_off16(r16, c));
+                }
+            }
         }
         bool kin[2] = {true, true};
         if ((uint32_t)st * 128u + 128u > kbytes) {  // the last, partial step
@@ -921,36 +1185,20 @@ __global__ __launch_bounds__(WAVES * 64) void normproj_mvl_kernel(
     }
 }
 
-// W [K, N] -> w_fold [N, K] = bf16(gamma[k] * W[k, n]) through a 64 x 64 LDS tile.
+// W [K, N] -> w_fold [K, N] = bf16(gamma[k] * W[k, n]) (fp32 product, one rounding), in the
+// same row-major layout: one workgroup per k row, consecutive threads on consecutive columns.
+// In place (w_fold == w) each element is read and then written by the same thread.
 __global__ __launch_bounds__(kThreads) void fold_kernel(int64_t K, int64_t N,
-                                                        const uint16_t* __restrict__ w,
-                                                        int64_t ldw, const void* gamma,
-                                                        int gamma_bf16,
-                                                        uint16_t* __restrict__ wf, int64_t ldwf)
+                                                        const uint16_t* w, int64_t ldw,
+                                                        const void* gamma, int gamma_bf16,
+                                                        uint16_t* wf, int64_t ldwf)
 {
-    __shared__ uint16_t tile[64][66];
-    const int64_t k0 = (int64_t)blockIdx.y * 64, n0 = (int64_t)blockIdx.x * 64;
-    const int tx = (int)threadIdx.x % 64, ty = (int)threadIdx.x / 64;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int r = i * 4 + ty;  // k within tile
-        const int64_t k = k0 + r, n = n0 + tx;
-        uint16_t out = 0;
-        if (k < K && n < N) {
-            float g = 1.0f;
-            if (gamma) g = gamma_bf16 ? __uint_as_float((uint32_t)((const uint16_t*)gamma)[k] << 16)
-                                      : ((const float*)gamma)[k];
-            out = to_bf16(g * __uint_as_float((uint32_t)w[k * ldw + n] << 16));
-        }
-        tile[tx][r] = out;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int r = i * 4 + ty;  // n within tile
-        const int64_t n = n0 + r, k = k0 + tx;
-        if (k < K && n < N) wf[n * ldwf + k] = tile[r][tx];
-    }
+    const int64_t k = blockIdx.y;
+    float g = 1.0f;
+    if (gamma) g = gamma_bf16 ? bf16_at((const uint16_t*)gamma, k) : ((const float*)gamma)[k];
+    for (int64_t n = (int64_t)blockIdx.x * kThreads + threadIdx.x; n < N;
+         n += (int64_t)gridDim.x * kThreads)
+        wf[k * ldwf + n] = to_bf16(g * bf16_at(w, k * ldw + n));
 }
 
 // Statistics of the LayerNorm fold: c[n] = sum_k W'[k][n] over the folded values exactly as
@@ -1002,9 +1250,11 @@ __device__ __forceinline__ void load8(const void* p, int64_t k, bool bf, float* 
     }
 }
 
-// LayerNorm rows for the unfused baseline: one workgroup per row, 16-byte accesses (K % 8 == 0,
-// aligned rows, 16-byte aligned gamma and beta). Pass 1 sums x - x0 and its square (x0 = the row's first element), pass 2
-// re-reads the row from cache and writes bf16((x - mu) * r * gamma + beta).
+// LayerNorm rows for the unfused baseline: one workgroup per row. Pass 1 sums x - x0 and its
+// square (x0 = the row's first element), pass 2 re-reads the row from cache and writes
+// bf16((x - mu) * r * gamma + beta). VEC: 16-byte accesses (K % 8 == 0, 16-byte aligned rows,
+// gamma and beta); otherwise one element per access.
+template <bool VEC>
 __global__ __launch_bounds__(kThreads) void layernorm_rows_kernel(
     int64_t K, float eps, float inv_k, const uint16_t* __restrict__ x, int64_t ldx,
     const void* gamma, const void* beta, int gb_bf16, uint16_t* __restrict__ y, int64_t ldy)
@@ -1014,8 +1264,16 @@ __global__ __launch_bounds__(kThreads) void layernorm_rows_kernel(
     const uint16_t* xr = x + t * ldx;
     const float x0 = bf16_at(xr, 0);
     float s1 = 0.0f, s2 = 0.0f;
-    for (int64_t k = (int64_t)threadIdx.x * 8; k < K; k += kThreads * 8)
-        accum_stats<kEpiLayerNorm>(*(const u32x4*)(xr + k), x0, s1, s2);
+    if constexpr (VEC) {
+        for (int64_t k = (int64_t)threadIdx.x * 8; k < K; k += kThreads * 8)
+            accum_stats<kEpiLayerNorm>(*(const u32x4*)(xr + k), x0, s1, s2);
+    } else {
+        for (int64_t k = threadIdx.x; k < K; k += kThreads) {
+            const float d = bf16_at(xr, k) - x0;
+            s1 += d;
+            s2 = fmaf(d, d, s2);
+        }
+    }
     s1 = wave_sum(s1);
     s2 = wave_sum(s2);
     const int wave = (int)threadIdx.x / kWave;
@@ -1032,18 +1290,27 @@ __global__ __launch_bounds__(kThreads) void layernorm_rows_kernel(
     }
     float rs, mu;
     row_scale<kEpiLayerNorm>(q1, q2, x0, inv_k, eps, rs, mu);
-    for (int64_t k = (int64_t)threadIdx.x * 8; k < K; k += kThreads * 8) {
-        float e[8], g[8], be[8];
-        load8(xr, k, true, e);
-        if (gamma) load8(gamma, k, gb_bf16, g);
-        if (beta) load8(beta, k, gb_bf16, be);
-        float o[8];
+    if constexpr (VEC) {
+        for (int64_t k = (int64_t)threadIdx.x * 8; k < K; k += kThreads * 8) {
+            float e[8], g[8], be[8];
+            load8(xr, k, true, e);
+            if (gamma) load8(gamma, k, gb_bf16, g);
+            if (beta) load8(beta, k, gb_bf16, be);
+            float o[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            o[j] = fmaf((e[j] - mu) * rs, gamma ? g[j] : 1.0f, beta ? be[j] : 0.0f);
-        const u32x4 out = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
-                           pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])};
-        *(u32x4*)(y + t * ldy + k) = out;
+            for (int j = 0; j < 8; ++j)
+                o[j] = fmaf((e[j] - mu) * rs, gamma ? g[j] : 1.0f, beta ? be[j] : 0.0f);
+            const u32x4 out = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
+                               pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])};
+            *(u32x4*)(y + t * ldy + k) = out;
+        }
+    } else {
+        for (int64_t k = threadIdx.x; k < K; k += kThreads) {
+            float g = 1.0f, be = 0.0f;
+            if (gamma) g = gb_bf16 ? bf16_at((const uint16_t*)gamma, k) : ((const float*)gamma)[k];
+            if (beta) be = gb_bf16 ? bf16_at((const uint16_t*)beta, k) : ((const float*)beta)[k];
+            y[t * ldy + k] = to_bf16(fmaf((bf16_at(xr, k) - mu) * rs, g, be));
+        }
     }
 }
 
@@ -1090,7 +1357,8 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(char* __restrict__ dst,
     for (int64_t i = done + tid; i < nbytes; i += stride) dst[i] = src[i];
 }
 
-template <int BM, int BN, int WM, int WN, int NST, int BK, int EPI, bool RING, bool NTS>
+template <int BM, int BN, int WM, int WN, int NST, int BK, int EPI, bool RING, bool NTS,
+          bool WKN>
 hipError_t launch_pipe_t(int64_t T, int64_t K, int64_t N, float eps, float inv_k,
                          const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
                          uint16_t* y, int64_t ldy, const float* colsum, const float* bias,
@@ -1098,7 +1366,7 @@ hipError_t launch_pipe_t(int64_t T, int64_t K, int64_t N, float eps, float inv_k
 {
     const int64_t nbm = (T + BM - 1) / BM, nbn = (N + BN - 1) / BN;
     if (nbm * nbn > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((normproj_pipe_kernel<BM, BN, WM, WN, NST, BK, EPI, RING, NTS>),
+    hipLaunchKernelGGL((normproj_pipe_kernel<BM, BN, WM, WN, NST, BK, EPI, RING, NTS, WKN>),
                        dim3((unsigned)(nbm * nbn)), dim3(WM * WN * kWave), 0, st, T, K, N, eps,
                        inv_k, x, ldx, w, ldw, y, ldy, (int)nbm, (int)nbn, colsum, bias, rowstats);
     return hipGetLastError();
@@ -1106,7 +1374,7 @@ hipError_t launch_pipe_t(int64_t T, int64_t K, int64_t N, float eps, float inv_k
 
 // Ordinary output stores exist for the epilogues whose output the library reads back itself
 // (the pre-norm elimination: plain or RMSNorm).
-template <int BM, int BN, int WM, int WN, int NST, int BK, int EPI, bool RING>
+template <int BM, int BN, int WM, int WN, int NST, int BK, int EPI, bool RING, bool WKN>
 hipError_t launch_pipe(int64_t T, int64_t K, int64_t N, float eps, float inv_k,
                        const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
                        uint16_t* y, int64_t ldy, const float* colsum, const float* bias,
@@ -1114,10 +1382,10 @@ hipError_t launch_pipe(int64_t T, int64_t K, int64_t N, float eps, float inv_k,
 {
     if constexpr (EPI == kEpiPlain || EPI == kEpiRms) {
         if (!nts)
-            return launch_pipe_t<BM, BN, WM, WN, NST, BK, EPI, RING, false>(
+            return launch_pipe_t<BM, BN, WM, WN, NST, BK, EPI, RING, false, WKN>(
                 T, K, N, eps, inv_k, x, ldx, w, ldw, y, ldy, colsum, bias, rowstats, st);
     }
-    return launch_pipe_t<BM, BN, WM, WN, NST, BK, EPI, RING, true>(
+    return launch_pipe_t<BM, BN, WM, WN, NST, BK, EPI, RING, true, WKN>(
         T, K, N, eps, inv_k, x, ldx, w, ldw, y, ldy, colsum, bias, rowstats, st);
 }
 
@@ -1134,13 +1402,13 @@ struct MvJob {
     hipStream_t st;
 };
 
-template <int EPI, int NTILE, int XR, int WAVES, int S>
+template <int EPI, int NTILE, int XR, int WAVES, int S, bool WKN>
 hipError_t launch_mvl(const MvJob& j)
 {
     constexpr int kCols = 16 * NTILE;
     const int64_t nblk = (j.N + kCols - 1) / kCols;
     if (nblk > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((normproj_mvl_kernel<EPI, NTILE, XR, WAVES, S>), dim3((unsigned)nblk),
+    hipLaunchKernelGGL((normproj_mvl_kernel<EPI, NTILE, XR, WAVES, S, WKN>), dim3((unsigned)nblk),
                        dim3(WAVES * kWave), 0, j.st, (int)j.T, j.K, j.N, j.eps, j.inv_k, j.x,
                        j.ldx, j.w, j.ldw, j.y, j.ldy, j.colsum, j.bias);
     return hipGetLastError();
@@ -1150,31 +1418,38 @@ hipError_t launch_mvl(const MvJob& j)
 // wavefronts (two workgroups per CU) for outputs up to 4096 wide or up to 4 tokens; otherwise
 // two tiles (one workgroup per CU), each x fragment then feeding two MFMAs. The step count
 // fills the LDS the workgroups per CU leave.
-template <int EPI>
+template <int EPI, bool WKN>
 hipError_t launch_mv(const MvJob& j)
 {
     if (j.N <= 4096 || j.T <= 4) {
-        if (j.T <= 1) return launch_mvl<EPI, 1, 1, 8, 4>(j);
-        if (j.T <= 2) return launch_mvl<EPI, 1, 2, 8, 4>(j);
-        if (j.T <= 4) return launch_mvl<EPI, 1, 4, 8, 4>(j);
-        if (j.T <= 8) return launch_mvl<EPI, 1, 8, 8, 3>(j);
-        return launch_mvl<EPI, 1, 16, 8, 2>(j);
+        if (j.T <= 1) return launch_mvl<EPI, 1, 1, 8, 4, WKN>(j);
+        if (j.T <= 2) return launch_mvl<EPI, 1, 2, 8, 4, WKN>(j);
+        if (j.T <= 4) return launch_mvl<EPI, 1, 4, 8, 4, WKN>(j);
+        if (j.T <= 8) return launch_mvl<EPI, 1, 8, 8, 3, WKN>(j);
+        return launch_mvl<EPI, 1, 16, 8, 2, WKN>(j);
     }
-    if (j.T <= 8) return launch_mvl<EPI, 2, 8, 8, 4>(j);
-    return launch_mvl<EPI, 2, 16, 8, 3>(j);
+    if (j.T <= 8) return launch_mvl<EPI, 2, 8, 8, 4, WKN>(j);
+    return launch_mvl<EPI, 2, 16, 8, 3, WKN>(j);
 }
 
 // Kernel choice for a product shape.
-enum Path { kPathMv, kPathBig64, kPathBig32, kPathMid, kPathMidDeep, kPathGeneric };
+enum Path { kPathMv, kPathBig64, kPathBig32, kPathMid, kPathMidDeep, kPathGeneric, kPathElem };
 
-Path choose_path(int64_t T, int64_t K, int64_t N, int64_t ldx, int64_t ldw, int64_t ldy,
-                 const void* y)
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+Path choose_path(int64_t T, int64_t K, int64_t N, const void* x, int64_t ldx, const void* w,
+                 int64_t ldw, int64_t ldy, const void* y, bool wkn)
 {
+    // 16-byte accesses along k of x (and of W' [N, K]) or along n of W' [K, N]; anything else
+    // takes the element kernel
+    const bool vec = K % 8 == 0 && ldx % 8 == 0 && ldw % 8 == 0 && aligned16(x) &&
+                     aligned16(w) && (!wkn || N % 8 == 0);
+    if (!vec) return kPathElem;
     // the matrix-vector kernel addresses W' and x rows with 32-bit byte offsets from the
-    // first row of a tile (at most 32 rows) or of x (at most 16)
-    if (T <= kGemvMaxT && ldx < (int64_t(1) << 26) && ldw < (int64_t(1) << 26)) return kPathMv;
+    // first row of a tile (at most 32 rows, or 64 k rows of a row-major W') or of x (at most 16)
+    if (T <= kGemvMaxT && ldx < (int64_t(1) << 25) && ldw < (int64_t(1) << 25)) return kPathMv;
     // the pipelined kernels address a tile's rows with 32-bit byte offsets from its first row
-    const bool pipe_ok = N % 8 == 0 && ldy % 8 == 0 && ((uintptr_t)y & 15u) == 0 &&
+    const bool pipe_ok = N % 8 == 0 && ldy % 8 == 0 && aligned16(y) &&
                          ldx < (int64_t(1) << 23) && ldw < (int64_t(1) << 23);
     const int64_t big_tiles = ((T + 255) / 256) * ((N + 255) / 256);
     // at least one 256 x 256 tile per CU: 8 wavefronts of 64 x 128, k-tiles of 64 through the
@@ -1187,34 +1462,30 @@ Path choose_path(int64_t T, int64_t K, int64_t N, int64_t ldx, int64_t ldw, int6
     // the second workgroup would have used
     const int64_t mid_tiles = ((T + 127) / 128) * ((N + 127) / 128);
     if (pipe_ok && K % 64 == 0) return mid_tiles <= 256 ? kPathMidDeep : kPathMid;
-    return kPathGeneric;
+    // the 16-byte generic kernel reads W' along k only
+    return wkn ? kPathElem : kPathGeneric;
 }
 
-template <int EPI>
-hipError_t launch_epi(int64_t T, int64_t K, int64_t N, float eps, const uint16_t* xp,
+template <int EPI, bool WKN>
+hipError_t launch_epi(Path path, int64_t T, int64_t K, int64_t N, float eps, const uint16_t* xp,
                       int64_t ldx, const uint16_t* wp, int64_t ldw, uint16_t* yp, int64_t ldy,
                       const float* colsum, const float* bias, const float* rowstats,
                       bool nts, hipStream_t st)
 {
     const float inv_k = (float)(1.0 / (double)K);
-    const Path path = choose_path(T, K, N, ldx, ldw, ldy, yp);
     switch (path) {
     case kPathBig64:
-        return launch_pipe<256, 256, 4, 2, 5, 64, EPI, true>(T, K, N, eps, inv_k, xp, ldx, wp,
-                                                             ldw, yp, ldy, colsum, bias,
-                                                             rowstats, nts, st);
+        return launch_pipe<256, 256, 4, 2, 5, 64, EPI, true, WKN>(
+            T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp, ldy, colsum, bias, rowstats, nts, st);
     case kPathBig32:
-        return launch_pipe<256, 256, 4, 2, 4, 32, EPI, false>(T, K, N, eps, inv_k, xp, ldx, wp,
-                                                              ldw, yp, ldy, colsum, bias,
-                                                              rowstats, nts, st);
+        return launch_pipe<256, 256, 4, 2, 4, 32, EPI, false, WKN>(
+            T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp, ldy, colsum, bias, rowstats, nts, st);
     case kPathMid:
-        return launch_pipe<128, 128, 4, 2, 2, 64, EPI, false>(T, K, N, eps, inv_k, xp, ldx, wp,
-                                                              ldw, yp, ldy, colsum, bias,
-                                                              rowstats, nts, st);
+        return launch_pipe<128, 128, 4, 2, 2, 64, EPI, false, WKN>(
+            T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp, ldy, colsum, bias, rowstats, nts, st);
     case kPathMidDeep:
-        return launch_pipe<128, 128, 4, 2, 4, 64, EPI, false>(T, K, N, eps, inv_k, xp, ldx, wp,
-                                                              ldw, yp, ldy, colsum, bias,
-                                                              rowstats, nts, st);
+        return launch_pipe<128, 128, 4, 2, 4, 64, EPI, false, WKN>(
+            T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp, ldy, colsum, bias, rowstats, nts, st);
     default:
         break;
     }
@@ -1222,23 +1493,47 @@ hipError_t launch_epi(int64_t T, int64_t K, int64_t N, float eps, const uint16_t
         return hipErrorInvalidValue;  // statistics from memory: pipelined kernels only
     } else {
         if (path == kPathMv)
-            return launch_mv<EPI>(MvJob{T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp, ldy, colsum,
-                                        bias, st});
+            return launch_mv<EPI, WKN>(MvJob{T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp, ldy,
+                                             colsum, bias, st});
         const int64_t nbm = (T + kBM - 1) / kBM, nbn = (N + kBN - 1) / kBN;
         if (nbm * nbn > 0x7fffffff) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL(normproj_mfma_kernel<EPI>, dim3((unsigned)(nbm * nbn)), dim3(kThreads),
-                           0, st, T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp, ldy, (int)nbm,
-                           (int)nbn, colsum, bias);
-        return hipGetLastError();
+        if (path == kPathElem) {
+            hipLaunchKernelGGL((normproj_elem_kernel<EPI, WKN>), dim3((unsigned)(nbm * nbn)),
+                               dim3(kThreads), 0, st, T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp,
+                               ldy, (int)nbm, (int)nbn, colsum, bias);
+            return hipGetLastError();
+        }
+        if constexpr (WKN) {
+            return hipErrorInvalidValue;  // the 16-byte generic kernel reads W' [N, K] only
+        } else {
+            hipLaunchKernelGGL(normproj_mfma_kernel<EPI>, dim3((unsigned)(nbm * nbn)),
+                               dim3(kThreads), 0, st, T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp,
+                               ldy, (int)nbm, (int)nbn, colsum, bias);
+            return hipGetLastError();
+        }
     }
+}
+
+template <int EPI>
+hipError_t launch_layout(int64_t T, int64_t K, int64_t N, float eps, const uint16_t* xp,
+                         int64_t ldx, const uint16_t* wp, int64_t ldw, uint16_t* yp, int64_t ldy,
+                         const float* colsum, const float* bias, const float* rowstats,
+                         bool nts, bool wkn, hipStream_t st)
+{
+    const Path path = choose_path(T, K, N, xp, ldx, wp, ldw, ldy, yp, wkn);
+    if (wkn)
+        return launch_epi<EPI, true>(path, T, K, N, eps, xp, ldx, wp, ldw, yp, ldy, colsum, bias,
+                                     rowstats, nts, st);
+    return launch_epi<EPI, false>(path, T, K, N, eps, xp, ldx, wp, ldw, yp, ldy, colsum, bias,
+                                  rowstats, nts, st);
 }
 
 }  // namespace
 
-bool normproj_pipelined(int64_t T, int64_t K, int64_t N, int64_t ldx, int64_t ldw, int64_t ldy,
-                        const void* y)
+bool normproj_pipelined(int64_t T, int64_t K, int64_t N, const void* x, int64_t ldx,
+                        const void* w, int64_t ldw, int64_t ldy, const void* y, int epi)
 {
-    const Path p = choose_path(T, K, N, ldx, ldw, ldy, y);
+    const Path p = choose_path(T, K, N, x, ldx, w, ldw, ldy, y, (epi & kWeightRowMajor) != 0);
     return p == kPathBig64 || p == kPathBig32 || p == kPathMid || p == kPathMidDeep;
 }
 
@@ -1250,23 +1545,24 @@ hipError_t launch_normproj(int64_t T, int64_t K, int64_t N, float eps, int epi,
     if (T == 0 || N == 0) return hipSuccess;
     // outputs leave the library: non-temporal stores, unless the caller reads them back next
     const bool nts = (epi & kEpiKeepCached) == 0;
-    epi &= ~kEpiKeepCached;
+    const bool wkn = (epi & kWeightRowMajor) != 0;
+    epi &= ~(kEpiKeepCached | kWeightRowMajor);
     const uint16_t* xp = (const uint16_t*)x;
     const uint16_t* wp = (const uint16_t*)w;
     uint16_t* yp = (uint16_t*)y;
     switch (epi) {
     case kEpiPlain:
-        return launch_epi<kEpiPlain>(T, K, N, eps, xp, ldx, wp, ldw, yp, ldy, colsum, bias,
-                                     rowstats, nts, st);
+        return launch_layout<kEpiPlain>(T, K, N, eps, xp, ldx, wp, ldw, yp, ldy, colsum, bias,
+                                        rowstats, nts, wkn, st);
     case kEpiRms:
-        return launch_epi<kEpiRms>(T, K, N, eps, xp, ldx, wp, ldw, yp, ldy, colsum, bias,
-                                   rowstats, nts, st);
+        return launch_layout<kEpiRms>(T, K, N, eps, xp, ldx, wp, ldw, yp, ldy, colsum, bias,
+                                      rowstats, nts, wkn, st);
     case kEpiLayerNorm:
-        return launch_epi<kEpiLayerNorm>(T, K, N, eps, xp, ldx, wp, ldw, yp, ldy, colsum, bias,
-                                         rowstats, nts, st);
+        return launch_layout<kEpiLayerNorm>(T, K, N, eps, xp, ldx, wp, ldw, yp, ldy, colsum,
+                                            bias, rowstats, nts, wkn, st);
     case kEpiLayerNormStats:
-        return launch_epi<kEpiLayerNormStats>(T, K, N, eps, xp, ldx, wp, ldw, yp, ldy, colsum,
-                                              bias, rowstats, nts, st);
+        return launch_layout<kEpiLayerNormStats>(T, K, N, eps, xp, ldx, wp, ldw, yp, ldy, colsum,
+                                                 bias, rowstats, nts, wkn, st);
     default:
         return hipErrorInvalidValue;
     }
@@ -1302,9 +1598,17 @@ hipError_t launch_layernorm_rows(int64_t T, int64_t K, float eps, const void* x,
 {
     if (T == 0) return hipSuccess;
     if (T > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(layernorm_rows_kernel, dim3((unsigned)T), dim3(kThreads), 0, st, K, eps,
-                       (float)(1.0 / (double)K), (const uint16_t*)x, ldx, gamma, beta, gb_bf16,
-                       (uint16_t*)y, ldy);
+    const bool vec = K % 8 == 0 && ldx % 8 == 0 && ldy % 8 == 0 && aligned16(x) &&
+                     aligned16(y) && (gamma == nullptr || aligned16(gamma)) &&
+                     (beta == nullptr || aligned16(beta));
+    if (vec)
+        hipLaunchKernelGGL(layernorm_rows_kernel<true>, dim3((unsigned)T), dim3(kThreads), 0, st,
+                           K, eps, (float)(1.0 / (double)K), (const uint16_t*)x, ldx, gamma,
+                           beta, gb_bf16, (uint16_t*)y, ldy);
+    else
+        hipLaunchKernelGGL(layernorm_rows_kernel<false>, dim3((unsigned)T), dim3(kThreads), 0,
+                           st, K, eps, (float)(1.0 / (double)K), (const uint16_t*)x, ldx, gamma,
+                           beta, gb_bf16, (uint16_t*)y, ldy);
     return hipGetLastError();
 }
 
@@ -1312,9 +1616,10 @@ hipError_t launch_fold(int64_t K, int64_t N, const void* w, int64_t ldw, const v
                        int gamma_bf16, void* w_fold, int64_t ldwf, hipStream_t st)
 {
     if (K == 0 || N == 0) return hipSuccess;
-    const int64_t gx = (N + 63) / 64, gy = (K + 63) / 64;
-    if (gx > 0x7fffffff || gy > 65535) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(fold_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(kThreads), 0, st, K, N,
+    int64_t gx = (N + kThreads - 1) / kThreads;
+    if (gx > 64) gx = 64;  // wide rows: each thread strides over the rest
+    if (K > 65535) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(fold_kernel, dim3((unsigned)gx, (unsigned)K), dim3(kThreads), 0, st, K, N,
                        (const uint16_t*)w, ldw, gamma, gamma_bf16, (uint16_t*)w_fold, ldwf);
     return hipGetLastError();
 }

@@ -46,11 +46,12 @@ struct RowJob {
 // two-pass kernel (16-byte or element accesses).
 hipError_t launch_rows(const RowJob& job, hipStream_t stream);
 
-// W [K, N] (stride ldw) -> w_fold [N, K] (stride ldwf) = bf16(gamma[k] * W[k, n]).
+// W [K, N] (stride ldw) -> w_fold [K, N] (stride ldwf) = bf16(gamma[k] * W[k, n]).
 hipError_t launch_fold(int64_t K, int64_t N, const void* w, int64_t ldw, const void* gamma,
                        int gamma_bf16, void* w_fold, int64_t ldwf, hipStream_t stream);
 
-// Epilogue of the projection acc = x [T, K] . w [N, K]^T.
+// Epilogue of the projection acc = x [T, K] . W' with W' given as w [N, K] (row n holds column
+// n of W') or, with kWeightRowMajor, as w [K, N].
 enum Epi : int {
     kEpiPlain = 0,      // y = bf16(acc)
     kEpiRms = 1,        // y = bf16(acc / rms(x row))
@@ -60,6 +61,8 @@ enum Epi : int {
 // Flag or-ed into the epilogue: the caller reads y again right away, so the tiled kernels
 // store it with ordinary stores (it stays in the caches) instead of non-temporal ones.
 constexpr int kEpiKeepCached = 16;
+// Flag or-ed into the epilogue: w is row-major [K, N] (N contiguous).
+constexpr int kWeightRowMajor = 32;
 // rowstats is read by kEpiLayerNormStats only, which runs on the pipelined kernels alone
 // (normproj_pipelined() must hold).
 hipError_t launch_normproj(int64_t T, int64_t K, int64_t N, float eps, int epi,
@@ -67,9 +70,10 @@ hipError_t launch_normproj(int64_t T, int64_t K, int64_t N, float eps, int epi,
                            int64_t ldy, const float* colsum, const float* bias,
                            const float* rowstats, hipStream_t stream);
 
-// Whether launch_normproj runs one of the pipelined matrix-core kernels for this shape.
-bool normproj_pipelined(int64_t T, int64_t K, int64_t N, int64_t ldx, int64_t ldw, int64_t ldy,
-                        const void* y);
+// Whether launch_normproj runs one of the pipelined matrix-core kernels for this shape, these
+// operands and the weight layout in epi (kWeightRowMajor or not).
+bool normproj_pipelined(int64_t T, int64_t K, int64_t N, const void* x, int64_t ldx,
+                        const void* w, int64_t ldw, int64_t ldy, const void* y, int epi);
 
 // rowstats[t] = (mean of x row t, 1 / sqrt(var + eps)) in fp32, K % 8 == 0, rows 16-byte aligned.
 hipError_t launch_layernorm_stats(int64_t T, int64_t K, float eps, const void* x, int64_t ldx,
@@ -81,7 +85,8 @@ hipError_t launch_fold_stats(int64_t K, int64_t N, const void* w, int64_t ldw, c
                              const void* beta, int gb_bf16, float* colsum, float* bias,
                              hipStream_t stream);
 
-// y [T, K] = bf16(LayerNorm(x) * gamma + beta), rows 16-byte aligned, K % 8 == 0.
+// y [T, K] = bf16(LayerNorm(x) * gamma + beta), any alignment (16-byte accesses where x, y,
+// gamma and beta allow them).
 hipError_t launch_layernorm_rows(int64_t T, int64_t K, float eps, const void* x, int64_t ldx,
                                  const void* gamma, const void* beta, int gb_bf16, void* y,
                                  int64_t ldy, hipStream_t stream);

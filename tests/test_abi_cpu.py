@@ -139,13 +139,27 @@ def test_normproj_validation(L):
     F = L.normproj_fold_weight
     assert F(16, 16, F32, BF16, A, 16, G1, B, 16, None) == DTYPE
     assert F(16, 16, BF16, BF16, A, 8, G1, B, 16, None) == SHAPE      # ldw < N
-    assert F(16, 16, BF16, BF16, A, 16, G1, B + 2, 16, None) == ALIGN
-    assert F(16, 16, BF16, BF16, A, 16, G1, A, 16, None) == ALIAS
+    assert F(16, 16, BF16, BF16, A, 16, G1, B, 8, None) == SHAPE      # ldw_fold < N
+    # W' is written [K, N] like W: any alignment and stride, in place allowed
+    assert F(16, 16, BF16, BF16, A, 16, G1, B + 2, 17, None) == HIPERR
+    assert F(16, 16, BF16, BF16, A, 16, G1, A, 16, None) == HIPERR
+    assert F(16, 16, BF16, BF16, A, 16, G1, A + 32, 16, None) == ALIAS  # shifted overlap
+    assert F(16, 16, BF16, BF16, A, 16, G1, A, 24, None) == ALIAS       # same base, other ld
+    assert F(16, 16, BF16, BF16, A, 16, G1, G1 - 32, 16, None) == ALIAS
     assert F(16, 16, BF16, BF16, None, 16, G1, B, 16, None) == NULL
     P = L.normproj_deferred
     assert P(4, 16, 16, 1e-6, F32, A, 16, B, 16, C, 16, None) == DTYPE
-    assert P(4, 12, 16, 1e-6, BF16, A, 12, B, 12, C, 16, None) == ALIGN   # K % 8
-    assert P(4, 16, 16, 1e-6, BF16, A + 2, 16, B, 16, C, 16, None) == ALIGN
+    # w_fold is [K, N]: its stride covers N, not K
+    assert P(4, 16, 24, 1e-6, BF16, A, 16, B, 16, C, 24, None) == SHAPE   # ldw < N
+    assert P(4, 16, 8, 1e-6, BF16, A, 16, B, 8, C, 8, None) == HIPERR    # ldw < K is fine
+    # any K, stride and 2-byte alignment runs (an element-load kernel where 16 bytes do not)
+    assert P(4, 12, 16, 1e-6, BF16, A, 12, B, 16, C, 16, None) == HIPERR  # K % 8
+    assert P(4, 1001, 16, 1e-6, BF16, A + 2, 1003, B + 2, 17, C + 2, 19, None) == HIPERR
+    assert P(4, 16, 16, 1e-6, BF16, A + 1, 16, B, 16, C, 16, None) == ALIGN  # odd address
+    assert P(4, 16, 16, 1e-6, BF16, A, 16, B + 1, 16, C, 16, None) == ALIGN
+    assert P(4, 16, 16, 1e-6, BF16, A, 16, B, 16, C + 1, 16, None) == ALIGN
+    assert P(4, 16, 64, 1e-6, BF16, A, 16, B, 64, B + 1024, 64, None) == ALIAS  # y on W' row 8
+    assert P(4, 16, 64, 1e-6, BF16, A, 16, B, 64, B + 2048, 64, None) == HIPERR  # just past W'
     assert P(4, 16, 16, 1e-6, BF16, A, 16, B, 16, A + 32, 16, None) == ALIAS
     assert P(4, 16, 16, -1.0, BF16, A, 16, B, 16, C, 16, None) == EPS
     assert P(4, 16, 16, 1e-6, BF16, A, 16, B, 16, None, 16, None) == NULL
@@ -165,21 +179,23 @@ def test_layernorm_projection_validation(L):
     F = L.normproj_fold_layernorm
     assert F(16, 16, F32, BF16, A, 16, G1, G2, B, 16, C, D, None) == DTYPE
     assert F(16, 16, BF16, BF16, A, 8, G1, G2, B, 16, C, D, None) == SHAPE     # ldw < N
-    assert F(16, 16, BF16, BF16, A, 16, G1, G2, B + 2, 16, C, D, None) == ALIGN
+    assert F(16, 16, BF16, BF16, A, 16, G1, G2, B + 2, 16, C, D, None) == HIPERR
     assert F(16, 16, BF16, BF16, A, 16, G1, G2, B, 16, None, D, None) == NULL  # colsum needed
     assert F(16, 16, BF16, BF16, A, 16, G1, G2, B, 16, A, D, None) == ALIAS    # colsum on W
     assert F(16, 16, BF16, BF16, A, 16, G1, G2, B, 16, C, C + 32, None) == ALIAS
     assert F(16, 16, BF16, BF16, A, 16, G1, G2, B, 16, C, G2, None) == ALIAS   # bias on beta
-    assert F(0, 16, BF16, BF16, None, 16, None, None, None, 0, None, None, None) == OK
+    assert F(0, 16, BF16, BF16, None, 16, None, None, None, 16, None, None, None) == OK
     P = L.normproj_deferred_layernorm
     assert P(4, 16, 16, 1e-5, F32, A, 16, B, 16, C, D, G1, 16, None, None) == DTYPE
-    assert P(4, 12, 16, 1e-5, BF16, A, 12, B, 12, C, D, G1, 16, None, None) == ALIGN
+    assert P(4, 12, 16, 1e-5, BF16, A, 12, B, 16, C, D, G1, 16, None, None) == HIPERR  # K % 8
+    assert P(4, 12, 16, 1e-5, BF16, A, 12, B, 12, C, D, G1, 16, None, None) == SHAPE  # ldw < N
     assert P(4, 16, 16, -1.0, BF16, A, 16, B, 16, C, D, G1, 16, None, None) == EPS
     assert P(4, 16, 16, 1e-5, BF16, A, 16, B, 16, None, D, G1, 16, None, None) == NULL
     assert P(4, 16, 16, 1e-5, BF16, A, 16, B, 16, C, D, C, 16, None, None) == ALIAS  # y on colsum
     assert P(4, 16, 16, 1e-5, BF16, A, 16, B, 16, C, D, D, 16, None, None) == ALIAS  # y on bias
-    # the row-statistics workspace: 8-byte aligned, clear of every other operand
-    assert P(4, 16, 16, 1e-5, BF16, A, 16, B, 16, C, D, G1, 16, E + 4, None) == ALIGN
+    # the row-statistics workspace: clear of every other operand (one that is not 8-byte
+    # aligned is accepted and left unused)
+    assert P(4, 16, 16, 1e-5, BF16, A, 16, B, 16, C, D, G1, 16, E + 4, None) == HIPERR
     assert P(4, 16, 16, 1e-5, BF16, A, 16, B, 16, C, D, G1, 16, G1 + 8, None) == ALIAS  # on y
     assert P(4, 16, 16, 1e-5, BF16, A, 16, B, 16, C, D, G1, 16, A + 64, None) == ALIAS  # on x
     assert P(4, 16, 16, 1e-5, BF16, A, 16, B, 16, C, D, G1, 16, B, None) == ALIAS      # on W'
@@ -199,7 +215,9 @@ def test_layernorm_projection_validation(L):
     U = L.normproj_layernorm_unfused
     assert U(4, 16, 16, 1e-5, BF16, BF16, A, 16, G1, G2, B, 16, A, 16, C, 16, None) == ALIAS
     assert U(4, 16, 16, 1e-5, BF16, BF16, A, 16, G1, G2, B, 16, None, 16, C, 16, None) == NULL
-    assert U(4, 16, 16, 1e-5, BF16, BF16, A, 16, G1 + 2, G2, B, 16, D, 16, C, 16, None) == ALIGN
+    assert U(4, 16, 16, 1e-5, BF16, BF16, A, 16, G1 + 2, G2, B, 16, D, 16, C, 16, None) == HIPERR
+    assert U(4, 16, 16, 1e-5, BF16, BF16, A, 16, G1 + 1, G2, B, 16, D, 16, C, 16, None) == ALIGN
+    assert U(4, 16, 16, 1e-5, BF16, F32, A, 16, G1 + 2, G2, B, 16, D, 16, C, 16, None) == ALIGN
     assert U(4, 16, 16, 1e-5, BF16, 9, A, 16, G1, G2, B, 16, D, 16, C, 16, None) == DTYPE
     assert U(4, 16, 16, 1e-5, BF16, BF16, A, 16, G1, G2, B, 16, D, 16, G1 - 32, 16, None) == ALIAS
     assert U(4, 16, 16, 1e-5, BF16, BF16, A, 16, G1, G2, B, 16, D, 16, G2 - 32, 16, None) == ALIAS
@@ -219,7 +237,9 @@ def test_project_eliminated_validation(L):
     assert E(e2=float("nan")) == EPS
     assert E(e1=-1.0) == EPS
     assert E(gdt=3) == DTYPE
-    assert E(K=12, ldx=12, ldw=12) == ALIGN
+    assert E(K=12, ldx=12) == HIPERR            # any K
+    assert E(ldw=15) == SHAPE                   # ldw < nq + nk
+    assert E(x=A + 1) == ALIGN
     assert E(gq=None) == NULL
     assert E(gk=None) == NULL
     assert E(y=A) == ALIAS                     # output over x
@@ -241,8 +261,9 @@ def test_project_unfused_validation(L):
     assert U(e2=float("nan")) == EPS
     assert U(e1=-1.0) == EPS
     assert U(gdt=3) == DTYPE
-    assert U(K=12, ldx=12, ldw=12, ldxn=12) == ALIGN
-    assert U(xn=D + 2) == ALIGN
+    assert U(K=12, ldx=12, ldxn=12) == HIPERR   # any K
+    assert U(xn=D + 2) == HIPERR
+    assert U(xn=D + 1) == ALIGN
     assert U(gq=None) == NULL
     assert U(gk=None) == NULL
     assert U(g1=None) == NULL

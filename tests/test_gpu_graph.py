@@ -30,7 +30,7 @@ def test_graph_replays_match_eager():
     el_x = {T: to_dev(c["x"]) for T, c in el.items()}
     el_w = Q.normproj_fold_weight(to_dev(el[200]["w"]), to_dev(el[200]["gamma_pre"]))
     el_gq, el_gk = to_dev(el[200]["gamma_q"]), to_dev(el[200]["gamma_k"])
-    el_g1, el_wp = to_dev(el[200]["gamma_pre"]), Q.normproj_fold_weight(to_dev(el[200]["w"]), None)
+    el_g1, el_wp = to_dev(el[200]["gamma_pre"]), to_dev(el[200]["w"])
     ln = {T: inputs.make_layernorm_case(T, seed=8, K=512, N=256, x_mean=1.0) for T in (300, 5)}
     ln_x = {T: to_dev(c["x"]) for T, c in ln.items()}
     ln_w, ln_c, ln_b = Q.normproj_fold_layernorm(to_dev(ln[300]["w"]), to_dev(ln[300]["gamma"]),

@@ -64,7 +64,7 @@ def run_elimination(Q, c, exact, rows, what, chain_rows=None):
     y = Q.qknorm_project_eliminated(to_dev(c["x"]), wqk, nq, to_dev(c["gamma_q"]), gk,
                                     eps_qk=c["eps_qk"], eps_pre=c["eps_pre"], exact=exact)
     sync()
-    assert np.array_equal(to_host(wqk), wf_ref.T)
+    assert np.array_equal(to_host(wqk), wf_ref)
     got = to_host(y)[rows]
     xs = np.ascontiguousarray(c["x"][rows])
     wq_ref = np.ascontiguousarray(wf_ref[:, :nq])
@@ -126,13 +126,13 @@ def test_elimination_full_width(Q, T, exact):
                                        (37, 264, 200, 8), (129, 1024, 1024, 1024),
                                        (2048, 4096, 4096, 4096)])
 def test_project_unfused_chain(Q, T, K, nq, nk):
-    """The unsimplified chain in one call (RMSNorm launch, plain product with the packed
-    unfolded weight, QK-Norm in place): xn against the oracle's RMSNorm, y against the oracle
+    """The unsimplified chain in one call (RMSNorm launch, plain product with the unfolded
+    weight, QK-Norm in place): xn against the oracle's RMSNorm, y against the oracle
     chain. The GPU rounds xn and p to bf16 on the way: the relative term covers p, and xn's
     rounding (2^-9 relative per element) enters the product's accumulation bound, hence the
     2^-8 absolute coefficient (as for the fold's rounding above)."""
     c = inputs.make_elimination_case(T, seed=T + K + nq + nk, K=K, nq=nq, nk=nk)
-    wp = Q.normproj_fold_weight(to_dev(c["w"]), None)
+    wp = to_dev(c["w"])
     xn, y = Q.qknorm_project_unfused(to_dev(c["x"]), to_dev(c["gamma_pre"]), wp, nq,
                                      to_dev(c["gamma_q"]), to_dev(c["gamma_k"]),
                                      eps_qk=c["eps_qk"], eps_pre=c["eps_pre"])
@@ -184,7 +184,7 @@ def test_fold_layernorm(Q):
     wf_ref, cs_ref, b_ref = ln_reference_parts(c)
     wf, cs, b = Q.normproj_fold_layernorm(to_dev(c["w"]), to_dev(c["gamma"]), to_dev(c["beta"]))
     sync()
-    assert np.array_equal(to_host(wf), wf_ref.T)
+    assert np.array_equal(to_host(wf), wf_ref)
     # fp64 sums rounded once to fp32: within an fp32 rounding of the exact sum
     tol_c = 2.0 ** -23 * np.abs(cs_ref) + 2.0 ** -40 * np.abs(widen(wf_ref)).sum(axis=0)
     assert np.all(np.abs(to_host(cs).astype(np.float64) - cs_ref) <= tol_c)
@@ -279,7 +279,7 @@ def test_deferred_layernorm_row_stats(Q, T, K, N, pass_runs):
 
 def test_layernorm_unfused_baseline(Q):
     c = inputs.make_layernorm_case(2048, seed=3, x_mean=1.0)
-    wp = Q.normproj_fold_weight(to_dev(c["w"]), None)
+    wp = to_dev(c["w"])
     xn, y = Q.normproj_layernorm_unfused(to_dev(c["x"]), to_dev(c["gamma"]), to_dev(c["beta"]),
                                          wp, eps=c["eps"])
     sync()
