@@ -415,7 +415,7 @@ QKN_API int normproj_deferred(int64_t T, int64_t K, int64_t N, float eps, int dt
 {
     const int st = check_normproj(T, K, N, eps, dtype, x, ldx, w_fold, ldw, y, ldy);
     if (st != QKN_OK || T == 0 || N == 0) return st;
-    return hip_status(qkn::launch_normproj(T, K, N, eps, qkn::kEpiRms | qkn::kWeightRowMajor, x,
+    return hip_status(qkn::launch_normproj(T, K, N, eps, qkn::kEpiRms, x,
                                            ldx, w_fold, ldw, y, ldy, nullptr, nullptr, nullptr,
                                            (hipStream_t)stream));
 }
@@ -455,7 +455,7 @@ int unfused_rms_product(int64_t T, int64_t K, int64_t N, float eps, int dtype, i
     hipError_t e = qkn::launch_rows(job, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e);
     return hip_status(qkn::launch_normproj(T, K, N, eps,
-                                           qkn::kEpiPlain | qkn::kWeightRowMajor |
+                                           qkn::kEpiPlain |
                                                (keep_y ? qkn::kEpiKeepCached : 0),
                                            xn, ldxn, w, ldw, y, ldy, nullptr, nullptr, nullptr,
                                            (hipStream_t)stream));
@@ -530,19 +530,18 @@ int run_deferred_layernorm(int64_t T, int64_t K, int64_t N, float eps, const voi
                            void* stream)
 {
     const hipStream_t s = (hipStream_t)stream;
-    const int wl = qkn::kWeightRowMajor;
     // the workspace holds (mean, 1/std) pairs as 8-byte stores: one that is not 8-byte aligned
     // is left unused
     if (row_stats && ((uintptr_t)row_stats & 7u) == 0 &&
-        qkn::normproj_pipelined(T, K, N, x, ldx, w_fold, ldw, ldy, y, wl)) {
+        qkn::normproj_pipelined(T, K, N, x, ldx, w_fold, ldw, ldy, y)) {
         // statistics from one streaming pass over x; the product applies them in its epilogue
         const hipError_t e = qkn::launch_layernorm_stats(T, K, eps, x, ldx, row_stats, s);
         if (e != hipSuccess) return hip_status(e);
-        return hip_status(qkn::launch_normproj(T, K, N, eps, qkn::kEpiLayerNormStats | wl, x,
+        return hip_status(qkn::launch_normproj(T, K, N, eps, qkn::kEpiLayerNormStats, x,
                                                ldx, w_fold, ldw, y, ldy, colsum, bias, row_stats,
                                                s));
     }
-    return hip_status(qkn::launch_normproj(T, K, N, eps, qkn::kEpiLayerNorm | wl, x, ldx, w_fold,
+    return hip_status(qkn::launch_normproj(T, K, N, eps, qkn::kEpiLayerNorm, x, ldx, w_fold,
                                            ldw, y, ldy, colsum, bias, nullptr, s));
 }
 
@@ -640,7 +639,7 @@ QKN_API int normproj_layernorm_unfused(int64_t T, int64_t K, int64_t N, float ep
                                               gamma_dtype == QKN_BF16, xn, ldxn,
                                               (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e);
-    return hip_status(qkn::launch_normproj(T, K, N, eps, qkn::kEpiPlain | qkn::kWeightRowMajor,
+    return hip_status(qkn::launch_normproj(T, K, N, eps, qkn::kEpiPlain,
                                            xn, ldxn, w, ldw, y, ldy, nullptr, nullptr, nullptr,
                                            (hipStream_t)stream));
 }
@@ -703,7 +702,7 @@ QKN_API int qknorm_project_eliminated(int64_t T, int64_t K, int64_t nq, int64_t 
     // (ordinary stores: the row kernel below reads y straight back)
     hipError_t e = qkn::launch_normproj(T, K, N, eps_pre,
                                         (exact ? qkn::kEpiRms : qkn::kEpiPlain) |
-                                            qkn::kEpiKeepCached | qkn::kWeightRowMajor,
+                                            qkn::kEpiKeepCached,
                                         x, ldx, w_qk, ldw, y, ldy, nullptr, nullptr, nullptr,
                                         (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e);

@@ -3,8 +3,10 @@
 // extension to LayerNorm), plus the one-time weight folds, the LayerNorm row kernel of the
 // unfused baseline and a plain streaming copy used for calibration.
 //
-// acc[t, n] = sum_k x[t, k] * w[n, k] with both operands K-contiguous (the fold writes W'
-// transposed), on v_mfma_f32_32x32x16_bf16. The epilogue is one of
+// acc[t, n] = sum_k x[t, k] * w[k, n] with x row-major [T, K] and W' row-major [K, N] (the
+// layout of the weight the fold scales), on v_mfma_f32_32x32x16_bf16; the W' fragments, which
+// hold 8 consecutive k of one column per lane, come from LDS through the gfx950 transpose load
+// ds_read_b64_tr_b16. The epilogue is one of
 //   plain      y = acc
 //   RMSNorm    y = r_t * acc,                          r_t = 1 / sqrt(mean(x_t^2) + eps)
 //   LayerNorm  y = r_t * (acc - mu_t * c[n]) + b[n],   r_t = 1 / sqrt(var(x_t) + eps)
@@ -16,7 +18,8 @@
 // x0 the row's first element, so that the one-pass variance does not cancel for rows whose mean
 // is large against their spread.
 //
-// Pipelined kernel (K a multiple of the k-tile, N of 8): a workgroup owns a BM x BN output tile.
+// Pipelined kernel (K a multiple of the k-tile; N, strides and pointers 16-byte friendly): a
+// workgroup owns a BM x BN output tile.
 // Its k-tiles of x and W' reach LDS by direct global->LDS DMA (global_load_lds_dwordx4, 1 KB per
 // wavefront instruction, tile base in scalar registers and a 32-bit offset per lane), either
 // through an NST-deep ring of whole k-tiles or, for 256 x 256 tiles with k-tiles of 64 (64 KB
@@ -24,9 +27,10 @@
 // a k-tile is requested two k-tiles ahead and its W' part one ahead, which keeps one and a half
 // k-tiles in flight instead of one. With five parts or with 3 or more whole-tile stages, the
 // requests are spread over the k steps of the current k-tile rather than issued in one burst.
-// Each tile
-// row's 16-byte chunks are XOR-swizzled so the fragment reads of 16 consecutive rows fall in
-// 16 distinct bank groups. Wavefronts own WM x WN sub-tiles of 32 x 32 MFMA blocks, with the W'
+// The x
+// tile's rows have their 16-byte chunks XOR-swizzled so the fragment reads of 16 consecutive
+// rows fall in 16 distinct bank groups; the W' tile's k rows have their 64-byte segments
+// swizzled by the row so that the 4 rows a transpose load reads fall in distinct bank groups. Wavefronts own WM x WN sub-tiles of 32 x 32 MFMA blocks, with the W'
 // fragment as the MFMA's first operand so that a lane's accumulator holds one output row and
 // runs of 4 consecutive columns. The WN wavefronts that hold the same rows' x fragments take
 // turns over the k steps to accumulate the row statistics (sums of squares through
@@ -36,12 +40,12 @@
 // the output straight back. Workgroups are remapped so that each XCD works on a block of the
 // tile grid whose row and column panels its L2 can share (the split chosen per grid shape).
 //
-// Generic kernel (any K % 8 == 0, any N): 128 x 128 tiles through padded LDS rows with register
-// staging of the next k-tile.
+// Element kernel (any K, strides and 2-byte alignment): 128 x 128 tiles staged element by
+// element through padded LDS rows.
 //
 // Small T (<= 16) is a matrix-vector product bound by streaming W' once: 16x16x32 MFMAs with the
-// tokens as rows, W' and x staged through per-wavefront LDS by whole-line DMA, K split across a
-// workgroup's wavefronts in an order rotated per workgroup (normproj_mvl_kernel).
+// tokens as rows, W' and x staged through per-wavefront LDS by DMA, K split across a
+// workgroup's wavefronts (normproj_mvl_kernel).
 
 #include "device.h"
 #include "launch.h"
@@ -57,8 +61,6 @@ constexpr int kBN = 128;
 constexpr int kBK = 64;
 constexpr int kPitch = kBK + 8;             // LDS row pitch in bf16 elements (144 bytes)
 constexpr int kThreads = 256;
-constexpr int kChunksPerRow = kBK / 8;      // 16-byte chunks per tile row
-constexpr int kLoadsPerThread = kBM * kChunksPerRow / kThreads;  // 4
 
 __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c)
 {
@@ -188,14 +190,13 @@ __device__ __forceinline__ u32x2 lds_tr16(const char* p)
 }
 
 // NTS: non-temporal output stores (the output leaves the library) or ordinary ones.
-// WKN: W' is row-major [K, N] (N contiguous) instead of [N, K]; its k-tile lands in LDS as BK
-// rows of BN columns and the MFMA fragments (8 consecutive k of one column per lane) are read
-// with the LDS transpose load ds_read_b64_tr_b16 (gfx950). Within each 16-lane group that
-// instruction hands lane i, element j the 16-bit element i % 4 of the 8 bytes that lane
-// 4 j + i / 4 addressed: when lane 4 r + c of a group addresses columns 4 c .. 4 c + 3 of row
-// r of a 4-row block, lane i receives column i of rows 0..3.
-template <int BM, int BN, int WM, int WN, int NST, int BK, int EPI, bool RING, bool NTS,
-          bool WKN>
+// W' is row-major [K, N]: its k-tile lands in LDS as BK rows of BN columns and the MFMA
+// fragments (8 consecutive k of one column per lane) are read with the LDS transpose load
+// ds_read_b64_tr_b16 (gfx950). Within each 16-lane group that instruction hands lane i,
+// element j the 16-bit element i % 4 of the 8 bytes that lane 4 j + i / 4 addressed: when lane
+// 4 r + c of a group addresses columns 4 c .. 4 c + 3 of row r of a 4-row block, lane i
+// receives column i of rows 0..3.
+template <int BM, int BN, int WM, int WN, int NST, int BK, int EPI, bool RING, bool NTS>
 __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
     int64_t T, int64_t K, int64_t N, float eps, float inv_k, const uint16_t* __restrict__ x,
     int64_t ldx, const uint16_t* __restrict__ w, int64_t ldw, uint16_t* __restrict__ y,
@@ -206,12 +207,12 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
     constexpr int ROWB = BK * 2;            // bytes per tile row
     constexpr int RPC = 1024 / ROWB;        // tile rows per 1 KB DMA chunk
     constexpr int LPR = ROWB / 16;          // lanes per tile row within a chunk
-    // W' part: BN rows of BK (k contiguous) or, row-major, BK rows of BN (n contiguous)
-    constexpr int ROWB_B = WKN ? BN * 2 : ROWB;
+    // W' part: BK rows of BN columns (n contiguous)
+    constexpr int ROWB_B = BN * 2;
     constexpr int RPC_B = 1024 / ROWB_B, LPR_B = ROWB_B / 16;
-    constexpr int PART_A = BM * ROWB, PART_B = BN * ROWB, STAGE = PART_A + PART_B;
-    constexpr int CA = BM / RPC, CB = (WKN ? BK : BN) / RPC_B;
-    static_assert(!WKN || (RPC_B >= 1 && LPR_B <= kWave), "row-major W' tile rows");
+    constexpr int PART_A = BM * ROWB, PART_B = BK * ROWB_B, STAGE = PART_A + PART_B;
+    constexpr int CA = BM / RPC, CB = BK / RPC_B;
+    static_assert(RPC_B >= 1 && LPR_B <= kWave, "W' tile rows");
     static_assert(CA % NW == 0 && CB % NW == 0, "DMA chunks must divide among the wavefronts");
     constexpr int CPA = CA / NW, CPB = CB / NW;  // DMA instructions per wavefront per part
     constexpr int KS = BK / 16;
@@ -282,28 +283,21 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
     }
 #pragma unroll
     for (int c = 0; c < CPB; ++c) {
-        if constexpr (WKN) {
-            // k row trow of the tile, 16-byte chunk (8 columns) given by the lane's slot; chunks
-            // past N (a multiple of 8) read the last chunk and feed columns never stored
-            const int trow = (wave * CPB + c) * RPC_B + lane / LPR_B;
-            const int64_t col = n0 + (int64_t)swz_kn(lane % LPR_B, trow) * 8;
-            offb[c] = (uint32_t)((trow * ldw + ((col < N ? col : N - 8) - n0)) * 2);
-        } else {
-            const int trow = (wave * CPB + c) * RPC + lrow;
-            const int64_t r = n0 + trow < N ? n0 + trow : N - 1;
-            offb[c] = (uint32_t)(((r - n0) * ldw + swz<BK>(lane % LPR, trow) * 8) * 2);
-        }
+        // k row trow of the tile, 16-byte chunk (8 columns) given by the lane's slot; chunks past
+        // N (a multiple of 8) read the last chunk and feed columns never stored
+        const int trow = (wave * CPB + c) * RPC_B + lane / LPR_B;
+        const int64_t col = n0 + (int64_t)swz_kn(lane % LPR_B, trow) * 8;
+        offb[c] = (uint32_t)((trow * ldw + ((col < N ? col : N - 8) - n0)) * 2);
     }
     const uint16_t* xa = x + m0 * ldx;
-    const uint16_t* wb = WKN ? w + n0 : w + n0 * ldw;
-    const int64_t wstep = WKN ? ldw : 1;  // elements from one k to the next in W'
+    const uint16_t* wb = w + n0;
 
     // part: byte offset of the destination part within the pipeline buffer
     auto dma_a = [&](int c, uint32_t part, int64_t k0) {
         dma16s((const void*)(xa + k0), offa[c], lds0 + part + (uint32_t)(wave * CPA + c) * 1024u);
     };
     auto dma_b = [&](int c, uint32_t part, int64_t k0) {
-        dma16s((const void*)(wb + k0 * wstep), offb[c],
+        dma16s((const void*)(wb + k0 * ldw), offb[c],
                lds0 + part + (uint32_t)(wave * CPB + c) * 1024u);
     };
     auto issue_tile = [&](int slot, int64_t k0) {
@@ -322,12 +316,12 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
     const int frow = lane & 31, fk = lane >> 5;
-    // WKN fragment reads: lane 4 r + c of its 16-lane group g addresses row 8 (g / 2) + r (+ 4
+    // W' fragment reads: lane 4 r + c of its 16-lane group g addresses row 8 (g / 2) + r (+ 4
     // for the second half of the 8 k) at columns 16 (g % 2) + 4 c .. + 3 of 32-column block j;
     // boff[j] is that byte offset within the first k step (later steps add 16 rows, which
     // keeps the row modulo 4 and so the swizzle)
     uint32_t boff[TN];
-    if constexpr (WKN) {
+    {
         const int g = lane >> 4, i = lane & 15;
         const int r = 8 * (g >> 1) + (i >> 2);
 #pragma unroll
@@ -409,15 +403,10 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
             }
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
-                if constexpr (WKN) {
-                    // rows ks * 16 + ...: the swizzle depends on the row modulo 4 only
-                    const char* p = Bs + ks * 16 * ROWB_B + boff[j];
-                    const u32x2 lo = lds_tr16(p), hi = lds_tr16(p + 4 * ROWB_B);
-                    bfr[j] = u32x4{lo.x, lo.y, hi.x, hi.y};
-                } else {
-                    const int r = wn * WTN + j * 32 + frow;
-                    bfr[j] = *(const u32x4*)(Bs + r * ROWB + (swz<BK>(kc, r) << 4));
-                }
+                // rows ks * 16 + ...: the swizzle depends on the row modulo 4 only
+                const char* p = Bs + ks * 16 * ROWB_B + boff[j];
+                const u32x2 lo = lds_tr16(p), hi = lds_tr16(p + 4 * ROWB_B);
+                bfr[j] = u32x4{lo.x, lo.y, hi.x, hi.y};
             }
             if constexpr (kStatsInLoop<EPI>) {
                 // the WN wavefronts holding the same rows take turns over the k steps
@@ -567,166 +556,12 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
     }
 }
 
-// ------------------------------------------------------------------------------------------
-// Generic kernel.
-
-template <int EPI>
-__global__ __launch_bounds__(kThreads) void normproj_mfma_kernel(
-    int64_t T, int64_t K, int64_t N, float eps, float inv_k, const uint16_t* __restrict__ x,
-    int64_t ldx, const uint16_t* __restrict__ w, int64_t ldw, uint16_t* __restrict__ y,
-    int64_t ldy, int nbm, int nbn, const float* __restrict__ colsum,
-    const float* __restrict__ bias)
-{
-    __shared__ __attribute__((aligned(16))) uint16_t As[kBM * kPitch];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[kBN * kPitch];
-    __shared__ float rstd[kBM];
-    __shared__ float mean[EPI == kEpiLayerNorm ? kBM : 1];
-
-    // Blocks are handed to the 8 XCDs round-robin; give each XCD a contiguous range of tiles
-    // (whole row panels of x) so that panel is fetched into one XCD's L2 only.
-    const int nb = nbm * nbn;
-    int bid = (int)blockIdx.x;
-    if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
-    const int tm = bid / nbn;
-    const int tn = bid % nbn;
-    const int64_t m0 = (int64_t)tm * kBM;
-    const int64_t n0 = (int64_t)tn * kBN;
-
-    const int tid = (int)threadIdx.x;
-    const int lane = lane_id();
-    const int wave = tid / kWave;
-    const int wm = wave >> 1, wn = wave & 1;
-
-    // Global -> register staging: chunk c of this thread is tile row (tid/8 + 32c), k-chunk tid%8.
-    const int ld_row = tid / kChunksPerRow;
-    const int ld_kc = tid % kChunksPerRow;
-    u32x4 ra[kLoadsPerThread], rb[kLoadsPerThread];
-    float s1[kLoadsPerThread], s2[kLoadsPerThread], x0[kLoadsPerThread];
-#pragma unroll
-    for (int c = 0; c < kLoadsPerThread; ++c) {
-        s1[c] = s2[c] = x0[c] = 0.0f;
-        if constexpr (EPI == kEpiLayerNorm) {
-            const int64_t gm = m0 + ld_row + c * (kThreads / kChunksPerRow);
-            x0[c] = bf16_at(x, (gm < T ? gm : T - 1) * ldx);
-        }
-    }
-
-    auto load_tiles = [&](int64_t k0) {
-        const int64_t k = k0 + ld_kc * 8;
-#pragma unroll
-        for (int c = 0; c < kLoadsPerThread; ++c) {
-            const int r = ld_row + c * (kThreads / kChunksPerRow);
-            const int64_t gm = m0 + r, gn = n0 + r;
-            ra[c] = (gm < T && k < K) ? *(const u32x4*)(x + gm * ldx + k) : u32x4{0u, 0u, 0u, 0u};
-            rb[c] = (gn < N && k < K) ? *(const u32x4*)(w + gn * ldw + k) : u32x4{0u, 0u, 0u, 0u};
-        }
-    };
-    // k0: first column of the tile just loaded; chunks past K were zero-filled and are left
-    // out of the LayerNorm sums (their shifted values would not be zero)
-    auto store_tiles = [&](int64_t k0) {
-        const bool kin = k0 + ld_kc * 8 < K;
-#pragma unroll
-        for (int c = 0; c < kLoadsPerThread; ++c) {
-            const int r = ld_row + c * (kThreads / kChunksPerRow);
-            *(u32x4*)(As + r * kPitch + ld_kc * 8) = ra[c];
-            *(u32x4*)(Bs + r * kPitch + ld_kc * 8) = rb[c];
-            if constexpr (EPI != kEpiPlain) {
-                if (kin) accum_stats<EPI>(ra[c], x0[c], s1[c], s2[c]);
-            }
-        }
-    };
-
-    f32x16 acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-    const int64_t nk = (K + kBK - 1) / kBK;
-    load_tiles(0);
-    store_tiles(0);
-    __syncthreads();
-
-    // MFMA operand fragments: lane holds row (lane % 32) of a 32-row block, 8 consecutive k
-    // starting at 8 * (lane / 32) within each 16-wide k step.
-    const int frag_row = lane & 31;
-    const int frag_k = (lane >> 5) * 8;
-    for (int64_t kt = 0; kt < nk; ++kt) {
-        if (kt + 1 < nk) load_tiles((kt + 1) * kBK);
-#pragma unroll
-        for (int ks = 0; ks < kBK / 16; ++ks) {
-            u32x4 af[2], bfr[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                af[i] = *(const u32x4*)(As + (wm * 64 + i * 32 + frag_row) * kPitch + ks * 16 + frag_k);
-                bfr[i] = *(const u32x4*)(Bs + (wn * 64 + i * 32 + frag_row) * kPitch + ks * 16 + frag_k);
-            }
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
-        }
-        __syncthreads();
-        if (kt + 1 < nk) {
-            store_tiles((kt + 1) * kBK);
-            __syncthreads();
-        }
-    }
-
-    if constexpr (EPI != kEpiPlain) {
-        // Combine the 8 threads that share each tile row, then the row's scale.
-#pragma unroll
-        for (int c = 0; c < kLoadsPerThread; ++c) {
-            const float q2 = sum8(s2[c]);
-            const float q1 = sum8(s1[c]);
-            float rs, mu;
-            row_scale<EPI>(q1, q2, x0[c], inv_k, eps, rs, mu);
-            if (ld_kc == 0) {
-                rstd[ld_row + c * (kThreads / kChunksPerRow)] = rs;
-                if constexpr (EPI == kEpiLayerNorm) mean[ld_row + c * (kThreads / kChunksPerRow)] = mu;
-            }
-        }
-        __syncthreads();
-    }
-
-    // Accumulator layout of a 32x32 block: lane holds column lane % 32, and for e in 0..15 the
-    // row 8 * (e / 4) + 4 * (lane / 32) + e % 4.
-    const int out_col = lane & 31;
-    const int out_row = (lane >> 5) * 4;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int64_t gn = n0 + wn * 64 + j * 32 + out_col;
-            float cs = 0.0f, bs = 0.0f;
-            if constexpr (EPI == kEpiLayerNorm) {
-                if (gn < N) {
-                    cs = colsum[gn];
-                    if (bias) bs = bias[gn];
-                }
-            }
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int r = wm * 64 + i * 32 + 8 * (e / 4) + out_row + (e % 4);
-                const int64_t gm = m0 + r;
-                float v = acc[i][j][e];
-                if constexpr (EPI == kEpiRms) v *= rstd[r];
-                if constexpr (EPI == kEpiLayerNorm) v = epilogue<EPI>(v, rstd[r], mean[r], cs, bs);
-                if (gm < T && gn < N) y[gm * ldy + gn] = to_bf16(v);
-            }
-        }
-    }
-}
-
-// Element kernel: any K, any row strides, any 2-byte alignment of x, W' and y, W' in either
-// layout. 128 x 128 tiles, k-tiles of 64; each thread loads 32 elements of x and of W' per
+// Element kernel: any K, any row strides, any 2-byte alignment of x, W' and y. 128 x 128 tiles, k-tiles of 64; each thread loads 32 elements of x and of W' per
 // k-tile with 2-byte loads (consecutive threads on consecutive elements of a row), which it
 // stores into padded LDS rows k-contiguous for both operands before the matrix-core loop of
 // the generic kernel. Elements past T, N or K are zero. The row statistics are summed from the
 // staged x tile in LDS (two threads per row, 32 columns each), elements past K left out.
-template <int EPI, bool WKN>
+template <int EPI>
 __global__ __launch_bounds__(kThreads) void normproj_elem_kernel(
     int64_t T, int64_t K, int64_t N, float eps, float inv_k, const uint16_t* __restrict__ x,
     int64_t ldx, const uint16_t* __restrict__ w, int64_t ldw, uint16_t* __restrict__ y,
@@ -752,22 +587,16 @@ __global__ __launch_bounds__(kThreads) void normproj_elem_kernel(
 
     uint16_t ra[kPer], rb[kPer];
     // element e of this thread: x tile row (e * 256 + tid) / 64, column tid % 64; W' element
-    // (n, k) with n = (e * 256 + tid) % 128 and k = (e * 256 + tid) / 128 when row-major (so
-    // consecutive threads read consecutive columns), else n = (e * 256 + tid) / 64,
-    // k = tid % 64
+    // (k, n) with n = (e * 256 + tid) % 128 and k = (e * 256 + tid) / 128 (consecutive threads
+    // read consecutive columns), stored transposed (k contiguous) for the fragment reads
     auto load_tiles = [&](int64_t k0) {
 #pragma unroll
         for (int e = 0; e < kPer; ++e) {
             const int idx = e * kThreads + tid;
             const int64_t gm = m0 + idx / kBK, gk = k0 + idx % kBK;
             ra[e] = (gm < T && gk < K) ? x[gm * ldx + gk] : (uint16_t)0;
-            if constexpr (WKN) {
-                const int64_t gn = n0 + idx % kBN, wk = k0 + idx / kBN;
-                rb[e] = (gn < N && wk < K) ? w[wk * ldw + gn] : (uint16_t)0;
-            } else {
-                const int64_t gn = n0 + idx / kBK;
-                rb[e] = (gn < N && gk < K) ? w[gn * ldw + gk] : (uint16_t)0;
-            }
+            const int64_t gn = n0 + idx % kBN, wk = k0 + idx / kBN;
+            rb[e] = (gn < N && wk < K) ? w[wk * ldw + gn] : (uint16_t)0;
         }
     };
     auto store_tiles = [&]() {
@@ -775,8 +604,7 @@ __global__ __launch_bounds__(kThreads) void normproj_elem_kernel(
         for (int e = 0; e < kPer; ++e) {
             const int idx = e * kThreads + tid;
             As[(idx / kBK) * kPitch + idx % kBK] = ra[e];
-            if constexpr (WKN) Bs[(idx % kBN) * kPitch + idx / kBN] = rb[e];
-            else Bs[(idx / kBK) * kPitch + idx % kBK] = rb[e];
+            Bs[(idx % kBN) * kPitch + idx / kBN] = rb[e];
         }
     };
 
@@ -886,29 +714,25 @@ __global__ __launch_bounds__(kThreads) void normproj_elem_kernel(
 }
 
 // Matrix-vector form for T <= 16 on the matrix cores: v_mfma_f32_16x16x32_bf16 with the (up
-// to 16) tokens as the M dimension and 16 W' rows (output columns) as N. Fragment layout: lane
-// l supplies A[l % 16][8 (l / 16) .. + 7] and B[8 (l / 16) .. + 7][l % 16]; it receives
+// to 16) tokens as the M dimension and 16 columns of W' as N. Fragment layout: lane l supplies
+// A[l % 16][8 (l / 16) .. + 7] and B[8 (l / 16) .. + 7][l % 16]; it receives
 // D[4 (l / 16) + i][l % 16] for i = 0..3.
 //
-// Loaded straight into registers, those fragments put 16 W' rows x 64 bytes under each load
-// instruction, a shape that streams at about three quarters of the rate of whole 128-byte
-// lines. Instead each wavefront fetches a step of 64 k of its tiles with the LDS DMA, every
-// instruction covering 8 rows x 128 B, into a region of LDS of its own, and reads the fragments
-// back with ds_read_b128. The x rows of the step travel the same way, so every global access of
-// the k loop is a DMA counted by vmcnt alone and the wavefront keeps S steps in flight under
-// its own waits (no barriers: nothing in the loop is shared between wavefronts). A workgroup
-// owns NTILE 16-column tiles; its wavefronts split K into interleaved steps and add their
-// partial products (and row sums) through LDS in a fixed order. Workgroup b starts its walk
-// over K kMvRotate * b steps in: in lockstep, every workgroup would read the same x lines and
-// the same k range of W' at a time, piling the requests onto a few L2 channels.
+// Each wavefront fetches a step of 64 k of its tiles with the LDS DMA into a region of LDS of
+// its own and reads the fragments back from there (x with ds_read_b128, W' with transpose
+// loads). The x rows of the step travel the same way, so every global access of the k loop is a
+// DMA counted by vmcnt alone and the wavefront keeps S steps in flight under its own waits (no
+// barriers: nothing in the loop is shared between wavefronts). A workgroup owns NTILE 16-column
+// tiles; its wavefronts split K into interleaved steps and add their partial products (and row
+// sums) through LDS in a fixed order. Every workgroup walks K from the start, so that at any
+// time the chip reads whole consecutive k rows of W'.
 //
-// Step layout (16 rows, 2 KB): row r, 16-byte chunk c (8 k values) at byte
+// x step layout (16 rows, 2 KB): row r, 16-byte chunk c (8 k values) at byte
 // (r & 1) * 1024 + (r >> 1) * 128 + (c ^ mvl_f(r)) * 16. One DMA instruction fills the even
 // rows and one the odd rows, each lane fetching the chunk its destination slot stands for; a
 // fragment read (16 rows at one chunk per 16-lane phase) then touches 16 distinct 16-byte bank
 // groups of the 256-byte bank row. Steps of up to 8 x rows use r * 128 + (c ^ (r >> 1)) * 16.
 constexpr int kGemvMaxT = 16;
-constexpr int kMvRotate = 7;
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
@@ -951,13 +775,30 @@ __device__ __forceinline__ void wait_steps(int later)
     }
 }
 
-// Row-major W' ([K, N], WKN): a tile's step is 64 k rows of 32 bytes (16 columns), row k of
-// the step in slot mvk_slot(k) (slot s at byte 32 s). A fragment is two transpose loads, each
-// 4 rows x 16 columns per 16-lane group; the slot order puts the two groups of a half-wavefront
-// (rows 8 apart) in different halves of the 256-byte bank row.
+// W' step layout: 64 k rows of the workgroup's 16 NTILE columns, each
+// row 32 NTILE contiguous bytes (one 32-byte segment per tile), so a DMA instruction covers
+// 32 / NTILE rows with whole 32 NTILE-byte runs of W' rows. A fragment is two transpose loads,
+// each 4 rows x 16 columns per 16-lane group; a half-wavefront's two groups read rows 8 apart.
+// With one tile, row k sits in slot mvk_slot(k) (32 bytes each), which puts those rows in
+// different halves of the 256-byte bank row; with two, row k sits at 64 k and tile j's
+// segment at physical segment j ^ mvk_seg<2>(k), so the 8 rows a half-wavefront reads at one
+// tile cover the 64 banks once.
 __device__ __forceinline__ int mvk_slot(int k) { return k ^ (((k >> 3) & 1) << 2); }
+template <int NTILE>
+__device__ __forceinline__ int mvk_seg(int k)
+{
+    static_assert(NTILE == 1 || NTILE == 2, "row-major W' tiles per workgroup");
+    return NTILE == 2 ? (k >> 3) & 1 : 0;
+}
+// Byte offset of row k, tile j, column c (a multiple of 4) within a W' step.
+template <int NTILE>
+__device__ __forceinline__ uint32_t mvk_off(int k, int j, int c)
+{
+    if constexpr (NTILE == 1) return (uint32_t)((mvk_slot(k) << 5) + (c << 1));
+    else return (uint32_t)(k * 32 * NTILE + ((j ^ mvk_seg<NTILE>(k)) << 5) + (c << 1));
+}
 
-template <int EPI, int NTILE, int XR, int WAVES, int S, bool WKN>
+template <int EPI, int NTILE, int XR, int WAVES, int S>
 __global__ __launch_bounds__(WAVES * 64) void normproj_mvl_kernel(
     int T, int64_t K, int64_t N, float eps, float inv_k, const uint16_t* __restrict__ x,
     int64_t ldx, const uint16_t* __restrict__ w, int64_t ldw, uint16_t* __restrict__ y,
@@ -977,35 +818,51 @@ __global__ __launch_bounds__(WAVES * 64) void normproj_mvl_kernel(
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
     const int r16 = lane & 15, g = lane >> 4;
-    const int64_t n0 = (int64_t)blockIdx.x * kCols;
+    // A 128-byte line of a k row of W' holds kShare tiles. Workgroup b runs on XCD b % 8;
+    // within each group of 8 kShare workgroups, those on one XCD take kShare adjacent tiles
+    // (and walk K in the same order), so each line is fetched into one L2 and served there to
+    // the workgroups that share it. Tiles past the last whole group keep their index.
+    constexpr int kShare = 4 / NTILE;
+    int tile = (int)blockIdx.x;
+    if constexpr (kShare > 1) {
+        const int full = ((int)gridDim.x / (8 * kShare)) * (8 * kShare);
+        if (tile < full) {
+            const int r = tile % (8 * kShare);
+            tile = tile - r + (r & 7) * kShare + (r >> 3);
+        }
+    }
+    const int64_t n0 = (int64_t)tile * kCols;
     char* region = smem + wave * REGION;
     const uint32_t lds_region = (uint32_t)(uintptr_t)(lds_void*)region;
 
-    // DMA sources, as a row byte offset (from the tile's first W' row, or from x) and a chunk
-    // byte offset within the step. Rows past N read row N - 1 and token rows past T read row
-    // T - 1: they feed outputs that are never stored. The offsets fit 32 bits for ld < 2^23.
+    // DMA sources, as a row byte offset (from the step's first k row of W', or from x) and a
+    // chunk byte offset. Token rows past T read row T - 1: they feed outputs that are never
+    // stored. The offsets fit 32 bits for ld < 2^25.
     const int drow = lane >> 3, dc = lane & 7;
     uint32_t wrow[NTILE][2], wch[NTILE][2], xrow[XH], xch[XH];
-    // WKN: instruction h of tile j fills slots 32 h .. 32 h + 31, lane l slot 32 h + l / 2 and
-    // its 16-byte half l % 2: wrow is that slot's k row within the step (scaled by the row
-    // stride later), wch the byte offset of the lane's 8 columns from column n0 (chunks past N,
-    // a multiple of 8, read the last chunk and feed columns never stored)
-    int wk[2] = {0, 0};
+    // W': instruction i = 2 j + h of a step fills bytes 1024 i .. 1024 i + 1023, rows
+    // R i .. R i + R - 1 (R = 32 / NTILE), lane l the row's 16-byte chunk l % (2 NTILE): wk
+    // is the k row the lane's slot holds, wrow its byte offset (from the step's first row), wch
+    // the byte offset of the lane's 8 columns from column n0 (chunks past N, a multiple of 8,
+    // read the last chunk and feed columns never stored)
+    int wk[NTILE][2];
 #pragma unroll
     for (int j = 0; j < NTILE; ++j)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            if constexpr (WKN) {
-                wk[h] = mvk_slot(32 * h + (lane >> 1));
-                const int64_t n = n0 + 16 * j + 8 * (lane & 1);
-                wrow[j][h] = (uint32_t)(wk[h] * ldw * 2);
-                wch[j][h] = (uint32_t)(((n < N ? n : N - 8) - n0) * 2);
+            constexpr int R = 32 / NTILE, LPRW = 2 * NTILE;
+            const int slot = (2 * j + h) * R + lane / LPRW, pc = lane % LPRW;
+            int col;
+            if constexpr (NTILE == 1) {
+                wk[j][h] = mvk_slot(slot);
+                col = 8 * pc;
             } else {
-                const int r = 2 * drow + h;
-                const int64_t n = n0 + 16 * j + r;
-                wrow[j][h] = (uint32_t)(((n < N ? n : N - 1) - n0) * ldw * 2);
-                wch[j][h] = (uint32_t)((dc ^ mvl_f(r)) << 4);
+                wk[j][h] = slot;
+                col = 16 * ((pc >> 1) ^ mvk_seg<NTILE>(slot)) + 8 * (pc & 1);
             }
+            const int64_t n = n0 + col;
+            wrow[j][h] = (uint32_t)(wk[j][h] * ldw * 2);
+            wch[j][h] = (uint32_t)(((n < N ? n : N - 8) - n0) * 2);
         }
 #pragma unroll
     for (int h = 0; h < XH; ++h) {
@@ -1013,7 +870,7 @@ __global__ __launch_bounds__(WAVES * 64) void normproj_mvl_kernel(
         xrow[h] = (uint32_t)((r < T ? r : T - 1) * ldx * 2);
         xch[h] = (uint32_t)((XH == 1 ? dc ^ (r >> 1) : dc ^ mvl_f(r)) << 4);
     }
-    const uint16_t* wb = WKN ? w + n0 : w + n0 * ldw;
+    const uint16_t* wb = w + n0;
     const uint32_t kbytes = (uint32_t)(K * 2);
 
     float x0 = 0.0f;
@@ -1028,27 +885,16 @@ __global__ __launch_bounds__(WAVES * 64) void normproj_mvl_kernel(
         const bool full = kb + 128u <= kbytes;
         const uint32_t dst = lds_region + (uint32_t)(slot * STAGE);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the slot's fragment reads are done
-        if constexpr (WKN) {
-            // the step's first k row as the scalar base; rows past K read row K - 1 (zeroed at
-            // use like the chunks past K of the other layout)
-            const uint16_t* wst = wb + st * 64 * ldw;
+        // the step's first k row as the scalar base; rows past K read row K - 1 (zeroed at use)
+        const uint16_t* wst = wb + st * 64 * ldw;
 #pragma unroll
-            for (int j = 0; j < NTILE; ++j)
+        for (int j = 0; j < NTILE; ++j)
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    uint32_t ro = wrow[j][h];
-                    if (!full && st * 64 + wk[h] >= K) ro = (uint32_t)((K - 1 - st * 64) * ldw * 2);
-                    dma16s(wst, ro + wch[j][h], dst + (uint32_t)(j * 2048 + h * 1024));
-                }
-        } else {
-#pragma unroll
-            for (int j = 0; j < NTILE; ++j)
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const uint32_t c = full ? kb + wch[j][h] : min(kb + wch[j][h], kbytes - 16u);
-                    dma16s(wb, wrow[j][h] + c, dst + (uint32_t)(j * 2048 + h * 1024));
-                }
-        }
+            for (int h = 0; h < 2; ++h) {
+                uint32_t ro = wrow[j][h];
+                if (!full && st * 64 + wk[j][h] >= K) ro = (uint32_t)((K - 1 - st * 64) * ldw * 2);
+                dma16s(wst, ro + wch[j][h], dst + (uint32_t)(j * 2048 + h * 1024));
+            }
 #pragma unroll
         for (int h = 0; h < XH; ++h) {
             const uint32_t c = full ? kb + xch[h] : min(kb + xch[h], kbytes - 16u);
@@ -1071,16 +917,11 @@ __global__ __launch_bounds__(WAVES * 64) void normproj_mvl_kernel(
                                                           : mvl_off8(r16 & (XR - 1), c)));
 #pragma unroll
             for (int j = 0; j < NTILE; ++j) {
-                if constexpr (WKN) {
-                    // rows 32 q + 8 g + (r16 >> 2) (+ 4), columns 4 (r16 & 3) .. + 3
-                    const int k0 = 32 * q + 8 * g + (r16 >> 2);
-                    const char* p = sp + j * 2048 + ((r16 & 3) << 3);
-                    const u32x2 lo = lds_tr16(p + (mvk_slot(k0) << 5));
-                    const u32x2 hi = lds_tr16(p + (mvk_slot(k0 + 4) << 5));
-                    b[j][q] = u32x4{lo.x, lo.y, hi.x, hi.y};
-                } else {
-                    b[j][q] = *(const u32x4*)(sp + j * 2048 + mvl_off16(r16, c));
-                }
+                // rows 32 q + 8 g + (r16 >> 2) (+ 4), columns 4 (r16 & 3) .. + 3 of tile j
+                const int k0 = 32 * q + 8 * g + (r16 >> 2);
+                const u32x2 lo = lds_tr16(sp + mvk_off<NTILE>(k0, j, 4 * (r16 & 3)));
+                const u32x2 hi = lds_tr16(sp + mvk_off<NTILE>(k0 + 4, j, 4 * (r16 & 3)));
+                b[j][q] = u32x4{lo.x, lo.y, hi.x, hi.y};
             }
         }
         bool kin[2] = {true, true};
@@ -1108,13 +949,7 @@ __global__ __launch_bounds__(WAVES * 64) void normproj_mvl_kernel(
 
     const int64_t nsteps = (K + 63) / 64;
     const int nmine = wave < nsteps ? (int)((nsteps - 1 - wave) / WAVES) + 1 : 0;
-    // (32-bit: nsteps < 2^20 for the strides this kernel accepts)
-    const uint32_t ns32 = (uint32_t)nsteps;
-    const int64_t rot = ns32 ? (int64_t)(((blockIdx.x % ns32) * kMvRotate) % ns32) : 0;
-    auto step = [&](int i) {
-        const int64_t st = wave + (int64_t)i * WAVES + rot;
-        return st >= nsteps ? st - nsteps : st;
-    };
+    auto step = [&](int i) { return wave + (int64_t)i * WAVES; };
 #pragma unroll
     for (int i = 0; i < S; ++i)
         if (i < nmine) issue(step(i), i);
@@ -1357,8 +1192,7 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(char* __restrict__ dst,
     for (int64_t i = done + tid; i < nbytes; i += stride) dst[i] = src[i];
 }
 
-template <int BM, int BN, int WM, int WN, int NST, int BK, int EPI, bool RING, bool NTS,
-          bool WKN>
+template <int BM, int BN, int WM, int WN, int NST, int BK, int EPI, bool RING, bool NTS>
 hipError_t launch_pipe_t(int64_t T, int64_t K, int64_t N, float eps, float inv_k,
                          const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
                          uint16_t* y, int64_t ldy, const float* colsum, const float* bias,
@@ -1366,7 +1200,7 @@ hipError_t launch_pipe_t(int64_t T, int64_t K, int64_t N, float eps, float inv_k
 {
     const int64_t nbm = (T + BM - 1) / BM, nbn = (N + BN - 1) / BN;
     if (nbm * nbn > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((normproj_pipe_kernel<BM, BN, WM, WN, NST, BK, EPI, RING, NTS, WKN>),
+    hipLaunchKernelGGL((normproj_pipe_kernel<BM, BN, WM, WN, NST, BK, EPI, RING, NTS>),
                        dim3((unsigned)(nbm * nbn)), dim3(WM * WN * kWave), 0, st, T, K, N, eps,
                        inv_k, x, ldx, w, ldw, y, ldy, (int)nbm, (int)nbn, colsum, bias, rowstats);
     return hipGetLastError();
@@ -1374,7 +1208,7 @@ hipError_t launch_pipe_t(int64_t T, int64_t K, int64_t N, float eps, float inv_k
 
 // Ordinary output stores exist for the epilogues whose output the library reads back itself
 // (the pre-norm elimination: plain or RMSNorm).
-template <int BM, int BN, int WM, int WN, int NST, int BK, int EPI, bool RING, bool WKN>
+template <int BM, int BN, int WM, int WN, int NST, int BK, int EPI, bool RING>
 hipError_t launch_pipe(int64_t T, int64_t K, int64_t N, float eps, float inv_k,
                        const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
                        uint16_t* y, int64_t ldy, const float* colsum, const float* bias,
@@ -1382,10 +1216,10 @@ hipError_t launch_pipe(int64_t T, int64_t K, int64_t N, float eps, float inv_k,
 {
     if constexpr (EPI == kEpiPlain || EPI == kEpiRms) {
         if (!nts)
-            return launch_pipe_t<BM, BN, WM, WN, NST, BK, EPI, RING, false, WKN>(
+            return launch_pipe_t<BM, BN, WM, WN, NST, BK, EPI, RING, false>(
                 T, K, N, eps, inv_k, x, ldx, w, ldw, y, ldy, colsum, bias, rowstats, st);
     }
-    return launch_pipe_t<BM, BN, WM, WN, NST, BK, EPI, RING, true, WKN>(
+    return launch_pipe_t<BM, BN, WM, WN, NST, BK, EPI, RING, true>(
         T, K, N, eps, inv_k, x, ldx, w, ldw, y, ldy, colsum, bias, rowstats, st);
 }
 
@@ -1402,13 +1236,13 @@ struct MvJob {
     hipStream_t st;
 };
 
-template <int EPI, int NTILE, int XR, int WAVES, int S, bool WKN>
+template <int EPI, int NTILE, int XR, int WAVES, int S>
 hipError_t launch_mvl(const MvJob& j)
 {
     constexpr int kCols = 16 * NTILE;
     const int64_t nblk = (j.N + kCols - 1) / kCols;
     if (nblk > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((normproj_mvl_kernel<EPI, NTILE, XR, WAVES, S, WKN>), dim3((unsigned)nblk),
+    hipLaunchKernelGGL((normproj_mvl_kernel<EPI, NTILE, XR, WAVES, S>), dim3((unsigned)nblk),
                        dim3(WAVES * kWave), 0, j.st, (int)j.T, j.K, j.N, j.eps, j.inv_k, j.x,
                        j.ldx, j.w, j.ldw, j.y, j.ldy, j.colsum, j.bias);
     return hipGetLastError();
@@ -1418,39 +1252,42 @@ hipError_t launch_mvl(const MvJob& j)
 // wavefronts (two workgroups per CU) for outputs up to 4096 wide or up to 4 tokens; otherwise
 // two tiles (one workgroup per CU), each x fragment then feeding two MFMAs. The step count
 // fills the LDS the workgroups per CU leave.
-template <int EPI, bool WKN>
+// x rows per step: T rounded up to a power of two. Two 16-column tiles (64-byte runs of W'
+// rows) per workgroup once that still gives 128 workgroups, else one (32-byte runs); measured
+// at T = 16, N = 8192: two tiles 22.8 us, four (whole 128-byte runs, half the workgroups)
+// 25.3 us, one 27.7 us. The step count fills the LDS.
+template <int EPI>
 hipError_t launch_mv(const MvJob& j)
 {
-    if (j.N <= 4096 || j.T <= 4) {
-        if (j.T <= 1) return launch_mvl<EPI, 1, 1, 8, 4, WKN>(j);
-        if (j.T <= 2) return launch_mvl<EPI, 1, 2, 8, 4, WKN>(j);
-        if (j.T <= 4) return launch_mvl<EPI, 1, 4, 8, 4, WKN>(j);
-        if (j.T <= 8) return launch_mvl<EPI, 1, 8, 8, 3, WKN>(j);
-        return launch_mvl<EPI, 1, 16, 8, 2, WKN>(j);
+    if (j.N >= 32 * 128) {
+        if (j.T <= 8) return launch_mvl<EPI, 2, 8, 8, 3>(j);
+        return launch_mvl<EPI, 2, 16, 8, 3>(j);
     }
-    if (j.T <= 8) return launch_mvl<EPI, 2, 8, 8, 4, WKN>(j);
-    return launch_mvl<EPI, 2, 16, 8, 3, WKN>(j);
+    if (j.T <= 1) return launch_mvl<EPI, 1, 1, 8, 4>(j);
+    if (j.T <= 2) return launch_mvl<EPI, 1, 2, 8, 4>(j);
+    if (j.T <= 4) return launch_mvl<EPI, 1, 4, 8, 4>(j);
+    if (j.T <= 8) return launch_mvl<EPI, 1, 8, 8, 3>(j);
+    return launch_mvl<EPI, 1, 16, 8, 2>(j);
 }
 
 // Kernel choice for a product shape.
-enum Path { kPathMv, kPathBig64, kPathBig32, kPathMid, kPathMidDeep, kPathGeneric, kPathElem };
+enum Path { kPathMv, kPathBig64, kPathBig32, kPathMid, kPathMidDeep, kPathElem };
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 Path choose_path(int64_t T, int64_t K, int64_t N, const void* x, int64_t ldx, const void* w,
-                 int64_t ldw, int64_t ldy, const void* y, bool wkn)
+                 int64_t ldw, int64_t ldy, const void* y)
 {
-    // 16-byte accesses along k of x (and of W' [N, K]) or along n of W' [K, N]; anything else
-    // takes the element kernel
-    const bool vec = K % 8 == 0 && ldx % 8 == 0 && ldw % 8 == 0 && aligned16(x) &&
-                     aligned16(w) && (!wkn || N % 8 == 0);
+    // 16-byte accesses along k of x and along n of W'; anything else takes the element kernel
+    const bool vec = K % 8 == 0 && N % 8 == 0 && ldx % 8 == 0 && ldw % 8 == 0 && aligned16(x) &&
+                     aligned16(w);
     if (!vec) return kPathElem;
-    // the matrix-vector kernel addresses W' and x rows with 32-bit byte offsets from the
-    // first row of a tile (at most 32 rows, or 64 k rows of a row-major W') or of x (at most 16)
+    // the matrix-vector kernel addresses W' and x rows with 32-bit byte offsets from the first
+    // of 64 k rows of W' or of x (at most 16 rows)
     if (T <= kGemvMaxT && ldx < (int64_t(1) << 25) && ldw < (int64_t(1) << 25)) return kPathMv;
     // the pipelined kernels address a tile's rows with 32-bit byte offsets from its first row
-    const bool pipe_ok = N % 8 == 0 && ldy % 8 == 0 && aligned16(y) &&
-                         ldx < (int64_t(1) << 23) && ldw < (int64_t(1) << 23);
+    const bool pipe_ok = ldy % 8 == 0 && aligned16(y) && ldx < (int64_t(1) << 23) &&
+                         ldw < (int64_t(1) << 23);
     const int64_t big_tiles = ((T + 255) / 256) * ((N + 255) / 256);
     // at least one 256 x 256 tile per CU: 8 wavefronts of 64 x 128, k-tiles of 64 through the
     // ring of five parts, or of 32 in 4 whole-tile stages when K needs it
@@ -1462,29 +1299,29 @@ Path choose_path(int64_t T, int64_t K, int64_t N, const void* x, int64_t ldx, co
     // the second workgroup would have used
     const int64_t mid_tiles = ((T + 127) / 128) * ((N + 127) / 128);
     if (pipe_ok && K % 64 == 0) return mid_tiles <= 256 ? kPathMidDeep : kPathMid;
-    // the 16-byte generic kernel reads W' along k only
-    return wkn ? kPathElem : kPathGeneric;
+    return kPathElem;
 }
 
-template <int EPI, bool WKN>
-hipError_t launch_epi(Path path, int64_t T, int64_t K, int64_t N, float eps, const uint16_t* xp,
+template <int EPI>
+hipError_t launch_epi(int64_t T, int64_t K, int64_t N, float eps, const uint16_t* xp,
                       int64_t ldx, const uint16_t* wp, int64_t ldw, uint16_t* yp, int64_t ldy,
                       const float* colsum, const float* bias, const float* rowstats,
                       bool nts, hipStream_t st)
 {
     const float inv_k = (float)(1.0 / (double)K);
+    const Path path = choose_path(T, K, N, xp, ldx, wp, ldw, ldy, yp);
     switch (path) {
     case kPathBig64:
-        return launch_pipe<256, 256, 4, 2, 5, 64, EPI, true, WKN>(
+        return launch_pipe<256, 256, 4, 2, 5, 64, EPI, true>(
             T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp, ldy, colsum, bias, rowstats, nts, st);
     case kPathBig32:
-        return launch_pipe<256, 256, 4, 2, 4, 32, EPI, false, WKN>(
+        return launch_pipe<256, 256, 4, 2, 4, 32, EPI, false>(
             T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp, ldy, colsum, bias, rowstats, nts, st);
     case kPathMid:
-        return launch_pipe<128, 128, 4, 2, 2, 64, EPI, false, WKN>(
+        return launch_pipe<128, 128, 4, 2, 2, 64, EPI, false>(
             T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp, ldy, colsum, bias, rowstats, nts, st);
     case kPathMidDeep:
-        return launch_pipe<128, 128, 4, 2, 4, 64, EPI, false, WKN>(
+        return launch_pipe<128, 128, 4, 2, 4, 64, EPI, false>(
             T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp, ldy, colsum, bias, rowstats, nts, st);
     default:
         break;
@@ -1493,47 +1330,23 @@ hipError_t launch_epi(Path path, int64_t T, int64_t K, int64_t N, float eps, con
         return hipErrorInvalidValue;  // statistics from memory: pipelined kernels only
     } else {
         if (path == kPathMv)
-            return launch_mv<EPI, WKN>(MvJob{T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp, ldy,
-                                             colsum, bias, st});
+            return launch_mv<EPI>(MvJob{T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp, ldy, colsum,
+                                        bias, st});
         const int64_t nbm = (T + kBM - 1) / kBM, nbn = (N + kBN - 1) / kBN;
         if (nbm * nbn > 0x7fffffff) return hipErrorInvalidConfiguration;
-        if (path == kPathElem) {
-            hipLaunchKernelGGL((normproj_elem_kernel<EPI, WKN>), dim3((unsigned)(nbm * nbn)),
-                               dim3(kThreads), 0, st, T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp,
-                               ldy, (int)nbm, (int)nbn, colsum, bias);
-            return hipGetLastError();
-        }
-        if constexpr (WKN) {
-            return hipErrorInvalidValue;  // the 16-byte generic kernel reads W' [N, K] only
-        } else {
-            hipLaunchKernelGGL(normproj_mfma_kernel<EPI>, dim3((unsigned)(nbm * nbn)),
-                               dim3(kThreads), 0, st, T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp,
-                               ldy, (int)nbm, (int)nbn, colsum, bias);
-            return hipGetLastError();
-        }
+        hipLaunchKernelGGL((normproj_elem_kernel<EPI>), dim3((unsigned)(nbm * nbn)),
+                           dim3(kThreads), 0, st, T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp, ldy,
+                           (int)nbm, (int)nbn, colsum, bias);
+        return hipGetLastError();
     }
-}
-
-template <int EPI>
-hipError_t launch_layout(int64_t T, int64_t K, int64_t N, float eps, const uint16_t* xp,
-                         int64_t ldx, const uint16_t* wp, int64_t ldw, uint16_t* yp, int64_t ldy,
-                         const float* colsum, const float* bias, const float* rowstats,
-                         bool nts, bool wkn, hipStream_t st)
-{
-    const Path path = choose_path(T, K, N, xp, ldx, wp, ldw, ldy, yp, wkn);
-    if (wkn)
-        return launch_epi<EPI, true>(path, T, K, N, eps, xp, ldx, wp, ldw, yp, ldy, colsum, bias,
-                                     rowstats, nts, st);
-    return launch_epi<EPI, false>(path, T, K, N, eps, xp, ldx, wp, ldw, yp, ldy, colsum, bias,
-                                  rowstats, nts, st);
 }
 
 }  // namespace
 
 bool normproj_pipelined(int64_t T, int64_t K, int64_t N, const void* x, int64_t ldx,
-                        const void* w, int64_t ldw, int64_t ldy, const void* y, int epi)
+                        const void* w, int64_t ldw, int64_t ldy, const void* y)
 {
-    const Path p = choose_path(T, K, N, x, ldx, w, ldw, ldy, y, (epi & kWeightRowMajor) != 0);
+    const Path p = choose_path(T, K, N, x, ldx, w, ldw, ldy, y);
     return p == kPathBig64 || p == kPathBig32 || p == kPathMid || p == kPathMidDeep;
 }
 
@@ -1545,24 +1358,23 @@ hipError_t launch_normproj(int64_t T, int64_t K, int64_t N, float eps, int epi,
     if (T == 0 || N == 0) return hipSuccess;
     // outputs leave the library: non-temporal stores, unless the caller reads them back next
     const bool nts = (epi & kEpiKeepCached) == 0;
-    const bool wkn = (epi & kWeightRowMajor) != 0;
-    epi &= ~(kEpiKeepCached | kWeightRowMajor);
+    epi &= ~kEpiKeepCached;
     const uint16_t* xp = (const uint16_t*)x;
     const uint16_t* wp = (const uint16_t*)w;
     uint16_t* yp = (uint16_t*)y;
     switch (epi) {
     case kEpiPlain:
-        return launch_layout<kEpiPlain>(T, K, N, eps, xp, ldx, wp, ldw, yp, ldy, colsum, bias,
-                                        rowstats, nts, wkn, st);
+        return launch_epi<kEpiPlain>(T, K, N, eps, xp, ldx, wp, ldw, yp, ldy, colsum, bias,
+                                        rowstats, nts, st);
     case kEpiRms:
-        return launch_layout<kEpiRms>(T, K, N, eps, xp, ldx, wp, ldw, yp, ldy, colsum, bias,
-                                      rowstats, nts, wkn, st);
+        return launch_epi<kEpiRms>(T, K, N, eps, xp, ldx, wp, ldw, yp, ldy, colsum, bias,
+                                      rowstats, nts, st);
     case kEpiLayerNorm:
-        return launch_layout<kEpiLayerNorm>(T, K, N, eps, xp, ldx, wp, ldw, yp, ldy, colsum,
-                                            bias, rowstats, nts, wkn, st);
+        return launch_epi<kEpiLayerNorm>(T, K, N, eps, xp, ldx, wp, ldw, yp, ldy, colsum,
+                                            bias, rowstats, nts, st);
     case kEpiLayerNormStats:
-        return launch_layout<kEpiLayerNormStats>(T, K, N, eps, xp, ldx, wp, ldw, yp, ldy, colsum,
-                                                 bias, rowstats, nts, wkn, st);
+        return launch_epi<kEpiLayerNormStats>(T, K, N, eps, xp, ldx, wp, ldw, yp, ldy, colsum,
+                                                 bias, rowstats, nts, st);
     default:
         return hipErrorInvalidValue;
     }

@@ -50,8 +50,7 @@ hipError_t launch_rows(const RowJob& job, hipStream_t stream);
 hipError_t launch_fold(int64_t K, int64_t N, const void* w, int64_t ldw, const void* gamma,
                        int gamma_bf16, void* w_fold, int64_t ldwf, hipStream_t stream);
 
-// Epilogue of the projection acc = x [T, K] . W' with W' given as w [N, K] (row n holds column
-// n of W') or, with kWeightRowMajor, as w [K, N].
+// Epilogue of the projection acc = x [T, K] . w with w = W' row-major [K, N].
 enum Epi : int {
     kEpiPlain = 0,      // y = bf16(acc)
     kEpiRms = 1,        // y = bf16(acc / rms(x row))
@@ -61,8 +60,6 @@ enum Epi : int {
 // Flag or-ed into the epilogue: the caller reads y again right away, so the tiled kernels
 // store it with ordinary stores (it stays in the caches) instead of non-temporal ones.
 constexpr int kEpiKeepCached = 16;
-// Flag or-ed into the epilogue: w is row-major [K, N] (N contiguous).
-constexpr int kWeightRowMajor = 32;
 // rowstats is read by kEpiLayerNormStats only, which runs on the pipelined kernels alone
 // (normproj_pipelined() must hold).
 hipError_t launch_normproj(int64_t T, int64_t K, int64_t N, float eps, int epi,
@@ -70,10 +67,10 @@ hipError_t launch_normproj(int64_t T, int64_t K, int64_t N, float eps, int epi,
                            int64_t ldy, const float* colsum, const float* bias,
                            const float* rowstats, hipStream_t stream);
 
-// Whether launch_normproj runs one of the pipelined matrix-core kernels for this shape, these
-// operands and the weight layout in epi (kWeightRowMajor or not).
+// Whether launch_normproj runs one of the pipelined matrix-core kernels for this shape and
+// these operands.
 bool normproj_pipelined(int64_t T, int64_t K, int64_t N, const void* x, int64_t ldx,
-                        const void* w, int64_t ldw, int64_t ldy, const void* y, int epi);
+                        const void* w, int64_t ldw, int64_t ldy, const void* y);
 
 // rowstats[t] = (mean of x row t, 1 / sqrt(var + eps)) in fp32, K % 8 == 0, rows 16-byte aligned.
 hipError_t launch_layernorm_stats(int64_t T, int64_t K, float eps, const void* x, int64_t ldx,

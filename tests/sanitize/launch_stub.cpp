@@ -20,7 +20,7 @@ hipError_t launch_normproj(int64_t, int64_t, int64_t, float, int, const void*, i
     return hipErrorNoDevice;
 }
 bool normproj_pipelined(int64_t, int64_t, int64_t, const void*, int64_t, const void*, int64_t,
-                        int64_t, const void*, int)
+                        int64_t, const void*)
 {
     return true;
 }
