@@ -276,14 +276,40 @@ __device__ __forceinline__ void run_team(const RowSeg& s, int64_t T, float eps, 
     }
 }
 
+// Row block handled by the i-th of n workgroups of one tensor. Aggregation + scale reads the
+// own and the peers' partials, 4 bytes per row each: a 128-byte line of them spans G row
+// blocks. Workgroup i runs on XCD i % 8 (the tensors' block ranges start at multiples of 8
+// when the rows fill whole groups), so within each group of 8 G workgroups those on one XCD
+// take G consecutive blocks: each line of partials is then fetched into one L2 only. The other
+// modes read no partials and keep the plain order.
+template <int MODE, int SH>
+__device__ __forceinline__ int64_t block_order(int64_t i, int64_t n)
+{
+    if constexpr (MODE != kApply) {
+        return i;
+    } else {
+        constexpr int G = 32 / shape_rows_per_block(MODE, SH);
+        const int64_t full = n / (8 * G) * (8 * G);
+        if (i >= full) return i;
+        const int r = (int)(i % (8 * G));
+        return i - r + (r & 7) * G + (r >> 3);
+    }
+}
+
 // Blocks [0, nblk0) serve seg[0] with shape SH0, the rest seg[1] with shape SH1.
 template <int MODE, bool BF, bool GBF, int SH0, int SH1, bool NTS = true>
 __global__ __launch_bounds__(kBlock) void rows_team_kernel(RowJob job, int nblk0)
 {
     __shared__ float red[32];
     const int b = (int)blockIdx.x;
-    if (b < nblk0) run_team<MODE, BF, GBF, SH0, NTS>(job.seg[0], job.T, job.eps, b, red);
-    else run_team<MODE, BF, GBF, SH1, NTS>(job.seg[1], job.T, job.eps, b - nblk0, red);
+    if (b < nblk0)
+        run_team<MODE, BF, GBF, SH0, NTS>(job.seg[0], job.T, job.eps,
+                                          block_order<MODE, SH0>(b, nblk0), red);
+    else
+        run_team<MODE, BF, GBF, SH1, NTS>(job.seg[1], job.T, job.eps,
+                                          block_order<MODE, SH1>(b - nblk0,
+                                                                 (int)gridDim.x - nblk0),
+                                          red);
 }
 
 // ------------------------------------------------------------------------------------------
