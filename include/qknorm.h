@@ -140,7 +140,11 @@ QKN_API int qknorm_apply_with_stats(int64_t T, float eps, int dtype, int gamma_d
  * a new epoch (mailboxes start zeroed, epoch 0 never matches a wait).
  *   persistent  1: the grid occupies at most three quarters of the device's resident
  *               workgroups and strides over the row blocks, so a producer of the words running
- *               on another stream of the SAME device always makes progress (required then);
+ *               on another stream of the SAME device always finds room to run (required then)
+ *               provided its work is not queued behind this pass: streams are mapped onto a
+ *               few hardware queues, and a producer submitted later to a stream that shares
+ *               the pass's queue starts only after the pass ends (the pass then times out).
+ *               Submitting the producer's work before the pass avoids that on any mapping;
  *               0: one workgroup per row block (faster), for producers that do not run on this
  *               device, such as the peer ranks under tensor parallelism; every rank must then
  *               launch the same grid so that row blocks are dispatched in the same ascending

@@ -65,6 +65,16 @@ __device__ __forceinline__ float wave_sum(float v)
     return (r0 + r1) + (r2 + r3);
 }
 
+typedef __bf16 bf16x2_dot __attribute__((ext_vector_type(2)));
+
+// s + lo*lo + hi*hi for the two bf16 packed in u (v_dot2_f32_bf16: the products of bf16 values
+// are exact in fp32; one instruction per two elements, no widening).
+__device__ __forceinline__ float sumsq_bf16x2(uint32_t u, float s)
+{
+    const bf16x2_dot v = __builtin_bit_cast(bf16x2_dot, u);
+    return __builtin_amdgcn_fdot2_f32_bf16(v, v, s, false);
+}
+
 __device__ __forceinline__ float lane_read(float v, int lane)
 {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));

@@ -124,7 +124,9 @@ struct Gamma {
 };
 
 // The rows of block `blk` of one tensor under team shape SH; NTS: non-temporal output stores.
-template <int MODE, bool BF, bool GBF, int SH, bool NTS>
+// FULL: the row width fills the shape exactly (d == kShapeCap[SH] * EPV), so no vector is past
+// the end of the row and the loads and stores need no column mask.
+template <int MODE, bool BF, bool GBF, int SH, bool NTS, bool FULL>
 __device__ __forceinline__ void run_team(const RowSeg& s, int64_t T, float eps, int64_t blk,
                                          float* red)
 {
@@ -140,6 +142,10 @@ __device__ __forceinline__ void run_team(const RowSeg& s, int64_t T, float eps, 
     const int wave = (int)(threadIdx.x / kWave);
     const int tm = wave / WPR, wt = wave % WPR;
     const int64_t row0 = (blk * TEAMS + tm) * RR;
+    // with one row per workgroup the grid has exactly T blocks: every row exists
+    constexpr bool kRowsExact = TEAMS * RR == 1;
+    auto col_in = [&](int64_t col) { return FULL || col < s.d; };
+    auto row_in = [&](int r) { return kRowsExact || row0 + r < T; };
 
     // gamma first: its cache hits are back before the row loads are.
     u32x4 graw[NVW][G::kGv];
@@ -147,7 +153,7 @@ __device__ __forceinline__ void run_team(const RowSeg& s, int64_t T, float eps, 
 #pragma unroll
         for (int j = 0; j < NVW; ++j) {
             const int64_t col = (int64_t)((wt * NVW + j) * kWave + lane) * EPV;
-            if (col < s.d) {
+            if (col_in(col)) {
                 G::load(s.g, col, graw[j]);
             } else {
 #pragma unroll
@@ -176,12 +182,12 @@ __device__ __forceinline__ void run_team(const RowSeg& s, int64_t T, float eps, 
     u32x4 v[RR][NVW];
 #pragma unroll
     for (int r = 0; r < RR; ++r) {
-        const bool row_ok = row0 + r < T;
+        const bool row_ok = row_in(r);
         const char* xr = (const char*)s.x + (row0 + r) * s.ldx * ES;
 #pragma unroll
         for (int j = 0; j < NVW; ++j) {
             const int64_t col = (int64_t)((wt * NVW + j) * kWave + lane) * EPV;
-            v[r][j] = (row_ok && col < s.d) ? load_stream(xr + col * ES) : u32x4{0u, 0u, 0u, 0u};
+            v[r][j] = (row_ok && col_in(col)) ? load_stream(xr + col * ES) : u32x4{0u, 0u, 0u, 0u};
         }
     }
 
@@ -206,12 +212,20 @@ __device__ __forceinline__ void run_team(const RowSeg& s, int64_t T, float eps, 
             float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
             for (int j = 0; j < NVW; ++j) {
-                float f[EPV];
-                unpack<BF>(v[r][j], f);
+                if constexpr (BF) {
+                    // two bf16 per instruction, squares exact, one rounding per pair
+                    a0 = sumsq_bf16x2(v[r][j].x, a0);
+                    a1 = sumsq_bf16x2(v[r][j].y, a1);
+                    a0 = sumsq_bf16x2(v[r][j].z, a0);
+                    a1 = sumsq_bf16x2(v[r][j].w, a1);
+                } else {
+                    float f[EPV];
+                    unpack<BF>(v[r][j], f);
 #pragma unroll
-                for (int e = 0; e < EPV; e += 2) {
-                    a0 = fmaf(f[e], f[e], a0);
-                    a1 = fmaf(f[e + 1], f[e + 1], a1);
+                    for (int e = 0; e < EPV; e += 2) {
+                        a0 = fmaf(f[e], f[e], a0);
+                        a1 = fmaf(f[e + 1], f[e + 1], a1);
+                    }
                 }
             }
             tot[r] = wave_sum(a0 + a1);
@@ -257,12 +271,12 @@ __device__ __forceinline__ void run_team(const RowSeg& s, int64_t T, float eps, 
 
 #pragma unroll
         for (int r = 0; r < RR; ++r) {
-            if (row0 + r < T) {
+            if (row_in(r)) {
                 char* yr = (char*)s.y + (row0 + r) * s.ldy * ES;
 #pragma unroll
                 for (int j = 0; j < NVW; ++j) {
                     const int64_t col = (int64_t)((wt * NVW + j) * kWave + lane) * EPV;
-                    if (col < s.d) {
+                    if (col_in(col)) {
                         float f[EPV], o[EPV];
                         unpack<BF>(v[r][j], f);
 #pragma unroll
@@ -296,20 +310,21 @@ __device__ __forceinline__ int64_t block_order(int64_t i, int64_t n)
     }
 }
 
-// Blocks [0, nblk0) serve seg[0] with shape SH0, the rest seg[1] with shape SH1.
-template <int MODE, bool BF, bool GBF, int SH0, int SH1, bool NTS = true>
+// Blocks [0, nblk0) serve seg[0] with shape SH0, the rest seg[1] with shape SH1; FULL: both
+// tensors' widths fill their shapes exactly.
+template <int MODE, bool BF, bool GBF, int SH0, int SH1, bool NTS = true, bool FULL = false>
 __global__ __launch_bounds__(kBlock) void rows_team_kernel(RowJob job, int nblk0)
 {
     __shared__ float red[32];
     const int b = (int)blockIdx.x;
     if (b < nblk0)
-        run_team<MODE, BF, GBF, SH0, NTS>(job.seg[0], job.T, job.eps,
-                                          block_order<MODE, SH0>(b, nblk0), red);
+        run_team<MODE, BF, GBF, SH0, NTS, FULL>(job.seg[0], job.T, job.eps,
+                                                block_order<MODE, SH0>(b, nblk0), red);
     else
-        run_team<MODE, BF, GBF, SH1, NTS>(job.seg[1], job.T, job.eps,
-                                          block_order<MODE, SH1>(b - nblk0,
-                                                                 (int)gridDim.x - nblk0),
-                                          red);
+        run_team<MODE, BF, GBF, SH1, NTS, FULL>(job.seg[1], job.T, job.eps,
+                                                block_order<MODE, SH1>(b - nblk0,
+                                                                       (int)gridDim.x - nblk0),
+                                                red);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -402,7 +417,7 @@ __global__ __launch_bounds__(kBlock) void rows_generic_kernel(RowJob job)
 
 typedef hipError_t (*RowLaunch)(const RowJob&, hipStream_t);
 
-template <int MODE, bool BF, bool GBF, int SH0, int SH1, bool NTS = true>
+template <int MODE, bool BF, bool GBF, int SH0, int SH1, bool NTS = true, bool FULL = false>
 hipError_t launch_team(const RowJob& job, hipStream_t st)
 {
     const int64_t per0 = shape_rows_per_block(MODE, SH0);
@@ -410,7 +425,7 @@ hipError_t launch_team(const RowJob& job, hipStream_t st)
     const int64_t nblk0 = (job.T + per0 - 1) / per0;
     const int64_t nblk1 = job.nseg > 1 ? (job.T + per1 - 1) / per1 : 0;
     if (nblk0 + nblk1 > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((rows_team_kernel<MODE, BF, GBF, SH0, SH1, NTS>),
+    hipLaunchKernelGGL((rows_team_kernel<MODE, BF, GBF, SH0, SH1, NTS, FULL>),
                        dim3((unsigned)(nblk0 + nblk1)), dim3(kBlock), 0, st, job, (int)nblk0);
     return hipGetLastError();
 }
@@ -424,11 +439,18 @@ RowLaunch pick_second(int j, std::integer_sequence<int, J...>)
 }
 
 // Fused launches: every pair (i >= j) of shapes; the caller orders the segments so that the
-// first has the larger shape. Split launches use one shape (the larger) for both tensors.
+// first has the larger shape. Split launches use one shape (the larger) for both tensors. When
+// both tensors share one shape and fill it exactly (full), the unmasked instantiation runs.
 template <int MODE, bool BF, bool GBF, int... I>
-RowLaunch pick_team(int i, int j, std::integer_sequence<int, I...>)
+RowLaunch pick_team(int i, int j, bool full, std::integer_sequence<int, I...>)
 {
     RowLaunch r = nullptr;
+    if constexpr (MODE != kApply) {
+        if (full && i == j) {
+            ((i == I ? (r = launch_team<MODE, BF, GBF, I, I, true, true>, 0) : 0), ...);
+            return r;
+        }
+    }
     if constexpr (MODE == kFused) {
         ((i == I ? (r = pick_second<MODE, BF, GBF, I>(j, std::make_integer_sequence<int, I + 1>{}),
                     0)
@@ -499,13 +521,17 @@ hipError_t dispatch_mode(const RowJob& job_in, hipStream_t st)
         cls[1] = c;
     }
     const int i = cls[0], j = MODE == kFused ? cls[1] : cls[0];
+    // (aggregation + scale keeps the masked form: unmasked it measured 6% slower)
+    bool full = MODE != kApply;
+    for (int t = 0; t < job.nseg; ++t) full = full && job.seg[t].d == (int64_t)kShapeCap[i] * EPV;
     if constexpr (MODE == kFused) {
         if (job.nseg == 1 && job.keep_cached) {
             RowLaunch f = pick_cached<BF, GBF>(i, std::make_integer_sequence<int, kShapeCount>{});
             return f ? f(job, st) : hipErrorInvalidValue;
         }
     }
-    RowLaunch f = pick_team<MODE, BF, GBF>(i, j, std::make_integer_sequence<int, kShapeCount>{});
+    RowLaunch f = pick_team<MODE, BF, GBF>(i, j, full,
+                                           std::make_integer_sequence<int, kShapeCount>{});
     return f ? f(job, st) : hipErrorInvalidValue;
 }
 

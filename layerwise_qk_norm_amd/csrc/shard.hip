@@ -24,7 +24,11 @@
 // hangs. Two launch policies: persistent, where the grid holds at most three quarters of the
 // workgroups the device can keep resident and strides over the row blocks (prefetching the
 // next block's rows), so that a producer launched on another stream of the same device always
-// finds free slots; or one workgroup per row block, for producers that do not run on this
+// finds free slots, provided that stream is not queued behind this kernel: HIP maps streams
+// onto a few hardware queues, and two streams that share one run their work in submission
+// order, so a producer submitted after the pass to the same queue cannot start before it ends
+// (the pass then waits out max_spin and reports the timeout); or one workgroup per row block,
+// for producers that do not run on this
 // device (the peers under tensor parallelism). The second streams faster; with it, progress
 // rests on every rank dispatching row blocks in the same ascending order, so that the lowest
 // unfinished block is resident, and has been published, everywhere.

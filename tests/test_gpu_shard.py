@@ -128,8 +128,12 @@ def test_shard_fused_peer_counts(Q, n_ext):
 
 
 def test_shard_fused_concurrent_publisher(Q):
-    """The pass starts first on one stream and waits; the simulated peers publish from another
-    stream of the same GPU while it runs (the pass leaves a quarter of the device free)."""
+    """The simulated peers publish from another stream of the same GPU while the pass runs (the
+    pass leaves a quarter of the device free). The publisher's work is submitted first, behind
+    a spin of a few milliseconds on its stream: when the two streams run on different hardware
+    queues the pass starts first and waits for the words; when HIP has put both streams on one
+    queue, the queue runs the publisher first and the pass finds the words ready. Either way
+    the pass must not time out."""
     import torch
 
     c = inputs.make_case("tp8-shard", 65536, seed=9)
@@ -139,11 +143,12 @@ def test_shard_fused_concurrent_publisher(Q):
     to = zeros_i32(1)
     sync()
     sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    with torch.cuda.stream(sb):
+        torch.cuda._sleep(5_000_000)
+        Q.qknorm_shard_publish(part_q, mail_q, 3, part_k, mail_k)
     with torch.cuda.stream(sa):
         got = Q.qknorm_shard_fused(q, gq, mail_q, 4096, k, gk, mail_k, 4096, eps=c["eps"],
                                    epoch=3, timed_out=to)
-    with torch.cuda.stream(sb):
-        Q.qknorm_shard_publish(part_q, mail_q, 3, part_k, mail_k)
     sync()
     assert int(to.item()) == 0, "the pass timed out waiting for the publisher"
     check_all(got, reference(c, 4096, c["eps"]), "concurrent", 3)
