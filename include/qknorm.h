@@ -123,8 +123,9 @@ QKN_API int qknorm_apply_with_stats(int64_t T, float eps, int dtype, int gamma_d
  * qknorm_shard_fused - the shard stage in ONE pass over this rank's slice.
  *
  * ("SwiftQK: ...", abstract: ranks exchange per-row scalars only, and waiting for the peers'
- * scalars is hidden behind element-wise work in one persistent kernel that cannot deadlock.) Computes what qknorm_partial_sumsq followed by qknorm_apply_with_stats computes,
- * reading x once. Exchanged partials travel as mailbox WORDS: uint64 = (epoch << 32) | the
+ * scalars is hidden behind element-wise work in one persistent kernel that cannot deadlock.)
+ * Computes what qknorm_partial_sumsq followed by qknorm_apply_with_stats computes, reading x
+ * once. Exchanged partials travel as mailbox WORDS: uint64 = (epoch << 32) | the
  * fp32 bits of the value, each stored and loaded as one aligned 64-bit device-coherent access,
  * so a word that carries the current epoch carries its value (no separate flags). Per row:
  *   1. s_own = sum of squares of the slice's row; if psq_*_out != NULL it is published there
@@ -138,17 +139,19 @@ QKN_API int qknorm_apply_with_stats(int64_t T, float eps, int dtype, int gamma_d
  * mail_* are the mailboxes the peers fill ([n_ext, T] words, row stride ld_mail >= T,
  * 8-byte aligned), for instance by qknorm_shard_publish. A new pass over the same mailbox uses
  * a new epoch (mailboxes start zeroed, epoch 0 never matches a wait).
- *   persistent  1: the grid occupies at most three quarters of the device's resident
- *               workgroups and strides over the row blocks, so a producer of the words running
- *               on another stream of the SAME device always finds room to run (required then)
- *               provided its work is not queued behind this pass: streams are mapped onto a
- *               few hardware queues, and a producer submitted later to a stream that shares
- *               the pass's queue starts only after the pass ends (the pass then times out).
- *               Submitting the producer's work before the pass avoids that on any mapping;
- *               0: one workgroup per row block (faster), for producers that do not run on this
- *               device, such as the peer ranks under tensor parallelism; every rank must then
- *               launch the same grid so that row blocks are dispatched in the same ascending
- *               order everywhere. Ignored when epoch == 0 (nothing waits).
+ *   persistent  1: every workgroup (one per row block, dispatched in ascending order) reserves
+ *               LDS it does not use, so that at most three quarters of the workgroups the
+ *               registers allow are resident on a CU at once; a producer of the words running
+ *               on another stream of the SAME device then always finds a quarter of the slots
+ *               and of the LDS free (required then), provided its work is not queued behind
+ *               this pass: streams are mapped onto a few hardware queues, and a producer
+ *               submitted later to a stream that shares the pass's queue starts only after the
+ *               pass ends (the pass then times out). Submitting the producer's work before the
+ *               pass avoids that on any mapping;
+ *               0: no reservation, for producers that do not run on this device, such as the
+ *               peer ranks under tensor parallelism; every rank must then launch the same grid
+ *               so that row blocks are dispatched in the same ascending order everywhere.
+ *               Ignored when epoch == 0 (nothing waits). Both policies stream at the same rate.
  *   n_ext     0..64
  *   timed_out device int (required when epoch != 0), set to 1 on a timeout, never cleared
  *   slices    16-byte aligned, ld * sizeof(dtype) and d_local multiples of 16 bytes

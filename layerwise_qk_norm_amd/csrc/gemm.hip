@@ -165,6 +165,19 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Wait until at most `later` k-tiles of CPT DMA requests each are still in flight (0 <= later
+// <= L): the requests complete in issue order, so everything issued before them has landed.
+template <int CPT, int L>
+__device__ __forceinline__ void wait_tiles(int later)
+{
+    if constexpr (L == 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (later >= L) wait_vmcnt<L * CPT>();
+        else wait_tiles<CPT, L - 1>(later);
+    }
+}
+
 // Physical 16-byte chunk of logical chunk kc in tile row r. ds_read_b128 is served 16 lanes
 // (256 bytes, 64 banks) at a time and the fragment reads touch 16 consecutive rows at one
 // logical chunk: rows of 128 B (k-tile 64) pair up per 256 B, so kc is xored with
@@ -196,14 +209,20 @@ __device__ __forceinline__ u32x2 lds_tr16(const char* p)
 // element j the 16-bit element i % 4 of the 8 bytes that lane 4 j + i / 4 addressed: when lane
 // 4 r + c of a group addresses columns 4 c .. 4 c + 3 of row r of a 4-row block, lane i
 // receives column i of rows 0..3.
-template <int BM, int BN, int WM, int WN, int NST, int BK, int EPI, bool RING, bool NTS>
-__global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
+// KG > 1 splits every k-tile's k steps among KG groups of WM x WN wavefronts (group g takes the
+// steps s with s % KG == g): each wavefront then holds a KG times larger share of the output
+// tile for the same number of wavefronts per CU, which cuts the LDS fragment bytes per MFMA;
+// after the last k-tile groups 1..KG-1 hand their accumulators to group 0 through LDS, which
+// adds them in group order (a fixed order, so results do not depend on timing).
+template <int BM, int BN, int WM, int WN, int NST, int BK, int EPI, bool RING, bool NTS, int KG>
+__global__ __launch_bounds__(WM * WN * KG * 64) void normproj_pipe_kernel(
     int64_t T, int64_t K, int64_t N, float eps, float inv_k, const uint16_t* __restrict__ x,
     int64_t ldx, const uint16_t* __restrict__ w, int64_t ldw, uint16_t* __restrict__ y,
     int64_t ldy, int nbm, int nbn, const float* __restrict__ colsum,
     const float* __restrict__ bias, const float* __restrict__ rowstats)
 {
-    constexpr int NW = WM * WN, NT = NW * kWave;
+    constexpr int NWP = WM * WN;            // wavefront positions on the output tile
+    constexpr int NW = NWP * KG, NT = NW * kWave;
     constexpr int ROWB = BK * 2;            // bytes per tile row
     constexpr int RPC = 1024 / ROWB;        // tile rows per 1 KB DMA chunk
     constexpr int LPR = ROWB / 16;          // lanes per tile row within a chunk
@@ -216,27 +235,32 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
     static_assert(CA % NW == 0 && CB % NW == 0, "DMA chunks must divide among the wavefronts");
     constexpr int CPA = CA / NW, CPB = CB / NW;  // DMA instructions per wavefront per part
     constexpr int KS = BK / 16;
-    static_assert(!RING || (BM == BN && (CPA + CPB) % KS == 0), "ring: five equal parts");
+    static_assert(KS % KG == 0, "k groups take equal shares of the k steps");
+    constexpr int KSG = KS / KG;            // k steps per wavefront per k-tile
+    static_assert(!RING || (BM == BN && (CPA + CPB) % KSG == 0), "ring: five equal parts");
     constexpr int PIPE = RING ? 5 * PART_A : NST * STAGE;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int TM = WTM / 32, TN = WTN / 32;
     constexpr int CP = BN + 8;              // epilogue tile pitch (bf16)
-    // after the k loop the pipeline's LDS holds the output tile and the per-row / per-column
-    // epilogue operands
-    constexpr int OFF_RS = BM * CP * 2, OFF_MU = OFF_RS + BM * 4;
-    constexpr int OFF_PART = OFF_MU + BM * 4, OFF_CS = OFF_PART + 2 * WN * BM * 4;
+    // after the k loop the pipeline's LDS holds the output tile (where the k groups' accumulators
+    // are exchanged first) and the per-row / per-column epilogue operands
+    constexpr int CT_BYTES = BM * CP * 2;
+    constexpr int XCH = (KG - 1) * NWP * TM * TN * 16 * kWave * 4;
+    constexpr int OFF_RS = CT_BYTES > XCH ? CT_BYTES : XCH, OFF_MU = OFF_RS + BM * 4;
+    constexpr int OFF_PART = OFF_MU + BM * 4, OFF_CS = OFF_PART + 2 * WN * KG * BM * 4;
     constexpr int OFF_BS = OFF_CS + BN * 4, EPI_END = OFF_BS + BN * 4;
     constexpr int SMEM = PIPE > EPI_END ? PIPE : EPI_END;
     __shared__ __attribute__((aligned(1024))) char smem[SMEM];
     float* rs_lds = (float*)(smem + OFF_RS);
     float* mu_lds = (float*)(smem + OFF_MU);
-    float* part_lds = (float*)(smem + OFF_PART);  // per wave column: partial row sums
+    float* part_lds = (float*)(smem + OFF_PART);  // per wave column and k group: row sums
     float* cs_lds = (float*)(smem + OFF_CS);
     float* bs_lds = (float*)(smem + OFF_BS);
 
     const int tid = (int)threadIdx.x, lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wavefront-uniform
-    const int wm = wave / WN, wn = wave % WN;
+    const int kg = KG == 1 ? 0 : wave / NWP, wp = KG == 1 ? wave : wave % NWP;
+    const int wm = wp / WN, wn = wp % WN;
     const int nb = nbm * nbn;
     int bid = (int)blockIdx.x;
     // Workgroup b runs on XCD b % 8. Each XCD takes a block of the tile grid: the row panels
@@ -372,28 +396,20 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
         } else {
             // k-tile kt must have landed; up to NST-2 later tiles stay in flight
             const int later = (nk - 1 - kt) < (NST - 2) ? (nk - 1 - kt) : (NST - 2);
-            if constexpr (NST >= 4) {
-                if (later >= 2) wait_vmcnt<2 * CPT>();
-                else if (later == 1) wait_vmcnt<CPT>();
-                else wait_vmcnt<0>();
-            } else if constexpr (NST == 3) {
-                if (later >= 1) wait_vmcnt<CPT>();
-                else wait_vmcnt<0>();
-            } else {
-                wait_vmcnt<0>();
-            }
+            wait_tiles<CPT, (NST > 2 ? NST - 2 : 0)>(later);
         }
         __syncthreads();  // every wavefront's DMA has landed; the parts of k-tile kt-1 are free
         // whole-tile stages: with NST >= 3 the next k-tile's requests are spread over the k steps
         // (two later k-tiles are still in flight meanwhile); with 2 stages they go out at once
-        constexpr bool SPREAD = !RING && NST >= 3 && CPT % KS == 0;
+        constexpr bool SPREAD = !RING && NST >= 3 && CPT % KSG == 0;
         if constexpr (!RING && !SPREAD) {
             if (kt + NST - 1 < nk) issue_tile((kt + NST - 1) % NST, (int64_t)(kt + NST - 1) * BK);
         }
         const char* As = RING ? smem + pa * PART_A : smem + (kt % NST) * STAGE;
         const char* Bs = RING ? smem + pb * PART_A : As + PART_A;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
+        for (int q = 0; q < KSG; ++q) {
+            const int ks = KG == 1 ? q : q * KG + kg;  // this wavefront's q-th k step
             u32x4 af[TM], bfr[TN];
             const int kc = ks * 2 + fk;
 #pragma unroll
@@ -409,8 +425,8 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
                 bfr[j] = u32x4{lo.x, lo.y, hi.x, hi.y};
             }
             if constexpr (kStatsInLoop<EPI>) {
-                // the WN wavefronts holding the same rows take turns over the k steps
-                if (ks % WN == wn) {
+                // the WN wavefronts of a k group holding the same rows take turns over its steps
+                if (q % WN == wn) {
 #pragma unroll
                     for (int i = 0; i < TM; ++i) accum_stats<EPI>(af[i], x0[i], s1[i], s2[i]);
                 }
@@ -425,10 +441,10 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
                 // this k step's share of the next DMA requests, spread over the k steps so the
                 // MFMA issue is never held behind a burst of them: the W' part of k-tile kt+1
                 // first, then the x part of k-tile kt+2 (parts freed by the barrier above)
-                constexpr int PER = CPT / KS;
+                constexpr int PER = CPT / KSG;
 #pragma unroll
                 for (int h = 0; h < PER; ++h) {
-                    const int c = ks * PER + h;
+                    const int c = q * PER + h;
                     if (c < CPB) {
                         if (kt + 1 < nk)
                             dma_b(c, (uint32_t)(pnb * PART_A), (int64_t)(kt + 1) * BK);
@@ -439,12 +455,12 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
                 }
             }
             if constexpr (SPREAD) {
-                constexpr int PER = CPT / KS;
+                constexpr int PER = CPT / KSG;
                 const int nt = kt + NST - 1;
                 const uint32_t base = (uint32_t)((nt % NST) * STAGE);
 #pragma unroll
                 for (int h = 0; h < PER; ++h) {
-                    const int c = ks * PER + h;
+                    const int c = q * PER + h;
                     if (nt < nk) {
                         if (c < CPA) dma_a(c, base, (int64_t)nt * BK);
                         else dma_b(c - CPA, base + PART_A, (int64_t)nt * BK);
@@ -455,6 +471,43 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
         pa = pa >= 3 ? pa - 3 : pa + 2;
     }
     __syncthreads();  // every wavefront is done with the pipeline's LDS (no DMA is in flight)
+    if constexpr (KG > 1) {
+        // k groups 1.. store their accumulators (16 bytes per lane, lanes contiguous); group 0
+        // adds them in group order
+        f32x4* xch = (f32x4*)smem;
+        auto slot = [&](int g, int i, int j, int e4) {
+            return ((((g - 1) * NWP + wp) * TM + i) * TN * 4 + j * 4 + e4) * kWave + lane;
+        };
+        if (kg > 0) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int e4 = 0; e4 < 4; ++e4)
+                        xch[slot(kg, i, j, e4)] = f32x4{acc[i][j][4 * e4], acc[i][j][4 * e4 + 1],
+                                                        acc[i][j][4 * e4 + 2],
+                                                        acc[i][j][4 * e4 + 3]};
+        }
+        __syncthreads();
+        if (kg == 0) {
+#pragma unroll
+            for (int g = 1; g < KG; ++g)
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+#pragma unroll
+                        for (int e4 = 0; e4 < 4; ++e4) {
+                            const f32x4 v = xch[slot(g, i, j, e4)];
+                            acc[i][j][4 * e4] += v.x;
+                            acc[i][j][4 * e4 + 1] += v.y;
+                            acc[i][j][4 * e4 + 2] += v.z;
+                            acc[i][j][4 * e4 + 3] += v.w;
+                        }
+        }
+        __syncthreads();  // the exchange area becomes the output tile
+    }
 
     if constexpr (kLayerNormOut<EPI>) {
         for (int c = tid; c < BN; c += NT) {
@@ -479,8 +532,8 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
             const float q2 = s2[i] + __shfl_xor(s2[i], 32);
             const float q1 = s1[i] + __shfl_xor(s1[i], 32);
             if (lane < 32) {
-                part_lds[(0 * WN + wn) * BM + wm * WTM + i * 32 + lane] = q1;
-                part_lds[(1 * WN + wn) * BM + wm * WTM + i * 32 + lane] = q2;
+                part_lds[(0 * WN * KG + kg * WN + wn) * BM + wm * WTM + i * 32 + lane] = q1;
+                part_lds[(1 * WN * KG + kg * WN + wn) * BM + wm * WTM + i * 32 + lane] = q2;
             }
         }
         __syncthreads();
@@ -488,9 +541,9 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
         for (int r = tid; r < BM; r += NT) {
             float q1 = 0.0f, q2 = 0.0f;
 #pragma unroll
-            for (int c = 0; c < WN; ++c) {
-                q1 += part_lds[(0 * WN + c) * BM + r];
-                q2 += part_lds[(1 * WN + c) * BM + r];
+            for (int c = 0; c < WN * KG; ++c) {
+                q1 += part_lds[(0 * WN * KG + c) * BM + r];
+                q2 += part_lds[(1 * WN * KG + c) * BM + r];
             }
             const int64_t gr = m0 + r;
             const float xr0 = EPI == kEpiLayerNorm ? bf16_at(x, (gr < T ? gr : T - 1) * ldx) : 0.0f;
@@ -505,33 +558,36 @@ __global__ __launch_bounds__(WM * WN * 64) void normproj_pipe_kernel(
     // output row wm*WTM + i*32 + lane%32; columns wn*WTN + j*32 + 8g + 4(lane/32) + 0..3 in
     // accumulator entries 4g .. 4g+3, rounded to bf16 and written 8 bytes at a time
     uint16_t* ct = (uint16_t*)smem;
+    if (KG == 1 || kg == 0) {  // group 0 holds the summed accumulators
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int r = wm * WTM + i * 32 + (lane & 31);
-        float rs = 1.0f, mu = 0.0f;
-        if constexpr (EPI != kEpiPlain) rs = rs_lds[r];
-        if constexpr (kLayerNormOut<EPI>) mu = mu_lds[r];
+        for (int i = 0; i < TM; ++i) {
+            const int r = wm * WTM + i * 32 + (lane & 31);
+            float rs = 1.0f, mu = 0.0f;
+            if constexpr (EPI != kEpiPlain) rs = rs_lds[r];
+            if constexpr (kLayerNormOut<EPI>) mu = mu_lds[r];
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+            for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int c = wn * WTN + j * 32 + 8 * g + 4 * (lane >> 5);
-                float v[4];
+                for (int g = 0; g < 4; ++g) {
+                    const int c = wn * WTN + j * 32 + 8 * g + 4 * (lane >> 5);
+                    float v[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
-                if constexpr (EPI == kEpiRms) {
+                    for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
+                    if constexpr (EPI == kEpiRms) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] *= rs;
+                        for (int e = 0; e < 4; ++e) v[e] *= rs;
+                    }
+                    if constexpr (kLayerNormOut<EPI>) {
+                        const f32x4 cs = *(const f32x4*)(cs_lds + c);
+                        const f32x4 bs = *(const f32x4*)(bs_lds + c);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            v[e] = epilogue<EPI>(v[e], rs, mu, cs[e], bs[e]);
+                    }
+                    const u32x2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                    *(u32x2*)(ct + r * CP + c) = pk;
                 }
-                if constexpr (kLayerNormOut<EPI>) {
-                    const f32x4 cs = *(const f32x4*)(cs_lds + c);
-                    const f32x4 bs = *(const f32x4*)(bs_lds + c);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = epilogue<EPI>(v[e], rs, mu, cs[e], bs[e]);
-                }
-                const u32x2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-                *(u32x2*)(ct + r * CP + c) = pk;
-            }
+        }
     }
     __syncthreads();
     // each thread stores one 16-byte column chunk of every RSTEP-th row: all its LDS reads are
@@ -1192,7 +1248,7 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(char* __restrict__ dst,
     for (int64_t i = done + tid; i < nbytes; i += stride) dst[i] = src[i];
 }
 
-template <int BM, int BN, int WM, int WN, int NST, int BK, int EPI, bool RING, bool NTS>
+template <int BM, int BN, int WM, int WN, int NST, int BK, int EPI, bool RING, bool NTS, int KG>
 hipError_t launch_pipe_t(int64_t T, int64_t K, int64_t N, float eps, float inv_k,
                          const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
                          uint16_t* y, int64_t ldy, const float* colsum, const float* bias,
@@ -1200,15 +1256,15 @@ hipError_t launch_pipe_t(int64_t T, int64_t K, int64_t N, float eps, float inv_k
 {
     const int64_t nbm = (T + BM - 1) / BM, nbn = (N + BN - 1) / BN;
     if (nbm * nbn > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((normproj_pipe_kernel<BM, BN, WM, WN, NST, BK, EPI, RING, NTS>),
-                       dim3((unsigned)(nbm * nbn)), dim3(WM * WN * kWave), 0, st, T, K, N, eps,
+    hipLaunchKernelGGL((normproj_pipe_kernel<BM, BN, WM, WN, NST, BK, EPI, RING, NTS, KG>),
+                       dim3((unsigned)(nbm * nbn)), dim3(WM * WN * KG * kWave), 0, st, T, K, N, eps,
                        inv_k, x, ldx, w, ldw, y, ldy, (int)nbm, (int)nbn, colsum, bias, rowstats);
     return hipGetLastError();
 }
 
 // Ordinary output stores exist for the epilogues whose output the library reads back itself
 // (the pre-norm elimination: plain or RMSNorm).
-template <int BM, int BN, int WM, int WN, int NST, int BK, int EPI, bool RING>
+template <int BM, int BN, int WM, int WN, int NST, int BK, int EPI, bool RING, int KG>
 hipError_t launch_pipe(int64_t T, int64_t K, int64_t N, float eps, float inv_k,
                        const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
                        uint16_t* y, int64_t ldy, const float* colsum, const float* bias,
@@ -1216,10 +1272,10 @@ hipError_t launch_pipe(int64_t T, int64_t K, int64_t N, float eps, float inv_k,
 {
     if constexpr (EPI == kEpiPlain || EPI == kEpiRms) {
         if (!nts)
-            return launch_pipe_t<BM, BN, WM, WN, NST, BK, EPI, RING, false>(
+            return launch_pipe_t<BM, BN, WM, WN, NST, BK, EPI, RING, false, KG>(
                 T, K, N, eps, inv_k, x, ldx, w, ldw, y, ldy, colsum, bias, rowstats, st);
     }
-    return launch_pipe_t<BM, BN, WM, WN, NST, BK, EPI, RING, true>(
+    return launch_pipe_t<BM, BN, WM, WN, NST, BK, EPI, RING, true, KG>(
         T, K, N, eps, inv_k, x, ldx, w, ldw, y, ldy, colsum, bias, rowstats, st);
 }
 
@@ -1293,10 +1349,11 @@ Path choose_path(int64_t T, int64_t K, int64_t N, const void* x, int64_t ldx, co
     // ring of five parts, or of 32 in 4 whole-tile stages when K needs it
     if (pipe_ok && big_tiles >= 256 && K % 64 == 0) return kPathBig64;
     if (pipe_ok && big_tiles >= 256 && K % 32 == 0) return kPathBig32;
-    // 128 x 128 per workgroup of 8 wavefronts (32 x 64 each: two wavefronts per SIMD hide each
-    // other's LDS and barrier latency), k-tiles of 64: with more tiles than CUs, 2 stages and 2
-    // workgroups per CU; with at most one tile per CU, 4 stages (3 k-tiles in flight) in the LDS
-    // the second workgroup would have used
+    // 128 x 128 per workgroup of 8 wavefronts, k-tiles of 64: with more tiles than CUs, 2 stages
+    // and 2 workgroups per CU, the wavefronts in two k groups of 2 x 2 (64 x 64 each, half the
+    // k steps each); with at most one tile per CU, 4 stages (3 k-tiles in flight) in the LDS the
+    // second workgroup would have used, wavefronts 4 x 2 (32 x 64 each); two wavefronts per SIMD
+    // hide each other's LDS and barrier latency
     const int64_t mid_tiles = ((T + 127) / 128) * ((N + 127) / 128);
     if (pipe_ok && K % 64 == 0) return mid_tiles <= 256 ? kPathMidDeep : kPathMid;
     return kPathElem;
@@ -1312,16 +1369,16 @@ hipError_t launch_epi(int64_t T, int64_t K, int64_t N, float eps, const uint16_t
     const Path path = choose_path(T, K, N, xp, ldx, wp, ldw, ldy, yp);
     switch (path) {
     case kPathBig64:
-        return launch_pipe<256, 256, 4, 2, 5, 64, EPI, true>(
+        return launch_pipe<256, 256, 4, 2, 5, 64, EPI, true, 1>(
             T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp, ldy, colsum, bias, rowstats, nts, st);
     case kPathBig32:
-        return launch_pipe<256, 256, 4, 2, 4, 32, EPI, false>(
+        return launch_pipe<256, 256, 4, 2, 4, 32, EPI, false, 1>(
             T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp, ldy, colsum, bias, rowstats, nts, st);
     case kPathMid:
-        return launch_pipe<128, 128, 4, 2, 2, 64, EPI, false>(
+        return launch_pipe<128, 128, 2, 2, 2, 64, EPI, false, 2>(
             T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp, ldy, colsum, bias, rowstats, nts, st);
     case kPathMidDeep:
-        return launch_pipe<128, 128, 4, 2, 4, 64, EPI, false>(
+        return launch_pipe<128, 128, 4, 2, 4, 64, EPI, false, 1>(
             T, K, N, eps, inv_k, xp, ldx, wp, ldw, yp, ldy, colsum, bias, rowstats, nts, st);
     default:
         break;

@@ -110,7 +110,7 @@ struct ShardArgs {
     int64_t n_ext;
     int bf16, gamma_bf16;
     uint32_t epoch;           // 0: mailbox complete before launch, no tag checks, no waiting
-    int persistent;           // 1: persistent three-quarter-capacity grid, 0: one per row block
+    int persistent;           // 1: at most 3/4 of the resident workgroups at once, 0: no cap
     int64_t max_spin;
     int* timed_out;
 };

@@ -21,17 +21,18 @@
 //
 // Deadlock safety. A reader waits only on data that other work produces, and every wait is
 // bounded (max_spin polls, after which the kernel records a timeout and finishes), so it never
-// hangs. Two launch policies: persistent, where the grid holds at most three quarters of the
-// workgroups the device can keep resident and strides over the row blocks (prefetching the
-// next block's rows), so that a producer launched on another stream of the same device always
-// finds free slots, provided that stream is not queued behind this kernel: HIP maps streams
-// onto a few hardware queues, and two streams that share one run their work in submission
-// order, so a producer submitted after the pass to the same queue cannot start before it ends
-// (the pass then waits out max_spin and reports the timeout); or one workgroup per row block,
-// for producers that do not run on this
-// device (the peers under tensor parallelism). The second streams faster; with it, progress
-// rests on every rank dispatching row blocks in the same ascending order, so that the lowest
-// unfinished block is resident, and has been published, everywhere.
+// hangs. The grid is always one workgroup per row block, dispatched in ascending order. Two
+// residency policies: `persistent` (the name of the flag; no workgroup loops), where every
+// workgroup reserves LDS it does not use so that at most three quarters of the workgroups the
+// registers allow are resident on a CU at once, leaving a quarter of the slots (and of the LDS)
+// to a producer launched on another stream of the same device, provided that stream is not
+// queued behind this kernel: HIP maps streams onto a few hardware queues, and two streams that
+// share one run their work in submission order, so a producer submitted after the pass to the
+// same queue cannot start before it ends (the pass then waits out max_spin and reports the
+// timeout); or no reservation, for producers that do not run on this device (the peers under
+// tensor parallelism), where progress rests on every rank dispatching row blocks in the same
+// ascending order, so that the lowest unfinished block is resident, and has been published,
+// everywhere.
 
 #include <atomic>
 
@@ -63,7 +64,7 @@ struct ShardJob {
     int64_t T, nib, n_ext;  // nib: row blocks per tensor
     float eps;
     uint32_t epoch;         // 0: the mailbox is complete before launch, tags are not checked
-    int persistent;         // 1: three-quarter-capacity grid striding over the row blocks
+    int persistent;         // 1: at most 3/4 of the resident workgroups at once
     int64_t max_spin;
     int* timed_out;
 };
@@ -82,7 +83,8 @@ struct ShardItem {
     bool mine[NG];
 };
 
-// NG: peer groups of 16 the kernel is built for (1 when n_ext <= 16, else 4).
+// NG: peer groups of 16 the kernel is built for (1 when n_ext <= 16, else 4). One workgroup per
+// row block (item).
 template <bool BF, bool GBF, int NV, int NG>
 __global__ __launch_bounds__(kBlock) void shard_fused_kernel(ShardJob job)
 {
@@ -139,15 +141,8 @@ __global__ __launch_bounds__(kBlock) void shard_fused_kernel(ShardJob job)
         }
     };
 
-    ShardItem<NV, NG> cur, nxt;
-    int64_t item = blockIdx.x;
-    issue(item, cur);
-    for (;;) {
-        // the next item's loads are in flight while this one is finished
-        const int64_t next = item + gridDim.x;
-        const bool has_next = next < items;
-        if (has_next) issue(next, nxt);
-
+    // finish one item whose loads were issued into `cur`
+    auto process = [&](int64_t item, ShardItem<NV, NG>& cur) {
         const int tsel = item >= job.nib ? 1 : 0;
         const ShardTensor& s = job.t[tsel];
         const int64_t row0 = (tsel ? item - job.nib : item) * kShardItemRows + wave * RR;
@@ -231,9 +226,12 @@ __global__ __launch_bounds__(kBlock) void shard_fused_kernel(ShardJob job)
                 }
             }
         }
-        if (!has_next) break;
-        cur = nxt;
-        item = next;
+    };
+
+    ShardItem<NV, NG> a;
+    for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
+        issue(item, a);
+        process(item, a);
     }
 }
 
@@ -280,15 +278,42 @@ int device_cus()
     return cus;
 }
 
+// LDS per streaming multiprocessor (CU) of the current device, cached per device id
+int device_lds_per_cu()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 65536;
+    if (dev < 64) {
+        const int v = cache[dev].load(std::memory_order_relaxed);
+        if (v > 0) return v;
+    }
+    int lds = 0;
+    if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+            hipSuccess ||
+        lds <= 0)
+        lds = 65536;
+    if (dev < 64) cache[dev].store(lds, std::memory_order_relaxed);
+    return lds;
+}
+
 template <bool BF, bool GBF, int NV>
 hipError_t launch_shard_nv(const ShardJob& job, hipStream_t st)
 {
     auto kernel = job.n_ext <= kPeersPerGroup ? shard_fused_kernel<BF, GBF, NV, 1>
                                               : shard_fused_kernel<BF, GBF, NV, kMaxPeerGroups>;
     const int64_t items = job.nib * job.nseg;
-    int64_t grid = items;
+    if (items > 0x7fffffff) return hipErrorInvalidConfiguration;
+    size_t lds = 0;
     if (job.epoch != 0 && job.persistent) {
+        // Room for a producer on the same device: each workgroup reserves LDS it does not use,
+        // sized so that at most three quarters of the workgroups the registers allow are
+        // resident on a CU at once. The rest of the grid waits in the dispatcher, which hands
+        // out row blocks in ascending order as workgroups finish (a grid that strides over the
+        // blocks instead gives every workgroup a fixed share, and the slowest share sets the
+        // time).
         static std::atomic<int> occupancy[2] = {{0}, {0}};
+        static std::atomic<int> attr_set[2] = {{0}, {0}};
         const int which = job.n_ext <= kPeersPerGroup ? 0 : 1;
         int occ = occupancy[which].load(std::memory_order_relaxed);
         if (occ <= 0) {
@@ -298,14 +323,19 @@ hipError_t launch_shard_nv(const ShardJob& job, hipStream_t st)
                 occ = 1;
             occupancy[which].store(occ, std::memory_order_relaxed);
         }
-        // at most three quarters of the resident capacity, as a whole number of workgroups per
-        // CU so that every CU streams the same share
-        const int cus = device_cus();
-        const int64_t cap = (int64_t)cus * ((occ * 3) / 4 > 0 ? (occ * 3) / 4 : 1);
-        grid = items < cap ? items : (cap > 0 ? cap : 1);
+        const int cap = (occ * 3) / 4 > 0 ? (occ * 3) / 4 : 1;
+        const int lds_cu = device_lds_per_cu();
+        // cap workgroups fit in lds_cu, cap + 1 do not (1 KB steps)
+        lds = (size_t)((lds_cu / (cap + 1) + 1024) / 1024 * 1024);
+        if ((int64_t)lds * cap > lds_cu) lds = (size_t)(lds_cu / cap) / 1024 * 1024;
+        if (lds > 65536 && !attr_set[which].load(std::memory_order_relaxed)) {
+            const hipError_t e = hipFuncSetAttribute(
+                (const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+            attr_set[which].store(1, std::memory_order_relaxed);
+        }
     }
-    if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kBlock), 0, st, job);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)items), dim3(kBlock), lds, st, job);
     return hipGetLastError();
 }
 

@@ -69,7 +69,7 @@ def check_all(got, ref, what, epoch):
 @pytest.mark.parametrize("persistent", [True, False])
 def test_shard_fused_prepublished_tp8(Q, persistent):
     """TP-8 shard at T = 131072: peers' partials published (same stream) before the pass, with
-    the persistent grid and with one workgroup per row block."""
+    and without the residency cap that leaves room for a same-device producer."""
     c = inputs.make_case("tp8-shard", 131072)
     q, k, gq, gk = (to_dev(c[n]) for n in ("q", "k", "gamma_q", "gamma_k"))
     part_q, part_k = to_dev(c["ext_q"]), to_dev(c["ext_k"])
