@@ -325,7 +325,8 @@ hipError_t launch_shard_nv(const ShardJob& job, hipStream_t st)
         }
         const int cap = (occ * 3) / 4 > 0 ? (occ * 3) / 4 : 1;
         const int lds_cu = device_lds_per_cu();
-        // cap workgroups fit in lds_cu, cap + 1 do not (1 KB steps)
+        // cap workgroups fit in lds_cu, cap + 1 do not (1 KB steps; the hardware allocates LDS
+        // in 1280-byte granules on gfx950, which keeps cap * allocation <= lds_cu for cap <= 7)
         lds = (size_t)((lds_cu / (cap + 1) + 1024) / 1024 * 1024);
         if ((int64_t)lds * cap > lds_cu) lds = (size_t)(lds_cu / cap) / 1024 * 1024;
         if (lds > 65536 && !attr_set[which].load(std::memory_order_relaxed)) {
