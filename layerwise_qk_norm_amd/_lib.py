@@ -287,7 +287,8 @@ def qknorm_shard_fused(q, gamma_q, mail_q, dq_full: int, k=None, gamma_k=None, m
     """One-pass shard stage. mail_* [n_ext, T] int64 mailbox words filled by the peers
     (qknorm_shard_publish); psq_* [T] int64 words receive this rank's own partials (not
     written when publish is False). epoch == 0: the mailbox is complete, no waiting.
-    persistent=False launches one workgroup per row block (producers on other devices only).
+    persistent=True leaves a quarter of each CU to a producer on the same device;
+    persistent=False reserves nothing (producers on other devices only).
     Returns (q_out, k_out, psq_q, psq_k)."""
     torch = _torch()
     _check_device(q, k, gamma_q, gamma_k, mail_q, mail_k, timed_out)

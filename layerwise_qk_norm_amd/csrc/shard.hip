@@ -261,39 +261,29 @@ __global__ __launch_bounds__(kBlock) void shard_publish_kernel(PublishJob job)
     }
 }
 
-int device_cus()
+// The device a stream's work runs on (the current device for the null stream), or -1.
+int stream_device(hipStream_t st)
 {
-    static std::atomic<int> cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-    if (dev < 64) {
-        const int v = cache[dev].load(std::memory_order_relaxed);
-        if (v > 0) return v;
-    }
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-        cus = 256;
-    if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
-    return cus;
+    int dev = -1;
+    const hipError_t e = st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+    return e == hipSuccess ? dev : -1;
 }
 
-// LDS per streaming multiprocessor (CU) of the current device, cached per device id
-int device_lds_per_cu()
+// LDS per CU of device dev, cached per device id
+int device_lds_per_cu(int dev)
 {
     static std::atomic<int> cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 65536;
-    if (dev < 64) {
+    if (dev >= 0 && dev < 64) {
         const int v = cache[dev].load(std::memory_order_relaxed);
         if (v > 0) return v;
     }
     int lds = 0;
-    if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+    if (dev < 0 ||
+        hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
             hipSuccess ||
         lds <= 0)
         lds = 65536;
-    if (dev < 64) cache[dev].store(lds, std::memory_order_relaxed);
+    if (dev >= 0 && dev < 64) cache[dev].store(lds, std::memory_order_relaxed);
     return lds;
 }
 
@@ -313,7 +303,7 @@ hipError_t launch_shard_nv(const ShardJob& job, hipStream_t st)
         // blocks instead gives every workgroup a fixed share, and the slowest share sets the
         // time).
         static std::atomic<int> occupancy[2] = {{0}, {0}};
-        static std::atomic<int> attr_set[2] = {{0}, {0}};
+        static std::atomic<int> attr_set[2][64];  // per device: the attribute is per context
         const int which = job.n_ext <= kPeersPerGroup ? 0 : 1;
         int occ = occupancy[which].load(std::memory_order_relaxed);
         if (occ <= 0) {
@@ -324,16 +314,23 @@ hipError_t launch_shard_nv(const ShardJob& job, hipStream_t st)
             occupancy[which].store(occ, std::memory_order_relaxed);
         }
         const int cap = (occ * 3) / 4 > 0 ? (occ * 3) / 4 : 1;
-        const int lds_cu = device_lds_per_cu();
+        const int dev = stream_device(st);
+        const int lds_cu = device_lds_per_cu(dev);
         // cap workgroups fit in lds_cu, cap + 1 do not (1 KB steps; the hardware allocates LDS
         // in 1280-byte granules on gfx950, which keeps cap * allocation <= lds_cu for cap <= 7)
         lds = (size_t)((lds_cu / (cap + 1) + 1024) / 1024 * 1024);
         if ((int64_t)lds * cap > lds_cu) lds = (size_t)(lds_cu / cap) / 1024 * 1024;
-        if (lds > 65536 && !attr_set[which].load(std::memory_order_relaxed)) {
-            const hipError_t e = hipFuncSetAttribute(
-                (const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-            if (e != hipSuccess) return e;
-            attr_set[which].store(1, std::memory_order_relaxed);
+        if (lds > 65536) {
+            // more than 64 KB of dynamic LDS must be allowed explicitly (workgroups with one
+            // resident per CU reserve half the LDS)
+            const bool known = dev >= 0 && dev < 64 &&
+                               attr_set[which][dev].load(std::memory_order_relaxed) != 0;
+            if (!known) {
+                const hipError_t e = hipFuncSetAttribute(
+                    (const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                if (e != hipSuccess) return e;
+                if (dev >= 0 && dev < 64) attr_set[which][dev].store(1, std::memory_order_relaxed);
+            }
         }
     }
     hipLaunchKernelGGL(kernel, dim3((unsigned)items), dim3(kBlock), lds, st, job);

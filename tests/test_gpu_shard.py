@@ -106,6 +106,32 @@ def test_shard_fused_complete_mailbox(Q, dtype, dl):
     check_all(got, reference(c, d_full, 1e-6), f"complete mailbox d={dl}", 0)
 
 
+@pytest.mark.parametrize("persistent", [True, False])
+@pytest.mark.parametrize("dtype,dl,n_ext", [("bf16", 520, 3), ("bf16", 2048, 17), ("f32", 1024, 3),
+                                            ("f32", 8, 17)])
+def test_shard_fused_widths_waiting(Q, dtype, dl, n_ext, persistent):
+    """Slices of 1, 2 and 4 vectors per lane with the mailbox checked (epoch != 0), in both
+    residency policies and with one and four 16-peer lane groups. With 4 vectors per lane one
+    workgroup fits per CU, and the reservation that leaves room for a producer takes half the
+    LDS (more than 64 KB of dynamic LDS, allowed explicitly)."""
+    rng = np.random.default_rng(dl + n_ext)
+    T = 1001
+    c = dict(q=inputs.random_rows(rng, T, dl, dtype), k=inputs.random_rows(rng, T, dl, dtype),
+             gamma_q=inputs.random_gamma(rng, dl, dtype), gamma_k=inputs.random_gamma(rng, dl, dtype),
+             ext_q=rng.chisquare(dl, size=(n_ext, T)).astype(np.float32),
+             ext_k=rng.chisquare(dl, size=(n_ext, T)).astype(np.float32))
+    d_full = dl * (n_ext + 1)
+    mail_q, mail_k = Q.mailbox_words(n_ext, T), Q.mailbox_words(n_ext, T)
+    Q.qknorm_shard_publish(to_dev(c["ext_q"]), mail_q, 6, to_dev(c["ext_k"]), mail_k)
+    to = zeros_i32(1)
+    got = Q.qknorm_shard_fused(to_dev(c["q"]), to_dev(c["gamma_q"]), mail_q, d_full,
+                               to_dev(c["k"]), to_dev(c["gamma_k"]), mail_k, d_full, eps=1e-6,
+                               epoch=6, timed_out=to, persistent=persistent)
+    sync()
+    assert int(to.item()) == 0
+    check_all(got, reference(c, d_full, 1e-6), f"{dtype} d={dl} n_ext={n_ext}", 6)
+
+
 @pytest.mark.parametrize("n_ext", [1, 16, 17, 64])
 def test_shard_fused_peer_counts(Q, n_ext):
     """Peer counts that fill one, several and all four 16-peer lane groups of the gather."""
