@@ -1304,10 +1304,6 @@ hipError_t launch_mvl(const MvJob& j)
     return hipGetLastError();
 }
 
-// x rows per step: T rounded up to a power of two. One 16-column tile per workgroup of 8
-// wavefronts (two workgroups per CU) for outputs up to 4096 wide or up to 4 tokens; otherwise
-// two tiles (one workgroup per CU), each x fragment then feeding two MFMAs. The step count
-// fills the LDS the workgroups per CU leave.
 // x rows per step: T rounded up to a power of two. Two 16-column tiles (64-byte runs of W'
 // rows) per workgroup once that still gives 128 workgroups, else one (32-byte runs); measured
 // at T = 16, N = 8192: two tiles 22.8 us, four (whole 128-byte runs, half the workgroups)
