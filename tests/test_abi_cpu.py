@@ -103,7 +103,7 @@ def test_fused_validation(L):
     assert fused(L, **blk) == HIPERR           # accepted; the launch then finds no device
     # ... while a K block starting one column early runs into Q's last column
     assert fused(L, **dict(blk, k=A + 126, ko=A + 126)) == ALIAS
-    # and blocks of different strides are judged by their hulls
+    # and blocks of different strides are compared by their hulls
     assert fused(L, **dict(blk, ldk=136, ldko=136)) == ALIAS
 
 
