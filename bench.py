@@ -167,7 +167,7 @@ def fused_setup(torch, Q, inputs, workload, T, stream):
             raise Q.QknError("qknorm_fused", status, L)
 
     # the argument tuples hold raw device addresses: the step owns the tensors behind them, so
-    # they stay allocated (and are not returned to the driver by an emptied cache) as long as
+    # they stay allocated (an emptied allocator cache cannot release them) as long as
     # the step can be called
     step.tensors = (sets, gq, gk)
     step.args = args
