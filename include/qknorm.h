@@ -28,9 +28,9 @@
  *     full before it is written. Any other overlap between an output and an input or another
  *     output is QKN_ERR_ALIAS.
  *   - Misaligned pointers and strides are accepted: 16-byte accesses run where every operand
- *     allows them, element accesses otherwise (the norm-then-project calls only require bf16
- *     pointers to be 2-byte aligned). The single-launch shard stage (qknorm_shard_fused) is
- *     the one call that requires 16-byte alignment (QKN_ERR_ALIGN).
+ *     allows them, element accesses otherwise. Elements must sit at their natural alignment
+ *     (2 bytes for bf16, 4 for fp32) where a call checks it (the norm-then-project calls and
+ *     the single-launch shard stage, whose 64-bit mailbox words need 8 bytes: QKN_ERR_ALIGN).
  *   - Projection weights (W, the folded W', the stacked Q/K weights) are row-major [K, N] with
  *     row stride ldw >= N, the layout y = x W reads them in.
  *   - Results are deterministic: fixed reduction orders, no atomic read-modify-write (the shard
@@ -154,8 +154,9 @@ QKN_API int qknorm_apply_with_stats(int64_t T, float eps, int dtype, int gamma_d
  *               Ignored when epoch == 0 (nothing waits). Both policies stream at the same rate.
  *   n_ext     0..64
  *   timed_out device int (required when epoch != 0), set to 1 on a timeout, never cleared
- *   slices    16-byte aligned, ld * sizeof(dtype) and d_local multiples of 16 bytes
- *             (QKN_ERR_ALIGN otherwise), d_local <= 2048 bf16 / 1024 fp32 (QKN_ERR_SHAPE)
+ *   slices    any strides and widths d_local <= 2048 bf16 / 1024 fp32 (QKN_ERR_SHAPE); 16-byte
+ *             accesses where the slices are 16-byte aligned with ld * sizeof(dtype) and d_local
+ *             multiples of 16 bytes, element accesses otherwise
  * Other arguments as for qknorm_apply_with_stats; K optional in the same way.
  */
 QKN_API int qknorm_shard_fused(int64_t T, float eps, int dtype, int gamma_dtype, int64_t n_ext,

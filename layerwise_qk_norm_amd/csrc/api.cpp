@@ -291,8 +291,10 @@ QKN_API int qknorm_shard_fused(int64_t T, float eps, int dtype, int gamma_dtype,
         if (st != QKN_OK) return st;
         if (c.df < c.dl || c.dl > dmax || (n_ext > 0 && c.ldm < T)) return QKN_ERR_SHAPE;
         if (T > 0 && (c.g == nullptr || (n_ext > 0 && c.mail == nullptr))) return QKN_ERR_NULL;
-        if (((uintptr_t)c.x & 15u) || ((uintptr_t)c.y & 15u) || ((uintptr_t)c.g & 15u) ||
-            (c.ldx * es) % 16 || (c.ldy * es) % 16 || c.dl % epv || ((uintptr_t)c.psq & 7u) ||
+        // elements at their natural alignment, mailbox words at 8 bytes; 16-byte accesses run
+        // where every slice allows them, element accesses otherwise
+        if (((uintptr_t)c.x % (uintptr_t)es) || ((uintptr_t)c.y % (uintptr_t)es) ||
+            ((uintptr_t)c.g % (uintptr_t)gs) || ((uintptr_t)c.psq & 7u) ||
             ((uintptr_t)c.mail & 7u))
             return QKN_ERR_ALIGN;
     }

@@ -83,9 +83,75 @@ struct ShardItem {
     bool mine[NG];
 };
 
-// NG: peer groups of 16 the kernel is built for (1 when n_ext <= 16, else 4). One workgroup per
-// row block (item).
-template <bool BF, bool GBF, int NV, int NG>
+// Element accesses for slices the 16-byte vectors cannot serve (a pointer or a row stride off
+// 16 bytes, or a width that is not a whole number of vectors): the EPV elements a lane owns,
+// one at a time, those at or past d read as 0 and not written. The packing is that of the
+// vector path, so the arithmetic is shared.
+template <bool BF>
+__device__ __forceinline__ u32x4 load_elems(const char* row, int64_t col, int64_t d)
+{
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    if constexpr (BF) {
+        const uint16_t* p = (const uint16_t*)row;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (col + e < d)
+                w[e >> 1] |= (uint32_t)__builtin_nontemporal_load(p + col + e) << (16 * (e & 1));
+    } else {
+        const uint32_t* p = (const uint32_t*)row;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (col + e < d) w[e] = __builtin_nontemporal_load(p + col + e);
+    }
+    return u32x4{w[0], w[1], w[2], w[3]};
+}
+
+template <bool BF>
+__device__ __forceinline__ void store_elems(char* row, int64_t col, int64_t d, const u32x4& v)
+{
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    if constexpr (BF) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (col + e < d)
+                __builtin_nontemporal_store((uint16_t)(w[e >> 1] >> (16 * (e & 1))),
+                                            (uint16_t*)row + col + e);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (col + e < d) __builtin_nontemporal_store(w[e], (uint32_t*)row + col + e);
+    }
+}
+
+// gamma for the EPV columns from col, element by element, in Gamma<BF, GBF>'s packing
+template <bool BF, bool GBF>
+__device__ __forceinline__ void load_gamma_elems(const void* g, int64_t col, int64_t d,
+                                                 u32x4* raw)
+{
+    constexpr int EPV = Io<BF>::kEpv;
+    constexpr int GV = Gamma<BF, GBF>::kGv;
+    uint32_t w[4 * GV];
+#pragma unroll
+    for (int i = 0; i < 4 * GV; ++i) w[i] = 0u;
+    if constexpr (GBF) {
+        const uint16_t* p = (const uint16_t*)g;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e)
+            if (col + e < d) w[e >> 1] |= (uint32_t)p[col + e] << (16 * (e & 1));
+    } else {
+        const uint32_t* p = (const uint32_t*)g;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e)
+            if (col + e < d) w[e] = p[col + e];
+    }
+#pragma unroll
+    for (int h = 0; h < GV; ++h) raw[h] = u32x4{w[4 * h], w[4 * h + 1], w[4 * h + 2], w[4 * h + 3]};
+}
+
+// NG: peer groups of 16 the kernel is built for (1 when n_ext <= 16, else 4). VEC: 16-byte
+// accesses (slices aligned to 16 bytes, widths a whole number of vectors), else element
+// accesses. One workgroup per row block (item).
+template <bool BF, bool GBF, int NV, int NG, bool VEC>
 __global__ __launch_bounds__(kBlock) void shard_fused_kernel(ShardJob job)
 {
     constexpr int EPV = Io<BF>::kEpv;
@@ -107,7 +173,8 @@ __global__ __launch_bounds__(kBlock) void shard_fused_kernel(ShardJob job)
         for (int j = 0; j < NV; ++j) {
             const int64_t col = (int64_t)(j * kWave + lane) * EPV;
             if (ts < job.nseg && col < job.t[ts].d) {
-                G::load(job.t[ts].g, col, graw[ts][j]);
+                if constexpr (VEC) G::load(job.t[ts].g, col, graw[ts][j]);
+                else load_gamma_elems<BF, GBF>(job.t[ts].g, col, job.t[ts].d, graw[ts][j]);
             } else {
 #pragma unroll
                 for (int h = 0; h < G::kGv; ++h) graw[ts][j][h] = u32x4{0u, 0u, 0u, 0u};
@@ -135,8 +202,12 @@ __global__ __launch_bounds__(kBlock) void shard_fused_kernel(ShardJob job)
 #pragma unroll
             for (int j = 0; j < NV; ++j) {
                 const int64_t col = (int64_t)(j * kWave + lane) * EPV;
-                it.v[r][j] = (row_ok && col < s.d) ? load_stream(xr + col * ES)
-                                                   : u32x4{0u, 0u, 0u, 0u};
+                if constexpr (VEC)
+                    it.v[r][j] = (row_ok && col < s.d) ? load_stream(xr + col * ES)
+                                                       : u32x4{0u, 0u, 0u, 0u};
+                else
+                    it.v[r][j] = (row_ok && col < s.d) ? load_elems<BF>(xr, col, s.d)
+                                                       : u32x4{0u, 0u, 0u, 0u};
             }
         }
     };
@@ -221,7 +292,8 @@ __global__ __launch_bounds__(kBlock) void shard_fused_kernel(ShardJob job)
 #pragma unroll
                         for (int e = 0; e < EPV; ++e)
                             o[e] = (f[e] * G::at(graw[tsel][j], e)) * rs;
-                        store_stream(yr + col * ES, pack<BF>(o));
+                        if constexpr (VEC) store_stream(yr + col * ES, pack<BF>(o));
+                        else store_elems<BF>(yr, col, s.d, pack<BF>(o));
                     }
                 }
             }
@@ -287,11 +359,12 @@ int device_lds_per_cu(int dev)
     return lds;
 }
 
-template <bool BF, bool GBF, int NV>
+template <bool BF, bool GBF, int NV, bool VEC>
 hipError_t launch_shard_nv(const ShardJob& job, hipStream_t st)
 {
-    auto kernel = job.n_ext <= kPeersPerGroup ? shard_fused_kernel<BF, GBF, NV, 1>
-                                              : shard_fused_kernel<BF, GBF, NV, kMaxPeerGroups>;
+    auto kernel = job.n_ext <= kPeersPerGroup
+                      ? shard_fused_kernel<BF, GBF, NV, 1, VEC>
+                      : shard_fused_kernel<BF, GBF, NV, kMaxPeerGroups, VEC>;
     const int64_t items = job.nib * job.nseg;
     if (items > 0x7fffffff) return hipErrorInvalidConfiguration;
     size_t lds = 0;
@@ -338,12 +411,19 @@ hipError_t launch_shard_nv(const ShardJob& job, hipStream_t st)
 }
 
 template <bool BF, bool GBF>
-hipError_t launch_shard_types(const ShardJob& job, int nv, hipStream_t st)
+hipError_t launch_shard_types(const ShardJob& job, int nv, bool vec, hipStream_t st)
 {
+    if (vec) {
+        switch (nv) {
+        case 1: return launch_shard_nv<BF, GBF, 1, true>(job, st);
+        case 2: return launch_shard_nv<BF, GBF, 2, true>(job, st);
+        default: return launch_shard_nv<BF, GBF, 4, true>(job, st);
+        }
+    }
     switch (nv) {
-    case 1: return launch_shard_nv<BF, GBF, 1>(job, st);
-    case 2: return launch_shard_nv<BF, GBF, 2>(job, st);
-    default: return launch_shard_nv<BF, GBF, 4>(job, st);
+    case 1: return launch_shard_nv<BF, GBF, 1, false>(job, st);
+    case 2: return launch_shard_nv<BF, GBF, 2, false>(job, st);
+    default: return launch_shard_nv<BF, GBF, 4, false>(job, st);
     }
 }
 
@@ -363,19 +443,24 @@ hipError_t launch_shard_fused(const ShardArgs& a, hipStream_t st)
     job.max_spin = a.max_spin;
     job.timed_out = a.timed_out;
     const int epv = a.bf16 ? 8 : 4;
+    const int64_t es = a.bf16 ? 2 : 4;
     int64_t vmax = 0;
+    bool vec = true;
+    auto a16 = [](const void* p) { return ((uintptr_t)p & 15u) == 0; };
     for (int i = 0; i < a.nseg; ++i) {
         const ShardSeg& r = a.seg[i];
         job.t[i] = {r.x, r.y, r.g, r.ldx, r.ldy, r.d, r.inv_dfull, r.psq_out, r.mail, r.ld_mail};
         const int64_t v = (r.d + epv - 1) / epv;
         vmax = v > vmax ? v : vmax;
+        vec = vec && a16(r.x) && a16(r.y) && a16(r.g) && (r.ldx * es) % 16 == 0 &&
+              (r.ldy * es) % 16 == 0 && r.d % epv == 0;
     }
     const int64_t per = (int64_t)kWave;
     const int nv = vmax <= per ? 1 : vmax <= 2 * per ? 2 : 4;
-    if (a.bf16) return a.gamma_bf16 ? launch_shard_types<true, true>(job, nv, st)
-                                    : launch_shard_types<true, false>(job, nv, st);
-    return a.gamma_bf16 ? launch_shard_types<false, true>(job, nv, st)
-                        : launch_shard_types<false, false>(job, nv, st);
+    if (a.bf16) return a.gamma_bf16 ? launch_shard_types<true, true>(job, nv, vec, st)
+                                    : launch_shard_types<true, false>(job, nv, vec, st);
+    return a.gamma_bf16 ? launch_shard_types<false, true>(job, nv, vec, st)
+                        : launch_shard_types<false, false>(job, nv, vec, st);
 }
 
 hipError_t launch_shard_publish(int64_t T, int64_t n_ext, int nseg, const float* const* src,

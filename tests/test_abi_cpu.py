@@ -291,8 +291,9 @@ def test_shard_validation(L):
     assert shard(dl=4096, ldq=4096) == SHAPE       # slice wider than 2048 bf16
     assert shard(df=256) == SHAPE                  # d_full < d_local
     assert shard(ldm=63) == SHAPE                  # mailbox stride < T
-    assert shard(q=A + 2) == ALIGN
-    assert shard(dl=500, ldq=512) == ALIGN         # slice width not a multiple of 8
+    assert shard(q=A + 1) == ALIGN                 # bf16 elements off their 2-byte alignment
+    assert shard(q=A + 2, ldq=515) == HIPERR       # any element-aligned slice is accepted
+    assert shard(dl=500, ldq=512) == HIPERR        # (element accesses; no device here)
     assert shard(mail=D + 0x10004) == ALIGN        # mailbox words not 8-byte aligned
     assert shard(psq=D + 4) == ALIGN
     assert shard(to=None) == NULL                  # waiting needs a timeout flag

@@ -132,6 +132,46 @@ def test_shard_fused_widths_waiting(Q, dtype, dl, n_ext, persistent):
     check_all(got, reference(c, d_full, 1e-6), f"{dtype} d={dl} n_ext={n_ext}", 6)
 
 
+@pytest.mark.parametrize("persistent", [True, False])
+@pytest.mark.parametrize("dtype,dl,off,pad", [("bf16", 500, 1, 3), ("bf16", 1030, 3, 5),
+                                              ("bf16", 512, 1, 1), ("f32", 300, 1, 1),
+                                              ("f32", 1021, 2, 3)])
+def test_shard_fused_any_alignment(Q, dtype, dl, off, pad, persistent):
+    """Slices off a 16-byte boundary (inputs, outputs and gamma one or more elements in), odd
+    row strides and widths that are not a whole number of 16-byte vectors take the element
+    accesses; the outputs' padding stays untouched."""
+    import torch
+
+    rng = np.random.default_rng(dl + 7 * off)
+    T, n_ext = 777, 5
+    qf = inputs.random_rows(rng, T, dl + pad, dtype)
+    kf = inputs.random_rows(rng, T, dl + pad, dtype)
+    gqf = inputs.random_gamma(rng, dl + off, dtype)
+    gkf = inputs.random_gamma(rng, dl + off, dtype)
+    c = dict(q=np.ascontiguousarray(qf[:, off:off + dl]), k=np.ascontiguousarray(kf[:, off:off + dl]),
+             gamma_q=gqf[off:], gamma_k=gkf[off:],
+             ext_q=rng.chisquare(dl, size=(n_ext, T)).astype(np.float32),
+             ext_k=rng.chisquare(dl, size=(n_ext, T)).astype(np.float32))
+    d_full = dl * (n_ext + 1)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    qo_buf = torch.full((T, dl + pad), 7.0, dtype=tdt, device="cuda")
+    ko_buf = torch.full((T, dl + pad), 7.0, dtype=tdt, device="cuda")
+    mail_q, mail_k = Q.mailbox_words(n_ext, T), Q.mailbox_words(n_ext, T)
+    Q.qknorm_shard_publish(to_dev(c["ext_q"]), mail_q, 3, to_dev(c["ext_k"]), mail_k)
+    to = zeros_i32(1)
+    got = Q.qknorm_shard_fused(to_dev(qf)[:, off:off + dl], to_dev(gqf)[off:], mail_q, d_full,
+                               to_dev(kf)[:, off:off + dl], to_dev(gkf)[off:], mail_k, d_full,
+                               eps=1e-6, q_out=qo_buf[:, off:off + dl],
+                               k_out=ko_buf[:, off:off + dl], epoch=3, timed_out=to,
+                               persistent=persistent)
+    sync()
+    assert int(to.item()) == 0
+    check_all(got, reference(c, d_full, 1e-6), f"{dtype} d={dl} off={off}", 3)
+    for buf in (qo_buf, ko_buf):
+        h = buf.float().cpu().numpy()
+        assert np.all(h[:, :off] == 7.0) and np.all(h[:, off + dl:] == 7.0), "padding written"
+
+
 @pytest.mark.parametrize("n_ext", [1, 16, 17, 64])
 def test_shard_fused_peer_counts(Q, n_ext):
     """Peer counts that fill one, several and all four 16-peer lane groups of the gather."""
