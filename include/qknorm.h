@@ -28,9 +28,9 @@
  *     full before it is written. Any other overlap between an output and an input or another
  *     output is QKN_ERR_ALIAS.
  *   - Misaligned pointers and strides are accepted: 16-byte accesses run where every operand
- *     allows them, element accesses otherwise. Elements must sit at their natural alignment
- *     (2 bytes for bf16, 4 for fp32) where a call checks it (the norm-then-project calls and
- *     the single-launch shard stage, whose 64-bit mailbox words need 8 bytes: QKN_ERR_ALIGN).
+ *     allows them, element accesses otherwise. Elements must sit at their natural alignment:
+ *     2 bytes for bf16, 4 for fp32 (statistics included), 8 for the shard stage's 64-bit
+ *     mailbox words; an element off it is QKN_ERR_ALIGN.
  *   - Projection weights (W, the folded W', the stacked Q/K weights) are row-major [K, N] with
  *     row stride ldw >= N, the layout y = x W reads them in.
  *   - Results are deterministic: fixed reduction orders, no atomic read-modify-write (the shard

@@ -90,6 +90,9 @@ int check_rows(int64_t T, const void* x, int64_t ldx, const void* y, int64_t ldy
     return QKN_OK;
 }
 
+// a pointer off the natural alignment of its elements (null is aligned)
+bool misaligned(const void* p, int64_t bytes) { return ((uintptr_t)p % (uintptr_t)bytes) != 0; }
+
 }  // namespace
 
 extern "C" {
@@ -132,6 +135,9 @@ QKN_API int qknorm_fused(int64_t T, float eps, int dtype, int gamma_dtype, const
     if (T == 0) return QKN_OK;
 
     const int64_t es = elem_size(dtype), gs = elem_size(gamma_dtype);
+    if (misaligned(q, es) || misaligned(q_out, es) || misaligned(gamma_q, gs) ||
+        (has_k && (misaligned(k, es) || misaligned(k_out, es) || misaligned(gamma_k, gs))))
+        return QKN_ERR_ALIGN;
     const Range rq = span(q, T, dq, ldq, es), rqo = span(q_out, T, dq, ldq_out, es);
     const Range rgq = span(gamma_q, 1, dq, dq, gs);
     Range rk, rko, rgk;
@@ -180,6 +186,8 @@ QKN_API int qknorm_partial_sumsq(int64_t T, int dtype, const void* q, int64_t ld
     if (T == 0) return QKN_OK;
 
     const int64_t es = elem_size(dtype);
+    if (misaligned(q, es) || misaligned(k, es) || misaligned(psq_q, 4) || misaligned(psq_k, 4))
+        return QKN_ERR_ALIGN;
     const Range rq = span(q, T, dq_local, ldq, es), rk = has_k ? span(k, T, dk_local, ldk, es) : Range();
     const Range rpq = span(psq_q, 1, T, T, 4), rpk = has_k ? span(psq_k, 1, T, T, 4) : Range();
     if (overlap(rpq, rq) || overlap(rpq, rk) || overlap(rpq, rpk) || overlap(rpk, rq) ||
@@ -227,6 +235,11 @@ QKN_API int qknorm_apply_with_stats(int64_t T, float eps, int dtype, int gamma_d
     if (T == 0) return QKN_OK;
 
     const int64_t es = elem_size(dtype), gs = elem_size(gamma_dtype);
+    if (misaligned(q, es) || misaligned(q_out, es) || misaligned(gamma_q, gs) ||
+        misaligned(psq_q, 4) || misaligned(ext_q, 4) ||
+        (has_k && (misaligned(k, es) || misaligned(k_out, es) || misaligned(gamma_k, gs) ||
+                   misaligned(psq_k, 4) || misaligned(ext_k, 4))))
+        return QKN_ERR_ALIGN;
     const Range rq = span(q, T, dq_local, ldq, es), rqo = span(q_out, T, dq_local, ldq_out, es);
     const Range rgq = span(gamma_q, 1, dq_local, dq_local, gs);
     const Range rpq = span(psq_q, 1, T, T, 4);

@@ -91,6 +91,10 @@ def test_fused_validation(L):
     assert fused(L, ldko=10) == SHAPE
     # T == 0 is a no-op whatever the pointers
     assert fused(L, T=0, q=None, qo=None, gq=None, k=None, ko=None, gk=None) == OK
+    assert fused(L, q=A + 1) == ALIGN           # bf16 elements off their 2-byte alignment
+    assert fused(L, ko=C + 1) == ALIGN
+    assert fused(L, gdt=F32, gq=G1 + 2) == ALIGN  # fp32 gamma off 4 bytes
+    assert fused(L, q=A + 2, qo=B + 2) == HIPERR  # element-aligned: accepted
     # partial overlap of q_out with q (shifted by one row) is rejected; so is K's output
     # landing on Q's input, or Q's output on a gamma
     assert fused(L, qo=A + 128) == ALIAS
@@ -117,6 +121,8 @@ def test_partial_and_apply_validation(L):
     assert P(4, BF16, A, 64, 64, A, C, 64, 64, D, None) == ALIAS   # psq on top of q
     assert P(4, BF16, A, 64, 64, B, C, 64, 64, B + 4, None) == ALIAS
     assert P(0, BF16, None, 1, 1, None, None, 0, 0, None, None) == OK
+    assert P(4, BF16, A + 1, 64, 64, B, C, 64, 64, D, None) == ALIGN   # odd bf16 address
+    assert P(4, BF16, A, 64, 64, B + 2, C, 64, 64, D, None) == ALIGN   # partials off 4 bytes
 
     def apply(T=4, eps=1e-6, n_ext=7, q=A, ldq=64, qo=B, ldqo=64, gq=G1, dl=64, df=512, pq=D,
               eq=D + 0x1000, lde=4):
@@ -132,6 +138,8 @@ def test_partial_and_apply_validation(L):
     assert apply(eps=float("inf")) == EPS
     assert apply(qo=D) == ALIAS                # output over the own partials
     assert apply(qo=D + 0x1000 - 64) == ALIAS  # output running into ext
+    assert apply(pq=D + 2) == ALIGN            # fp32 partials off 4 bytes
+    assert apply(eq=D + 0x1000 + 2) == ALIGN
 
 
 @no_gpu
