@@ -116,8 +116,13 @@ def _ptr(t):
 
 
 def _ld(t) -> int:
-    """Row stride of a 2-D tensor whose rows are contiguous."""
-    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+    """Row stride of a 2-D tensor whose rows are contiguous (an empty tensor's strides are
+    arbitrary, so it gets its width)."""
+    if t.dim() != 2:
+        raise ValueError("expected a 2-D tensor with unit column stride")
+    if t.numel() == 0:
+        return max(t.shape[1], 1)
+    if t.shape[1] > 1 and t.stride(1) != 1:
         raise ValueError("expected a 2-D tensor with unit column stride")
     ld = t.stride(0)
     return ld if t.shape[0] > 1 else max(ld, t.shape[1])

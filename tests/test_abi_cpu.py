@@ -359,6 +359,25 @@ def test_python_binding_refuses_undersized_matrices():
             _lib._mat(bad, 4, 8, "y")
 
 
+def test_python_binding_row_strides():
+    """Row strides come from the tensor; an empty tensor (numpy gives it zero strides) gets its
+    width, and a view whose columns are not adjacent is refused."""
+    torch = pytest.importorskip("torch")
+    import numpy as np
+
+    assert _lib._ld(torch.zeros(4, 8)) == 8
+    assert _lib._ld(torch.zeros(4, 16)[:, 3:11]) == 16
+    assert _lib._ld(torch.zeros(1, 8)) == 8
+    empty = torch.from_numpy(np.zeros((0, 1001), np.float32))
+    assert empty.stride() == (0, 0)
+    assert _lib._ld(empty) == 1001
+    assert _lib._ld(torch.zeros(5, 0)) == 1
+    with pytest.raises(ValueError):
+        _lib._ld(torch.zeros(4, 16)[:, ::2])
+    with pytest.raises(ValueError):
+        _lib._ld(torch.zeros(8))
+
+
 def test_python_binding_refuses_mismatched_dtypes():
     """One dtype code travels per group of operands: a companion of another dtype is refused."""
     torch = pytest.importorskip("torch")

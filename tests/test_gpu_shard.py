@@ -108,12 +108,12 @@ def test_shard_fused_complete_mailbox(Q, dtype, dl):
 
 @pytest.mark.parametrize("persistent", [True, False])
 @pytest.mark.parametrize("dtype,dl,n_ext", [("bf16", 520, 3), ("bf16", 2048, 17), ("f32", 1024, 3),
-                                            ("f32", 8, 17)])
+                                            ("f32", 8, 17), ("bf16", 512, 0)])
 def test_shard_fused_widths_waiting(Q, dtype, dl, n_ext, persistent):
     """Slices of 1, 2 and 4 vectors per lane with the mailbox checked (epoch != 0), in both
-    residency policies and with one and four 16-peer lane groups. With 4 vectors per lane one
-    workgroup fits per CU, and the reservation that leaves room for a producer takes half the
-    LDS (more than 64 KB of dynamic LDS, allowed explicitly)."""
+    residency policies and with no peers, one and four 16-peer lane groups. With 4 vectors per
+    lane one workgroup fits per CU, and the reservation that leaves room for a producer takes
+    half the LDS (more than 64 KB of dynamic LDS, allowed explicitly)."""
     rng = np.random.default_rng(dl + n_ext)
     T = 1001
     c = dict(q=inputs.random_rows(rng, T, dl, dtype), k=inputs.random_rows(rng, T, dl, dtype),
