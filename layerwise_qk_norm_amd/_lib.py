@@ -577,7 +577,12 @@ def qknorm_project_unfused(x, gamma_pre, w, nq: int, gamma_q, gamma_k=None,
 
 
 def qkn_device_copy(dst, src, nbytes: int | None = None):
+    """Copy nbytes (default: all of src) from src to dst, both contiguous device tensors that
+    hold at least that many bytes."""
     _check_device(dst, src)
     n = src.numel() * src.element_size() if nbytes is None else nbytes
+    for t, what in ((dst, "dst"), (src, "src")):
+        if not t.is_contiguous() or t.numel() * t.element_size() < n:
+            raise ValueError(f"{what} must be a contiguous tensor of at least {n} bytes")
     _check("qkn_device_copy", lib().qkn_device_copy(_ptr(dst), _ptr(src), n, _stream(src)))
     return dst

@@ -378,6 +378,21 @@ def test_python_binding_row_strides():
         _lib._ld(torch.zeros(8))
 
 
+def test_python_binding_copy_checks_sizes(monkeypatch):
+    """The copy's byte count is checked against both tensors before the library is reached."""
+    torch = pytest.importorskip("torch")
+    monkeypatch.setattr(_lib, "_check_device", lambda *ts: None)
+    reached = []
+    monkeypatch.setattr(_lib, "lib", lambda: reached.append(1))
+    u8 = torch.uint8
+    for dst, src in ((torch.zeros(4, dtype=u8), torch.zeros(8, dtype=u8)),
+                     (torch.zeros(8, dtype=u8), torch.zeros(4, dtype=u8)),
+                     (torch.zeros(16, dtype=u8)[::2], torch.zeros(8, dtype=u8))):
+        with pytest.raises(ValueError):
+            _lib.qkn_device_copy(dst, src, 8)
+    assert not reached
+
+
 def test_python_binding_refuses_mismatched_dtypes():
     """One dtype code travels per group of operands: a companion of another dtype is refused."""
     torch = pytest.importorskip("torch")

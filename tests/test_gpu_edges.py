@@ -250,3 +250,21 @@ def test_fused_column_blocks_in_place(Q):
     got = to_host(yd)
     check_rows(got[:, :nq], oracle.rmsnorm_rows(np.ascontiguousarray(y[:, :nq]), gq, 1e-6), "Q")
     check_rows(got[:, nq:], oracle.rmsnorm_rows(np.ascontiguousarray(y[:, nq:]), gk, 1e-6), "K")
+
+
+@pytest.mark.parametrize("n,doff,soff", [(1, 0, 0), (15, 0, 0), (16, 0, 0), (17, 3, 0),
+                                         (4097, 0, 5), ((1 << 20) + 3, 16, 32),
+                                         ((1 << 28) + 4099, 0, 0), ((1 << 28) + 77, 1, 1)])
+def test_device_copy(Q, n, doff, soff):
+    """The reference copy the benchmark calibrates against: every byte lands, aligned (16-byte
+    vectors plus a byte tail) or not (bytes), including sizes past the grid cap, where the
+    threads stride; the bytes around the destination stay untouched."""
+    import torch
+
+    gen = torch.Generator(device="cuda").manual_seed(n)
+    src = torch.randint(0, 256, (n + soff,), dtype=torch.uint8, device="cuda", generator=gen)
+    dst = torch.full((n + doff + 64,), 0xAB, dtype=torch.uint8, device="cuda")
+    Q.qkn_device_copy(dst[doff:doff + n], src[soff:], n)
+    sync()
+    assert torch.equal(dst[doff:doff + n], src[soff:soff + n])
+    assert bool((dst[:doff] == 0xAB).all()) and bool((dst[doff + n:] == 0xAB).all())
