@@ -399,8 +399,18 @@ hipError_t launch_shard_nv(const ShardJob& job, hipStream_t st)
             const bool known = dev >= 0 && dev < 64 &&
                                attr_set[which][dev].load(std::memory_order_relaxed) != 0;
             if (!known) {
-                const hipError_t e = hipFuncSetAttribute(
-                    (const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                // the attribute applies to the current device: make it the stream's for the call
+                int cur = -1;
+                hipError_t e = hipGetDevice(&cur);
+                if (e != hipSuccess) return e;
+                const bool swap = dev >= 0 && dev != cur;
+                if (swap && (e = hipSetDevice(dev)) != hipSuccess) return e;
+                e = hipFuncSetAttribute((const void*)kernel,
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                if (swap) {
+                    const hipError_t r = hipSetDevice(cur);
+                    if (e == hipSuccess) e = r;
+                }
                 if (e != hipSuccess) return e;
                 if (dev >= 0 && dev < 64) attr_set[which][dev].store(1, std::memory_order_relaxed);
             }
