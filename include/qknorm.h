@@ -21,6 +21,8 @@
  *     array, looked up once per GPU under a lock), so calls are thread-safe.
  *   - dtype codes: QKN_F32 (float) and QKN_BF16 (bfloat16). Outputs have the input's dtype;
  *     arithmetic is fp32 with one rounding at the output (round to nearest even for bf16).
+ *     Row statistics are fp32 sums: a row whose sum of squares exceeds the fp32 range gets
+ *     r = 0 (outputs 0); squares below it are lost, which eps makes immaterial.
  *   - Arguments are validated before any HIP call; a non-zero status is returned without
  *     touching the device. T == 0 is a valid no-op. Launch failures return QKN_ERR_HIP and
  *     the raw hipError_t is kept for qkn_last_hip_error(). No exception crosses the ABI.
