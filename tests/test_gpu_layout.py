@@ -212,3 +212,85 @@ def test_eliminated_any_alignment(Q):
     s = np.concatenate([np.repeat(sq[:, None], nq, 1), np.repeat(sk[:, None], nk, 1)], 1)
     check_projection(to_host(y), ref, s * np.abs(gam)[None, :] * (np.abs(x) @ np.abs(wfw)),
                      "eliminated misaligned")
+
+
+def strided_rows(x_host, ld):
+    """A device tensor viewing x_host's rows at row stride ld (elements) inside one buffer of
+    rows x ld; the columns past x_host's width are left unwritten."""
+    import torch
+
+    T, K = x_host.shape
+    buf = torch.empty((T, ld), dtype=torch.bfloat16, device="cuda")
+    view = buf[:, :K]
+    view.copy_(to_dev(x_host))
+    return buf, view
+
+
+@pytest.mark.parametrize("T,K,N,ldx,ldw", [
+    # 256 x 256 tiles: per-lane DMA offsets up to 255 * (2^23 - 8) * 2 bytes, past 2^31
+    (512, 64, 32768, (1 << 23) - 8, None),
+    # strides from 2^23 elements take the element-load kernel
+    (300, 256, 264, 1 << 23, None),
+    (300, 64, 264, None, 1 << 23),
+    # the matrix-vector form: W' offsets up to 63 * (2^25 - 8) * 2 bytes; from 2^25 elements on,
+    # the element kernel
+    (16, 64, 264, None, (1 << 25) - 8),
+    (16, 64, 264, None, 1 << 25),
+    (16, 64, 264, (1 << 25) - 8, None),
+])
+def test_deferred_huge_row_strides(Q, T, K, N, ldx, ldw):
+    """Row strides near and past the 32-bit offset range of the pipelined and matrix-vector
+    kernels (buffers of up to 8.6 GB): the offsets stay unsigned, and larger strides route to
+    the element kernel."""
+    import torch
+
+    rng = np.random.default_rng(K + N)
+    x = inputs.random_rows(rng, T, K, "bf16")
+    w = inputs.random_rows(rng, K, N, "bf16", scale=0.02)
+    g = inputs.random_gamma(rng, K, "bf16")
+    wf = oracle_folded(w, g)
+    xbuf, xd = strided_rows(x, ldx) if ldx else (None, to_dev(x))
+    wbuf, wd = strided_rows(wf, ldw) if ldw else (None, to_dev(wf))
+    y = Q.normproj_deferred(xd, wd, eps=1e-6)
+    sync()
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 254, 255, T - 2, T - 1],
+                                     np.random.default_rng(1).choice(T, 24)]) % T)
+    xs = np.ascontiguousarray(x[rows])
+    check_projection(to_host(y)[rows], oracle.normproj(xs, wf, 1e-6), bound(xs, wf, 1e-6),
+                     f"strides T={T} K={K} N={N} ldx={ldx} ldw={ldw}")
+    del xbuf, wbuf, xd, wd, y
+    torch.cuda.empty_cache()
+
+
+def test_row_kernels_huge_row_strides(Q):
+    """Row strides of 2^26 + 8 elements (5.4 GB buffers): row offsets past 2^32 bytes in the
+    fused, partial-sum and single-launch shard kernels."""
+    import torch
+
+    rng = np.random.default_rng(5)
+    T, d, ld = 40, 4096, (1 << 26) + 8
+    q = inputs.random_rows(rng, T, d, "bf16")
+    g = inputs.random_gamma(rng, d, "bf16")
+    qbuf, qd = strided_rows(q, ld)
+    obuf, od = strided_rows(np.zeros((T, d), np.uint16), ld)
+    Q.qknorm_fused(qd, to_dev(g), q_out=od)
+    psq, _ = Q.qknorm_partial_sumsq(qd)
+    sync()
+    check_rows(to_host(od), oracle.rmsnorm_rows(q, g, 1e-6), "fused, huge stride")
+    ref_psq = oracle.partial_sumsq(q)
+    assert np.all(np.abs(to_host(psq) - ref_psq) <= 1e-5 * ref_psq)
+    # the shard stage takes slices of up to 2048 bf16 columns: the first half of each row
+    ds = 2048
+    qs, gs = np.ascontiguousarray(q[:, :ds]), g[:ds]
+    ext = rng.chisquare(ds, size=(3, T)).astype(np.float32)
+    mail = Q.mailbox_words(3, T)
+    Q.qknorm_shard_publish(to_dev(ext), mail, 4)
+    od.zero_()
+    Q.qknorm_shard_fused(qd[:, :ds], to_dev(gs), mail, 4 * ds, eps=1e-6, epoch=4,
+                         q_out=od[:, :ds])
+    sync()
+    check_rows(to_host(od[:, :ds]),
+               oracle.apply_with_stats(qs, gs, oracle.partial_sumsq(qs), ext, 4 * ds, 1e-6),
+               "shard, huge stride")
+    del qbuf, obuf, qd, od
+    torch.cuda.empty_cache()
