@@ -5,10 +5,10 @@ a fixed seed, so every run checks the same configurations and a failure names it
 
 Operations: layerwise QK-Norm in one launch, its scalar-statistics split (partial sums, then
 aggregation and scale) and the single-launch shard stage ("SwiftQK: Fast and
-Communication-Efficient Tensor Parallelism for Query-Key Normalization", abstract), and the
-deferred norm-then-project products, RMSNorm and LayerNorm ("FlashNorm: Fast Normalization for
-Transformers", abstract, items (i) and (ii)). Outputs' padding around the written views must
-stay untouched."""
+Communication-Efficient Tensor Parallelism for Query-Key Normalization", abstract), the
+deferred norm-then-project products, RMSNorm and LayerNorm, and the projection with the
+pre-norm eliminated ("FlashNorm: Fast Normalization for Transformers", abstract). Outputs'
+padding around the written views must stay untouched."""
 
 import numpy as np
 import pytest
@@ -90,7 +90,7 @@ def layout(rng):
 
 
 # ----------------------------------------------------------------------------- fused Q + K
-@pytest.mark.parametrize("case", range(40))
+@pytest.mark.parametrize("case", range(80))
 def test_random_fused(Q, case):
     rng = np.random.default_rng(7000 + case)
     dtype = str(rng.choice(["bf16", "f32"]))
@@ -129,7 +129,7 @@ def test_random_fused(Q, case):
 
 
 # ----------------------------------------------------------------------------- split stage
-@pytest.mark.parametrize("case", range(24))
+@pytest.mark.parametrize("case", range(48))
 def test_random_split(Q, case):
     """Partial sums of a slice, then aggregation with n_ext peers' fp32 partials (a row slice of
     a wider buffer) and the scale over the full width."""
@@ -161,7 +161,7 @@ def test_random_split(Q, case):
 
 
 # ----------------------------------------------------------------------------- shard stage
-@pytest.mark.parametrize("case", range(24))
+@pytest.mark.parametrize("case", range(48))
 def test_random_shard(Q, case):
     """The single-launch shard stage with a published mailbox, the mailbox checked or taken as
     complete, either residency policy, Q alone or Q and K."""
@@ -249,7 +249,7 @@ def sample(T, rng, n=40):
     return np.unique(np.concatenate([[0, T - 1], rng.choice(T, n, replace=False)]))
 
 
-@pytest.mark.parametrize("case", range(30))
+@pytest.mark.parametrize("case", range(48))
 def test_random_deferred(Q, case):
     """The fold, then the deferred RMSNorm product: x, W' and y at random offsets and row
     strides; the matrix-vector, element-load and 128 x 128 kernels are each reached by some
@@ -279,7 +279,7 @@ def test_random_deferred(Q, case):
     padding_intact(ybuf, y_off, N, what + " y")
 
 
-@pytest.mark.parametrize("case", range(20))
+@pytest.mark.parametrize("case", range(32))
 def test_random_deferred_layernorm(Q, case):
     """The LayerNorm fold and the deferred LayerNorm product with beta or without, x with a
     random mean, the statistics from the workspace pass or from inside the product."""
@@ -311,3 +311,55 @@ def test_random_deferred_layernorm(Q, case):
                      oracle.normproj_layernorm(xs, wf_ref, cs_ref, b_ref, 1e-5),
                      ln_bound(xs, wf_ref, 1e-5), what)
     padding_intact(ybuf, y_off, N, what + " y")
+
+
+def elim_bound(x_bits, wf_bits, g_bits, eps_qk, eps_pre, exact):
+    x, wf, g = widen(x_bits), widen(wf_bits), widen(g_bits)
+    p = x @ wf
+    eps = eps_qk * ((x * x).mean(axis=1) + eps_pre) if exact else np.full(len(x), eps_qk)
+    s = 1.0 / np.sqrt((p * p).mean(axis=1) + eps)
+    return s[:, None] * np.abs(g)[None, :] * (np.abs(x) @ np.abs(wf))
+
+
+@pytest.mark.parametrize("case", range(20))
+def test_random_eliminated(Q, case):
+    """The stacked Q/K projection without the pre-norm, then layerwise QK-Norm of its two
+    column blocks ("FlashNorm", abstract, scale invariance), plain or exact, Q alone or with K,
+    at random widths and offsets."""
+    rng = np.random.default_rng(12000 + case)
+    T = int(rng.choice([int(rng.integers(1, 17)), int(rng.integers(17, 600))]))
+    K = width(rng, "bf16", 1500)
+    nq = width(rng, "bf16", 1500)
+    nk = width(rng, "bf16", 700) if rng.random() < 0.8 else 0
+    exact = bool(rng.random() < 0.5)
+    eps_qk, eps_pre = float(rng.choice([1e-6, 1e-5])), float(rng.choice([1e-6, 1e-5]))
+    what = f"case {case}: T={T} K={K} nq={nq} nk={nk} exact={exact}"
+    x = inputs.random_rows(rng, T, K, "bf16")
+    w = inputs.random_rows(rng, K, nq + nk, "bf16", scale=0.02)
+    gp = inputs.random_gamma(rng, K, "bf16")
+    gq = inputs.random_gamma(rng, nq, "bf16")
+    gk = inputs.random_gamma(rng, nk, "bf16") if nk else None
+    wf_ref = oracle.round_bf16(oracle.fold_weight(w, gp))
+    _, wd = place(w, "bf16", *layout(rng))
+    wqk = Q.normproj_fold_weight(wd, place(gp, "bf16", 1, 0)[1])
+    _, xd = place(x, "bf16", *layout(rng))
+    y_off, y_pad = layout(rng)
+    ybuf, yd = place(np.zeros((T, nq + nk), np.uint16), "bf16", y_off, y_pad)
+    Q.qknorm_project_eliminated(xd, wqk, nq, place(gq, "bf16", 2, 0)[1],
+                                place(gk, "bf16", 0, 1)[1] if nk else None, eps_qk=eps_qk,
+                                eps_pre=eps_pre, exact=exact, y=yd)
+    sync()
+    rows = sample(T, rng, n=24)
+    xs = np.ascontiguousarray(x[rows])
+    wq_ref = np.ascontiguousarray(wf_ref[:, :nq])
+    if nk:
+        wk_ref, gk_h = np.ascontiguousarray(wf_ref[:, nq:]), gk
+    else:  # Q only: a one-column K the oracle computes and the check ignores
+        wk_ref, gk_h = np.zeros((K, 1), np.uint16), np.zeros(1, np.uint16) + 0x3F80
+    rq, rk = oracle.qk_eliminated(xs, wq_ref, wk_ref, gq, gk_h, eps_qk, eps_pre, exact=exact)
+    got = to_host(yd)[rows]
+    args = (eps_qk, eps_pre, exact)
+    check_projection(got[:, :nq], rq, elim_bound(xs, wq_ref, gq, *args), what + " Q")
+    if nk:
+        check_projection(got[:, nq:], rk, elim_bound(xs, wk_ref, gk, *args), what + " K")
+    padding_intact(ybuf, y_off, nq + nk, what + " y")
