@@ -11,7 +11,9 @@
  *   Tensor Parallelism for Query-Key Normalization", abstract).
  *
  * Conventions shared by every call:
- *   - Tensors are row-major [T, d] with a row stride ld (in elements, ld >= d).
+ *   - Tensors are row-major [T, d] with a row stride ld (in elements, ld >= d). A tensor
+ *     whose extent ((T - 1) * ld + d elements) exceeds 2^56 bytes is QKN_ERR_SHAPE, so that no
+ *     size arithmetic can wrap.
  *   - Every pointer argument is a DEVICE pointer that the caller allocates and owns; the
  *     library allocates no memory. It keeps no workspace between calls, except the one
  *     device array per GPU that normproj_deferred_layernorm_noalloc uses.

@@ -33,6 +33,22 @@ bool valid_dtype(int dt) { return dt == QKN_F32 || dt == QKN_BF16; }
 int64_t elem_size(int dt) { return dt == QKN_F32 ? 4 : 2; }
 bool valid_eps(float eps) { return std::isfinite(eps) && eps >= 0.0f; }
 
+// Largest byte extent a tensor argument may span: 2^56 bytes, far beyond any device, so that
+// the extents, the overlap checks and the launches' 64-bit index arithmetic cannot wrap.
+constexpr int64_t kMaxExtentBytes = int64_t(1) << 56;
+
+// Whether a [rows, cols] tensor with row stride ld of es-byte elements spans more than
+// kMaxExtentBytes (an empty one never does).
+bool too_large(int64_t rows, int64_t cols, int64_t ld, int64_t es)
+{
+    if (rows <= 0 || cols <= 0) return false;
+    int64_t e = 0;
+    if (__builtin_mul_overflow(rows - 1, ld, &e) || __builtin_add_overflow(e, cols, &e) ||
+        __builtin_mul_overflow(e, es, &e))
+        return true;
+    return e > kMaxExtentBytes;
+}
+
 // Bytes touched by a [rows, cols] tensor with row stride ld: the hull [lo, hi) and, per row,
 // `width` bytes every `pitch` bytes (one row: width == pitch == hi - lo).
 struct Range {
@@ -86,6 +102,7 @@ int check_rows(int64_t T, const void* x, int64_t ldx, const void* y, int64_t ldy
                bool need_y)
 {
     if (d < 1 || ldx < d || (need_y && ldy < d)) return QKN_ERR_SHAPE;
+    if (too_large(T, d, ldx, 4) || (need_y && too_large(T, d, ldy, 4))) return QKN_ERR_SHAPE;
     if (T > 0 && (x == nullptr || (need_y && y == nullptr))) return QKN_ERR_NULL;
     return QKN_OK;
 }
@@ -221,14 +238,15 @@ QKN_API int qknorm_apply_with_stats(int64_t T, float eps, int dtype, int gamma_d
     int st = check_rows(T, q, ldq, q_out, ldq_out, dq_local, true);
     if (st != QKN_OK) return st;
     if (dq_full < dq_local) return QKN_ERR_SHAPE;
-    if (n_ext > 0 && ld_ext_q < T) return QKN_ERR_SHAPE;
+    if (n_ext > 0 && (ld_ext_q < T || too_large(n_ext, T, ld_ext_q, 4))) return QKN_ERR_SHAPE;
     if (T > 0 && (gamma_q == nullptr || psq_q == nullptr || (n_ext > 0 && ext_q == nullptr)))
         return QKN_ERR_NULL;
     if (has_k) {
         st = check_rows(T, k, ldk, k_out, ldk_out, dk_local, true);
         if (st != QKN_OK) return st;
         if (dk_full < dk_local) return QKN_ERR_SHAPE;
-        if (n_ext > 0 && ld_ext_k < T) return QKN_ERR_SHAPE;
+        if (n_ext > 0 && (ld_ext_k < T || too_large(n_ext, T, ld_ext_k, 4)))
+            return QKN_ERR_SHAPE;
         if (T > 0 && (gamma_k == nullptr || psq_k == nullptr || (n_ext > 0 && ext_k == nullptr)))
             return QKN_ERR_NULL;
     }
@@ -302,7 +320,8 @@ QKN_API int qknorm_shard_fused(int64_t T, float eps, int dtype, int gamma_dtype,
         const S& c = segs[i];
         int st = check_rows(T, c.x, c.ldx, c.y, c.ldy, c.dl, true);
         if (st != QKN_OK) return st;
-        if (c.df < c.dl || c.dl > dmax || (n_ext > 0 && c.ldm < T)) return QKN_ERR_SHAPE;
+        if (c.df < c.dl || c.dl > dmax) return QKN_ERR_SHAPE;
+        if (n_ext > 0 && (c.ldm < T || too_large(n_ext, T, c.ldm, 8))) return QKN_ERR_SHAPE;
         if (T > 0 && (c.g == nullptr || (n_ext > 0 && c.mail == nullptr))) return QKN_ERR_NULL;
         // elements at their natural alignment, mailbox words at 8 bytes; 16-byte accesses run
         // where every slice allows them, element accesses otherwise
@@ -373,6 +392,9 @@ QKN_API int qknorm_shard_publish(int64_t T, int64_t n_ext, const float* part_q, 
         return QKN_ERR_NULL;
     if (ld_part_q < T || ld_mail_q < T || (has_k && (ld_part_k < T || ld_mail_k < T)))
         return QKN_ERR_SHAPE;
+    if (too_large(n_ext, T, ld_mail_q, 8) || too_large(n_ext, T, ld_part_q, 4) ||
+        (has_k && (too_large(n_ext, T, ld_mail_k, 8) || too_large(n_ext, T, ld_part_k, 4))))
+        return QKN_ERR_SHAPE;
     if (((uintptr_t)mail_q & 7u) || ((uintptr_t)mail_k & 7u)) return QKN_ERR_ALIGN;
     const Range rq = span(mail_q, n_ext, T, ld_mail_q, 8);
     const Range rk = has_k ? span(mail_k, n_ext, T, ld_mail_k, 8) : Range();
@@ -393,6 +415,7 @@ QKN_API int normproj_fold_weight(int64_t K, int64_t N, int dtype, int gamma_dtyp
                                  int64_t ldw_fold, void* stream)
 {
     if (K < 0 || N < 0 || ldw < N || ldw_fold < N) return QKN_ERR_SHAPE;
+    if (too_large(K, N, ldw, 2) || too_large(K, N, ldw_fold, 2)) return QKN_ERR_SHAPE;
     if (dtype != QKN_BF16 || !valid_dtype(gamma_dtype)) return QKN_ERR_DTYPE;
     if (K == 0 || N == 0) return QKN_OK;
     if (w == nullptr || w_fold == nullptr) return QKN_ERR_NULL;
@@ -411,6 +434,8 @@ int check_normproj(int64_t T, int64_t K, int64_t N, float eps, int dtype, const 
                    int64_t ldx, const void* w, int64_t ldw, const void* y, int64_t ldy)
 {
     if (T < 0 || K < 1 || N < 0 || ldx < K || ldw < N || ldy < N) return QKN_ERR_SHAPE;
+    if (too_large(T, K, ldx, 2) || too_large(K, N, ldw, 2) || too_large(T, N, ldy, 2))
+        return QKN_ERR_SHAPE;
     if (dtype != QKN_BF16) return QKN_ERR_DTYPE;
     if (!valid_eps(eps)) return QKN_ERR_EPS;
     if (T == 0 || N == 0) return QKN_OK;
@@ -447,7 +472,7 @@ int unfused_rms_product(int64_t T, int64_t K, int64_t N, float eps, int dtype, i
     int st = check_normproj(T, K, N, eps, dtype, x, ldx, w, ldw, y, ldy);
     if (st != QKN_OK) return st;
     if (!valid_dtype(gamma_dtype)) return QKN_ERR_DTYPE;
-    if (ldxn < K) return QKN_ERR_SHAPE;
+    if (ldxn < K || too_large(T, K, ldxn, 2)) return QKN_ERR_SHAPE;
     if (T == 0 || N == 0) return QKN_OK;
     if (xn == nullptr || gamma == nullptr) return QKN_ERR_NULL;
     if (((uintptr_t)xn & 1u) != 0) return QKN_ERR_ALIGN;
@@ -493,6 +518,7 @@ QKN_API int normproj_fold_layernorm(int64_t K, int64_t N, int dtype, int gamma_d
                                     float* colsum, float* bias, void* stream)
 {
     if (K < 0 || N < 0 || ldw < N || ldw_fold < N) return QKN_ERR_SHAPE;
+    if (too_large(K, N, ldw, 2) || too_large(K, N, ldw_fold, 2)) return QKN_ERR_SHAPE;
     if (dtype != QKN_BF16 || !valid_dtype(gamma_dtype)) return QKN_ERR_DTYPE;
     if (K == 0 || N == 0) return QKN_OK;
     if (w == nullptr || w_fold == nullptr || colsum == nullptr) return QKN_ERR_NULL;
@@ -637,7 +663,7 @@ QKN_API int normproj_layernorm_unfused(int64_t T, int64_t K, int64_t N, float ep
     int st = check_normproj(T, K, N, eps, dtype, x, ldx, w, ldw, y, ldy);
     if (st != QKN_OK) return st;
     if (!valid_dtype(gamma_dtype)) return QKN_ERR_DTYPE;
-    if (ldxn < K) return QKN_ERR_SHAPE;
+    if (ldxn < K || too_large(T, K, ldxn, 2)) return QKN_ERR_SHAPE;
     if (T == 0 || N == 0) return QKN_OK;
     if (xn == nullptr) return QKN_ERR_NULL;
     const int64_t gs = elem_size(gamma_dtype);
@@ -705,7 +731,7 @@ QKN_API int qknorm_project_eliminated(int64_t T, int64_t K, int64_t nq, int64_t 
                                       const void* gamma_q, const void* gamma_k, void* y,
                                       int64_t ldy, void* stream)
 {
-    if (nq < 1 || nk < 0) return QKN_ERR_SHAPE;
+    if (nq < 1 || nk < 0 || nq > kMaxExtentBytes || nk > kMaxExtentBytes) return QKN_ERR_SHAPE;
     if (!valid_eps(eps_pre)) return QKN_ERR_EPS;
     if (exact != 0 && exact != 1) return QKN_ERR_SHAPE;
     const int64_t N = nq + nk;
@@ -731,7 +757,7 @@ QKN_API int qknorm_project_unfused(int64_t T, int64_t K, int64_t nq, int64_t nk,
                                    const void* gamma_q, const void* gamma_k, void* xn,
                                    int64_t ldxn, void* y, int64_t ldy, void* stream)
 {
-    if (nq < 1 || nk < 0) return QKN_ERR_SHAPE;
+    if (nq < 1 || nk < 0 || nq > kMaxExtentBytes || nk > kMaxExtentBytes) return QKN_ERR_SHAPE;
     if (!valid_eps(eps_qk)) return QKN_ERR_EPS;
     const int64_t N = nq + nk;
     // shapes, pointers and aliasing of the norm and the product are checked by
@@ -757,7 +783,7 @@ QKN_API int qknorm_project_unfused(int64_t T, int64_t K, int64_t nq, int64_t nk,
 
 QKN_API int qkn_device_copy(void* dst, const void* src, int64_t nbytes, void* stream)
 {
-    if (nbytes < 0) return QKN_ERR_SHAPE;
+    if (nbytes < 0 || nbytes > kMaxExtentBytes) return QKN_ERR_SHAPE;
     if (nbytes == 0) return QKN_OK;
     if (dst == nullptr || src == nullptr) return QKN_ERR_NULL;
     if (overlap(span(dst, 1, nbytes, nbytes, 1), span(src, 1, nbytes, nbytes, 1)))

@@ -321,6 +321,38 @@ def test_shard_validation(L):
     assert P(0, 7, None, 0, None, 0, None, 0, None, 0, 1, None) == OK
 
 
+@no_gpu
+def test_oversized_extents_are_rejected(L):
+    """Sizes whose byte extent ((rows - 1) * ld + cols elements) passes 2^56 bytes, products
+    that overflow 64 bits included, are QKN_ERR_SHAPE before any other check can wrap."""
+    big = 1 << 40
+    assert fused(L, T=big, ldq=big) == SHAPE
+    assert fused(L, T=1 << 62, ldq=1 << 62) == SHAPE            # (T - 1) * ld overflows int64
+    assert fused(L, T=big, ldk=big, ldko=big) == SHAPE
+    # the bound itself: bf16 rows are sized as 4-byte elements, 2^54 elements in all
+    edge = (1 << 54) - 64
+    assert fused(L, T=2, ldq=edge, ldqo=64) != SHAPE          # exactly 2^56 bytes: accepted
+    assert fused(L, T=2, ldq=edge + 1, ldqo=64) == SHAPE
+    assert L.qknorm_partial_sumsq(big, BF16, A, big, 64, D, None, 0, 0, None, None) == SHAPE
+    assert L.qknorm_apply_with_stats(4, 1e-6, BF16, BF16, big, A, 64, B, 64, G1, 64, 512, D,
+                                     E, big, None, 0, None, 0, None, 0, 0, None, None, 0,
+                                     None) == SHAPE            # ext [n_ext, ld_ext] too large
+    assert L.qknorm_shard_fused(64, 1e-6, BF16, BF16, 7, A, 512, B, 512, G1, 512, 4096, D,
+                                E, 1 << 62, None, 0, None, 0, None, 0, 0, None, None, 0, 1, 1,
+                                100, G2, None) == SHAPE        # mailbox stride overflows
+    assert L.qknorm_shard_publish(64, big, A, big, B, 64, None, 0, None, 0, 1, None) == SHAPE
+    assert L.normproj_fold_weight(big, 64, BF16, BF16, A, big, G1, B, 64, None) == SHAPE
+    assert L.normproj_fold_layernorm(big, 64, BF16, BF16, A, 64, G1, G2, B, big, D, E,
+                                     None) == SHAPE
+    assert L.normproj_deferred(big, 64, 64, 1e-6, BF16, A, big, B, 64, C, 64, None) == SHAPE
+    assert L.normproj_deferred(4, 64, 64, 1e-6, BF16, A, 64, B, 64, C, 1 << 62, None) == SHAPE
+    assert L.normproj_unfused(4, 64, 64, 1e-6, BF16, BF16, A, 64, G1, B, 64, D, 1 << 62, C, 64,
+                              None) == SHAPE                   # the normalised-x workspace
+    assert L.qknorm_project_eliminated(4, 16, 1 << 62, 1 << 62, 1e-6, 1e-6, 0, BF16, A, 16, B,
+                                       16, G1, G2, C, 16, None) == SHAPE   # nq + nk overflows
+    assert L.qkn_device_copy(A, B, (1 << 56) + 1, None) == SHAPE
+
+
 def test_library_has_gfx950_code_object():
     """The shared object embeds a gfx950 offload bundle (checked on the file's bytes for the
     target id the build embeds)."""
