@@ -214,7 +214,7 @@ def test_deferred_layernorm(Q, T, x_mean, stats):
     check_projection(to_host(y)[rows], ref, ln_bound(xs, wf_ref, c["eps"]),
                      f"deferred LN T={T} mean={x_mean}")
     if T == 2048 and x_mean == 0.0:
-        # the exact reformulation: the unfused LayerNorm-then-project in fp64 agrees too
+        # the rewritten order is exact: the unfused LayerNorm-then-project in fp64 agrees too
         ref_u = oracle.layernorm_proj_unfused(xs[:16], c["gamma"], c["beta"], c["w"], c["eps"])
         check_projection(to_host(y)[rows[:16]], ref_u, ln_bound(xs[:16], wf_ref, c["eps"]),
                          "deferred LN vs unfused definition", abs_coeff=2.0 ** -8)
