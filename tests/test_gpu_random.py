@@ -2,6 +2,7 @@
 beyond the hand-picked cases. Each case draws its own shapes, storage types, row strides,
 pointer offsets (elements past a 16-byte boundary), in-place use, peer counts and epsilon from
 a fixed seed, so every run checks the same configurations and a failure names its case.
+QKN_RANDOM_SEED_BASE (default 0) shifts every seed, to sweep another set of configurations.
 
 Operations: layerwise QK-Norm in one launch, its scalar-statistics split (partial sums, then
 aggregation and scale) and the single-launch shard stage ("SwiftQK: Fast and
@@ -9,6 +10,8 @@ Communication-Efficient Tensor Parallelism for Query-Key Normalization", abstrac
 deferred norm-then-project products, RMSNorm and LayerNorm, and the projection with the
 pre-norm eliminated ("FlashNorm: Fast Normalization for Transformers", abstract). Outputs'
 padding around the written views must stay untouched."""
+
+import os
 
 import numpy as np
 import pytest
@@ -20,6 +23,7 @@ from layerwise_qk_norm_amd import inputs
 pytestmark = pytest.mark.gpu
 
 SENTINEL = 5.0
+SEED_BASE = int(os.environ.get("QKN_RANDOM_SEED_BASE", "0"))
 
 
 @pytest.fixture(scope="module")
@@ -92,7 +96,7 @@ def layout(rng):
 # ----------------------------------------------------------------------------- fused Q + K
 @pytest.mark.parametrize("case", range(80))
 def test_random_fused(Q, case):
-    rng = np.random.default_rng(7000 + case)
+    rng = np.random.default_rng(SEED_BASE + 7000 + case)
     dtype = str(rng.choice(["bf16", "f32"]))
     gdtype = str(rng.choice(["bf16", "f32"]))
     T = int(rng.integers(1, 300))
@@ -101,7 +105,8 @@ def test_random_fused(Q, case):
     dk = width(rng, dtype, 5000) if has_k else 0
     eps = float(rng.choice([1e-6, 1e-5, 0.0]))
     inplace = rng.random() < 0.25
-    what = f"case {case}: {dtype}/{gdtype} T={T} dq={dq} dk={dk} eps={eps} inplace={inplace}"
+    what = (f"case {case} (seed base {SEED_BASE}): {dtype}/{gdtype} T={T} dq={dq} dk={dk} "
+            f"eps={eps} inplace={inplace}")
     q = inputs.random_rows(rng, T, dq, dtype, scale=float(rng.uniform(0.1, 3.0)))
     gq = inputs.random_gamma(rng, dq, gdtype)
     (qo_off, qo_pad), (q_off, q_pad), g_off = layout(rng), layout(rng), int(rng.integers(0, 3))
@@ -133,14 +138,14 @@ def test_random_fused(Q, case):
 def test_random_split(Q, case):
     """Partial sums of a slice, then aggregation with n_ext peers' fp32 partials (a row slice of
     a wider buffer) and the scale over the full width."""
-    rng = np.random.default_rng(8000 + case)
+    rng = np.random.default_rng(SEED_BASE + 8000 + case)
     dtype = str(rng.choice(["bf16", "f32"]))
     gdtype = str(rng.choice(["bf16", "f32"]))
     T = int(rng.integers(1, 400))
     dl = width(rng, dtype, 5000)
     n_ext = int(rng.integers(0, 24))
     eps = float(rng.choice([1e-6, 1e-5]))
-    what = f"case {case}: {dtype}/{gdtype} T={T} d_local={dl} n_ext={n_ext}"
+    what = f"case {case} (seed base {SEED_BASE}): {dtype}/{gdtype} T={T} d_local={dl} n_ext={n_ext}"
     x = inputs.random_rows(rng, T, dl, dtype)
     g = inputs.random_gamma(rng, dl, gdtype)
     ext = rng.chisquare(dl, size=(n_ext, T)).astype(np.float32)
@@ -167,7 +172,7 @@ def test_random_shard(Q, case):
     complete, either residency policy, Q alone or Q and K."""
     import torch
 
-    rng = np.random.default_rng(9000 + case)
+    rng = np.random.default_rng(SEED_BASE + 9000 + case)
     dtype = str(rng.choice(["bf16", "f32"]))
     gdtype = str(rng.choice(["bf16", "f32"]))
     T = int(rng.integers(1, 700))
@@ -176,8 +181,8 @@ def test_random_shard(Q, case):
     epoch = int(rng.choice([0, int(rng.integers(1, 1 << 31))]))
     persistent = bool(rng.random() < 0.5)
     has_k = rng.random() < 0.6
-    what = (f"case {case}: {dtype}/{gdtype} T={T} d_local={dl} n_ext={n_ext} epoch={epoch} "
-            f"persistent={persistent} k={has_k}")
+    what = (f"case {case} (seed base {SEED_BASE}): {dtype}/{gdtype} T={T} d_local={dl} "
+            f"n_ext={n_ext} epoch={epoch} persistent={persistent} k={has_k}")
     x = inputs.random_rows(rng, T, dl, dtype)
     g = inputs.random_gamma(rng, dl, gdtype)
     ext = rng.chisquare(dl, size=(n_ext, T)).astype(np.float32)
@@ -254,9 +259,9 @@ def test_random_deferred(Q, case):
     """The fold, then the deferred RMSNorm product: x, W' and y at random offsets and row
     strides; the matrix-vector, element-load and 128 x 128 kernels are each reached by some
     draw (the 256 x 256 ones need more tiles than these shapes give)."""
-    rng = np.random.default_rng(10000 + case)
+    rng = np.random.default_rng(SEED_BASE + 10000 + case)
     T, K, N = product_shape(rng)
-    what = f"case {case}: T={T} K={K} N={N}"
+    what = f"case {case} (seed base {SEED_BASE}): T={T} K={K} N={N}"
     x = inputs.random_rows(rng, T, K, "bf16")
     w = inputs.random_rows(rng, K, N, "bf16", scale=0.02)
     g = inputs.random_gamma(rng, K, "bf16")
@@ -283,12 +288,13 @@ def test_random_deferred(Q, case):
 def test_random_deferred_layernorm(Q, case):
     """The LayerNorm fold and the deferred LayerNorm product with beta or without, x with a
     random mean, the statistics from the workspace pass or from inside the product."""
-    rng = np.random.default_rng(11000 + case)
+    rng = np.random.default_rng(SEED_BASE + 11000 + case)
     T, K, N = product_shape(rng)
     with_beta = rng.random() < 0.6
     stats = "auto" if rng.random() < 0.5 else None
     mean = float(rng.choice([0.0, 2.0, -3.0]))
-    what = f"case {case}: T={T} K={K} N={N} beta={with_beta} stats={stats} mean={mean}"
+    what = (f"case {case} (seed base {SEED_BASE}): T={T} K={K} N={N} beta={with_beta} "
+            f"stats={stats} mean={mean}")
     x = inputs.f32_to_bf16_bits((widen(inputs.random_rows(rng, T, K, "bf16")) + mean)
                                 .astype(np.float32))
     w = inputs.random_rows(rng, K, N, "bf16", scale=0.02)
@@ -326,14 +332,14 @@ def test_random_eliminated(Q, case):
     """The stacked Q/K projection without the pre-norm, then layerwise QK-Norm of its two
     column blocks ("FlashNorm", abstract, scale invariance), plain or exact, Q alone or with K,
     at random widths and offsets."""
-    rng = np.random.default_rng(12000 + case)
+    rng = np.random.default_rng(SEED_BASE + 12000 + case)
     T = int(rng.choice([int(rng.integers(1, 17)), int(rng.integers(17, 600))]))
     K = width(rng, "bf16", 1500)
     nq = width(rng, "bf16", 1500)
     nk = width(rng, "bf16", 700) if rng.random() < 0.8 else 0
     exact = bool(rng.random() < 0.5)
     eps_qk, eps_pre = float(rng.choice([1e-6, 1e-5])), float(rng.choice([1e-6, 1e-5]))
-    what = f"case {case}: T={T} K={K} nq={nq} nk={nk} exact={exact}"
+    what = f"case {case} (seed base {SEED_BASE}): T={T} K={K} nq={nq} nk={nk} exact={exact}"
     x = inputs.random_rows(rng, T, K, "bf16")
     w = inputs.random_rows(rng, K, nq + nk, "bf16", scale=0.02)
     gp = inputs.random_gamma(rng, K, "bf16")
