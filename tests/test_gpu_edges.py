@@ -62,17 +62,25 @@ def test_odd_and_wide_widths(Q, dtype, dq, dk):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("gdtype", ["bf16", "f32"])
 @pytest.mark.parametrize("vectors", [64, 128, 256, 512, 768, 1024, 2048])
-def test_fused_widths_that_fill_a_shape(Q, dtype, vectors):
-    """Q and K whose width fills a team shape exactly (64 .. 2048 vectors of 16 bytes): the
-    unmasked kernels, with one row per workgroup (every row exists) or several (the last
-    workgroup's extra rows skipped); T = 37 is ragged for every rows-per-workgroup count."""
-    rng = np.random.default_rng(vectors + (1 if dtype == "f32" else 0))
+@pytest.mark.parametrize("T", [1, 37])
+def test_fused_widths_that_fill_a_shape(Q, dtype, gdtype, vectors, T):
+    """Q and K whose width fills a team shape exactly (64 .. 2048 vectors of 16 bytes), gamma
+    stored either way: the unmasked kernels, with one row per workgroup (every row exists) or
+    several (the last workgroup's extra rows skipped); T = 37 is ragged for every
+    rows-per-workgroup count; T = 1, Q alone, leaves the one workgroup's other rows empty
+    where it holds several."""
+    rng = np.random.default_rng(vectors * 16 + (dtype == "f32") + 2 * (gdtype == "f32") + 4 * T)
     d = vectors * (8 if dtype == "bf16" else 4)
-    T = 37
     q = inputs.random_rows(rng, T, d, dtype, scale=1.5)
     k = inputs.random_rows(rng, T, d, dtype, scale=0.5)
-    gq, gk = inputs.random_gamma(rng, d, dtype), inputs.random_gamma(rng, d, dtype)
+    gq, gk = inputs.random_gamma(rng, d, gdtype), inputs.random_gamma(rng, d, gdtype)
+    if T == 1:
+        qo, _ = Q.qknorm_fused(to_dev(q), to_dev(gq), eps=1e-6)
+        sync()
+        check_rows(to_host(qo), oracle.rmsnorm_rows(q, gq, 1e-6), f"Q alone d={d}")
+        return
     qo, ko = Q.qknorm_fused(to_dev(q), to_dev(gq), to_dev(k), to_dev(gk), eps=1e-6)
     sync()
     check_rows(to_host(qo), oracle.rmsnorm_rows(q, gq, 1e-6), f"Q d={d}")
